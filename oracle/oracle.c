@@ -1,0 +1,199 @@
+/*
+ * CPU oracle for one IndexShare layer group.  TEST INFRASTRUCTURE ONLY: only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it; the GPU library neither links nor calls it, and the two share no
+ * code, header, table or constant.
+ *
+ * Sources (the pages describing GLM-5.2's sparse attention):
+ *  - "GLM-5.2 Explained: 1M Token Context AI Agent Model", section 2.1
+ *    (IndexShare: Cross-Layer Index Sharing for DSA Sparse Attention): the
+ *    lightning indexer scores every earlier token against the current query,
+ *    I(t,s) = w * sigma(q_t . h_s), keeps the top-K positions, and attention
+ *    loads keys and values only at those positions; the first layer of a
+ *    group of index_topk_freq layers computes the set and the others reuse it.
+ *    Section 2.2.1: only the first MTP draft step runs the indexer; later
+ *    steps reuse its top-k and append nothing to the cache.
+ *  - "GLM-5.2核心技术解析：IndexShare架构与MTP层优化详解", the config.json
+ *    fragments: index_topk = 2048, index_topk_freq = 4,
+ *    index_share_for_mtp_iteration = true, kv_lora_rank = 512.
+ *  - "GLM-5.2 技术报告解读：IndexShare 稀疏注意力与反奖励作弊强化学习",
+ *    section 1, training-strategy table (indexer only in the first of every
+ *    four sparse layers; the other three reuse its top-k) and the MTP notes.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes):
+ *  - sigma is ReLU and the score sums over indexer heads with one weight per
+ *    (query, head): S = sum_h w_h * ReLU(q_h . k), one shared key per token;
+ *  - a query at position pos sees keys 0..pos, itself included;
+ *  - the set holds the min(k, pos+1) best keys under (score descending,
+ *    position ascending), is listed in ascending position and padded with -1;
+ *  - attention uses the absorbed latent form: the key is the whole latent
+ *    row and the value is its first D_v entries.
+ *
+ * Arithmetic: indexer dot products in exact 64-bit integers; the head sum
+ * and every attention quantity in double.  Built with -ffp-contract=off.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static long visible_len(const int32_t* kv_len, int b, int L_cap) {
+    long len = kv_len[b];
+    if (len < 0) len = 0;
+    if (len > L_cap) len = L_cap;
+    return len;
+}
+
+/* Position of query t of a sequence whose last query sits at len-1
+ * (the Tq queries are the last Tq entries of the cache). */
+static long query_pos(long len, int Tq, int t) { return len - Tq + t; }
+
+void oracle_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
+                           const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
+                           int L_cap, float* S) {
+    for (int b = 0; b < B; ++b) {
+        long len = visible_len(kv_len, b, L_cap);
+        for (int t = 0; t < Tq; ++t) {
+            long pos = query_pos(len, Tq, t);
+            const int8_t* q = qI + ((size_t)b * Tq + t) * H_I * D_I;
+            const float* wt = w + ((size_t)b * Tq + t) * H_I;
+            float* row = S + ((size_t)b * Tq + t) * L_cap;
+            for (long s = 0; s < L_cap; ++s) {
+                if (s > pos) {
+                    row[s] = -INFINITY;
+                    continue;
+                }
+                const int8_t* key = kI + ((size_t)b * L_cap + s) * D_I;
+                double score = 0.0;
+                for (int h = 0; h < H_I; ++h) {
+                    long long dot = 0;
+                    for (int d = 0; d < D_I; ++d)
+                        dot += (long long)q[h * D_I + d] * (long long)key[d];
+                    long long relu = dot > 0 ? dot : 0;
+                    score += (double)wt[h] * (double)relu;
+                }
+                row[s] = (float)score;
+            }
+        }
+    }
+}
+
+typedef struct {
+    float v;
+    int32_t s;
+} scored_pos;
+
+/* Total order of the selection: larger score first; equal scores (with -0.0
+ * equal to +0.0, as float comparison gives) keep the lower position first. */
+static int by_score_desc_pos_asc(const void* pa, const void* pb) {
+    const scored_pos* a = (const scored_pos*)pa;
+    const scored_pos* b = (const scored_pos*)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->s > b->s) - (a->s < b->s);
+}
+
+static int by_int_asc(const void* pa, const void* pb) {
+    int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    return (a > b) - (a < b);
+}
+
+void oracle_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
+                        int k, int32_t* idx) {
+    scored_pos* cand = (scored_pos*)malloc(sizeof(scored_pos) * (size_t)(L_cap > 0 ? L_cap : 1));
+    for (int b = 0; b < B; ++b) {
+        long len = visible_len(kv_len, b, L_cap);
+        for (int t = 0; t < Tq; ++t) {
+            long pos = query_pos(len, Tq, t);
+            long n = pos + 1 > 0 ? pos + 1 : 0;
+            const float* row = S + ((size_t)b * Tq + t) * L_cap;
+            int32_t* out = idx + ((size_t)b * Tq + t) * k;
+            for (long s = 0; s < n; ++s) {
+                cand[s].v = row[s];
+                cand[s].s = (int32_t)s;
+            }
+            qsort(cand, (size_t)n, sizeof(scored_pos), by_score_desc_pos_asc);
+            long m = n < k ? n : k;
+            for (long j = 0; j < m; ++j) out[j] = cand[j].s;
+            qsort(out, (size_t)m, sizeof(int32_t), by_int_asc);
+            for (long j = m; j < k; ++j) out[j] = -1;
+        }
+    }
+    free(cand);
+}
+
+static double bf16_to_double(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+void oracle_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
+                              int B, int Tq, int H, int D, int D_v, int L_cap, int k,
+                              float sm_scale, double* out, double* lse) {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    const double scale = (double)sm_scale;
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < Tq; ++t) {
+            const int32_t* sel = idx + ((size_t)b * Tq + t) * k;
+            for (int h = 0; h < H; ++h) {
+                const uint16_t* q = Q + (((size_t)b * Tq + t) * H + h) * D;
+                double* o = out + (((size_t)b * Tq + t) * H + h) * D_v;
+                double m = -INFINITY;
+                int n_valid = 0;
+                for (int j = 0; j < k; ++j) {
+                    int32_t s = sel[j];
+                    if (s < 0 || s >= L_cap) continue;
+                    const uint16_t* c = C + ((size_t)b * L_cap + s) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += bf16_to_double(q[d]) * bf16_to_double(c[d]);
+                    z[j] = scale * dot;
+                    if (z[j] > m) m = z[j];
+                    ++n_valid;
+                }
+                for (int v = 0; v < D_v; ++v) o[v] = 0.0;
+                if (n_valid == 0) {
+                    if (lse) lse[((size_t)b * Tq + t) * H + h] = -INFINITY;
+                    continue;
+                }
+                double denom = 0.0;
+                for (int j = 0; j < k; ++j) {
+                    int32_t s = sel[j];
+                    if (s < 0 || s >= L_cap) continue;
+                    double e = exp(z[j] - m);
+                    denom += e;
+                    const uint16_t* c = C + ((size_t)b * L_cap + s) * D;
+                    for (int v = 0; v < D_v; ++v) o[v] += e * bf16_to_double(c[v]);
+                }
+                for (int v = 0; v < D_v; ++v) o[v] /= denom;
+                if (lse) lse[((size_t)b * Tq + t) * H + h] = m + log(denom);
+            }
+        }
+    }
+    free(z);
+}
+
+void oracle_group_forward(int B, int Tq, int L_cap, int H_I, int D_I, int k, int H, int D,
+                          int D_v, int n_layers, float sm_scale,
+                          const int8_t* const* qI, const float* const* w,
+                          const int8_t* const* kI, const int32_t* kv_len,
+                          const uint16_t* const* Q, const uint16_t* const* C,
+                          double* const* out, double* const* lse, int32_t* idx,
+                          int reuse_idx, int per_layer_indexer, float* S_scratch) {
+    if (!per_layer_indexer && !reuse_idx) {
+        /* first layer of the group: indexer + top-k, written once */
+        oracle_indexer_scores(qI[0], w[0], kI[0], kv_len, B, Tq, H_I, D_I, L_cap, S_scratch);
+        oracle_topk_select(S_scratch, kv_len, B, Tq, L_cap, k, idx);
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        if (per_layer_indexer) {
+            oracle_indexer_scores(qI[l], w[l], kI[l], kv_len, B, Tq, H_I, D_I, L_cap, S_scratch);
+            oracle_topk_select(S_scratch, kv_len, B, Tq, L_cap, k, idx);
+        }
+        oracle_sparse_mla_attend(Q[l], C[l], idx, B, Tq, H, D, D_v, L_cap, k, sm_scale, out[l],
+                                 lse ? lse[l] : 0);
+    }
+}

@@ -1,0 +1,348 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test ties one oracle function to something independent: exact rational
+brute force, exhaustive subset enumeration, a library routine the definition
+reduces to (torch scaled_dot_product_attention, logsumexp), closed forms, or
+an invariant of the method.  The score, selection and attention definitions
+follow "GLM-5.2 Explained: 1M Token Context AI Agent Model", section 2.1
+(lightning-indexer relevance score, top-K positions, attention over the
+selected positions only), with the readings stated in oracle.c.
+"""
+import itertools
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _positions(kv_len, L_cap, Tq, b, t):
+    ln = min(max(int(kv_len[b]), 0), L_cap)
+    return ln - Tq + t
+
+
+# ---------------------------------------------------------------- scores ----
+
+def _exact_score(q, w, key):
+    """sum_h w_h * ReLU(q_h . key) as an exact rational, rounded once to float32."""
+    total = Fraction(0)
+    for h in range(q.shape[0]):
+        dot = sum(int(a) * int(b) for a, b in zip(q[h], key))
+        total += Fraction(float(w[h])) * max(dot, 0)
+    return np.float32(float(total))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_scores_match_exact_rational_bruteforce(seed):
+    r = _rng(seed)
+    B, Tq, L_cap = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(1, 9))
+    H_I, D_I = int(r.integers(1, 5)), int(r.integers(1, 7))
+    qI = r.integers(-128, 128, size=(B, Tq, H_I, D_I), dtype=np.int8)
+    kI = r.integers(-128, 128, size=(B, L_cap, D_I), dtype=np.int8)
+    # general fp32 weights of either sign, exponents kept close so every
+    # double partial sum is exact and the only rounding is the final one
+    mant = r.integers(-(1 << 23), 1 << 23, size=(B, Tq, H_I))
+    expo = r.integers(-3, 3, size=(B, Tq, H_I))
+    w = (mant * np.exp2(expo - 23.0)).astype(np.float32)
+    kv_len = r.integers(-1, L_cap + 3, size=(B,), dtype=np.int32)
+    S = oracle.indexer_scores(qI, w, kI, kv_len)
+    for b in range(B):
+        for t in range(Tq):
+            pos = _positions(kv_len, L_cap, Tq, b, t)
+            for s in range(L_cap):
+                if s > pos:
+                    assert S[b, t, s] == -np.inf
+                else:
+                    want = _exact_score(qI[b, t], w[b, t], kI[b, s])
+                    assert S[b, t, s].tobytes() == want.tobytes(), (b, t, s)
+
+
+@pytest.mark.parametrize("a,c", [(3, 2), (-3, 2), (7, -8), (-8, -8), (0, 5)])
+def test_scores_closed_form_constant_inputs(a, c):
+    # qI == a, kI == c  =>  S = D_I * max(a*c, 0) * sum_h w_h on visible keys
+    B, Tq, L_cap, H_I, D_I = 2, 3, 11, 5, 16
+    qI = np.full((B, Tq, H_I, D_I), a, dtype=np.int8)
+    kI = np.full((B, L_cap, D_I), c, dtype=np.int8)
+    w = np.array(synth.W_TABLE, dtype=np.float32)[_rng(7).integers(0, 4, size=(B, Tq, H_I))]
+    kv_len = np.array([L_cap, 6], dtype=np.int32)
+    S = oracle.indexer_scores(qI, w, kI, kv_len)
+    for b in range(B):
+        for t in range(Tq):
+            pos = _positions(kv_len, L_cap, Tq, b, t)
+            want = np.float32(D_I * max(a * c, 0) * float(np.sum(w[b, t].astype(np.float64))))
+            for s in range(L_cap):
+                assert S[b, t, s] == (want if s <= pos else -np.inf)
+
+
+def test_scores_hand_worked_example():
+    # Worked by hand from the definition (two heads of dim 2, four keys, the
+    # second query one position later than the first):
+    #  t=0 (sees s<=2): s0: 0.5*3 + 2*2 = 5.5; s1: 0.5*0 + 2*ReLU(-5) = 0;
+    #                   s2: 0.5*ReLU(-1) + 2*6 = 12; s3 hidden.
+    #  t=1 (sees s<=3): s0: 1*2 + 0.25*ReLU(-1) = 2; s1: 1*4 + 0.25*1 = 4.25;
+    #                   s2: 0; s3: 0.
+    qI = np.array([[[[1, 2], [-1, 3]], [[2, 0], [0, -1]]]], dtype=np.int8)
+    w = np.array([[[0.5, 2.0], [1.0, 0.25]]], dtype=np.float32)
+    kI = np.array([[[1, 1], [2, -1], [-3, 1], [0, 2]]], dtype=np.int8)
+    kv_len = np.array([4], dtype=np.int32)
+    S = oracle.indexer_scores(qI, w, kI, kv_len)
+    np.testing.assert_array_equal(S[0, 0], [5.5, 0.0, 12.0, -np.inf])
+    np.testing.assert_array_equal(S[0, 1], [2.0, 4.25, 0.0, 0.0])
+    np.testing.assert_array_equal(oracle.topk_select(S, kv_len, 2)[0], [[0, 2], [0, 1]])
+    # the tie at 0.0 between s2 and s3 goes to the lower position
+    np.testing.assert_array_equal(oracle.topk_select(S, kv_len, 3)[0], [[0, 1, 2], [0, 1, 2]])
+    np.testing.assert_array_equal(oracle.topk_select(S, kv_len, 5)[0],
+                                  [[0, 1, 2, -1, -1], [0, 1, 2, 3, -1]])
+
+
+def test_power_of_two_weights_make_every_fp32_order_exact():
+    # With int8 in [-8,7] (|q.k| <= 2^13 for D_I=128) and w in {1/4,..,2}, every
+    # partial head sum is a multiple of 1/4 below 2^22, so any fp32 summation
+    # order gives the same bits.  This is what lets a GPU kernel that sums heads
+    # in its own order agree with the oracle bit for bit.
+    wl = synth.WORKLOADS["C2"].scaled(B=1, L_cap=64, kv_len=64)
+    inp = synth.indexer_inputs(wl)
+    S = oracle.indexer_scores(inp["qI"], inp["w"], inp["kI"], inp["kv_len"])
+    q = inp["qI"][0, 0].numpy().astype(np.int64)
+    kk = inp["kI"][0].numpy().astype(np.int64)
+    relu = np.maximum(kk @ q.T, 0).astype(np.float32)       # [L, H_I], exact
+    wt = inp["w"][0, 0].numpy()
+    perm = np.random.default_rng(1).permutation(wl.H_I)
+    acc = np.zeros(64, dtype=np.float32)
+    for h in perm:                                           # scrambled fp32 order
+        acc = (acc + wt[h] * relu[:, h]).astype(np.float32)
+    assert acc.tobytes() == S[0, 0].tobytes()
+    assert np.all(np.abs(S[0, 0]) < 2.0 ** 22)
+
+
+# ----------------------------------------------------------------- top-k ----
+
+def _order_key(v, s):
+    # total order of the selection: higher score first, then lower position;
+    # -0.0 and +0.0 are the same score
+    return (-float(v) + 0.0, s)
+
+
+def _bruteforce_topk(row, n, k):
+    m = min(k, n)
+    winners = []
+    for subset in itertools.combinations(range(n), m):
+        rest = [u for u in range(n) if u not in subset]
+        if all(_order_key(row[s], s) < _order_key(row[u], u) for s in subset for u in rest):
+            winners.append(subset)
+    assert len(winners) == 1          # exactly one subset dominates the others
+    return list(winners[0]) + [-1] * (k - m)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_topk_matches_subset_enumeration(seed):
+    r = _rng(100 + seed)
+    B, Tq, L_cap = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(1, 10))
+    k = int(r.integers(1, 12))
+    palette = np.array([-np.inf, -2.5, -0.0, 0.0, 1.0, 1.0, 3.25, 7.0], dtype=np.float32)
+    S = palette[r.integers(0, len(palette), size=(B, Tq, L_cap))]
+    kv_len = r.integers(0, L_cap + 2, size=(B,), dtype=np.int32)
+    idx = oracle.topk_select(S, kv_len, k)
+    for b in range(B):
+        for t in range(Tq):
+            n = max(_positions(kv_len, L_cap, Tq, b, t) + 1, 0)
+            assert idx[b, t].tolist() == _bruteforce_topk(S[b, t], n, k), (b, t)
+
+
+def test_topk_special_cases():
+    r = _rng(5)
+    L_cap, Tq = 300, 4
+    kv_len = np.array([L_cap], dtype=np.int32)
+    S = r.standard_normal((1, Tq, L_cap)).astype(np.float32)
+    # k >= visible count: the whole causal prefix, then -1
+    idx = oracle.topk_select(S, kv_len, 400)
+    for t in range(Tq):
+        pos = L_cap - Tq + t
+        assert idx[0, t, : pos + 1].tolist() == list(range(pos + 1))
+        assert np.all(idx[0, t, pos + 1:] == -1)
+    # all scores equal: the k lowest positions
+    idx = oracle.topk_select(np.full_like(S, 2.0), kv_len, 17)
+    assert np.all(idx[0] == np.arange(17))
+    # distinct scores: the same set as a library top-k
+    k = 37
+    idx = oracle.topk_select(S, kv_len, k)
+    for t in range(Tq):
+        pos = L_cap - Tq + t
+        lib = torch.topk(torch.from_numpy(S[0, t, : pos + 1].copy()), k).indices.numpy()
+        assert idx[0, t].tolist() == sorted(lib.tolist())
+
+
+# ------------------------------------------------------------- attention ----
+
+def _bf16(shape, g):
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _sdpa_reference(Q, C, idx, D_v, scale):
+    """torch SDPA in float64 with a boolean mask that keeps only the selected positions."""
+    B, Tq, H, D = Q.shape
+    L_cap = C.shape[1]
+    out = torch.zeros(B, Tq, H, D_v, dtype=torch.float64)
+    lse = torch.full((B, Tq, H), -math.inf, dtype=torch.float64)
+    for b in range(B):
+        for t in range(Tq):
+            sel = [int(s) for s in idx[b, t] if 0 <= int(s) < L_cap]
+            if not sel:
+                continue
+            mask = torch.zeros(1, L_cap, dtype=torch.bool)
+            mask[0, sel] = True
+            q = Q[b, t].double().unsqueeze(1)                    # [H, 1, D]
+            kmat = C[b].double().unsqueeze(0).expand(H, L_cap, D)
+            v = C[b, :, :D_v].double().unsqueeze(0).expand(H, L_cap, D_v)
+            o = torch.nn.functional.scaled_dot_product_attention(q, kmat, v, attn_mask=mask,
+                                                                 scale=scale)
+            out[b, t] = o[:, 0]
+            logits = (q[:, 0] @ C[b].double().T) * scale       # [H, L_cap]
+            lse[b, t] = torch.logsumexp(logits[:, sel], dim=-1)
+    return out, lse
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attend_matches_masked_sdpa(seed):
+    g = torch.Generator().manual_seed(seed)
+    r = _rng(200 + seed)
+    B, Tq, H = int(r.integers(1, 3)), int(r.integers(1, 3)), int(r.integers(1, 5))
+    D_v = int(r.integers(1, 9))
+    D = D_v + int(r.integers(0, 5))
+    L_cap, k = int(r.integers(1, 40)), int(r.integers(1, 12))
+    Q, C = _bf16((B, Tq, H, D), g), _bf16((B, L_cap, D), g)
+    idx = np.full((B, Tq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            m = int(r.integers(0, min(k, L_cap) + 1))
+            idx[b, t, :m] = r.choice(L_cap, size=m, replace=False)
+            r.shuffle(idx[b, t])
+            if r.random() < 0.3:
+                idx[b, t, r.integers(0, k)] = L_cap + 5       # out of range: skipped
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    out, lse = oracle.sparse_mla_attend(Q, C, idx, D_v, scale)
+    ref_out, ref_lse = _sdpa_reference(Q, C, idx, D_v, scale)
+    np.testing.assert_allclose(out, ref_out.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attend_high_precision_bruteforce():
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 40
+    g = torch.Generator().manual_seed(3)
+    H, D, D_v, L_cap = 2, 5, 3, 7
+    Q, C = _bf16((1, 1, H, D), g), _bf16((1, L_cap, D), g)
+    idx = np.array([[[4, -1, 0, 6, 2]]], dtype=np.int32)
+    scale = 0.37
+    out, lse = oracle.sparse_mla_attend(Q, C, idx, D_v, scale)
+    sel = [4, 0, 6, 2]
+    sc = mpmath.mpf(float(np.float32(scale)))
+    for h in range(H):
+        z = [sc * mpmath.fsum(mpmath.mpf(float(Q[0, 0, h, d])) * mpmath.mpf(float(C[0, s, d]))
+                              for d in range(D)) for s in sel]
+        Z = mpmath.fsum(mpmath.exp(x) for x in z)
+        for v in range(D_v):
+            want = mpmath.fsum(mpmath.exp(x) * mpmath.mpf(float(C[0, s, v]))
+                               for x, s in zip(z, sel)) / Z
+            assert abs(out[0, 0, h, v] - float(want)) < 1e-14
+        assert abs(lse[0, 0, h] - float(mpmath.log(Z))) < 1e-14
+
+
+def test_attend_closed_forms():
+    g = torch.Generator().manual_seed(11)
+    H, D, D_v, L_cap, k = 3, 12, 8, 20, 6
+    C = _bf16((1, L_cap, D), g)
+    Cd = C.double().numpy()
+    idx = np.array([[[3, 17, -1, 8, 0, -1]]], dtype=np.int32)
+    sel = [3, 17, 8, 0]
+    # Q = 0: uniform weights, the mean of the selected value rows; lse = log n
+    out, lse = oracle.sparse_mla_attend(torch.zeros(1, 1, H, D, dtype=torch.bfloat16), C, idx,
+                                        D_v, 0.25)
+    for h in range(H):
+        np.testing.assert_allclose(out[0, 0, h], Cd[0, sel, :D_v].mean(axis=0), rtol=0,
+                                   atol=1e-15)
+        assert abs(lse[0, 0, h] - math.log(len(sel))) < 1e-15
+    Q = _bf16((1, 1, H, D), g)
+    # one valid slot: exactly that row; lse = its logit
+    one = np.array([[[-1, -1, 9, -1, -1, -1]]], dtype=np.int32)
+    out, lse = oracle.sparse_mla_attend(Q, C, one, D_v, 0.25)
+    for h in range(H):
+        np.testing.assert_array_equal(out[0, 0, h], Cd[0, 9, :D_v])
+        want = 0.25 * float(np.dot(Q[0, 0, h].double().numpy(), Cd[0, 9]))
+        assert abs(lse[0, 0, h] - want) < 1e-12
+    # a value column that is constant over the selected rows stays that constant
+    C2 = C.clone()
+    C2[0, :, 2] = 1.5
+    out, _ = oracle.sparse_mla_attend(Q, C2, idx, D_v, 0.25)
+    np.testing.assert_allclose(out[0, 0, :, 2], 1.5, rtol=0, atol=1e-15)
+    # no valid slot: zeros and lse = -inf
+    none = np.full((1, 1, k), -1, dtype=np.int32)
+    out, lse = oracle.sparse_mla_attend(Q, C, none, D_v, 0.25)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+    # the order of the slots does not matter
+    out_a, lse_a = oracle.sparse_mla_attend(Q, C, idx, D_v, 0.25)
+    out_b, lse_b = oracle.sparse_mla_attend(Q, C, idx[:, :, ::-1].copy(), D_v, 0.25)
+    np.testing.assert_allclose(out_a, out_b, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse_a, lse_b, rtol=1e-14, atol=1e-15)
+
+
+def test_dense_causal_when_context_fits_k():
+    # When every query sees at most k keys, the sparse layer is plain causal
+    # attention; checked against torch SDPA(is_causal) on a scaled-down C1.
+    wl = synth.WORKLOADS["C1"].scaled(Tq=48, kv_len=48, L_cap=48, k=64)
+    inp = synth.group_inputs(wl, layers=1)
+    idx, outs, lses = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]], inp["kv_len"],
+                                           inp["Q"], inp["C"], wl.k, wl.D_v, wl.sm_scale)
+    for t in range(wl.Tq):
+        assert idx[0, t].tolist() == list(range(t + 1)) + [-1] * (wl.k - t - 1)
+    Q = inp["Q"][0][0].double().transpose(0, 1)                # [H, Tq, D]
+    C = inp["C"][0][0].double()
+    K = C.unsqueeze(0).expand(wl.H, -1, -1)
+    V = C[:, : wl.D_v].unsqueeze(0).expand(wl.H, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True,
+                                                           scale=float(np.float32(wl.sm_scale)))
+    np.testing.assert_allclose(outs[0][0], ref.transpose(0, 1).numpy(), rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------- group ----
+
+def test_group_shares_one_index_set_and_composes():
+    wl = synth.WORKLOADS["C1"].scaled(Tq=96, kv_len=200, L_cap=224, k=16)
+    inp = synth.group_inputs(wl)
+    idx, outs, lses = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]], inp["kv_len"],
+                                           inp["Q"], inp["C"], wl.k, wl.D_v, wl.sm_scale)
+    S = oracle.indexer_scores(inp["qI"], inp["w"], inp["kI"], inp["kv_len"])
+    idx_one = oracle.topk_select(S, inp["kv_len"], wl.k)
+    np.testing.assert_array_equal(idx, idx_one)
+    for l in range(wl.n_layers):
+        o, s = oracle.sparse_mla_attend(inp["Q"][l], inp["C"][l], idx_one, wl.D_v, wl.sm_scale)
+        np.testing.assert_array_equal(outs[l], o)
+        np.testing.assert_array_equal(lses[l], s)
+    # later MTP steps: the given set is used as is, by every layer
+    rng = random.Random(0)
+    given = idx.copy()
+    for row in given.reshape(-1, wl.k):
+        rng.shuffle(row)
+    idx2, outs2, _ = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]], inp["kv_len"],
+                                          inp["Q"], inp["C"], wl.k, wl.D_v, wl.sm_scale,
+                                          idx=given, reuse_idx=True)
+    np.testing.assert_array_equal(idx2, given)
+    for l in range(wl.n_layers):
+        np.testing.assert_allclose(outs2[l], outs[l], rtol=1e-13, atol=1e-15)
+    # per-layer indexers fed identical inputs reproduce the shared group
+    n = wl.n_layers
+    idx3, outs3, _ = oracle.group_forward([inp["qI"]] * n, [inp["w"]] * n, [inp["kI"]] * n,
+                                          inp["kv_len"], inp["Q"], inp["C"], wl.k, wl.D_v,
+                                          wl.sm_scale, per_layer_indexer=True)
+    np.testing.assert_array_equal(idx3, idx)
+    for l in range(n):
+        np.testing.assert_array_equal(outs3[l], outs[l])
