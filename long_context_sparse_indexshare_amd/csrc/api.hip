@@ -1,0 +1,263 @@
+// C ABI of libisa: host-side argument checks, workspace carving, and the
+// IndexShare group driver.  The group rule follows "GLM-5.2 技术报告解读"
+// section 1 (training-strategy table: the indexer runs in the first of every
+// four sparse layers and the other three reuse its top-k) and "GLM-5.2
+// Explained: 1M Token Context AI Agent Model" section 2.1 (compute the index
+// set, or reuse the previous one) and 2.2.1 (later MTP draft steps reuse the
+// first step's set).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/isa.h"
+#include "isa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+isa_status fail(isa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+isa_status fail(isa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+isa_status ok() {
+    g_last_error.clear();
+    return ISA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define ISA_CHECK(cond, st, ...) \
+    do {                         \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+isa_status check_hip(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+isa_status check_indexer(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
+                         int B, int Tq, int H_I, int D_I, int L_cap, const float* S) {
+    ISA_CHECK(qI && w && kI && kv_len && S, ISA_ERR_INVALID_ARG, "indexer: NULL tensor pointer");
+    ISA_CHECK(B > 0 && Tq > 0 && H_I > 0 && D_I > 0 && L_cap > 0, ISA_ERR_INVALID_ARG,
+              "indexer: sizes must be positive (B=%d Tq=%d H_I=%d D_I=%d L_cap=%d)", B, Tq, H_I,
+              D_I, L_cap);
+    ISA_CHECK(L_cap <= ISA_MAX_LCAP, ISA_ERR_INVALID_ARG, "indexer: L_cap=%d exceeds %d", L_cap,
+              ISA_MAX_LCAP);
+    ISA_CHECK(isa::indexer_shape_supported(H_I, D_I), ISA_ERR_UNSUPPORTED,
+              "indexer: (H_I=%d, D_I=%d) not compiled; H_I in {4,8,16,32,64}, D_I in {32,64,128}",
+              H_I, D_I);
+    ISA_CHECK(aligned(qI, 16) && aligned(kI, 16) && aligned(w, 4) && aligned(S, 4) &&
+                  aligned(kv_len, 4),
+              ISA_ERR_INVALID_ARG, "indexer: qI and kI need 16-byte alignment");
+    return ISA_OK;
+}
+
+isa_status check_topk(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap, int k,
+                      const int32_t* idx) {
+    ISA_CHECK(S && kv_len && idx, ISA_ERR_INVALID_ARG, "topk: NULL tensor pointer");
+    ISA_CHECK(B > 0 && Tq > 0 && L_cap > 0, ISA_ERR_INVALID_ARG,
+              "topk: sizes must be positive (B=%d Tq=%d L_cap=%d)", B, Tq, L_cap);
+    ISA_CHECK(k >= 1 && k <= ISA_MAX_TOPK, ISA_ERR_INVALID_ARG, "topk: k=%d outside [1, %d]", k,
+              ISA_MAX_TOPK);
+    ISA_CHECK(L_cap <= ISA_MAX_LCAP, ISA_ERR_INVALID_ARG, "topk: L_cap=%d exceeds %d", L_cap,
+              ISA_MAX_LCAP);
+    ISA_CHECK((long long)B * Tq <= 65535, ISA_ERR_UNSUPPORTED, "topk: B*Tq=%lld exceeds 65535",
+              (long long)B * Tq);
+    ISA_CHECK(aligned(S, 4) && aligned(idx, 4) && aligned(kv_len, 4), ISA_ERR_INVALID_ARG,
+              "topk: misaligned pointer");
+    return ISA_OK;
+}
+
+isa_status check_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B, int Tq,
+                        int H, int D, int D_v, int L_cap, int k, float sm_scale,
+                        const uint16_t* out) {
+    ISA_CHECK(Q && C && idx && out, ISA_ERR_INVALID_ARG, "attend: NULL tensor pointer");
+    ISA_CHECK(B > 0 && Tq > 0 && H > 0 && D > 0 && D_v > 0 && L_cap > 0, ISA_ERR_INVALID_ARG,
+              "attend: sizes must be positive (B=%d Tq=%d H=%d D=%d D_v=%d L_cap=%d)", B, Tq, H, D,
+              D_v, L_cap);
+    ISA_CHECK(k >= 1 && k <= ISA_MAX_TOPK, ISA_ERR_INVALID_ARG, "attend: k=%d outside [1, %d]", k,
+              ISA_MAX_TOPK);
+    ISA_CHECK(L_cap <= ISA_MAX_LCAP, ISA_ERR_INVALID_ARG, "attend: L_cap=%d exceeds %d", L_cap,
+              ISA_MAX_LCAP);
+    ISA_CHECK(std::isfinite(sm_scale), ISA_ERR_INVALID_ARG, "attend: sm_scale is not finite");
+    ISA_CHECK(isa::attend_shape_supported(H, D, D_v), ISA_ERR_UNSUPPORTED,
+              "attend: (H=%d, D=%d, D_v=%d) not compiled; (576,512) with H<=64 or (160,128) with "
+              "H<=32",
+              H, D, D_v);
+    ISA_CHECK((long long)B * Tq <= 65535, ISA_ERR_UNSUPPORTED, "attend: B*Tq=%lld exceeds 65535",
+              (long long)B * Tq);
+    ISA_CHECK(aligned(Q, 16) && aligned(C, 16) && aligned(out, 16) && aligned(idx, 4),
+              ISA_ERR_INVALID_ARG, "attend: Q, C and out need 16-byte alignment");
+    return ISA_OK;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Group workspace: [top-k state (zero-kept) | scores S | attention partials]
+struct GroupLayout {
+    size_t topk, scores, attend, total;
+};
+
+GroupLayout group_layout(const isa_group_args* a) {
+    GroupLayout L;
+    const bool need_index = !a->reuse_idx || a->per_layer_indexer;
+    const size_t rows = (size_t)a->B * a->Tq;
+    L.topk = 0;
+    size_t off = need_index ? round_up(isa::topk_layout((int)rows, a->L_cap).total) : 0;
+    L.scores = off;
+    off += need_index ? round_up(rows * (size_t)a->L_cap * sizeof(float)) : 0;
+    L.attend = off;
+    off += round_up(isa::attend_plan(a->B, a->Tq, a->H, a->D_v, a->k).partial_bytes);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int isa_abi_version(void) { return ISA_ABI_VERSION; }
+
+const char* isa_last_error(void) { return g_last_error.c_str(); }
+
+isa_status isa_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
+                              const int32_t* kv_len, int B, int Tq, int H_I, int D_I, int L_cap,
+                              float* S, void* stream) {
+    isa_status st = check_indexer(qI, w, kI, kv_len, B, Tq, H_I, D_I, L_cap, S);
+    if (st != ISA_OK) return st;
+    return check_hip(isa::launch_indexer_scores(qI, w, kI, kv_len, B, Tq, H_I, D_I, L_cap, S,
+                                                static_cast<hipStream_t>(stream)),
+                     "indexer launch");
+}
+
+size_t isa_topk_workspace_bytes(int B, int Tq, int L_cap, int k) {
+    (void)k;
+    if (B <= 0 || Tq <= 0 || L_cap <= 0) return 0;
+    return isa::topk_layout(B * Tq, L_cap).total;
+}
+
+isa_status isa_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap, int k,
+                           int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    isa_status st = check_topk(S, kv_len, B, Tq, L_cap, k, idx);
+    if (st != ISA_OK) return st;
+    const size_t need = isa_topk_workspace_bytes(B, Tq, L_cap, k);
+    ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
+              "topk: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+    return check_hip(isa::launch_topk_select(S, kv_len, B, Tq, L_cap, k, idx, ws,
+                                             static_cast<hipStream_t>(stream)),
+                     "topk launch");
+}
+
+size_t isa_attend_workspace_bytes(int B, int Tq, int H, int D, int D_v, int k) {
+    (void)D;
+    if (B <= 0 || Tq <= 0 || H <= 0 || D_v <= 0 || k <= 0) return 0;
+    return isa::attend_plan(B, Tq, H, D_v, k).partial_bytes;
+}
+
+isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B,
+                                 int Tq, int H, int D, int D_v, int L_cap, int k, float sm_scale,
+                                 uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    isa_status st = check_attend(Q, C, idx, B, Tq, H, D, D_v, L_cap, k, sm_scale, out);
+    if (st != ISA_OK) return st;
+    ISA_CHECK(!lse || aligned(lse, 4), ISA_ERR_INVALID_ARG, "attend: misaligned lse");
+    const size_t need = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k);
+    if (need) {
+        ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
+                  "attend: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+    }
+    return check_hip(isa::launch_sparse_mla_attend(Q, C, idx, B, Tq, H, D, D_v, L_cap, k, sm_scale,
+                                                   out, lse, ws, static_cast<hipStream_t>(stream)),
+                     "attend launch");
+}
+
+size_t isa_group_workspace_bytes(const isa_group_args* a) {
+    if (!a || a->B <= 0 || a->Tq <= 0 || a->L_cap <= 0 || a->H <= 0 || a->D_v <= 0 || a->k <= 0)
+        return 0;
+    return group_layout(a).total;
+}
+
+isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
+    ISA_CHECK(a, ISA_ERR_INVALID_ARG, "group: NULL args");
+    ISA_CHECK(a->n_layers >= 1 && a->n_layers <= 64, ISA_ERR_INVALID_ARG,
+              "group: n_layers=%d outside [1, 64]", a->n_layers);
+    ISA_CHECK(a->Q && a->C && a->out && a->idx && a->kv_len, ISA_ERR_INVALID_ARG,
+              "group: NULL pointer array or tensor");
+    const bool per_layer = a->per_layer_indexer != 0;
+    const bool need_index = !a->reuse_idx || per_layer;
+    const int n_ix = per_layer ? a->n_layers : (need_index ? 1 : 0);
+    if (n_ix) {
+        ISA_CHECK(a->qI && a->w && a->kI, ISA_ERR_INVALID_ARG, "group: NULL indexer arrays");
+    }
+    // the score buffer lives in the workspace: stand in an aligned non-NULL
+    // address for it while checking the caller's tensors
+    const float* ws_scores = reinterpret_cast<const float*>(256);
+    for (int l = 0; l < n_ix; ++l) {
+        isa_status st = check_indexer(a->qI[l], a->w[l], a->kI[l], a->kv_len, a->B, a->Tq, a->H_I,
+                                      a->D_I, a->L_cap, ws_scores);
+        if (st != ISA_OK) return st;
+    }
+    if (need_index) {
+        isa_status st = check_topk(ws_scores, a->kv_len, a->B, a->Tq,
+                                   a->L_cap, a->k, a->idx);
+        if (st != ISA_OK) return st;
+    }
+    for (int l = 0; l < a->n_layers; ++l) {
+        isa_status st = check_attend(a->Q[l], a->C[l], a->idx, a->B, a->Tq, a->H, a->D, a->D_v,
+                                     a->L_cap, a->k, a->sm_scale, a->out[l]);
+        if (st != ISA_OK) return st;
+        if (a->lse && a->lse[l]) {
+            ISA_CHECK(aligned(a->lse[l], 4), ISA_ERR_INVALID_ARG, "group: misaligned lse[%d]", l);
+        }
+    }
+    const GroupLayout L = group_layout(a);
+    ISA_CHECK(a->ws && a->ws_bytes >= L.total && aligned(a->ws, 256), ISA_ERR_WORKSPACE,
+              "group: workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, a->ws_bytes);
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    char* ws = static_cast<char*>(a->ws);
+    float* S = reinterpret_cast<float*>(ws + L.scores);
+    void* topk_ws = ws + L.topk;
+    void* attend_ws = ws + L.attend;
+    auto index = [&](int l) -> isa_status {
+        isa_status st = check_hip(isa::launch_indexer_scores(a->qI[l], a->w[l], a->kI[l], a->kv_len,
+                                                             a->B, a->Tq, a->H_I, a->D_I, a->L_cap,
+                                                             S, stream),
+                                  "group: indexer launch");
+        if (st != ISA_OK) return st;
+        return check_hip(isa::launch_topk_select(S, a->kv_len, a->B, a->Tq, a->L_cap, a->k, a->idx,
+                                                 topk_ws, stream),
+                         "group: topk launch");
+    };
+    if (need_index && !per_layer) {
+        isa_status st = index(0);
+        if (st != ISA_OK) return st;
+    }
+    for (int l = 0; l < a->n_layers; ++l) {
+        if (per_layer) {
+            isa_status st = index(l);
+            if (st != ISA_OK) return st;
+        }
+        float* lse = a->lse ? a->lse[l] : nullptr;
+        isa_status st = check_hip(isa::launch_sparse_mla_attend(a->Q[l], a->C[l], a->idx, a->B,
+                                                                a->Tq, a->H, a->D, a->D_v,
+                                                                a->L_cap, a->k, a->sm_scale,
+                                                                a->out[l], lse, attend_ws, stream),
+                                  "group: attend launch");
+        if (st != ISA_OK) return st;
+    }
+    return ok();
+}
+
+}  // extern "C"

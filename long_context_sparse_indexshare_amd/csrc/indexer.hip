@@ -1,0 +1,168 @@
+// Lightning-indexer scores on int8 MFMA (gfx950).
+//
+// Definition ("GLM-5.2 Explained: 1M Token Context AI Agent Model", section
+// 2.1, relevance score I(t,s) = w * sigma(q_t . h_s), read with sigma = ReLU,
+// a sum over indexer heads and one weight per query and head):
+//   S[b,t,s] = sum_h w[b,t,h] * ReLU(qI[b,t,h,:] . kI[b,s,:])  for s <= pos(b,t), else -inf.
+//
+// Work split: the GEMM rows are (query, head) pairs, 64 per workgroup
+// (64 / H_I queries of one sequence); the columns are keys.  Each of the
+// 4 waves owns a 32-key block per step, so the 64 query rows stay in
+// registers (A operands) and every key byte is read from HBM exactly once
+// per workgroup with 16-byte loads straight into B operands.  The MFMA is
+// v_mfma_i32_32x32x32_i8 (exact int32 dot products).  The epilogue applies
+// ReLU and the head weight in fp32 and reduces the heads of a query in
+// registers plus one cross-lane swap; blocks past the last visible key of
+// every query in the workgroup skip the loads and write -inf.
+#include "isa_internal.h"
+
+namespace isa {
+namespace {
+
+constexpr int IX_THREADS = 256;
+constexpr int IX_ROWS = 64;              // (query, head) rows per workgroup
+constexpr int IX_KEYS_PER_STEP = 128;    // 4 waves x 32 keys
+constexpr int IX_STEPS = 8;
+constexpr int IX_KEYS_PER_WG = IX_KEYS_PER_STEP * IX_STEPS;
+
+__device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
+
+template <int H_I, int D_I>
+__global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
+    const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
+    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S) {
+    constexpr int QPW = IX_ROWS / H_I;             // queries per workgroup
+    constexpr int KS = D_I / 32;                   // MFMA k-steps over the indexer dim
+    constexpr int NQL = H_I >= 8 ? 64 / H_I : 8;   // query slots held per lane
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane & 31;
+    const int g = lane >> 5;
+    const int b = blockIdx.z;
+    const int t0 = blockIdx.y * QPW;
+    const int len = clamp_len(kv_len[b], L_cap);
+    const int t_last = min(t0 + QPW, Tq) - 1;
+    const int pos_max = len - Tq + t_last;          // last key any query here can see
+
+    // A operands: row m = 32*rb + j is (query m / H_I, head m % H_I); k bytes 32*ks + 16*g .. +16.
+    v4i a[2][KS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int m = 32 * rb + j;
+        const int t = t0 + m / H_I;
+        const int h = m % H_I;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (t < Tq) {
+                a[rb][ks] = *reinterpret_cast<const v4i*>(
+                    qI + (((size_t)b * Tq + t) * H_I + h) * D_I + 32 * ks + 16 * g);
+            } else {
+                a[rb][ks] = v4i{0, 0, 0, 0};
+            }
+        }
+    }
+    // Head weight of every accumulator register: register r of block rb holds row
+    // 32*rb + 8*(r/4) + 4*g + r%4 (the 32x32 MFMA output layout).
+    float wr[2][16];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 32 * rb + 8 * (r / 4) + 4 * g + (r % 4);
+            const int t = t0 + m / H_I;
+            wr[rb][r] = t < Tq ? w[((size_t)b * Tq + t) * H_I + (m % H_I)] : 0.0f;
+        }
+    }
+
+    const int key_base = blockIdx.x * IX_KEYS_PER_WG;
+    for (int step = 0; step < IX_STEPS; ++step) {
+        const int s0 = key_base + step * IX_KEYS_PER_STEP + wave * 32;
+        if (s0 >= L_cap) break;
+        const int s = s0 + j;
+        float sum[NQL];
+#pragma unroll
+        for (int q = 0; q < NQL; ++q) sum[q] = 0.0f;
+        if (s0 <= pos_max) {
+            v4i bk[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bk[ks] = s < L_cap ? *reinterpret_cast<const v4i*>(
+                                         kI + ((size_t)b * L_cap + s) * D_I + 32 * ks + 16 * g)
+                                   : v4i{0, 0, 0, 0};
+            }
+            v16i acc[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                acc[rb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc[rb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int sl = H_I >= 8 ? (32 * rb + 8 * (r / 4)) / H_I : 4 * rb + r / 4;
+                    const int dot = acc[rb][r];
+                    sum[sl] += wr[rb][r] * (float)(dot > 0 ? dot : 0);
+                }
+            }
+            if (H_I >= 8) {
+#pragma unroll
+                for (int q = 0; q < NQL; ++q) sum[q] += __shfl_xor(sum[q], 32);
+            }
+        }
+        if (s < L_cap) {
+#pragma unroll
+            for (int q = 0; q < NQL; ++q) {
+                int qt;
+                if (H_I >= 8) {
+                    if (g != 0) continue;        // both halves hold the total; one writes
+                    qt = q;
+                } else {
+                    qt = 2 * q + g;
+                }
+                const int t = t0 + qt;
+                if (t >= Tq) continue;
+                const int pos = len - Tq + t;
+                S[((size_t)b * Tq + t) * L_cap + s] = s <= pos ? sum[q] : -__builtin_inff();
+            }
+        }
+    }
+}
+
+template <int H_I, int D_I>
+hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
+                     int B, int Tq, int L_cap, float* S, hipStream_t stream) {
+    constexpr int QPW = IX_ROWS / H_I;
+    dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
+    hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I>), grid, dim3(IX_THREADS), 0, stream, qI,
+                       w, kI, kv_len, Tq, L_cap, S);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_shape_supported(int H_I, int D_I) {
+    const bool h_ok = H_I == 4 || H_I == 8 || H_I == 16 || H_I == 32 || H_I == 64;
+    const bool d_ok = D_I == 32 || D_I == 64 || D_I == 128;
+    return h_ok && d_ok;
+}
+
+#define ISA_IX_CASE(HH, DD)                                                              \
+    if (H_I == HH && D_I == DD)                                                          \
+        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, stream);
+
+hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
+                                 const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
+                                 int L_cap, float* S, hipStream_t stream) {
+    ISA_IX_CASE(64, 128) ISA_IX_CASE(64, 64) ISA_IX_CASE(64, 32)
+    ISA_IX_CASE(32, 128) ISA_IX_CASE(32, 64) ISA_IX_CASE(32, 32)
+    ISA_IX_CASE(16, 128) ISA_IX_CASE(16, 64) ISA_IX_CASE(16, 32)
+    ISA_IX_CASE(8, 128) ISA_IX_CASE(8, 64) ISA_IX_CASE(8, 32)
+    ISA_IX_CASE(4, 128) ISA_IX_CASE(4, 64) ISA_IX_CASE(4, 32)
+    return hipErrorInvalidValue;
+}
+#undef ISA_IX_CASE
+
+}  // namespace isa

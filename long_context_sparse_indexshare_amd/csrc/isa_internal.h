@@ -1,0 +1,56 @@
+// Internal declarations shared by the HIP translation units of libisa.
+// Not part of the public ABI (that is include/isa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace isa {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+
+// Top-k geometry (shared by the host sizing code and the kernels).
+constexpr int TOPK_THREADS = 256;
+constexpr int TOPK_CHUNK = 4096;            // scores per workgroup
+constexpr int TOPK_PER_THREAD = TOPK_CHUNK / TOPK_THREADS;
+constexpr int TOPK_HIST_BITS = 12;          // first radix digit: key bits [31:20]
+constexpr int TOPK_HIST_BINS = 1 << TOPK_HIST_BITS;
+constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bits
+
+struct TopkLayout {
+    size_t hist, cand_cnt, ticket, row_state, count_above, chunk_off, cand, total;
+    int rows, nchunks;
+    uint32_t cap;
+};
+TopkLayout topk_layout(int rows, int L_cap);
+
+// Attention split geometry.
+struct AttendPlan {
+    int splits;        // workgroups per (query, head block) along the k slots
+    int slots_per_split;
+    int head_blocks;   // 32-head blocks per workgroup (2 for 576-wide rows, 1 for 160-wide)
+    size_t partial_bytes;
+};
+AttendPlan attend_plan(int B, int Tq, int H, int D_v, int k);
+
+// Launchers (host side; argument checking happens in the API layer).
+hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
+                                 const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
+                                 int L_cap, float* S, hipStream_t stream);
+hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
+                              int k, int32_t* idx, void* ws, hipStream_t stream);
+hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
+                                    int B, int Tq, int H, int D, int D_v, int L_cap, int k,
+                                    float sm_scale, uint16_t* out, float* lse, void* ws,
+                                    hipStream_t stream);
+
+bool indexer_shape_supported(int H_I, int D_I);
+bool attend_shape_supported(int H, int D, int D_v);
+
+}  // namespace isa

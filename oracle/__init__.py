@@ -129,16 +129,16 @@ def group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence, 
     ablation baseline) and leaves the last layer's set in idx.
     """
     n_layers = len(Q)
-    n_ix = n_layers if per_layer_indexer else 1
-    qI = [_np(x, np.int8) for x in qI[:n_ix]]
-    w = [_np(x, np.float32) for x in w[:n_ix]]
-    kI = [_np(x, np.int8) for x in kI[:n_ix]]
+    n_ix = n_layers if per_layer_indexer else (0 if reuse_idx else 1)
+    qI = [_np(x, np.int8) for x in list(qI or [])[:n_ix]]
+    w = [_np(x, np.float32) for x in list(w or [])[:n_ix]]
+    kI = [_np(x, np.int8) for x in list(kI or [])[:n_ix]]
     kv_len = _np(kv_len, np.int32)
     Q = [_np(x, np.uint16) for x in Q]
     C = [_np(x, np.uint16) for x in C]
-    B, Tq, H_I, D_I = qI[0].shape
-    L_cap = kI[0].shape[1]
-    _, _, H, D = Q[0].shape
+    B, Tq, H, D = Q[0].shape
+    L_cap = C[0].shape[1]
+    H_I, D_I = (qI[0].shape[2], qI[0].shape[3]) if n_ix else (1, 1)
     if reuse_idx:
         if idx is None:
             raise ValueError("reuse_idx needs idx")
@@ -147,7 +147,7 @@ def group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence, 
         idx_out = np.empty((B, Tq, k), dtype=np.int32)
     outs = [np.empty((B, Tq, H, D_v), dtype=np.float64) for _ in range(n_layers)]
     lses = [np.empty((B, Tq, H), dtype=np.float64) for _ in range(n_layers)]
-    S = np.empty((B, Tq, L_cap), dtype=np.float32)
+    S = np.empty((B, Tq, L_cap) if n_ix else (1,), dtype=np.float32)
 
     def parr(arrs):
         return (ctypes.c_void_p * len(arrs))(*[_ptr(a) for a in arrs])

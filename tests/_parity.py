@@ -1,0 +1,63 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest).
+
+Tolerances: indexer scores and top-k indices are compared bit for bit (the
+inputs are integer-valued, so every score is exact); attention outputs, bf16
+with fp32 accumulation, must be within max-abs 2e-2 and relative L2 5e-3 of
+the fp64 oracle per (config, layer, step) tensor; lse within 1e-3 absolute.
+"""
+import numpy as np
+import torch
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+LSE_ABS = 1e-3
+
+
+def dev(t):
+    return t.to("cuda", non_blocking=False)
+
+
+def host(t):
+    return t.detach().to("cpu")
+
+
+def assert_scores_bitwise(S_gpu, S_ref, what=""):
+    g = host(S_gpu).numpy()
+    assert g.shape == S_ref.shape, what
+    same = g.view(np.uint32) == S_ref.view(np.uint32)
+    if not same.all():
+        bad = np.argwhere(~same)[:5]
+        raise AssertionError(f"{what}: {int((~same).sum())} score mismatches, first at "
+                             f"{bad.tolist()}: gpu {g[tuple(bad[0])]} ref {S_ref[tuple(bad[0])]}")
+
+
+def assert_idx_equal(idx_gpu, idx_ref, what=""):
+    g = host(idx_gpu).numpy()
+    assert g.shape == idx_ref.shape, what
+    same = g == idx_ref
+    if not same.all():
+        rows = np.argwhere(~same.all(axis=-1))[:3]
+        r = tuple(rows[0])
+        raise AssertionError(f"{what}: {len(np.argwhere(~same.all(axis=-1)))} rows differ; row {r}: "
+                             f"gpu {g[r][:12]} ref {idx_ref[r][:12]}")
+
+
+def attn_errors(out_gpu, ref):
+    g = host(out_gpu).double().numpy()
+    d = g - ref
+    max_abs = float(np.abs(d).max()) if d.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d) / nref) if nref > 0 else float(np.linalg.norm(d))
+    return max_abs, rel
+
+
+def assert_attn_close(out_gpu, ref, what=""):
+    max_abs, rel = attn_errors(out_gpu, ref)
+    assert max_abs <= MAX_ABS and rel <= REL_L2, f"{what}: max_abs {max_abs:.3g} rel_l2 {rel:.3g}"
+
+
+def assert_lse_close(lse_gpu, ref, what=""):
+    g = host(lse_gpu).double().numpy()
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    d = np.where(both_inf, 0.0, np.abs(g - ref))
+    assert np.all(np.isfinite(d)) and d.max(initial=0.0) <= LSE_ABS, f"{what}: lse err {d.max()}"

@@ -1,0 +1,137 @@
+"""GPU parity of the IndexShare group entry point against the oracle, and the
+group's invariants: one index set shared by every layer, each layer equal to
+a standalone sparse layer fed that set, later MTP steps reusing the step-1
+set, the per-layer-indexer baseline, and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_indexshare_amd as isa
+import oracle
+import synth
+from _parity import assert_attn_close, assert_idx_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _to_dev(inp):
+    return {k: ([dev(x) for x in v] if isinstance(v, list) else dev(v)) for k, v in inp.items()}
+
+
+SMALL = {
+    "C1": synth.WORKLOADS["C1"],
+    "C2-8K": synth.WORKLOADS["C2"].scaled(name="C2-8K", kv_len=8000, L_cap=8192),
+    "decode-B3-Tq2": synth.WORKLOADS["C2"].scaled(name="decode-B3-Tq2", B=3, Tq=2, kv_len=6000,
+                                                  L_cap=6100),
+    "prefill-96": synth.WORKLOADS["C3"].scaled(name="prefill-96", Tq=96, kv_len=5000, L_cap=5000),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_group_matches_oracle(name):
+    wl = SMALL[name]
+    _print_case("group", wl)
+    inp = synth.group_inputs(wl)
+    idx_ref, outs_ref, lses_ref = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]],
+                                                       inp["kv_len"], inp["Q"], inp["C"], wl.k,
+                                                       wl.D_v, wl.sm_scale)
+    d = _to_dev(inp)
+    lse = [torch.empty(wl.B, wl.Tq, wl.H, device="cuda") for _ in range(wl.n_layers)]
+    idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                         d["C"], wl.k, wl.D_v, wl.sm_scale, lse=lse)
+    torch.cuda.synchronize()
+    assert_idx_equal(idx, idx_ref, name)
+    for l in range(wl.n_layers):
+        assert_attn_close(outs[l], outs_ref[l], f"{name} layer {l}")
+        g = host(lse[l]).double().numpy()
+        assert np.nanmax(np.abs(np.where(np.isneginf(lses_ref[l]), 0, g - lses_ref[l]))) < 1e-3
+
+    # each layer equals a standalone sparse layer fed the same index set, bit for bit
+    for l in range(wl.n_layers):
+        o, _ = isa.isa_sparse_mla_attend(d["Q"][l], d["C"][l], idx, wl.D_v, wl.sm_scale)
+        assert torch.equal(o, outs[l]), f"layer {l} differs from standalone"
+    # and a second run gives identical bits (deterministic reductions)
+    idx2, outs2, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                           d["C"], wl.k, wl.D_v, wl.sm_scale)
+    assert torch.equal(idx2, idx)
+    for l in range(wl.n_layers):
+        assert torch.equal(outs2[l], outs[l])
+
+
+def test_group_dense_causal_when_context_fits_k():
+    # context <= k: every query keeps its whole causal prefix (dense attention)
+    wl = synth.WORKLOADS["C1"].scaled(Tq=60, kv_len=60, L_cap=64)
+    inp = synth.group_inputs(wl, layers=1)
+    d = _to_dev(inp)
+    idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                         d["C"], wl.k, wl.D_v, wl.sm_scale)
+    want = np.full((1, wl.Tq, wl.k), -1, dtype=np.int32)
+    for t in range(wl.Tq):
+        want[0, t, : t + 1] = np.arange(t + 1)
+    assert_idx_equal(idx, want, "dense")
+    _, outs_ref, _ = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]], inp["kv_len"],
+                                          inp["Q"], inp["C"], wl.k, wl.D_v, wl.sm_scale)
+    assert_attn_close(outs[0], outs_ref[0], "dense")
+
+
+def test_mtp_steps_reuse_step1_index_set():
+    wl = synth.WORKLOADS["C5"].scaled(B=4, kv_len=9000, L_cap=9000, mtp_steps=3)
+    _print_case("mtp", wl)
+    inp = synth.group_inputs(wl)
+    d = _to_dev(inp)
+    idx = None
+    step_idx = []
+    for step in range(1, wl.mtp_steps + 1):
+        Qs = synth.mtp_queries(wl, step)
+        Qd = [dev(x) for x in Qs]
+        if step == 1:
+            idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qd,
+                                                 d["C"], wl.k, wl.D_v, wl.sm_scale)
+            idx_ref, outs_ref, _ = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]],
+                                                        inp["kv_len"], Qs, inp["C"], wl.k, wl.D_v,
+                                                        wl.sm_scale)
+            assert_idx_equal(idx, idx_ref, "mtp step 1")
+        else:
+            before = idx.clone()
+            _, outs, _ = isa.isa_group_forward(None, None, None, d["kv_len"], Qd, d["C"], wl.k,
+                                               wl.D_v, wl.sm_scale, idx=idx, reuse_idx=True)
+            assert torch.equal(idx, before), "reuse must not touch idx"
+            _, outs_ref, _ = oracle.group_forward(None, None, None, inp["kv_len"], Qs, inp["C"],
+                                                  wl.k, wl.D_v, wl.sm_scale, idx=host(idx).numpy(),
+                                                  reuse_idx=True)
+        step_idx.append(host(idx).clone())
+        for l in range(wl.n_layers):
+            assert_attn_close(outs[l], outs_ref[l], f"mtp step {step} layer {l}")
+    for s in step_idx[1:]:
+        assert torch.equal(s, step_idx[0])
+
+
+def test_per_layer_indexer_ablation():
+    wl = synth.WORKLOADS["C4"].scaled(kv_len=7000, L_cap=7000)
+    _print_case("ablation", wl)
+    inp = synth.group_inputs(wl)
+    ix = [synth.indexer_inputs(wl, seed=s) for s in wl.ablation_seeds]
+    qI, w, kI = [x["qI"] for x in ix], [x["w"] for x in ix], [x["kI"] for x in ix]
+    d = _to_dev(inp)
+    idx, outs, _ = isa.isa_group_forward([dev(x) for x in qI], [dev(x) for x in w],
+                                         [dev(x) for x in kI], d["kv_len"], d["Q"], d["C"], wl.k,
+                                         wl.D_v, wl.sm_scale, per_layer_indexer=True)
+    idx_ref, outs_ref, _ = oracle.group_forward(qI, w, kI, inp["kv_len"], inp["Q"], inp["C"],
+                                                wl.k, wl.D_v, wl.sm_scale, per_layer_indexer=True)
+    assert_idx_equal(idx, idx_ref, "ablation last layer")
+    for l in range(wl.n_layers):
+        assert_attn_close(outs[l], outs_ref[l], f"ablation layer {l}")
+    # identical indexer inputs in every layer reproduce the shared group exactly
+    n = wl.n_layers
+    idx_a, outs_a, _ = isa.isa_group_forward([d["qI"]] * n, [d["w"]] * n, [d["kI"]] * n,
+                                             d["kv_len"], d["Q"], d["C"], wl.k, wl.D_v,
+                                             wl.sm_scale, per_layer_indexer=True)
+    idx_s, outs_s, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                             d["C"], wl.k, wl.D_v, wl.sm_scale)
+    assert torch.equal(idx_a, idx_s)
+    for l in range(n):
+        assert torch.equal(outs_a[l], outs_s[l])

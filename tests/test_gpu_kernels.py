@@ -1,0 +1,196 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles and ragged tails,
+plus the degenerate cases of the method (empty and short contexts, ties,
+invalid slots)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_indexshare_amd as isa
+import oracle
+import synth
+from _parity import (assert_attn_close, assert_idx_equal, assert_lse_close, assert_scores_bitwise,
+                     dev, host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+# ------------------------------------------------------------------ indexer ----
+
+INDEXER_CASES = [
+    # (name, B, Tq, kv_len list, L_cap, H_I, D_I)
+    ("C1-full", 1, 1024, [1024], 1024, 4, 32),
+    ("decode-ragged", 3, 1, [5000, 1, 3333], 5000, 64, 128),
+    ("decode-Tq3", 2, 3, [2049, 700], 2100, 64, 128),
+    ("prefill-64h", 1, 70, [1500], 1531, 64, 128),
+    ("h8-d64", 2, 9, [400, 37], 410, 8, 64),
+    ("h16-d128", 1, 5, [3], 64, 16, 128),
+    ("h32-d32", 2, 4, [129, 0], 130, 32, 32),
+    ("short-ctx", 2, 6, [2, 9], 33, 64, 128),
+]
+
+
+@pytest.mark.parametrize("case", INDEXER_CASES, ids=[c[0] for c in INDEXER_CASES])
+def test_indexer_scores_bitwise(case):
+    name, B, Tq, lens, L_cap, H_I, D_I = case
+    _print_case("indexer", case)
+    g = torch.Generator().manual_seed(hash(name) & 0xFFFF)
+    qI = synth.int8_uniform((B, Tq, H_I, D_I), g, "cpu")
+    w = synth.pow2_weights((B, Tq, H_I), g, "cpu")
+    kI = synth.int8_uniform((B, L_cap, D_I), g, "cpu")
+    kv_len = torch.tensor(lens, dtype=torch.int32)
+    ref = oracle.indexer_scores(qI, w, kI, kv_len)
+    S = isa.isa_indexer_scores(dev(qI), dev(w), dev(kI), dev(kv_len))
+    torch.cuda.synchronize()
+    assert_scores_bitwise(S, ref, name)
+
+
+def test_indexer_full_int8_range_is_exact():
+    # |q.k| <= 128*128*128 stays exact in int32; weights 1 keep the fp32 head sum exact
+    B, Tq, L_cap, H_I, D_I = 1, 2, 2000, 64, 128
+    g = torch.Generator().manual_seed(9)
+    qI = torch.randint(-128, 128, (B, Tq, H_I, D_I), generator=g, dtype=torch.int8)
+    kI = torch.randint(-128, 128, (B, L_cap, D_I), generator=g, dtype=torch.int8)
+    w = torch.ones(B, Tq, H_I) * 0.5
+    kv_len = torch.tensor([L_cap], dtype=torch.int32)
+    ref = oracle.indexer_scores(qI, w, kI, kv_len)
+    S = isa.isa_indexer_scores(dev(qI), dev(w), dev(kI), dev(kv_len))
+    assert_scores_bitwise(S, ref, "full-range")
+
+
+# -------------------------------------------------------------------- top-k ----
+
+def _topk_check(S, kv_len, k, name):
+    _print_case("topk", name, tuple(S.shape), k)
+    ref = oracle.topk_select(S, kv_len, k)
+    idx = isa.isa_topk_select(dev(torch.from_numpy(np.ascontiguousarray(S))), dev(kv_len), k)
+    torch.cuda.synchronize()
+    assert_idx_equal(idx, ref, name)
+
+
+@pytest.mark.parametrize("n,k", [(10000, 2048), (4097, 2048), (2048, 2048), (2047, 2048),
+                                 (20000, 64), (70000, 1), (9000, 2047)])
+def test_topk_random_scores(n, k):
+    r = np.random.default_rng(n + k)
+    B, Tq = 2, 3
+    L_cap = n + 5
+    S = (r.integers(0, 5000, size=(B, Tq, L_cap)) * 0.25).astype(np.float32)  # many ties
+    kv_len = torch.tensor([n, max(n // 2, 1)], dtype=torch.int32)
+    _topk_check(S, kv_len, k, f"random n={n} k={k}")
+
+
+def test_topk_crafted_ties():
+    L_cap, k = 9000, 2048
+    kv_len = torch.tensor([L_cap] * 6, dtype=torch.int32)
+    S = np.zeros((6, 1, L_cap), dtype=np.float32)
+    S[1] = 3.5                                  # all equal
+    S[2, 0, ::2] = -0.0                         # -0.0 and +0.0 tie
+    S[3, 0, :] = np.arange(L_cap) % 7           # duplicates straddle the cut
+    S[4, 0, :] = -np.inf                        # every score -inf
+    S[4, 0, 5000:5003] = 1.0
+    S[5, 0, :] = np.linspace(-1e30, 1e30, L_cap).astype(np.float32)[::-1]
+    _topk_check(S, kv_len, k, "crafted")
+
+
+def test_topk_all_in_one_bin_overflows_candidates():
+    # every key in the first-digit bin: the candidate list overflows and the
+    # last workgroup re-reads the row
+    L_cap = 300000
+    r = np.random.default_rng(3)
+    S = (1000.0 + r.integers(0, 3, size=(1, 2, L_cap)) * 0.25).astype(np.float32)
+    kv_len = torch.tensor([L_cap], dtype=torch.int32)
+    _topk_check(S, kv_len, 2048, "overflow")
+
+
+def test_topk_short_and_empty_rows():
+    L_cap, k = 3000, 64
+    S = np.random.default_rng(4).standard_normal((3, 4, L_cap)).astype(np.float32)
+    kv_len = torch.tensor([2, 0, 70], dtype=torch.int32)   # pos < 0 rows see nothing
+    _topk_check(S, kv_len, k, "short")
+
+
+def test_topk_reuses_workspace_across_calls():
+    ws = isa.Workspace()
+    r = np.random.default_rng(5)
+    for it in range(3):
+        S = r.standard_normal((4, 1, 50000)).astype(np.float32)
+        kv_len = torch.tensor([50000, 30000, 49999, 4097], dtype=torch.int32)
+        ref = oracle.topk_select(S, kv_len, 2048)
+        idx = isa.isa_topk_select(dev(torch.from_numpy(S)), dev(kv_len), 2048, ws=ws)
+        assert_idx_equal(idx, ref, f"call {it}")
+
+
+# ---------------------------------------------------------------- attention ----
+
+def _attend_case(B, Tq, H, D, D_v, L_cap, k, idx_np, seed, name, want_lse=True):
+    _print_case("attend", name, B, Tq, H, D, D_v, L_cap, k)
+    g = torch.Generator().manual_seed(seed)
+    Q = synth.normal_bf16((B, Tq, H, D), g, "cpu")
+    C = synth.normal_bf16((B, L_cap, D), g, "cpu")
+    scale = 1.0 / math.sqrt(D)
+    idx = torch.from_numpy(idx_np.astype(np.int32))
+    ref_out, ref_lse = oracle.sparse_mla_attend(Q, C, idx, D_v, scale)
+    out, lse = isa.isa_sparse_mla_attend(dev(Q), dev(C), dev(idx), D_v, scale, want_lse=want_lse)
+    torch.cuda.synchronize()
+    assert_attn_close(out, ref_out, name)
+    if want_lse:
+        assert_lse_close(lse, ref_lse, name)
+    return Q, C, idx, out
+
+
+def _random_sets(B, Tq, L_cap, k, fill, r):
+    idx = np.full((B, Tq, k), -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(Tq):
+            m = min(fill, L_cap, k)
+            idx[b, t, :m] = np.sort(r.choice(L_cap, size=m, replace=False))
+    return idx
+
+
+@pytest.mark.parametrize("B,Tq,fill", [(8, 1, 2048), (2, 3, 1000), (1, 40, 2048), (3, 2, 77)])
+def test_attend_576(B, Tq, fill):
+    r = np.random.default_rng(B * 100 + Tq)
+    L_cap, k = 20000, 2048
+    idx = _random_sets(B, Tq, L_cap, k, fill, r)
+    _attend_case(B, Tq, 64, 576, 512, L_cap, k, idx, seed=B + Tq, name=f"576 B{B} Tq{Tq} fill{fill}")
+
+
+def test_attend_160_16_heads():
+    r = np.random.default_rng(7)
+    idx = _random_sets(1, 50, 1024, 64, 64, r)
+    idx[0, :5, 3:] = -1
+    _attend_case(1, 50, 16, 160, 128, 1024, 64, idx, seed=3, name="160x16")
+
+
+def test_attend_invalid_and_empty_slots():
+    r = np.random.default_rng(8)
+    B, Tq, L_cap, k = 2, 3, 5000, 2048
+    idx = _random_sets(B, Tq, L_cap, k, 1500, r)
+    idx[0, 0, :] = -1                 # empty set: zeros, lse = -inf
+    idx[0, 1, 7] = L_cap + 3          # out of range: skipped
+    idx[0, 1, 9] = -77
+    idx[1, 2, 1:] = -1                # one valid slot: exactly that row
+    r.shuffle(idx[1, 0])              # slot order does not matter
+    _, C, idx_t, out = _attend_case(B, Tq, 64, 576, 512, L_cap, k, idx, seed=11, name="invalid")
+    o = host(out)
+    assert torch.all(o[0, 0] == 0)
+    np.testing.assert_array_equal(o[1, 2].float().numpy(),
+                                  C[1, int(idx[1, 2, 0]), :512].float().expand(64, 512).numpy())
+
+
+def test_attend_fewer_heads_than_block():
+    r = np.random.default_rng(9)
+    idx = _random_sets(2, 1, 3000, 2048, 2048, r)
+    _attend_case(2, 1, 40, 576, 512, 3000, 2048, idx, seed=5, name="H40")
+
+
+def test_attend_small_k():
+    r = np.random.default_rng(10)
+    idx = _random_sets(4, 2, 3000, 100, 100, r)
+    _attend_case(4, 2, 64, 576, 512, 3000, 100, idx, seed=6, name="k100")
