@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""IndexShare group benchmark on one MI355X.
+
+A step is one IndexShare layer group: lightning indexer + top-k once, then
+sparse latent attention in each of the 4 layers that share the index set.
+The headline workload is the 128K-context decode group (batch 8, one query
+token per sequence, 131072 cached tokens, 64x128 int8 indexer, top-2048,
+4 layers of 64-head 576-wide bf16 latent attention).  With --prefill the
+4096-token prefill chunk over a 131072-token cache is measured as well and
+reported under "prefill".
+
+Inputs are synthetic (synth/), generated on the GPU; decode steps rotate over
+several independent input instances so the 256 MiB MALL cannot hold the
+working set between steps.  Timing: W untimed warm-up steps, then exactly K
+steps between two synchronised HIP events on the stream the library launches
+on.  The dominant kernel (the indexer for decode) is also timed per launch
+with HIP events for its roofline entry, and the CPU oracle is timed on one
+group of the same workload on the host.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("IndexShare group tokens/s (indexer+top-k+4 sparse MLA) at 128K ctx; "
+          "% HBM/MFMA peak")
+PEAK_HBM = 8.0e12          # bytes/s
+PEAK_BF16 = 2.5e15         # dense bf16 MFMA, FLOP/s
+PEAK_INT8 = 5.0e15         # dense int8 MFMA, OP/s
+
+
+def visible_counts(wl):
+    """Per query row: visible keys n = pos + 1 and selected rows min(k, n)."""
+    rows = []
+    for b in range(wl.B):
+        for t in range(wl.Tq):
+            n = max(min(wl.kv_len, wl.L_cap) - wl.Tq + t + 1, 0)
+            rows.append(n)
+    return rows
+
+
+def algorithmic(wl, n_layers=None):
+    """Bytes and ops the method must move/do per group (score and partial-output
+    traffic excluded): kI, qI, w, Q, the selected latent rows, out, idx."""
+    L = wl.n_layers if n_layers is None else n_layers
+    ns = visible_counts(wl)
+    rows = len(ns)
+    pairs = sum(ns)
+    sel = sum(min(wl.k, n) for n in ns)
+    keys_read = wl.B * min(wl.kv_len, wl.L_cap)
+    ix_bytes = keys_read * wl.D_I + rows * wl.H_I * (wl.D_I + 4)
+    ix_ops = 2 * wl.H_I * wl.D_I * pairs
+    topk_bytes = rows * wl.k * 4
+    at_bytes = sel * wl.D * 2 + rows * wl.H * (wl.D + wl.D_v) * 2
+    at_flops = sel * wl.H * 2 * (wl.D + wl.D_v)
+    t_ix = max(ix_ops / PEAK_INT8, ix_bytes / PEAK_HBM)
+    t_at = max(at_flops / PEAK_BF16, at_bytes / PEAK_HBM)
+    t_ideal = t_ix + topk_bytes / PEAK_HBM + L * t_at
+    return {"ix_bytes": ix_bytes, "ix_ops": ix_ops, "topk_bytes": topk_bytes,
+            "at_bytes_per_layer": at_bytes, "at_flops_per_layer": at_flops,
+            "group_bytes": ix_bytes + topk_bytes + L * at_bytes,
+            "t_ideal_s": t_ideal, "t_ix_s": t_ix, "t_at_s": t_at,
+            "ix_bound": "mfma" if ix_ops / PEAK_INT8 > ix_bytes / PEAK_HBM else "hbm",
+            "at_bound": "mfma" if at_flops / PEAK_BF16 > at_bytes / PEAK_HBM else "hbm"}
+
+
+def host_info():
+    cpu = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cpu, os.cpu_count()
+
+
+def make_instances(wl, n_inst, device):
+    import synth
+    insts = []
+    for i in range(n_inst):
+        inst = synth.group_inputs(wl.scaled(seed=wl.seed + 1000 * i), device=device)
+        insts.append(inst)
+    return insts
+
+
+def time_group(isa, calls, steps, warmup, torch):
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        calls[i % len(calls)]()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def time_per_launch(fn, n, torch):
+    """Average device duration of fn's launches, one event pair per launch."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / 1e3 / n
+
+
+def stage_times(isa, inst, wl, torch, reps=20):
+    """Per-stage device time of one group, each stage timed alone."""
+    d = inst
+    S = torch.empty((wl.B, wl.Tq, wl.L_cap), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda")
+    ws = isa.Workspace()
+    t_ix = time_per_launch(lambda: isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"],
+                                                          S=S), reps, torch)
+    t_tk = time_per_launch(lambda: isa.isa_topk_select(S, d["kv_len"], wl.k, idx=idx, ws=ws),
+                           reps, torch)
+    outs = [torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+            for _ in range(wl.n_layers)]
+    t_at = time_per_launch(lambda: isa.isa_sparse_mla_attend(d["Q"][0], d["C"][0], idx, wl.D_v,
+                                                             wl.sm_scale, out=outs[0], ws=ws),
+                           reps, torch)
+    return t_ix, t_tk, t_at
+
+
+def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
+    """Times the CPU oracle on one group over a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    sub = {}
+    bs = slice(0, n_seq)
+    if q_rows is None:
+        sub["qI"] = inst["qI"][bs].cpu()
+        sub["w"] = inst["w"][bs].cpu()
+        sub["kv_len"] = inst["kv_len"][bs].cpu()
+        sub["Q"] = [x[bs].cpu() for x in inst["Q"]]
+        tokens = n_seq * wl.Tq
+    else:
+        # prefill sample: query rows q_rows of sequence 0, each with its own
+        # visible length so that it sees exactly what it sees in the full chunk
+        sub["qI"] = None
+        tokens = len(q_rows)
+    sub["kI"] = inst["kI"][bs].cpu()
+    sub["C"] = [x[bs].cpu() for x in inst["C"]]
+    t0 = time.perf_counter()
+    if q_rows is None:
+        idx, outs, _ = oracle.group_forward([sub["qI"]], [sub["w"]], [sub["kI"]], sub["kv_len"],
+                                            sub["Q"], sub["C"], wl.k, wl.D_v, wl.sm_scale)
+        results = (idx, outs)
+    else:
+        results = []
+        for t in q_rows:
+            kv = torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32)
+            qI = inst["qI"][0:1, t:t + 1].cpu()
+            w = inst["w"][0:1, t:t + 1].cpu()
+            Q = [x[0:1, t:t + 1].cpu() for x in inst["Q"]]
+            results.append(oracle.group_forward([qI], [w], [sub["kI"]], kv, Q, sub["C"], wl.k,
+                                                wl.D_v, wl.sm_scale))
+    dt = time.perf_counter() - t0
+    return tokens, dt, results
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_rows=None):
+    import numpy as np
+    log(f"{wl.name}: generating {n_inst} input instance(s) on the GPU")
+    insts = make_instances(wl, n_inst, "cuda")
+    torch.cuda.synchronize()
+    log(f"{wl.name}: timing {warmup} warm-up + {steps} steps")
+    ws = isa.Workspace()
+    calls = [isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], d["C"], wl.k,
+                           wl.D_v, wl.sm_scale, ws=ws) for d in insts]
+    t_step = time_group(isa, calls, steps, warmup, torch)
+    alg = algorithmic(wl)
+    log(f"{wl.name}: {t_step * 1e6:.1f} us/step; timing stages")
+    t_ix, t_tk, t_at = stage_times(isa, insts[0], wl, torch)
+    res = {
+        "t_step": t_step, "alg": alg,
+        "stages_us": {"indexer": t_ix * 1e6, "topk": t_tk * 1e6, "attend_per_layer": t_at * 1e6},
+    }
+    # CPU oracle on a bounded sample of the same workload, plus a parity spot check
+    if baseline_seq or q_rows:
+        calls[0]()
+        torch.cuda.synchronize()
+        gidx = calls[0].idx.cpu().numpy()
+        gout = [o.double().cpu().numpy() for o in calls[0].out]
+        log(f"{wl.name}: timing the CPU oracle on a sample")
+        tokens, dt, results = oracle_baseline(wl, insts[0], baseline_seq or 1, torch, q_rows)
+        log(f"{wl.name}: oracle {dt:.1f} s for {tokens} token(s)")
+        if q_rows is None:
+            idx, outs = results
+            exact = bool(np.array_equal(gidx[: baseline_seq], idx))
+            errs = [float(np.abs(gout[l][: baseline_seq] - outs[l]).max()) for l in range(len(outs))]
+        else:
+            exact = all(np.array_equal(gidx[0, t], r[0][0, 0]) for t, r in zip(q_rows, results))
+            errs = [max(float(np.abs(gout[l][0, t] - r[1][l][0, 0]).max())
+                        for t, r in zip(q_rows, results)) for l in range(wl.n_layers)]
+        res["oracle"] = {"tokens": tokens, "seconds": dt, "idx_exact": exact,
+                         "max_abs_err": max(errs)}
+    del calls, insts
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(only the one-GPU share of the work is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_sparse_indexshare_amd as isa
+    import synth
+    if not os.path.exists(isa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    isa.load_library()
+    torch.cuda.set_device(0)
+
+    # reference: what a plain device copy reaches on this machine (context for the
+    # roofline fractions, which use the published 8 TB/s)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    t_copy = time_per_launch(lambda: dst.copy_(src), 10, torch)
+    copy_GBps = 2 * src.numel() / t_copy / 1e9
+    del src, dst
+
+    wl = synth.WORKLOADS["C2_128K"]
+    dec = run_workload(isa, wl, args.steps, args.warmup, args.instances, torch,
+                       baseline_seq=None if args.no_cpu_baseline else wl.B)
+    alg = dec["alg"]
+    t = dec["t_step"]
+    tokens = wl.tokens_per_group
+    t_ix = dec["stages_us"]["indexer"] * 1e-6
+    ix_achieved = alg["ix_bytes"] / t_ix
+    cpu_name, ncpu = host_info()
+    line = {
+        "metric": METRIC,
+        "value": tokens / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {"workload": "C2_128K decode group: B=8 x 1 query, context 131072, indexer "
+                               "64x128 int8, top-2048, 4 layers x 64 heads x 576 bf16 latent",
+                   "input_instances": args.instances},
+        "roofline": {"kernel": "indexer_scores", "bound": "hbm",
+                     "achieved": ix_achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": ix_achieved / PEAK_HBM, "traffic": None},
+        "group_roofline": {"t_ideal_us": alg["t_ideal_s"] * 1e6, "t_measured_us": t * 1e6,
+                           "frac": alg["t_ideal_s"] / t,
+                           "algorithmic_bytes": alg["group_bytes"],
+                           "achieved_GBps": alg["group_bytes"] / t / 1e9},
+        "stages_us": dec["stages_us"],
+        "copy_GBps_measured": copy_GBps,
+    }
+    if "oracle" in dec:
+        o = dec["oracle"]
+        line["cpu_baseline"] = {"value": o["tokens"] / o["seconds"], "unit": "tokens/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"one whole C2_128K group ({o['tokens']} tokens) on one "
+                                          f"host core of {cpu_name} ({ncpu} cpus)",
+                                "seconds": o["seconds"], "idx_exact": o["idx_exact"],
+                                "max_abs_err_vs_gpu": o["max_abs_err"]}
+    if args.prefill:
+        wp = synth.WORKLOADS["C3"]
+        pre = run_workload(isa, wp, max(2, min(args.steps, 5)), 2, 1, torch,
+                           q_rows=None if args.no_cpu_baseline else [0, 1, 2047, 4095])
+        ap_ = pre["alg"]
+        tp = pre["t_step"]
+        line["prefill"] = {
+            "workload": "C3 prefill group: 4096 queries over a 135168-token cache (causal), "
+                        "64x128 int8 indexer, top-2048, 4 layers",
+            "tokens_per_s": wp.tokens_per_group / tp, "ms_per_step": tp * 1e3,
+            "t_ideal_ms": ap_["t_ideal_s"] * 1e3, "frac_of_roofline": ap_["t_ideal_s"] / tp,
+            "stages_us": pre["stages_us"],
+            "indexer_int8_TOPS": ap_["ix_ops"] / (pre["stages_us"]["indexer"] * 1e-6) / 1e12,
+            "attend_bf16_TFLOPS": ap_["at_flops_per_layer"] /
+                                  (pre["stages_us"]["attend_per_layer"] * 1e-6) / 1e12,
+        }
+        if "oracle" in pre:
+            o = pre["oracle"]
+            line["prefill"]["cpu_baseline"] = {
+                "value": o["tokens"] / o["seconds"], "unit": "tokens/s", "cores": 1,
+                "kind": "oracle", "sample": f"query rows 0, 1, 2047, 4095 of the chunk",
+                "idx_exact": o["idx_exact"], "max_abs_err_vs_gpu": o["max_abs_err"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

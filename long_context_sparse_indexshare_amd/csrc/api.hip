@@ -92,8 +92,8 @@ isa_status check_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx
               ISA_MAX_LCAP);
     ISA_CHECK(std::isfinite(sm_scale), ISA_ERR_INVALID_ARG, "attend: sm_scale is not finite");
     ISA_CHECK(isa::attend_shape_supported(H, D, D_v), ISA_ERR_UNSUPPORTED,
-              "attend: (H=%d, D=%d, D_v=%d) not compiled; (576,512) with H<=64 or (160,128) with "
-              "H<=32",
+              "attend: (H=%d, D=%d, D_v=%d) not compiled; (D, D_v) in {(576,512), (160,128)}, "
+              "H <= 64",
               H, D, D_v);
     ISA_CHECK((long long)B * Tq <= 65535, ISA_ERR_UNSUPPORTED, "attend: B*Tq=%lld exceeds 65535",
               (long long)B * Tq);
@@ -104,21 +104,30 @@ isa_status check_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Group workspace: [top-k state (zero-kept) | scores S | attention partials]
+// Group workspace: [top-k counters | top-k scratch | scores S | attention
+// partials]; the counters are zeroed by one fill kernel at the start of a call.
 struct GroupLayout {
-    size_t topk, scores, attend, total;
+    size_t topk, topk_zero_bytes, scores, attend, total;
+    bool need_index;
 };
 
 GroupLayout group_layout(const isa_group_args* a) {
     GroupLayout L;
-    const bool need_index = !a->reuse_idx || a->per_layer_indexer;
+    L.need_index = !a->reuse_idx || a->per_layer_indexer;
     const size_t rows = (size_t)a->B * a->Tq;
-    L.topk = 0;
-    size_t off = need_index ? round_up(isa::topk_layout((int)rows, a->L_cap).total) : 0;
+    const isa::AttendPlan ap = isa::attend_plan(a->B, a->Tq, a->H, a->D, a->D_v, a->k);
+    size_t off = 0;
+    L.topk = off;
+    L.topk_zero_bytes = 0;
+    if (L.need_index) {
+        const isa::TopkLayout tl = isa::topk_layout((int)rows, a->L_cap);
+        L.topk_zero_bytes = tl.row_state;            // hist and cand_cnt come first
+        off += round_up(tl.total);
+    }
     L.scores = off;
-    off += need_index ? round_up(rows * (size_t)a->L_cap * sizeof(float)) : 0;
+    off += L.need_index ? round_up(rows * (size_t)a->L_cap * sizeof(float)) : 0;
     L.attend = off;
-    off += round_up(isa::attend_plan(a->B, a->Tq, a->H, a->D_v, a->k).partial_bytes);
+    off += round_up(ap.partial_bytes);
     L.total = off;
     return L;
 }
@@ -137,7 +146,7 @@ isa_status isa_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI
     isa_status st = check_indexer(qI, w, kI, kv_len, B, Tq, H_I, D_I, L_cap, S);
     if (st != ISA_OK) return st;
     return check_hip(isa::launch_indexer_scores(qI, w, kI, kv_len, B, Tq, H_I, D_I, L_cap, S,
-                                                static_cast<hipStream_t>(stream)),
+                                                nullptr, static_cast<hipStream_t>(stream)),
                      "indexer launch");
 }
 
@@ -154,15 +163,14 @@ isa_status isa_topk_select(const float* S, const int32_t* kv_len, int B, int Tq,
     const size_t need = isa_topk_workspace_bytes(B, Tq, L_cap, k);
     ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
               "topk: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
-    return check_hip(isa::launch_topk_select(S, kv_len, B, Tq, L_cap, k, idx, ws,
+    return check_hip(isa::launch_topk_select(S, kv_len, B, Tq, L_cap, k, idx, ws, false, false,
                                              static_cast<hipStream_t>(stream)),
                      "topk launch");
 }
 
 size_t isa_attend_workspace_bytes(int B, int Tq, int H, int D, int D_v, int k) {
-    (void)D;
-    if (B <= 0 || Tq <= 0 || H <= 0 || D_v <= 0 || k <= 0) return 0;
-    return isa::attend_plan(B, Tq, H, D_v, k).partial_bytes;
+    if (B <= 0 || Tq <= 0 || H <= 0 || D <= 0 || D_v <= 0 || k <= 0) return 0;
+    return isa::attend_plan(B, Tq, H, D, D_v, k).partial_bytes;
 }
 
 isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B,
@@ -230,17 +238,37 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
     float* S = reinterpret_cast<float*>(ws + L.scores);
     void* topk_ws = ws + L.topk;
     void* attend_ws = ws + L.attend;
+    // one fill kernel zeroes the top-k counters (histograms, candidate counts)
+    if (L.need_index) {
+        isa_status st = check_hip(isa::launch_clear_u32(reinterpret_cast<uint32_t*>(topk_ws),
+                                                        L.topk_zero_bytes / 4, stream),
+                                  "group: clear launch");
+        if (st != ISA_OK) return st;
+    }
+    bool topk_clear = true;
     auto index = [&](int l) -> isa_status {
+        if (!topk_clear) {
+            // a second index set in the same call (per-layer indexers): clear again
+            isa_status st = check_hip(isa::launch_clear_u32(reinterpret_cast<uint32_t*>(topk_ws),
+                                                            L.topk_zero_bytes / 4, stream),
+                                      "group: clear launch");
+            if (st != ISA_OK) return st;
+        }
+        topk_clear = false;
+        // with one query per indexer workgroup the indexer also builds the
+        // top-k's first-digit histogram (the histogram leads the top-k scratch)
+        const bool fuse = isa::indexer_fuses_hist(a->H_I);
+        uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(topk_ws) : nullptr;
         isa_status st = check_hip(isa::launch_indexer_scores(a->qI[l], a->w[l], a->kI[l], a->kv_len,
                                                              a->B, a->Tq, a->H_I, a->D_I, a->L_cap,
-                                                             S, stream),
+                                                             S, hist, stream),
                                   "group: indexer launch");
         if (st != ISA_OK) return st;
         return check_hip(isa::launch_topk_select(S, a->kv_len, a->B, a->Tq, a->L_cap, a->k, a->idx,
-                                                 topk_ws, stream),
+                                                 topk_ws, true, fuse, stream),
                          "group: topk launch");
     };
-    if (need_index && !per_layer) {
+    if (L.need_index && !per_layer) {
         isa_status st = index(0);
         if (st != ISA_OK) return st;
     }

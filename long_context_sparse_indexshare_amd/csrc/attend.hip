@@ -7,39 +7,62 @@
 // the whole latent row and the value its first D_v entries):
 //   z_j = sm_scale * Q[h] . C[idx_j];  out[h] = sum_j softmax(z)_j * C[idx_j, :D_v].
 //
-// One workgroup = one query x a range of its k slots (a split), all heads.
-// Per tile of T gathered latent rows (each row is read from HBM once and
-// shared by every head):
-//   * the rows are gathered into LDS (row pitch D*2+16 bytes, so that the
-//     32 rows read by one ds_read_b128 land on distinct banks);
-//   * wave (rb, hb) computes S^T = C_rows(rb) . Q(hb)^T with
-//     v_mfma_f32_32x32x16_bf16: a 32-row x 32-head block, Q^T held in
-//     registers for the whole kernel;
+// A workgroup (4 waves) owns one query, HB blocks of 32 heads, 1/VS of the
+// value columns, and a range (split) of the query's k slots.  Per tile of 32
+// gathered latent rows (each row is read from HBM once and shared by all the
+// workgroup's heads):
+//   * gather: each thread loads 16-byte chunks of the tile's rows straight
+//     into registers (thread t owns chunks t, t+256, ... of the tile) and
+//     stores them to LDS once they land; one or two tiles are in flight in
+//     registers while another is computed from LDS (random 1152-byte rows
+//     need tens of KiB in flight per CU to approach HBM bandwidth; the
+//     direct-to-LDS load path measured ~3x slower for this pattern);
+//     slots that are -1 or out of range load a zero row;
+//   * LDS rows are unpadded; the 16-byte chunks of every aligned group of
+//     eight are XOR-swizzled by (row/2)%8, so the 16 rows one ds_read_b128
+//     quarter-wave touches fall in 16 distinct bank groups;
+//   * S^T = C_rows . Q^T on v_mfma_f32_32x32x16_bf16, a 32-row x 32-head
+//     block per head block, with the contraction over the latent dims split
+//     between the 4/HB waves of the head block (each holds only its share of
+//     Q^T in registers); the partial blocks are summed through LDS in a fixed
+//     order, so every wave of the block holds identical bits;
 //   * online softmax in the exp2 domain; a head's 32 rows sit in one lane
-//     pair, so its max and sum need one cross-lane swap plus one LDS exchange
-//     between the row-block waves;
-//   * the accumulator layout of S^T is exactly the k-permuted B-operand layout
-//     of the next product, so P^T goes to the PV MFMA straight from registers
-//     (bf16) -- the other row blocks' P^T comes through the LDS bytes that held
-//     the RoPE slice, which only the QK product reads;
-//   * O^T[cols x heads] += V^T . P^T, where the V^T operand comes from the
-//     row-major tile through ds_read_b64_tr_b16 (two transposing reads per
-//     operand, in the same k order as P^T).
-// With several splits per query, partial (O, max, sum) go to the workspace
-// and a merge kernel combines them in split order.
+//     pair (16 registers each), so max and sum need one cross-lane swap;
+//   * the accumulator layout of S^T is exactly the k-permuted B-operand
+//     layout of the next product, so P^T feeds the PV MFMA from registers;
+//     O^T[cols x heads] += V^T . P^T, with V^T read from the row-major tile by
+//     ds_read_b64_tr_b16 (two transposing reads per operand, same k order).
+// With several splits per query the partial (O, max, sum) go to the
+// workspace and a merge kernel combines them in split order (workgroups never
+// hand data to each other inside a kernel: on gfx950 a device-scope fence
+// writes back and invalidates the whole L2 of the XCD).
 #include "isa_internal.h"
 
 namespace isa {
 namespace {
 
 constexpr int AT_THREADS = 256;
+constexpr int TILE_ROWS = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef __attribute__((address_space(3))) v4bf* lds_v4bf_ptr;
 
+// Largest slot range one workgroup takes (the whole set when not split).
+constexpr int MAX_SPLIT_SLOTS = 2048;
+constexpr int MAX_SPLITS = 16;
+
+// Source of the zero rows that stand in for -1 / out-of-range slots.
+__device__ __attribute__((aligned(16))) uint4 g_zero_row[576 * 2 / 16];
+
 __device__ __forceinline__ v4bf lds_read_tr(const char* lds_base, int byte_off) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf_ptr)(lds_base + byte_off));
+}
+
+// Barrier that waits only for this wave's LDS operations, not for the
+// direct-to-LDS loads still in flight into the other buffer.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -47,119 +70,166 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
-template <int HB, int D, int DV>
+// Physical 16-byte chunk of logical chunk ch in LDS row r: the chunks of a
+// full aligned group of eight are permuted by (r/2)%8 (an involution); a
+// trailing partial group stays in place.
+template <int CH>
+__device__ __forceinline__ int swz(int r, int ch) {
+    return ((ch | 7) < CH) ? (ch ^ ((r >> 1) & 7)) : ch;
+}
+
+template <int HB, int VS, int D, int DV>
 struct AttendGeom {
-    static constexpr int NRB = 4 / HB;              // 32-row blocks per tile
-    static constexpr int T = 32 * NRB;              // tile rows
+    static constexpr int KSP = 4 / HB;              // waves sharing a head block (K split)
     static constexpr int KS = D / 16;               // k-steps of the QK product
+    static constexpr int KSW = KS / KSP;            // k-steps per wave
     static constexpr int CH = D * 2 / 16;           // 16-byte chunks per latent row
-    static constexpr int PITCH = D * 2 + 16;        // LDS row pitch (bytes)
-    static constexpr int DVW = DV / NRB;            // value columns per wave
-    static constexpr int NB = DVW / 32;             // 32-column blocks per wave
-    static constexpr int XSLOTS = (D - DV) * 2 / 32;                    // 32-byte exchange slots per row
-    static constexpr int LDS_BYTES = T * PITCH;
-    static_assert(D % 16 == 0 && DV % (32 * NRB) == 0, "tile shape");
-    static_assert(T * (D - DV) * 2 >= 4 * 64 * 32, "P exchange must fit the RoPE bytes");
+    static constexpr int ROWB = D * 2;              // LDS row bytes (unpadded, swizzled)
+    static constexpr int COLS = DV / VS;            // value columns of the workgroup
+    static constexpr int CW = COLS / KSP;           // value columns per wave
+    static constexpr int NB = CW / 32;              // 32-column MFMA blocks per wave
+    static constexpr int TILE_BYTES = TILE_ROWS * ROWB;
+    static constexpr int TILE_CHUNKS = TILE_ROWS * CH;
+    static constexpr int GPT = (TILE_CHUNKS + AT_THREADS - 1) / AT_THREADS;   // chunks per thread
+    // tiles in flight in registers while one is computed: two where the
+    // register budget allows (the decode variant), one for the wide variant
+    static constexpr int AHEAD = NB <= 4 ? 2 : 1;
+    static_assert(KS % KSP == 0, "the K split must divide the k-steps");
+    static_assert(CW % 32 == 0, "value columns per wave");
 };
 
-template <int HB, int D, int DV>
+template <int HB, int VS, int D, int DV>
 __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const int32_t* __restrict__ idx,
     int Tq, int H, int L_cap, int k, float scale_log2, int slots_per_split, int splits,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
-    using G = AttendGeom<HB, D, DV>;
-    constexpr int T = G::T;
-    constexpr int NRB = G::NRB;
-    constexpr int PITCH = G::PITCH;
+    using G = AttendGeom<HB, VS, D, DV>;
+    constexpr int ROWB = G::ROWB;
 
-    __shared__ __attribute__((aligned(16))) char tile[G::LDS_BYTES];
-    __shared__ int svalid[T];
-    __shared__ float red_max[4][32];
-    __shared__ float red_sum[4][32];
+    __shared__ __attribute__((aligned(16))) char tile[G::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) float xbuf[4][4][64][4];   // partial S^T blocks
+    __shared__ int sidx[MAX_SPLIT_SLOTS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int j = lane & 31;
     const int g = lane >> 5;
-    const int rb = wave / HB;
-    const int hb = wave % HB;
-    const int q = blockIdx.y;              // b * Tq + t
+    const int hbl = wave % HB;              // head block within the workgroup
+    const int kp = wave / HB;               // this wave's share of the K and column split
+    const int q = blockIdx.y;               // b * Tq + t
     const int sp = blockIdx.x;
+    const int hbg = blockIdx.z / VS;        // head-block group of the workgroup
+    const int vh = blockIdx.z - hbg * VS;   // column part
     const int b = q / Tq;
-    const int head = hb * 32 + j;
+    const int head = (hbg * HB + hbl) * 32 + j;
     const bool head_ok = head < H;
     const int slot0 = sp * slots_per_split;
     const int slot1 = min(slot0 + slots_per_split, k);
     const int32_t* qidx = idx + (size_t)q * k;
-    const uint16_t* Cb = C + (size_t)b * L_cap * D;
+    const char* Cb = reinterpret_cast<const char*>(C + (size_t)b * L_cap * D);
+    const int col0 = vh * G::COLS + kp * G::CW;   // first value column of this wave
 
-    // Q^T operand of this wave's heads: lane (head j, half g) holds dims 16*ks + 8*g .. +8
-    v8bf qb[G::KS];
+    // this split's positions, once, into LDS; invalid ones and the padding up
+    // to a whole number of tiles become -1
+    const int padded = ((slot1 - slot0 + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
+    for (int i = tid; i < padded; i += AT_THREADS) {
+        const int s = slot0 + i < slot1 ? qidx[slot0 + i] : -1;
+        sidx[i] = (s >= 0 && s < L_cap) ? s : -1;
+    }
+
+    // this wave's share of Q^T: lane (head j, half g) holds dims 16*ks + 8*g .. +8
+    // for ks in [kp*KSW, (kp+1)*KSW); heads past H read head 0 and are zeroed
+    v8bf qb[G::KSW];
     {
         const uint16_t* qrow = Q + ((size_t)q * H + (head_ok ? head : 0)) * D;
+        const uint32_t keep = head_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-            const uint4 v = head_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * g)
-                                    : make_uint4(0, 0, 0, 0);
-            qb[ks] = __builtin_bit_cast(v8bf, v);
+        for (int i = 0; i < G::KSW; ++i) {
+            uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * (kp * G::KSW + i) + 8 * g);
+            v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
+            qb[i] = __builtin_bit_cast(v8bf, v);
         }
     }
 
     v16f o[G::NB];
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
         for (int r = 0; r < 16; ++r) o[nb][r] = 0.0f;
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
 
-    // gather one tile of latent rows into LDS (rows past the split or with an
-    // invalid position are zero, so their value rows contribute nothing)
-    auto gather = [&](int tile_start) {
-        for (int c = tid; c < T * G::CH; c += AT_THREADS) {
-            const int r = c / G::CH;
-            const int ch = c - r * G::CH;
-            const int slot = tile_start + r;
-            const int s = slot < slot1 ? qidx[slot] : -1;
-            const bool valid = s >= 0 && s < L_cap;
-            const uint4 v = valid ? *reinterpret_cast<const uint4*>(Cb + (size_t)s * D + ch * 8)
-                                  : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(tile + r * PITCH + ch * 16) = v;
-            if (ch == 0) svalid[r] = valid;
-        }
-    };
+    // gather: thread tid owns chunks c = i*256 + tid of a tile (row c / CH,
+    // logical chunk c % CH); rows of -1 / out-of-range slots read a zero row.
+    // (Macros rather than lambdas keep the register arrays out of memory.)
+    const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_row);
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(Cb);
+#define ISA_LOAD_TILE(R, TS)                                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < G::GPT; ++i_) {                                   \
+        const int c_ = i_ * AT_THREADS + tid;                                                  \
+        if (G::TILE_CHUNKS % AT_THREADS == 0 || c_ < G::TILE_CHUNKS) {                         \
+            const int row_ = c_ / G::CH;                                                       \
+            const int ch_ = c_ - row_ * G::CH;                                                 \
+            const int s_ = sidx[(TS) - slot0 + row_];   /* -1 past the split (padded) */       \
+            const uintptr_t ra_ = cbase + (size_t)(s_ & ~(s_ >> 31)) * ROWB;                   \
+            R[i_] = *reinterpret_cast<const v4u*>((s_ >= 0 ? ra_ : zero_row) + ch_ * 16);      \
+        }                                                                                      \
+    }
+#define ISA_STORE_TILE(R)                                                                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < G::GPT; ++i_) {                                   \
+        const int c_ = i_ * AT_THREADS + tid;                                                  \
+        if (G::TILE_CHUNKS % AT_THREADS == 0 || c_ < G::TILE_CHUNKS) {                         \
+            const int row_ = c_ / G::CH;                                                       \
+            const int ch_ = c_ - row_ * G::CH;                                                 \
+            *reinterpret_cast<v4u*>(tile + row_ * ROWB + swz<G::CH>(row_, ch_) * 16) = R[i_];  \
+        }                                                                                      \
+    }
 
-    for (int tile_start = slot0; tile_start < slot1; tile_start += T) {
-        __syncthreads();                   // previous tile fully consumed
-        gather(tile_start);
-        __syncthreads();
-
-        // ---- S^T block: rows 32*rb .. +32 of the tile, heads of block hb
+    // one tile of the online softmax attention, from the LDS tile
+    auto compute_tile = [&](int tile_start) {
+        // ---- partial S^T (32 rows x 32 heads) over this wave's k-steps
         v16f st;
-        for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-        const char* arow = tile + (32 * rb + j) * PITCH + 16 * g;
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-            const v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(arow + 32 * ks));
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], st, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+        const char* arow = tile + j * ROWB;
+#pragma unroll
+        for (int i = 0; i < G::KSW; ++i) {
+            const int ch = 2 * (kp * G::KSW + i) + g;
+            const v8bf a = __builtin_bit_cast(
+                v8bf, *reinterpret_cast<const uint4*>(arow + swz<G::CH>(j, ch) * 16));
+            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i], st, 0, 0, 0);
         }
-        // register r holds tile row 32*rb + 8*(r/4) + 4*g + r%4, head j
+        // ---- sum the K-split partials of this head block, in kp order
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4*>(&xbuf[wave][r4][lane][0]) =
+                make_float4(st[4 * r4], st[4 * r4 + 1], st[4 * r4 + 2], st[4 * r4 + 3]);
+        lds_barrier();
+        v16f s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+        for (int p = 0; p < G::KSP; ++p) {
+            const int w2 = p * HB + hbl;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
+                s[4 * r4] += v.x; s[4 * r4 + 1] += v.y; s[4 * r4 + 2] += v.z; s[4 * r4 + 3] += v.w;
+            }
+        }
+        // register r holds tile row 8*(r/4) + 4*g + r%4, head j
         float mloc = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = 32 * rb + 8 * (r / 4) + 4 * g + (r % 4);
-            const float x = svalid[row] ? st[r] * scale_log2 : -__builtin_inff();
-            st[r] = x;
+            const bool valid = sidx[tile_start - slot0 + 8 * (r / 4) + 4 * g + (r % 4)] >= 0;
+            const float x = valid ? s[r] * scale_log2 : -__builtin_inff();
+            s[r] = x;
             mloc = fmaxf(mloc, x);
         }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        if (g == 0) red_max[wave][j] = mloc;
-        __syncthreads();                   // also: every wave finished reading the RoPE bytes
-        float mt = -__builtin_inff();
-#pragma unroll
-        for (int r2 = 0; r2 < NRB; ++r2) mt = fmaxf(mt, red_max[r2 * HB + hb][j]);
-        const float m_new = fmaxf(m_run, mt);
+        const float m_new = fmaxf(m_run, mloc);
         const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
         const float alpha = exp2f(m_run - m_use);
         m_run = m_new;
@@ -167,7 +237,7 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
         v8bf pk[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = exp2f(st[r] - m_use);
+            const float p = exp2f(s[r] - m_use);
             psum += p;
             pk[r / 8][r % 8] = (__bf16)p;
         }
@@ -177,58 +247,73 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
 
-        // ---- publish P^T through the RoPE bytes of the tile
-        {
-            const int e = wave * 64 + lane;
-            char* xs = tile + (e / G::XSLOTS) * PITCH + DV * 2 + (e % G::XSLOTS) * 32;
-            *reinterpret_cast<v8bf*>(xs) = pk[0];
-            *reinterpret_cast<v8bf*>(xs + 16) = pk[1];
-        }
-        __syncthreads();
-
-        // ---- O^T[cols of this wave x heads of hb] += V^T . P^T over all T rows
-        const int col0 = rb * G::DVW;
+        // ---- O^T[this wave's columns x heads] += V^T . P^T over the tile's 32 rows
         const int G16 = lane >> 4;
         const int i16 = lane & 15;
 #pragma unroll
-        for (int r2 = 0; r2 < NRB; ++r2) {
-            v8bf pb[2];
-            if (r2 == rb) {
-                pb[0] = pk[0];
-                pb[1] = pk[1];
-            } else {
-                const int e = (r2 * HB + hb) * 64 + lane;
-                const char* xs = tile + (e / G::XSLOTS) * PITCH + DV * 2 + (e % G::XSLOTS) * 32;
-                pb[0] = *reinterpret_cast<const v8bf*>(xs);
-                pb[1] = *reinterpret_cast<const v8bf*>(xs + 16);
-            }
+        for (int kk = 0; kk < 2; ++kk) {
+            const int row = 16 * kk + 4 * (G16 >> 1) + (i16 >> 2);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int row = 32 * r2 + 16 * kk + 4 * (G16 >> 1) + (i16 >> 2);
-#pragma unroll
-                for (int nb = 0; nb < G::NB; ++nb) {
-                    const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
-                    const int off = row * PITCH + col * 2;
-                    const v4bf lo = lds_read_tr(tile, off);
-                    const v4bf hi = lds_read_tr(tile, off + 8 * PITCH);
-                    const v8bf a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], o[nb], 0, 0, 0);
-                }
+            for (int nb = 0; nb < G::NB; ++nb) {
+                const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
+                const int sub = (col & 7) * 2;
+                const v4bf lo = lds_read_tr(tile, row * ROWB + swz<G::CH>(row, col >> 3) * 16 + sub);
+                const v4bf hi = lds_read_tr(tile, (row + 8) * ROWB +
+                                                      swz<G::CH>(row + 8, col >> 3) * 16 + sub);
+                const v8bf a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[nb], 0, 0, 0);
             }
         }
-    }
+    };
 
-    // ---- finish: total softmax denominator of each head over all row blocks
-    float lsum = l_run + __shfl_xor(l_run, 32);
-    __syncthreads();
-    if (g == 0) red_sum[wave][j] = lsum;
-    __syncthreads();
-    float l_tot = 0.0f;
-#pragma unroll
-    for (int r2 = 0; r2 < NRB; ++r2) l_tot += red_sum[r2 * HB + hb][j];
+    // software pipeline: two tiles in flight in registers (rA, rB) while the
+    // LDS tile is computed; the register sets alternate, so the loop body is
+    // unrolled by two to keep their roles static
+    const int ntiles = (slot1 - slot0 + TILE_ROWS - 1) / TILE_ROWS;
+    lds_barrier();                          // sidx visible
+    v4u rA[G::GPT], rB[G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
+    if constexpr (G::AHEAD == 2) {
+        if (ntiles > 0) { ISA_LOAD_TILE(rA, slot0) }
+        if (ntiles > 1) { ISA_LOAD_TILE(rB, slot0 + TILE_ROWS) }
+        if (ntiles > 0) { ISA_STORE_TILE(rA) }
+        if (ntiles > 2) { ISA_LOAD_TILE(rA, slot0 + 2 * TILE_ROWS) }
+        lds_barrier();
+        for (int it = 0; it < ntiles; it += 2) {
+            compute_tile(slot0 + it * TILE_ROWS);            // in flight: rB = it+1, rA = it+2
+            if (it + 1 >= ntiles) break;
+            lds_barrier();
+            ISA_STORE_TILE(rB)
+            if (it + 3 < ntiles) { ISA_LOAD_TILE(rB, slot0 + (it + 3) * TILE_ROWS) }
+            lds_barrier();
+            compute_tile(slot0 + (it + 1) * TILE_ROWS);      // in flight: rA = it+2, rB = it+3
+            if (it + 2 >= ntiles) break;
+            lds_barrier();
+            ISA_STORE_TILE(rA)
+            if (it + 4 < ntiles) { ISA_LOAD_TILE(rA, slot0 + (it + 4) * TILE_ROWS) }
+            lds_barrier();
+        }
+    } else {
+        (void)rB;
+        if (ntiles > 0) { ISA_LOAD_TILE(rA, slot0) }
+        if (ntiles > 0) { ISA_STORE_TILE(rA) }
+        if (ntiles > 1) { ISA_LOAD_TILE(rA, slot0 + TILE_ROWS) }
+        lds_barrier();
+        for (int it = 0; it < ntiles; ++it) {
+            compute_tile(slot0 + it * TILE_ROWS);            // in flight: rA = it+1
+            if (it + 1 >= ntiles) break;
+            lds_barrier();
+            ISA_STORE_TILE(rA)
+            if (it + 2 < ntiles) { ISA_LOAD_TILE(rA, slot0 + (it + 2) * TILE_ROWS) }
+            lds_barrier();
+        }
+    }
+#undef ISA_LOAD_TILE
+#undef ISA_STORE_TILE
+
+    // softmax denominator of head j over all rows (the lane pair splits them)
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
 
     // o[nb] register r holds value column col0 + 32*nb + 8*(r/4) + 4*g + r%4 of head j
-    const int col0 = rb * G::DVW;
     if (splits == 1) {
         if (!head_ok) return;
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -246,14 +331,14 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
                 *reinterpret_cast<ushort4*>(orow + col) = v;
             }
         }
-        if (lse && rb == 0 && g == 0) {
-            lse[(size_t)q * H + head] =
-                l_tot > 0.0f ? (m_run + log2f(l_tot)) * LN2 : -__builtin_inff();
-        }
-    } else {
-        if (!head_ok) return;
-        const size_t pbase = ((size_t)q * splits + sp) * H + head;
-        float* po = part_o + pbase * DV;
+        if (lse && kp == 0 && vh == 0 && g == 0)
+            lse[(size_t)q * H + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * LN2 : -__builtin_inff();
+        return;
+    }
+
+    // ---- split: publish the unnormalised partial and (max, sum) of this column part
+    if (head_ok) {
+        float* po = part_o + (((size_t)q * splits + sp) * H + head) * DV;
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb) {
 #pragma unroll
@@ -263,107 +348,120 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
                     make_float4(o[nb][4 * r4], o[nb][4 * r4 + 1], o[nb][4 * r4 + 2], o[nb][4 * r4 + 3]);
             }
         }
-        if (rb == 0 && g == 0) part_ml[pbase] = make_float2(m_run, l_tot);
+        if (kp == 0 && g == 0)
+            part_ml[(((size_t)q * splits + sp) * VS + vh) * H + head] = make_float2(m_run, l_tot);
     }
 }
 
-// Combines the splits of one (query, head): out = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
-template <int DV>
-__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml,
-                                                           int H, int splits,
-                                                           uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
+// Combines the splits of one (query, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// in split order; column part p uses the (max, sum) its own workgroups wrote.
+template <int DV, int VS>
+__global__ __launch_bounds__(DV / 4) void merge_splits_kernel(const float* __restrict__ part_o,
+                                                              const float2* __restrict__ part_ml,
+                                                              int H, int splits,
+                                                              uint16_t* __restrict__ out,
+                                                              float* __restrict__ lse) {
     const int qh = blockIdx.x;             // q * H + h
     const int q = qh / H;
     const int h = qh - q * H;
-    __shared__ float wts[64];
-    __shared__ float sh_norm[2];
-    if (threadIdx.x < 64) {
-        float M = -__builtin_inff();
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((size_t)q * splits + s) * H + h].x);
-        const float Mu = M == -__builtin_inff() ? 0.0f : M;
-        if (threadIdx.x == 0) {
-            float L = 0.0f;
-            for (int s = 0; s < splits; ++s) {
-                const float2 ml = part_ml[((size_t)q * splits + s) * H + h];
-                L += exp2f(ml.x - Mu) * ml.y;
-            }
-            sh_norm[0] = L > 0.0f ? 1.0f / L : 0.0f;
-            sh_norm[1] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
-        }
-        for (int s = threadIdx.x; s < splits; s += 64)
-            wts[s] = exp2f(part_ml[((size_t)q * splits + s) * H + h].x - Mu);
+    const int col = threadIdx.x * 4;
+    const int vh = col / (DV / VS);
+    float M = -__builtin_inff();
+    for (int sj = 0; sj < splits; ++sj)
+        M = fmaxf(M, part_ml[(((size_t)q * splits + sj) * VS + vh) * H + h].x);
+    const float Mu = M == -__builtin_inff() ? 0.0f : M;
+    float L = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sj = 0; sj < splits; ++sj) {
+        const float2 ml = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + h];
+        const float wgt = exp2f(ml.x - Mu);
+        L += wgt * ml.y;
+        const float4 v = *reinterpret_cast<const float4*>(
+            part_o + (((size_t)q * splits + sj) * H + h) * DV + col);
+        acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
     }
-    __syncthreads();
-    const float inv = sh_norm[0];
-    for (int col = threadIdx.x; col < DV; col += 256) {
-        float acc = 0.0f;
-        for (int s = 0; s < splits; ++s)
-            acc += wts[s] * part_o[(((size_t)q * splits + s) * H + h) * DV + col];
-        out[(size_t)qh * DV + col] = f2bf(acc * inv);
-    }
-    if (lse && threadIdx.x == 0) lse[qh] = sh_norm[1];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    ushort4 r;
+    r.x = f2bf(acc.x * inv); r.y = f2bf(acc.y * inv); r.z = f2bf(acc.z * inv); r.w = f2bf(acc.w * inv);
+    *reinterpret_cast<ushort4*>(out + (size_t)qh * DV + col) = r;
+    if (lse && threadIdx.x == 0) lse[qh] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
 }
 
-template <int HB, int D, int DV>
+template <int HB, int VS, int D, int DV>
 hipError_t launch_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B, int Tq,
                          int H, int L_cap, int k, float sm_scale, uint16_t* out, float* lse,
-                         void* ws, hipStream_t stream) {
-    const AttendPlan plan = attend_plan(B, Tq, H, DV, k);
+                         void* partials, hipStream_t stream) {
+    const AttendPlan plan = attend_plan(B, Tq, H, D, DV, k);
     const int nq = B * Tq;
-    float* part_o = static_cast<float*>(ws);
-    float2* part_ml = nullptr;
+    char* base = static_cast<char*>(partials);
+    float* part_o = reinterpret_cast<float*>(base + plan.part_o_off);
+    float2* part_ml = reinterpret_cast<float2*>(base + plan.part_ml_off);
+    const int n_hbg = (H + 32 * HB - 1) / (32 * HB);
+    dim3 grid(plan.splits, nq, n_hbg * VS);
+    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV>), grid, dim3(AT_THREADS), 0, stream, Q,
+                       C, idx, Tq, H, L_cap, k, sm_scale * LOG2E, plan.slots_per_split,
+                       plan.splits, out, lse, part_o, part_ml);
     if (plan.splits > 1)
-        part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                            (size_t)nq * plan.splits * H * DV * sizeof(float));
-    dim3 grid(plan.splits, nq);
-    hipLaunchKernelGGL((sparse_attend_kernel<HB, D, DV>), grid, dim3(AT_THREADS), 0, stream, Q, C,
-                       idx, Tq, H, L_cap, k, sm_scale * LOG2E, plan.slots_per_split, plan.splits,
-                       out, lse, part_o, part_ml);
-    if (plan.splits > 1) {
-        hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(nq * H), dim3(256), 0, stream, part_o,
-                           part_ml, H, plan.splits, out, lse);
-    }
+        hipLaunchKernelGGL((merge_splits_kernel<DV, VS>), dim3(nq * H), dim3(DV / 4), 0, stream,
+                           part_o, part_ml, H, plan.splits, out, lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
-AttendPlan attend_plan(int B, int Tq, int H, int D_v, int k) {
+AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k) {
     AttendPlan p;
-    p.head_blocks = D_v == 512 ? 2 : 1;
-    const int T = 32 * (4 / p.head_blocks);
     const int nq = B * Tq;
-    const int tiles = (k + T - 1) / T;
-    int splits = (512 + nq - 1) / nq;          // aim for >= 512 workgroups
+    // many queries: one workgroup per query holds both head blocks and every
+    // value column; few queries (decode): one head block and half the value
+    // columns per workgroup (their QK work is duplicated, their gathers meet
+    // in L2), and the k slots split across workgroups
+    const bool wide = nq >= 256 || D != 576;
+    p.head_blocks = wide ? 2 : 1;
+    p.col_parts = wide ? 1 : 2;
+    const int n_hbg = (H + 32 * p.head_blocks - 1) / (32 * p.head_blocks);
+    const int units = nq * n_hbg * p.col_parts;
+    const int tiles = (k + TILE_ROWS - 1) / TILE_ROWS;
+    int splits = units >= 256 ? 1 : (256 + units - 1) / units;
+    if (splits > MAX_SPLITS) splits = MAX_SPLITS;
     if (splits > tiles) splits = tiles;
-    if (splits > 64) splits = 64;
-    if (splits < 1) splits = 1;
     const int tiles_per_split = (tiles + splits - 1) / splits;
     splits = (tiles + tiles_per_split - 1) / tiles_per_split;
     p.splits = splits;
-    p.slots_per_split = tiles_per_split * T;
-    p.partial_bytes = splits > 1 ? (size_t)nq * splits * H * ((size_t)D_v + 2) * sizeof(float) : 0;
+    p.slots_per_split = tiles_per_split * TILE_ROWS;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    p.part_o_off = take(splits > 1 ? (size_t)nq * splits * H * D_v * 4 : 0);
+    p.part_ml_off = take(splits > 1 ? (size_t)nq * splits * p.col_parts * H * 8 : 0);
+    p.partial_bytes = off;
     return p;
 }
 
 bool attend_shape_supported(int H, int D, int D_v) {
     if (D == 576 && D_v == 512) return H >= 1 && H <= 64;
-    if (D == 160 && D_v == 128) return H >= 1 && H <= 32;
+    if (D == 160 && D_v == 128) return H >= 1 && H <= 64;
     return false;
 }
 
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,
-                                    float sm_scale, uint16_t* out, float* lse, void* ws,
+                                    float sm_scale, uint16_t* out, float* lse, void* partials,
                                     hipStream_t stream) {
-    // 576-wide rows: two 32-head blocks per workgroup (heads past H are zero);
-    // 160-wide rows: one 32-head block and 128-row tiles.
-    if (D == 576 && D_v == 512)
-        return launch_attend<2, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse, ws, stream);
+    const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
+    if (D == 576 && D_v == 512) {
+        if (plan.head_blocks == 2)
+            return launch_attend<2, 1, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+                                                 partials, stream);
+        return launch_attend<1, 2, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+                                             partials, stream);
+    }
     if (D == 160 && D_v == 128)
-        return launch_attend<1, 160, 128>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse, ws, stream);
+        return launch_attend<2, 1, 160, 128>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+                                             partials, stream);
     return hipErrorInvalidValue;
 }
 

@@ -13,7 +13,12 @@
 // v_mfma_i32_32x32x32_i8 (exact int32 dot products).  The epilogue applies
 // ReLU and the head weight in fp32 and reduces the heads of a query in
 // registers plus one cross-lane swap; blocks past the last visible key of
-// every query in the workgroup skip the loads and write -inf.
+// every query in the workgroup skip the loads and write -inf.  Each wave
+// keeps the next key block's loads in flight while it computes the current
+// one.  With one query per workgroup the kernel can also build the top-k's
+// first-digit histogram (top 12 bits of the order-preserving image of each
+// visible score) in LDS and add it to the row's global histogram, sparing
+// the top-k a pass over the scores.
 #include "isa_internal.h"
 
 namespace isa {
@@ -27,13 +32,23 @@ constexpr int IX_KEYS_PER_WG = IX_KEYS_PER_STEP * IX_STEPS;
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
-template <int H_I, int D_I>
+// Order-preserving 32-bit image of a score (larger score, larger key; -0 = +0).
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int H_I, int D_I, bool HIST>
 __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
-    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S) {
+    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
+    uint32_t* __restrict__ hist) {
     constexpr int QPW = IX_ROWS / H_I;             // queries per workgroup
     constexpr int KS = D_I / 32;                   // MFMA k-steps over the indexer dim
     constexpr int NQL = H_I >= 8 ? 64 / H_I : 8;   // query slots held per lane
+    static_assert(!HIST || QPW == 1, "the fused histogram needs one query per workgroup");
+    __shared__ uint32_t lh[HIST ? TOPK_HIST_BINS : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane & 31;
@@ -43,6 +58,9 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int len = clamp_len(kv_len[b], L_cap);
     const int t_last = min(t0 + QPW, Tq) - 1;
     const int pos_max = len - Tq + t_last;          // last key any query here can see
+    if (HIST) {
+        for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += IX_THREADS) lh[i] = 0;
+    }
 
     // A operands: row m = 32*rb + j is (query m / H_I, head m % H_I); k bytes 32*ks + 16*g .. +16.
     v4i a[2][KS];
@@ -73,23 +91,35 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
             wr[rb][r] = t < Tq ? w[((size_t)b * Tq + t) * H_I + (m % H_I)] : 0.0f;
         }
     }
+    if (HIST) __syncthreads();                      // histogram zeroed
 
-    const int key_base = blockIdx.x * IX_KEYS_PER_WG;
+    // B operands of one 32-key block: lane (key s0 + j, half g) holds k bytes 32*ks + 16*g .. +16
+    auto load_keys = [&](int s0, v4i* bk) {
+        const int s = s0 + j;
+        const bool live = s0 <= pos_max && s < L_cap;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + ((size_t)b * L_cap + s) * D_I +
+                                                          32 * ks + 16 * g)
+                          : v4i{0, 0, 0, 0};
+        }
+    };
+
+    const int key_base = blockIdx.x * IX_KEYS_PER_WG + wave * 32;
+    v4i bk_next[KS];
+    load_keys(key_base, bk_next);
     for (int step = 0; step < IX_STEPS; ++step) {
-        const int s0 = key_base + step * IX_KEYS_PER_STEP + wave * 32;
+        const int s0 = key_base + step * IX_KEYS_PER_STEP;
         if (s0 >= L_cap) break;
+        v4i bk[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = bk_next[ks];
+        if (step + 1 < IX_STEPS) load_keys(s0 + IX_KEYS_PER_STEP, bk_next);   // next block in flight
         const int s = s0 + j;
         float sum[NQL];
 #pragma unroll
         for (int q = 0; q < NQL; ++q) sum[q] = 0.0f;
         if (s0 <= pos_max) {
-            v4i bk[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bk[ks] = s < L_cap ? *reinterpret_cast<const v4i*>(
-                                         kI + ((size_t)b * L_cap + s) * D_I + 32 * ks + 16 * g)
-                                   : v4i{0, 0, 0, 0};
-            }
             v16i acc[2];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -125,19 +155,37 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
                 const int t = t0 + qt;
                 if (t >= Tq) continue;
                 const int pos = len - Tq + t;
-                S[((size_t)b * Tq + t) * L_cap + s] = s <= pos ? sum[q] : -__builtin_inff();
+                const bool vis = s <= pos;
+                S[((size_t)b * Tq + t) * L_cap + s] = vis ? sum[q] : -__builtin_inff();
+                if (HIST && vis) atomicAdd(&lh[score_key(sum[q]) >> (32 - TOPK_HIST_BITS)], 1u);
             }
+        }
+    }
+    if (HIST) {
+        __syncthreads();
+        uint32_t* gh = hist + ((size_t)b * Tq + t0) * TOPK_HIST_BINS;
+        for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += IX_THREADS) {
+            const uint32_t c = lh[i];
+            if (c) atomicAdd(&gh[i], c);
         }
     }
 }
 
 template <int H_I, int D_I>
 hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
-                     int B, int Tq, int L_cap, float* S, hipStream_t stream) {
+                     int B, int Tq, int L_cap, float* S, uint32_t* hist, hipStream_t stream) {
     constexpr int QPW = IX_ROWS / H_I;
     dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
-    hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I>), grid, dim3(IX_THREADS), 0, stream, qI,
-                       w, kI, kv_len, Tq, L_cap, S);
+    if constexpr (QPW == 1) {
+        if (hist) {
+            hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I, true>), grid, dim3(IX_THREADS), 0,
+                               stream, qI, w, kI, kv_len, Tq, L_cap, S, hist);
+            return hipGetLastError();
+        }
+    }
+    if (hist) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I, false>), grid, dim3(IX_THREADS), 0, stream,
+                       qI, w, kI, kv_len, Tq, L_cap, S, nullptr);
     return hipGetLastError();
 }
 
@@ -149,13 +197,15 @@ bool indexer_shape_supported(int H_I, int D_I) {
     return h_ok && d_ok;
 }
 
+bool indexer_fuses_hist(int H_I) { return H_I == IX_ROWS; }
+
 #define ISA_IX_CASE(HH, DD)                                                              \
     if (H_I == HH && D_I == DD)                                                          \
-        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, stream);
+        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, hist, stream);
 
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
-                                 int L_cap, float* S, hipStream_t stream) {
+                                 int L_cap, float* S, uint32_t* hist, hipStream_t stream) {
     ISA_IX_CASE(64, 128) ISA_IX_CASE(64, 64) ISA_IX_CASE(64, 32)
     ISA_IX_CASE(32, 128) ISA_IX_CASE(32, 64) ISA_IX_CASE(32, 32)
     ISA_IX_CASE(16, 128) ISA_IX_CASE(16, 64) ISA_IX_CASE(16, 32)

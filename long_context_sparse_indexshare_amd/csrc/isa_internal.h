@@ -9,6 +9,7 @@
 namespace isa {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -24,30 +25,39 @@ constexpr int TOPK_HIST_BINS = 1 << TOPK_HIST_BITS;
 constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bits
 
 struct TopkLayout {
-    size_t hist, cand_cnt, ticket, row_state, count_above, chunk_off, cand, total;
+    size_t hist, cand_cnt, row_state, count_above, chunk_off, cand, total;
     int rows, nchunks;
     uint32_t cap;
 };
 TopkLayout topk_layout(int rows, int L_cap);
 
-// Attention split geometry.
+// Attention split geometry; the workspace of one call holds the partials.
 struct AttendPlan {
-    int splits;        // workgroups per (query, head block) along the k slots
+    int splits;            // workgroups per (query, head block, column part) along the k slots
     int slots_per_split;
-    int head_blocks;   // 32-head blocks per workgroup (2 for 576-wide rows, 1 for 160-wide)
-    size_t partial_bytes;
+    int head_blocks;       // 32-head blocks per workgroup
+    int col_parts;         // value-column parts (workgroups) per head block
+    size_t part_o_off, part_ml_off, partial_bytes;   // 0 bytes when not split
 };
-AttendPlan attend_plan(int B, int Tq, int H, int D_v, int k);
+AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k);
 
 // Launchers (host side; argument checking happens in the API layer).
+hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream);
+// hist != NULL: also add each row's first-digit histogram of the visible
+// scores to hist[row][TOPK_HIST_BINS] (zeroed beforehand); only when
+// indexer_fuses_hist(H_I).
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
-                                 int L_cap, float* S, hipStream_t stream);
+                                 int L_cap, float* S, uint32_t* hist, hipStream_t stream);
+bool indexer_fuses_hist(int H_I);
+// counters_clear: the caller already zeroed the first topk_layout().row_state bytes;
+// hist_ready: the histogram was already built (by the fused indexer)
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
-                              int k, int32_t* idx, void* ws, hipStream_t stream);
+                              int k, int32_t* idx, void* ws, bool counters_clear, bool hist_ready,
+                              hipStream_t stream);
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,
-                                    float sm_scale, uint16_t* out, float* lse, void* ws,
+                                    float sm_scale, uint16_t* out, float* lse, void* partials,
                                     hipStream_t stream);
 
 bool indexer_shape_supported(int H_I, int D_I);

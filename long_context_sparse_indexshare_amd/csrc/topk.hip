@@ -13,17 +13,20 @@
 //   1. hist:    every workgroup histograms the top 12 key bits of a 4096-score
 //               chunk in LDS and adds its non-zero bins to the row's global
 //               histogram.
-//   2. refine:  every workgroup finds the bin that holds the k-th key, counts
+//   2. classify: every workgroup finds the bin that holds the k-th key, counts
 //               its keys above that bin, and appends the keys that fall in the
-//               bin to a per-row candidate list (one atomic per workgroup).  The
-//               last workgroup of the row (ticket counter) resolves the exact
-//               threshold key T and the position cut-off among keys equal to T
-//               (two radix passes over the low 20 key bits, two over the
-//               position bits), then turns per-chunk selected counts into
-//               output offsets.  If the candidate list overflowed it re-reads
-//               the row instead.
-//   3. compact: every workgroup re-reads its chunk and writes the selected
+//               bin to a per-row candidate list (one atomic per workgroup).
+//   3. finish:  the exact threshold key T and the position cut-off among keys
+//               equal to T (two radix passes over the low 20 key bits, two over
+//               the position bits, on the candidates staged in LDS), and the
+//               output offset of every chunk.  With few rows every compact
+//               workgroup does this itself; with many, one workgroup per row.
+//               If the candidate list overflowed the row is re-read instead.
+//   4. compact: every workgroup re-reads its chunk and writes the selected
 //               positions, in order, at its offset.
+// Workgroups never wait on each other inside a kernel: on gfx950 a device-
+// scope fence writes back and invalidates the whole L2 of the XCD, so each
+// hand-over between workgroups goes through a kernel boundary instead.
 #include "isa_internal.h"
 
 namespace isa {
@@ -106,12 +109,16 @@ __device__ void find_bin(const uint32_t* h, uint32_t need, uint32_t* bin_out, ui
     __syncthreads();
 }
 
-// Zeroes the per-row counters (histograms, candidate counts, tickets) at the
-// start of every call, so the workspace needs no initialisation.  A fill
-// kernel rather than a memset keeps the call capturable in a HIP graph.
-__global__ __launch_bounds__(256) void topk_clear_kernel(uint4* __restrict__ p, size_t n16) {
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
-        p[i] = make_uint4(0, 0, 0, 0);
+// Zeroes counters (histograms, candidate counts, tickets) at the start of a
+// call, so workspaces need no initialisation.  A fill kernel rather than a
+// memset keeps calls capturable in a HIP graph.
+__global__ __launch_bounds__(256) void clear_u32_kernel(uint32_t* __restrict__ p, size_t n) {
+    const size_t n4 = n / 4;
+    uint4* p4 = reinterpret_cast<uint4*>(p);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
+        p4[i] = make_uint4(0, 0, 0, 0);
+    for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = 0u;
 }
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_hist_kernel(const float* __restrict__ S,
@@ -147,12 +154,22 @@ struct RowState {
     uint32_t pad;
 };
 
-// Calls f(key, pos) for every key in the threshold bin: from the candidate
-// list, or by re-reading the row when the list overflowed.
+// Candidates the finishing workgroup stages in LDS (more fall back to global).
+constexpr int CAND_LDS = 6144;
+
+// Calls f(key, pos) for every key in the threshold bin: from the copy of the
+// candidate list staged in LDS, from the list in global memory, or by
+// re-reading the row when the list overflowed.
 template <class F>
-__device__ __forceinline__ void for_each_candidate(bool overflow, const uint2* cand, uint32_t nc,
-                                                   const float* rowp, int n, uint32_t bin, F f) {
-    if (!overflow) {
+__device__ __forceinline__ void for_each_candidate(int mode, const uint2* lcand, const uint2* cand,
+                                                   uint32_t nc, const float* rowp, int n,
+                                                   uint32_t bin, F f) {
+    if (mode == 0) {
+        for (uint32_t i = threadIdx.x; i < nc; i += TOPK_THREADS) {
+            const uint2 c = lcand[i];
+            f(c.x, (int)c.y);
+        }
+    } else if (mode == 1) {
         for (uint32_t i = threadIdx.x; i < nc; i += TOPK_THREADS) {
             const uint2 c = cand[i];
             f(c.x, (int)c.y);
@@ -165,11 +182,45 @@ __device__ __forceinline__ void for_each_candidate(bool overflow, const uint2* c
     }
 }
 
-__global__ __launch_bounds__(TOPK_THREADS) void topk_refine_kernel(
+// The bin of the first digit that holds the k-th key, and the number of
+// keys in the bins above it, from the row's global histogram.
+__device__ void threshold_bin(const uint32_t* gh, int k, uint32_t* sh, uint32_t* sh_waves,
+                              uint32_t* sh_res, uint32_t* bin1, uint32_t* above1) {
+    const int tid = threadIdx.x;
+    // the histogram has 4096 bins; scan it in two halves of 2048 through LDS
+    // (each half: 8 independent loads in flight per thread)
+    auto stage_half = [&](const uint32_t* src) {
+        uint32_t v[2048 / TOPK_THREADS];
+#pragma unroll
+        for (int u = 0; u < 2048 / TOPK_THREADS; ++u) v[u] = src[u * TOPK_THREADS + tid];
+#pragma unroll
+        for (int u = 0; u < 2048 / TOPK_THREADS; ++u) sh[u * TOPK_THREADS + tid] = v[u];
+    };
+    stage_half(gh + 2048);
+    __syncthreads();
+    uint32_t hi_local = 0;
+    for (int i = tid; i < 2048; i += TOPK_THREADS) hi_local += sh[i];
+    uint32_t hi_total;
+    block_exclusive_scan(hi_local, &hi_total, sh_waves);
+    if (hi_total >= (uint32_t)k) {
+        find_bin<8, true>(sh, (uint32_t)k, bin1, above1, sh_waves, sh_res);
+        *bin1 += 2048;
+    } else {
+        __syncthreads();
+        stage_half(gh);
+        __syncthreads();
+        find_bin<8, true>(sh, (uint32_t)k - hi_total, bin1, above1, sh_waves, sh_res);
+        *above1 += hi_total;
+    }
+}
+
+// Classify: every workgroup counts its chunk's keys above the threshold bin
+// and appends the keys inside it to the row's candidate list (one atomic per
+// workgroup reserves its slots).
+__global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ cand_cnt, uint32_t* __restrict__ ticket,
-    RowState* __restrict__ row_state, uint32_t* __restrict__ count_above,
-    uint32_t* __restrict__ chunk_off, uint2* __restrict__ cand, uint32_t cap, int nchunks_max) {
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ cand_cnt,
+    uint32_t* __restrict__ count_above, uint2* __restrict__ cand, uint32_t cap, int nchunks_max) {
     const int row = blockIdx.y;
     const int n = visible_count(kv_len, row, Tq, L_cap);
     if (n <= k) return;
@@ -177,37 +228,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_refine_kernel(
     const int c = blockIdx.x;
     if (c >= nch) return;
     const int tid = threadIdx.x;
-
-    __shared__ uint32_t sh[2048 + 512];          // histograms, then chunk counts
+    __shared__ uint32_t sh[2048];
     __shared__ uint32_t sh_waves[TOPK_THREADS / 64];
     __shared__ uint32_t sh_res[4];
     __shared__ uint32_t sh_base;
-    __shared__ int sh_last;
 
-    uint32_t* gh = hist + (size_t)row * TOPK_HIST_BINS;
-    // the row histogram has 4096 bins; reduce it in two halves of 2048 through LDS
     uint32_t bin1, above1;
-    {
-        // upper half first: bins 2048..4095
-        for (int i = tid; i < 2048; i += TOPK_THREADS) sh[i] = gh[2048 + i];
-        __syncthreads();
-        uint32_t hi_total_local = 0;
-        for (int i = tid; i < 2048; i += TOPK_THREADS) hi_total_local += sh[i];
-        uint32_t hi_total;
-        block_exclusive_scan(hi_total_local, &hi_total, sh_waves);
-        if (hi_total >= (uint32_t)k) {
-            find_bin<8, true>(sh, (uint32_t)k, &bin1, &above1, sh_waves, sh_res);
-            bin1 += 2048;
-        } else {
-            __syncthreads();
-            for (int i = tid; i < 2048; i += TOPK_THREADS) sh[i] = gh[i];
-            __syncthreads();
-            find_bin<8, true>(sh, (uint32_t)k - hi_total, &bin1, &above1, sh_waves, sh_res);
-            above1 += hi_total;
-        }
-    }
+    threshold_bin(hist + (size_t)row * TOPK_HIST_BINS, k, sh, sh_waves, sh_res, &bin1, &above1);
 
-    // classify this chunk's keys
     const float* rowp = S + (size_t)row * L_cap;
     const int start = c * TOPK_CHUNK;
     uint32_t keys[TOPK_PER_THREAD];
@@ -215,10 +243,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_refine_kernel(
 #pragma unroll
     for (int e = 0; e < TOPK_PER_THREAD; ++e) {
         const int s = start + e * TOPK_THREADS + tid;
-        const uint32_t key = s < n ? score_key(rowp[s]) : 0u;
+        const bool valid = s < n;
+        const uint32_t key = valid ? score_key(rowp[s]) : 0u;
         keys[e] = key;
         const uint32_t d = key >> (32 - TOPK_HIST_BITS);
-        const bool valid = s < n;
         n_above += (valid && d > bin1) ? 1u : 0u;
         n_cand += (valid && d == bin1) ? 1u : 0u;
     }
@@ -231,104 +259,156 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_refine_kernel(
         sh_base = cand_total ? atomicAdd(&cand_cnt[row], cand_total) : 0u;
     }
     __syncthreads();
-    {
-        uint32_t slot = sh_base + cand_before;
-        uint2* rc = cand + (size_t)row * cap;
+    uint32_t slot = sh_base + cand_before;
+    uint2* rc = cand + (size_t)row * cap;
 #pragma unroll
-        for (int e = 0; e < TOPK_PER_THREAD; ++e) {
-            const int s = start + e * TOPK_THREADS + tid;
-            if (s < n && (keys[e] >> (32 - TOPK_HIST_BITS)) == bin1) {
-                if (slot < cap) rc[slot] = make_uint2(keys[e], (uint32_t)s);
-                ++slot;
-            }
+    for (int e = 0; e < TOPK_PER_THREAD; ++e) {
+        const int s = start + e * TOPK_THREADS + tid;
+        if (s < n && (keys[e] >> (32 - TOPK_HIST_BITS)) == bin1) {
+            if (slot < cap) rc[slot] = make_uint2(keys[e], (uint32_t)s);
+            ++slot;
         }
     }
-    // publish, then let the last workgroup of the row finish it
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sh_last = atomicAdd(&ticket[row], 1u) == (uint32_t)(nch - 1);
-    __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
+}
 
-    const uint32_t nc = __hip_atomic_load(&cand_cnt[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool overflow = nc > cap;
+// LDS of the finishing step.
+struct FinishShared {
+    uint32_t sh[2048 + 512];          // digit histograms, then per-chunk counts / offsets
+    uint2 lcand[CAND_LDS];            // the row's candidates
+    uint32_t waves[TOPK_THREADS / 64];
+    uint32_t res[4];
+};
+
+// Finish a row: the exact k-th key T, the last selected position s_cut
+// among keys equal to T, and the output offset of every chunk, left in
+// f.sh[0..nch).  Needs the histogram, the candidate list and count_above of
+// the classify step.
+__device__ void finish_row(int row, int n, int k, int L_cap, const float* S,
+                           const uint32_t* hist, const uint32_t* cand_cnt, const uint2* cand,
+                           uint32_t cap, const uint32_t* count_above, int nchunks_max,
+                           FinishShared& f, RowState* st_out) {
+    const int tid = threadIdx.x;
+    const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+    const float* rowp = S + (size_t)row * L_cap;
+    uint32_t bin1, above1;
+    threshold_bin(hist + (size_t)row * TOPK_HIST_BINS, k, f.sh, f.waves, f.res, &bin1, &above1);
+    const uint32_t nc = cand_cnt[row];
     const uint2* rc = cand + (size_t)row * cap;
+    const int mode = nc <= (uint32_t)CAND_LDS ? 0 : (nc <= cap ? 1 : 2);
+    if (mode == 0) {
+        // stage the candidates: 8 independent loads in flight per thread
+        for (uint32_t base = 0; base < nc; base += 8 * TOPK_THREADS) {
+            uint2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t i = base + u * TOPK_THREADS + tid;
+                v[u] = i < nc ? rc[i] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t i = base + u * TOPK_THREADS + tid;
+                if (i < nc) f.lcand[i] = v[u];
+            }
+        }
+        __syncthreads();
+    }
+    uint32_t* sh = f.sh;
     uint32_t need = (uint32_t)k - above1;       // >= 1 keys still to take from the bin
 
     // key bits [19:10]
     for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
     __syncthreads();
-    for_each_candidate(overflow, rc, nc, rowp, n, bin1,
+    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1,
                        [&](uint32_t key, int) { atomicAdd(&sh[(key >> 10) & 1023u], 1u); });
     __syncthreads();
     uint32_t d2, above2;
-    find_bin<4, true>(sh, need, &d2, &above2, sh_waves, sh_res);
+    find_bin<4, true>(sh, need, &d2, &above2, f.waves, f.res);
     need -= above2;
     const uint32_t pre22 = (bin1 << 10) | d2;
     // key bits [9:0]
     for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
     __syncthreads();
-    for_each_candidate(overflow, rc, nc, rowp, n, bin1, [&](uint32_t key, int) {
+    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int) {
         if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
     });
     __syncthreads();
     uint32_t d3, above3;
-    find_bin<4, true>(sh, need, &d3, &above3, sh_waves, sh_res);
+    find_bin<4, true>(sh, need, &d3, &above3, f.waves, f.res);
     need -= above3;                              // keys equal to T still to take (>= 1)
     const uint32_t T = (pre22 << 10) | d3;
     // among keys equal to T, the need-th lowest position: position bits [20:10], then [9:0]
     for (int i = tid; i < 2048; i += TOPK_THREADS) sh[i] = 0;
     __syncthreads();
-    for_each_candidate(overflow, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
+    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
         if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
     });
     __syncthreads();
     uint32_t p2, below2;
-    find_bin<8, false>(sh, need, &p2, &below2, sh_waves, sh_res);
+    find_bin<8, false>(sh, need, &p2, &below2, f.waves, f.res);
     need -= below2;
     for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
     __syncthreads();
-    for_each_candidate(overflow, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
+    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
         if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
     });
     __syncthreads();
     uint32_t p3, below3;
-    find_bin<4, false>(sh, need, &p3, &below3, sh_waves, sh_res);
+    find_bin<4, false>(sh, need, &p3, &below3, f.waves, f.res);
     const int s_cut = (int)((p2 << 10) | p3);
 
-    // selected keys of the bin per chunk, then output offsets of every chunk
-    uint32_t* cc = sh;                          // nch <= 512 counters
-    for (int i = tid; i < nch; i += TOPK_THREADS) cc[i] = 0;
+    // selected keys of the bin per chunk, plus the keys above it: exclusive
+    // prefix over the chunks = each chunk's output offset (nch <= 512)
+    for (int i = tid; i < nch; i += TOPK_THREADS) sh[i] = 0;
     __syncthreads();
-    for_each_candidate(overflow, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
-        if (key > T || (key == T && s <= s_cut)) atomicAdd(&cc[s / TOPK_CHUNK], 1u);
+    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
+        if (key > T || (key == T && s <= s_cut)) atomicAdd(&sh[s / TOPK_CHUNK], 1u);
     });
     __syncthreads();
     {
         const uint32_t* ca = count_above + (size_t)row * nchunks_max;
-        // each thread owns two consecutive chunks (nch <= 512)
         const int c0 = 2 * tid, c1 = 2 * tid + 1;
-        const uint32_t v0 = c0 < nch ? cc[c0] + ca[c0] : 0u;
-        const uint32_t v1 = c1 < nch ? cc[c1] + ca[c1] : 0u;
+        const uint32_t v0 = c0 < nch ? sh[c0] + ca[c0] : 0u;
+        const uint32_t v1 = c1 < nch ? sh[c1] + ca[c1] : 0u;
         uint32_t tot;
-        const uint32_t ex = block_exclusive_scan(v0 + v1, &tot, sh_waves);
-        uint32_t* co = chunk_off + (size_t)row * nchunks_max;
-        if (c0 < nch) co[c0] = ex;
-        if (c1 < nch) co[c1] = ex + v0;
+        const uint32_t ex = block_exclusive_scan(v0 + v1, &tot, f.waves);   // barriers inside
+        if (c0 < nch) sh[c0] = ex;
+        if (c1 < nch) sh[c1] = ex + v0;
     }
-    if (tid == 0) {
-        RowState st;
-        st.bin = bin1;
-        st.T = T;
-        st.s_cut = s_cut;
-        st.pad = 0;
-        row_state[row] = st;
-    }
+    __syncthreads();
+    st_out->bin = bin1;
+    st_out->T = T;
+    st_out->s_cut = s_cut;
+    st_out->pad = 0;
 }
 
+// Finish kernel (many rows): one workgroup per row writes the row's state and
+// chunk offsets for the compact step.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
+    const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
+    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ cand_cnt,
+    const uint32_t* __restrict__ count_above, const uint2* __restrict__ cand, uint32_t cap,
+    int nchunks_max, RowState* __restrict__ row_state, uint32_t* __restrict__ chunk_off) {
+    const int row = blockIdx.x;
+    const int n = visible_count(kv_len, row, Tq, L_cap);
+    if (n <= k) return;
+    __shared__ FinishShared f;
+    RowState st;
+    finish_row(row, n, k, L_cap, S, hist, cand_cnt, cand, cap, count_above, nchunks_max, f, &st);
+    const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+    for (int i = threadIdx.x; i < nch; i += TOPK_THREADS)
+        chunk_off[(size_t)row * nchunks_max + i] = f.sh[i];
+    if (threadIdx.x == 0) row_state[row] = st;
+}
+
+// Compact: every workgroup re-reads its chunk and writes the selected
+// positions, in order, at the chunk's offset.  With SELF_FINISH (few rows)
+// each workgroup first finishes the row itself instead of reading the finish
+// kernel's results, which saves a launch.
+template <bool SELF_FINISH>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_compact_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
+    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ cand_cnt,
+    const uint32_t* __restrict__ count_above, const uint2* __restrict__ cand, uint32_t cap,
     const RowState* __restrict__ row_state, const uint32_t* __restrict__ chunk_off,
     int nchunks_max, int32_t* __restrict__ idx) {
     const int row = blockIdx.y;
@@ -345,7 +425,16 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_compact_kernel(
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
     if (c >= nch) return;
     __shared__ uint32_t sh_waves[TOPK_THREADS / 64];
-    const RowState st = row_state[row];
+    RowState st;
+    uint32_t off;
+    if constexpr (SELF_FINISH) {
+        __shared__ FinishShared f;
+        finish_row(row, n, k, L_cap, S, hist, cand_cnt, cand, cap, count_above, nchunks_max, f, &st);
+        off = f.sh[c];
+    } else {
+        st = row_state[row];
+        off = chunk_off[(size_t)row * nchunks_max + c];
+    }
     const float* rowp = S + (size_t)row * L_cap;
     const int first = c * TOPK_CHUNK + tid * TOPK_PER_THREAD;   // thread-contiguous run
     uint32_t selmask = 0, cnt = 0;
@@ -364,7 +453,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_compact_kernel(
         }
     }
     uint32_t total;
-    uint32_t pos = block_exclusive_scan(cnt, &total, sh_waves) + chunk_off[(size_t)row * nchunks_max + c];
+    uint32_t pos = block_exclusive_scan(cnt, &total, sh_waves) + off;
 #pragma unroll
     for (int e = 0; e < TOPK_PER_THREAD; ++e) {
         if (selmask & (1u << e)) {
@@ -394,7 +483,6 @@ TopkLayout topk_layout(int rows, int L_cap) {
     // counters zeroed at the start of every call come first
     L.hist = take((size_t)rows * TOPK_HIST_BINS * 4);
     L.cand_cnt = take((size_t)rows * 4);
-    L.ticket = take((size_t)rows * 4);
     // scratch overwritten by every call
     L.row_state = take((size_t)rows * sizeof(RowState));
     L.count_above = take((size_t)rows * L.nchunks * 4);
@@ -404,30 +492,51 @@ TopkLayout topk_layout(int rows, int L_cap) {
     return L;
 }
 
+hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n / 4 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
-                              int k, int32_t* idx, void* ws, hipStream_t stream) {
+                              int k, int32_t* idx, void* ws, bool counters_clear, bool hist_ready,
+                              hipStream_t stream) {
     const int rows = B * Tq;
     const TopkLayout L = topk_layout(rows, L_cap);
     char* base = static_cast<char*>(ws);
     uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
     uint32_t* cand_cnt = reinterpret_cast<uint32_t*>(base + L.cand_cnt);
-    uint32_t* ticket = reinterpret_cast<uint32_t*>(base + L.ticket);
     RowState* row_state = reinterpret_cast<RowState*>(base + L.row_state);
     uint32_t* count_above = reinterpret_cast<uint32_t*>(base + L.count_above);
     uint32_t* chunk_off = reinterpret_cast<uint32_t*>(base + L.chunk_off);
     uint2* cand = reinterpret_cast<uint2*>(base + L.cand);
-    const size_t n16 = L.row_state / 16;         // hist, cand_cnt and ticket precede row_state
-    const int clear_blocks = (int)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
-    hipLaunchKernelGGL(topk_clear_kernel, dim3(clear_blocks), dim3(256), 0, stream,
-                       reinterpret_cast<uint4*>(base), n16);
+    if (!counters_clear) {                      // hist and cand_cnt precede row_state
+        hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.row_state / 4, stream);
+        if (e != hipSuccess) return e;
+    }
     dim3 grid(L.nchunks, rows);
-    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq, L_cap,
-                       k, hist);
-    hipLaunchKernelGGL(topk_refine_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
-                       L_cap, k, hist, cand_cnt, ticket, row_state, count_above, chunk_off, cand,
-                       L.cap, L.nchunks);
-    hipLaunchKernelGGL(topk_compact_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
-                       L_cap, k, row_state, chunk_off, L.nchunks, idx);
+    if (!hist_ready)
+        hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
+                           L_cap, k, hist);
+    hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
+                       L_cap, k, hist, cand_cnt, count_above, cand, L.cap, L.nchunks);
+    // few rows: every compact workgroup finishes its row itself (one launch
+    // fewer); many rows: one finish workgroup per row
+    if ((size_t)rows * L.nchunks <= 2048) {
+        hipLaunchKernelGGL(topk_compact_kernel<true>, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len,
+                           Tq, L_cap, k, hist, cand_cnt, count_above, cand, L.cap, row_state,
+                           chunk_off, L.nchunks, idx);
+    } else {
+        hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(TOPK_THREADS), 0, stream, S,
+                           kv_len, Tq, L_cap, k, hist, cand_cnt, count_above, cand, L.cap,
+                           L.nchunks, row_state, chunk_off);
+        hipLaunchKernelGGL(topk_compact_kernel<false>, grid, dim3(TOPK_THREADS), 0, stream, S,
+                           kv_len, Tq, L_cap, k, hist, cand_cnt, count_above, cand, L.cap,
+                           row_state, chunk_off, L.nchunks, idx);
+    }
     return hipGetLastError();
 }
 

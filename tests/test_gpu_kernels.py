@@ -161,6 +161,14 @@ def test_attend_576(B, Tq, fill):
     _attend_case(B, Tq, 64, 576, 512, L_cap, k, idx, seed=B + Tq, name=f"576 B{B} Tq{Tq} fill{fill}")
 
 
+def test_attend_576_many_queries():
+    # >= 256 queries: one workgroup per query holds all 64 heads and columns
+    r = np.random.default_rng(12)
+    idx = _random_sets(2, 130, 9000, 128, 128, r)
+    idx[1, 5, 40:] = -1
+    _attend_case(2, 130, 64, 576, 512, 9000, 128, idx, seed=13, name="576 wide")
+
+
 def test_attend_160_16_heads():
     r = np.random.default_rng(7)
     idx = _random_sets(1, 50, 1024, 64, 64, r)
