@@ -1,6 +1,10 @@
 """Builds libisa.so (the HIP kernels and the C ABI) for gfx950, in place.
 
     python -m long_context_sparse_indexshare_amd.build
+
+Each source compiles to its own object (in parallel), so a source can carry
+code-generation flags of its own; the objects are then linked into one
+shared library.
 """
 from __future__ import annotations
 
@@ -8,37 +12,64 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libisa.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 math stays off: only scalar fp32 VALU forms are emitted
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
 
-def hipcc_command(out: str) -> list:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    return [
-        "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 math stays off: only scalar fp32 VALU forms are emitted
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
-        "-I", os.path.join(ROOT, "include"),
-        *srcs, "-o", out,
-    ]
+# The indexer's int32 MFMA results feed VALU math at once: with the
+# accumulators in VGPRs no accumulator-to-VGPR moves are needed per element.
+# (The attention kernels need AGPRs for their accumulators and keep the default.)
+PER_FILE = {
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+NOISE = "is not a recognized feature for this target"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
+def sources() -> list:
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def compile_command(src: str, obj: str) -> list:
+    return ["hipcc", *COMMON, *PER_FILE.get(os.path.basename(src), []),
+            "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+
+
+def link_command(objs: list, out: str) -> list:
+    return ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _run(cmd: list, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
+    err = "\n".join(l for l in (res.stderr or "").splitlines() if NOISE not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        for f in [ex.submit(_run, compile_command(s, o), verbose) for s, o in zip(srcs, objs)]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 

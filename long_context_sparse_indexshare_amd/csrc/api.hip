@@ -257,7 +257,7 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
         topk_clear = false;
         // with one query per indexer workgroup the indexer also builds the
         // top-k's first-digit histogram (the histogram leads the top-k scratch)
-        const bool fuse = isa::indexer_fuses_hist(a->H_I);
+        const bool fuse = isa::indexer_fuses_hist(a->H_I, a->Tq);
         uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(topk_ws) : nullptr;
         isa_status st = check_hip(isa::launch_indexer_scores(a->qI[l], a->w[l], a->kI[l], a->kv_len,
                                                              a->B, a->Tq, a->H_I, a->D_I, a->L_cap,

@@ -171,6 +171,109 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     }
 }
 
+// Many queries per sequence (prefill): every wave owns two queries (their
+// 2 x 64 head rows, four 32-row MFMA blocks, stay in registers) and streams
+// every key block up to its last visible key; the four waves of a workgroup
+// read the same key blocks at about the same time, so each key block comes
+// from HBM / L2 once per workgroup and from L1 for the other waves.  The
+// epilogue (ReLU, head weight, head sum) is the same as above.
+constexpr int PF_QPWAVE = 2;
+constexpr int PF_QPW = 4 * PF_QPWAVE;     // queries per workgroup
+constexpr int PF_MIN_TQ = 64;             // from this many queries per sequence on
+
+template <int D_I>
+__global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
+    const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
+    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S) {
+    constexpr int H_I = 64;
+    constexpr int KS = D_I / 32;
+    constexpr int RB = 2 * PF_QPWAVE;                 // 32-row blocks per wave
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane & 31;
+    const int g = lane >> 5;
+    const int b = blockIdx.y;
+    const int tw = blockIdx.x * PF_QPW + wave * PF_QPWAVE;   // first query of this wave
+    const int len = clamp_len(kv_len[b], L_cap);
+
+    // A operands: block rb holds heads 32*(rb%2) .. +32 of query tw + rb/2
+    v4i a[RB][KS];
+    float wr[RB][16];
+    int pos[PF_QPWAVE];
+#pragma unroll
+    for (int q = 0; q < PF_QPWAVE; ++q) pos[q] = tw + q < Tq ? len - Tq + tw + q : -1;
+    const int pos_max = max(pos[0], pos[PF_QPWAVE - 1]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int t = tw + rb / 2;
+        const bool tv = t < Tq;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            a[rb][ks] = tv ? *reinterpret_cast<const v4i*>(
+                                 qI + (((size_t)b * Tq + t) * H_I + 32 * (rb % 2) + j) * D_I +
+                                 32 * ks + 16 * g)
+                           : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int h = 32 * (rb % 2) + 8 * (r / 4) + 4 * g + (r % 4);
+            wr[rb][r] = tv ? w[((size_t)b * Tq + t) * H_I + h] : 0.0f;
+        }
+    }
+
+    auto load_keys = [&](int s0, v4i* bk) {
+        const int s = s0 + j;
+        const bool live = s0 <= pos_max && s < L_cap;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + ((size_t)b * L_cap + s) * D_I +
+                                                          32 * ks + 16 * g)
+                          : v4i{0, 0, 0, 0};
+        }
+    };
+
+    // scores of the 32 keys s0 .. s0+31 against both queries, from keys in bk
+    auto step = [&](int s0, const v4i* bk) {
+        const int s = s0 + j;
+        float sum[PF_QPWAVE];
+#pragma unroll
+        for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = 0.0f;
+        if (s0 <= pos_max) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                v16i acc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dot = acc[r];
+                    sum[rb / 2] += wr[rb][r] * (float)(dot > 0 ? dot : 0);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < PF_QPWAVE; ++q) sum[q] += __shfl_xor(sum[q], 32);
+        }
+        if (g == 0 && s < L_cap) {
+#pragma unroll
+            for (int q = 0; q < PF_QPWAVE; ++q) {
+                if (tw + q >= Tq) continue;                   // past the last query
+                S[((size_t)b * Tq + tw + q) * L_cap + s] = s <= pos[q] ? sum[q] : -__builtin_inff();
+            }
+        }
+    };
+
+    // two key buffers in turn: the next block is in flight while one is used
+    v4i k0[KS], k1[KS];
+    load_keys(0, k0);
+    for (int s0 = 0; s0 < L_cap; s0 += 64) {
+        load_keys(s0 + 32, k1);       // load_keys returns zeros past L_cap
+        step(s0, k0);
+        load_keys(s0 + 64, k0);
+        if (s0 + 32 < L_cap) step(s0 + 32, k1);
+    }
+}
+
 template <int H_I, int D_I>
 hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
                      int B, int Tq, int L_cap, float* S, uint32_t* hist, hipStream_t stream) {
@@ -184,6 +287,14 @@ hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const i
         }
     }
     if (hist) return hipErrorInvalidValue;
+    if constexpr (H_I == 64) {
+        if (Tq >= PF_MIN_TQ) {
+            dim3 pgrid((Tq + PF_QPW - 1) / PF_QPW, B);
+            hipLaunchKernelGGL((indexer_prefill_kernel<D_I>), pgrid, dim3(IX_THREADS), 0, stream, qI,
+                               w, kI, kv_len, Tq, L_cap, S);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I, false>), grid, dim3(IX_THREADS), 0, stream,
                        qI, w, kI, kv_len, Tq, L_cap, S, nullptr);
     return hipGetLastError();
@@ -197,7 +308,7 @@ bool indexer_shape_supported(int H_I, int D_I) {
     return h_ok && d_ok;
 }
 
-bool indexer_fuses_hist(int H_I) { return H_I == IX_ROWS; }
+bool indexer_fuses_hist(int H_I, int Tq) { return H_I == IX_ROWS && Tq < PF_MIN_TQ; }
 
 #define ISA_IX_CASE(HH, DD)                                                              \
     if (H_I == HH && D_I == DD)                                                          \

@@ -49,7 +49,7 @@ hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* hist, hipStream_t stream);
-bool indexer_fuses_hist(int H_I);
+bool indexer_fuses_hist(int H_I, int Tq);
 // counters_clear: the caller already zeroed the first topk_layout().row_state bytes;
 // hist_ready: the histogram was already built (by the fused indexer)
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,

@@ -33,6 +33,10 @@ INDEXER_CASES = [
     ("h16-d128", 1, 5, [3], 64, 16, 128),
     ("h32-d32", 2, 4, [129, 0], 130, 32, 32),
     ("short-ctx", 2, 6, [2, 9], 33, 64, 128),
+    # >= 64 queries per sequence take the prefill kernel (two queries per wave)
+    ("prefill-kv<Tq", 2, 65, [40, 1000], 1100, 64, 128),
+    ("prefill-d64", 1, 101, [3000], 3000, 64, 64),
+    ("prefill-d32", 2, 64, [64, 333], 350, 64, 32),
 ]
 
 
