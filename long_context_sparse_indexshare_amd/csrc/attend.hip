@@ -47,6 +47,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef __attribute__((address_space(3))) v4bf* lds_v4bf_ptr;
+// Gathers go through global-address-space pointers: a generic (flat) load
+// also counts against the LDS wait counter, so every LDS wait would stall on
+// the gathers still in flight.
+typedef const __attribute__((address_space(1))) v4u* global_v4u_ptr;
 
 // Largest slot range one workgroup takes (the whole set when not split).
 constexpr int MAX_SPLIT_SLOTS = 2048;
@@ -70,36 +74,39 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// Physical 16-byte chunk of logical chunk ch in LDS row r: the chunks of a
-// full aligned group of eight are permuted by (r/2)%8 (an involution); a
-// trailing partial group stays in place.
-template <int CH>
-__device__ __forceinline__ int swz(int r, int ch) {
-    return ((ch | 7) < CH) ? (ch ^ ((r >> 1) & 7)) : ch;
-}
-
 template <int HB, int VS, int D, int DV>
 struct AttendGeom {
     static constexpr int KSP = 4 / HB;              // waves sharing a head block (K split)
     static constexpr int KS = D / 16;               // k-steps of the QK product
     static constexpr int KSW = KS / KSP;            // k-steps per wave
     static constexpr int CH = D * 2 / 16;           // 16-byte chunks per latent row
-    static constexpr int ROWB = D * 2;              // LDS row bytes (unpadded, swizzled)
+    static constexpr int CROWB = D * 2;             // latent row bytes in HBM
+    // LDS row stride: one 16-byte pad per row puts the 16 rows a quarter-wave
+    // reads (same chunk, consecutive rows) in distinct 4-bank groups, and the
+    // transposing reads (4 rows x 32 bytes) in distinct banks too
+    static constexpr int ROWB = D * 2 + 16;
+    static_assert((ROWB / 4) % 8 == 4, "pad keeps row starts spread over the banks");
     static constexpr int COLS = DV / VS;            // value columns of the workgroup
     static constexpr int CW = COLS / KSP;           // value columns per wave
     static constexpr int NB = CW / 32;              // 32-column MFMA blocks per wave
     static constexpr int TILE_BYTES = TILE_ROWS * ROWB;
     static constexpr int TILE_CHUNKS = TILE_ROWS * CH;
     static constexpr int GPT = (TILE_CHUNKS + AT_THREADS - 1) / AT_THREADS;   // chunks per thread
-    // tiles in flight in registers while one is computed: two where the
-    // register budget allows (the decode variant), one for the wide variant
-    static constexpr int AHEAD = NB <= 4 ? 2 : 1;
+    // workgroups resident per CU: two where the accumulators are small
+    // enough for 256 registers per lane (one computes while the other waits
+    // on its gathers), else one
+    static constexpr int WG_PER_CU = NB <= 4 ? 2 : 1;
+    // tiles in flight in registers while one is computed
+    static constexpr int AHEAD = 1;
+    // QK accumulators per wave (two halve the dependent MFMA chain where
+    // registers allow)
+    static constexpr int QK_ACC = (WG_PER_CU == 2 && NB == 4) ? 1 : 2;
     static_assert(KS % KSP == 0, "the K split must divide the k-steps");
     static_assert(CW % 32 == 0, "value columns per wave");
 };
 
 template <int HB, int VS, int D, int DV>
-__global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
+__global__ __launch_bounds__(AT_THREADS, (AttendGeom<HB, VS, D, DV>::WG_PER_CU)) void sparse_attend_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const int32_t* __restrict__ idx,
     int Tq, int H, int L_cap, int k, float scale_log2, int slots_per_split, int splits,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
@@ -173,8 +180,8 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
             const int row_ = c_ / G::CH;                                                       \
             const int ch_ = c_ - row_ * G::CH;                                                 \
             const int s_ = sidx[(TS) - slot0 + row_];   /* -1 past the split (padded) */       \
-            const uintptr_t ra_ = cbase + (size_t)(s_ & ~(s_ >> 31)) * ROWB;                   \
-            R[i_] = *reinterpret_cast<const v4u*>((s_ >= 0 ? ra_ : zero_row) + ch_ * 16);      \
+            const uintptr_t ra_ = cbase + (size_t)(s_ & ~(s_ >> 31)) * G::CROWB;               \
+            R[i_] = *(global_v4u_ptr)((s_ >= 0 ? ra_ : zero_row) + ch_ * 16);                  \
         }                                                                                      \
     }
 #define ISA_STORE_TILE(R)                                                                      \
@@ -183,23 +190,31 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
         if (G::TILE_CHUNKS % AT_THREADS == 0 || c_ < G::TILE_CHUNKS) {                         \
             const int row_ = c_ / G::CH;                                                       \
             const int ch_ = c_ - row_ * G::CH;                                                 \
-            *reinterpret_cast<v4u*>(tile + row_ * ROWB + swz<G::CH>(row_, ch_) * 16) = R[i_];  \
+            *reinterpret_cast<v4u*>(tile + row_ * ROWB + ch_ * 16) = R[i_];                    \
         }                                                                                      \
     }
 
     // one tile of the online softmax attention, from the LDS tile
     auto compute_tile = [&](int tile_start) {
         // ---- partial S^T (32 rows x 32 heads) over this wave's k-steps
-        v16f st;
+        // two accumulators halve the dependent MFMA chain
+        v16f st, st2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+        for (int r = 0; r < 16; ++r) st[r] = st2[r] = 0.0f;
         const char* arow = tile + j * ROWB;
 #pragma unroll
         for (int i = 0; i < G::KSW; ++i) {
             const int ch = 2 * (kp * G::KSW + i) + g;
             const v8bf a = __builtin_bit_cast(
-                v8bf, *reinterpret_cast<const uint4*>(arow + swz<G::CH>(j, ch) * 16));
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i], st, 0, 0, 0);
+                v8bf, *reinterpret_cast<const uint4*>(arow + ch * 16));
+            if ((i & 1) && G::QK_ACC == 2)
+                st2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i], st2, 0, 0, 0);
+            else
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i], st, 0, 0, 0);
+        }
+        if (G::QK_ACC == 2) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[r] += st2[r];
         }
         // ---- sum the K-split partials of this head block, in kp order
 #pragma unroll
@@ -208,15 +223,28 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
                 make_float4(st[4 * r4], st[4 * r4 + 1], st[4 * r4 + 2], st[4 * r4 + 3]);
         lds_barrier();
         v16f s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-        for (int p = 0; p < G::KSP; ++p) {
-            const int w2 = p * HB + hbl;
+        if constexpr (G::KSP == 2) {
+            // own + partner: a sum of two is the same bits in either order
+            const int w2 = (1 - kp) * HB + hbl;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
-                s[4 * r4] += v.x; s[4 * r4 + 1] += v.y; s[4 * r4 + 2] += v.z; s[4 * r4 + 3] += v.w;
+                s[4 * r4] = st[4 * r4] + v.x;
+                s[4 * r4 + 1] = st[4 * r4 + 1] + v.y;
+                s[4 * r4 + 2] = st[4 * r4 + 2] + v.z;
+                s[4 * r4 + 3] = st[4 * r4 + 3] + v.w;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+            for (int p = 0; p < G::KSP; ++p) {
+                const int w2 = p * HB + hbl;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
+                    s[4 * r4] += v.x; s[4 * r4 + 1] += v.y; s[4 * r4 + 2] += v.z; s[4 * r4 + 3] += v.w;
+                }
             }
         }
         // register r holds tile row 8*(r/4) + 4*g + r%4, head j
@@ -231,13 +259,13 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         const float m_new = fmaxf(m_run, mloc);
         const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         m_run = m_new;
         float psum = 0.0f;
         v8bf pk[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = exp2f(s[r] - m_use);
+            const float p = __builtin_amdgcn_exp2f(s[r] - m_use);
             psum += p;
             pk[r / 8][r % 8] = (__bf16)p;
         }
@@ -256,10 +284,8 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
 #pragma unroll
             for (int nb = 0; nb < G::NB; ++nb) {
                 const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
-                const int sub = (col & 7) * 2;
-                const v4bf lo = lds_read_tr(tile, row * ROWB + swz<G::CH>(row, col >> 3) * 16 + sub);
-                const v4bf hi = lds_read_tr(tile, (row + 8) * ROWB +
-                                                      swz<G::CH>(row + 8, col >> 3) * 16 + sub);
+                const v4bf lo = lds_read_tr(tile, row * ROWB + col * 2);
+                const v4bf hi = lds_read_tr(tile, (row + 8) * ROWB + col * 2);
                 const v8bf a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[nb], 0, 0, 0);
             }
@@ -355,6 +381,8 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attend_kernel(
 
 // Combines the splits of one (query, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // in split order; column part p uses the (max, sum) its own workgroups wrote.
+// Every split's partial is requested before any is used (the loads are
+// independent, so their latencies overlap).
 template <int DV, int VS>
 __global__ __launch_bounds__(DV / 4) void merge_splits_kernel(const float* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml,
@@ -366,19 +394,31 @@ __global__ __launch_bounds__(DV / 4) void merge_splits_kernel(const float* __res
     const int h = qh - q * H;
     const int col = threadIdx.x * 4;
     const int vh = col / (DV / VS);
+    float2 ml[MAX_SPLITS];
+    float4 v[MAX_SPLITS];
+#pragma unroll
+    for (int sj = 0; sj < MAX_SPLITS; ++sj) {
+        if (sj < splits) {
+            ml[sj] = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + h];
+            v[sj] = *reinterpret_cast<const float4*>(part_o + (((size_t)q * splits + sj) * H + h) * DV + col);
+        } else {
+            ml[sj] = make_float2(-__builtin_inff(), 0.0f);
+            v[sj] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
     float M = -__builtin_inff();
-    for (int sj = 0; sj < splits; ++sj)
-        M = fmaxf(M, part_ml[(((size_t)q * splits + sj) * VS + vh) * H + h].x);
+#pragma unroll
+    for (int sj = 0; sj < MAX_SPLITS; ++sj) M = fmaxf(M, ml[sj].x);
     const float Mu = M == -__builtin_inff() ? 0.0f : M;
     float L = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sj = 0; sj < splits; ++sj) {
-        const float2 ml = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + h];
-        const float wgt = exp2f(ml.x - Mu);
-        L += wgt * ml.y;
-        const float4 v = *reinterpret_cast<const float4*>(
-            part_o + (((size_t)q * splits + sj) * H + h) * DV + col);
-        acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+#pragma unroll
+    for (int sj = 0; sj < MAX_SPLITS; ++sj) {
+        if (sj < splits) {
+            const float wgt = exp2f(ml[sj].x - Mu);
+            L += wgt * ml[sj].y;
+            acc.x += wgt * v[sj].x; acc.y += wgt * v[sj].y; acc.z += wgt * v[sj].z; acc.w += wgt * v[sj].w;
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     ushort4 r;
@@ -417,12 +457,15 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k) {
     // columns per workgroup (their QK work is duplicated, their gathers meet
     // in L2), and the k slots split across workgroups
     const bool wide = nq >= 256 || D != 576;
-    p.head_blocks = wide ? 2 : 1;
+    p.head_blocks = 2;
     p.col_parts = wide ? 1 : 2;
     const int n_hbg = (H + 32 * p.head_blocks - 1) / (32 * p.head_blocks);
     const int units = nq * n_hbg * p.col_parts;
     const int tiles = (k + TILE_ROWS - 1) / TILE_ROWS;
-    int splits = units >= 256 ? 1 : (256 + units - 1) / units;
+    // enough workgroups for every resident slot: 256 CUs, two workgroups per
+    // CU for the decode variant
+    const int target = wide ? 256 : 512;
+    int splits = units >= target ? 1 : (target + units - 1) / units;
     if (splits > MAX_SPLITS) splits = MAX_SPLITS;
     if (splits > tiles) splits = tiles;
     const int tiles_per_split = (tiles + splits - 1) / splits;
@@ -453,10 +496,10 @@ hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const 
                                     hipStream_t stream) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
     if (D == 576 && D_v == 512) {
-        if (plan.head_blocks == 2)
+        if (plan.col_parts == 1)
             return launch_attend<2, 1, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
                                                  partials, stream);
-        return launch_attend<1, 2, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+        return launch_attend<2, 2, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
                                              partials, stream);
     }
     if (D == 160 && D_v == 128)
