@@ -111,15 +111,19 @@ def time_group(isa, calls, steps, warmup, torch):
 
 
 def time_per_launch(fn, n, torch):
-    """Average device duration of fn's launches, one event pair per launch."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    for a, b in ev:
-        a.record()
-        fn()
-        b.record()
+    """Average device duration of fn's launches: n launches back to back on the
+    launch stream between one pair of HIP events (the events' own overhead is
+    spread over the n launches)."""
+    fn()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / 1e3 / n
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / n
 
 
 def stage_times(isa, inst, wl, torch, reps=20):
@@ -178,6 +182,64 @@ def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
     return tokens, dt, results
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scores_C2_128K_traffic.txt")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per indexer launch from the committed counter summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "csrc", "indexer.hip")
+    if kv.get("source_sha256", "").strip() != source_digest(src):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def run_stage(isa, wl, stage, reps, torch):
+    """One stage alone on one input instance, for profiler runs (one JSON line)."""
+    import synth
+    d = synth.group_inputs(wl, device="cuda")
+    S = torch.empty((wl.B, wl.Tq, wl.L_cap), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+    ws = isa.Workspace()
+    if stage == "indexer":
+        # a 1 GiB device copy first: its counters calibrate the traffic figures
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"], S=S)
+    isa.isa_topk_select(S, d["kv_len"], wl.k, idx=idx, ws=ws)
+    torch.cuda.synchronize()
+    fns = {
+        "indexer": lambda: isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"], S=S),
+        "topk": lambda: isa.isa_topk_select(S, d["kv_len"], wl.k, idx=idx, ws=ws),
+        "attend": lambda: isa.isa_sparse_mla_attend(d["Q"][0], d["C"][0], idx, wl.D_v,
+                                                    wl.sm_scale, out=out, ws=ws),
+    }
+    if stage == "group":
+        call = isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], d["C"], wl.k,
+                             wl.D_v, wl.sm_scale, ws=ws)
+        fn = call
+    else:
+        fn = fns[stage]
+    t = time_per_launch(fn, reps, torch)
+    print(json.dumps({"stage": stage, "workload": wl.name, "reps": reps, "avg_us": t * 1e6}),
+          flush=True)
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -231,6 +293,11 @@ def main():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group"],
+                    help="profiling mode: run one stage of --workload --reps times and print "
+                         "its average launch time instead of the benchmark line")
+    ap.add_argument("--workload", default="C2_128K")
+    ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -246,6 +313,9 @@ def main():
         __graft_entry__.build()
     isa.load_library()
     torch.cuda.set_device(0)
+    if args.stage:
+        run_stage(isa, synth.WORKLOADS[args.workload], args.stage, args.reps, torch)
+        return
 
     # reference: what a plain device copy reaches on this machine (context for the
     # roofline fractions, which use the published 8 TB/s)
@@ -284,7 +354,7 @@ def main():
                    "input_instances": args.instances},
         "roofline": {"kernel": "indexer_scores", "bound": "hbm",
                      "achieved": ix_achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": ix_achieved / PEAK_HBM, "traffic": None},
+                     "frac": ix_achieved / PEAK_HBM, "traffic": measured_traffic()},
         "group_roofline": {"t_ideal_us": alg["t_ideal_s"] * 1e6, "t_measured_us": t * 1e6,
                            "frac": alg["t_ideal_s"] / t,
                            "algorithmic_bytes": alg["group_bytes"],
