@@ -121,7 +121,7 @@ GroupLayout group_layout(const isa_group_args* a) {
     L.topk_zero_bytes = 0;
     if (L.need_index) {
         const isa::TopkLayout tl = isa::topk_layout((int)rows, a->L_cap);
-        L.topk_zero_bytes = tl.row_state;            // hist and cand_cnt come first
+        L.topk_zero_bytes = tl.zero_bytes;           // the counters come first
         off += round_up(tl.total);
     }
     L.scores = off;
@@ -146,7 +146,7 @@ isa_status isa_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI
     isa_status st = check_indexer(qI, w, kI, kv_len, B, Tq, H_I, D_I, L_cap, S);
     if (st != ISA_OK) return st;
     return check_hip(isa::launch_indexer_scores(qI, w, kI, kv_len, B, Tq, H_I, D_I, L_cap, S,
-                                                nullptr, static_cast<hipStream_t>(stream)),
+                                                nullptr, 0, static_cast<hipStream_t>(stream)),
                      "indexer launch");
 }
 
@@ -163,7 +163,7 @@ isa_status isa_topk_select(const float* S, const int32_t* kv_len, int B, int Tq,
     const size_t need = isa_topk_workspace_bytes(B, Tq, L_cap, k);
     ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
               "topk: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
-    return check_hip(isa::launch_topk_select(S, kv_len, B, Tq, L_cap, k, idx, ws, false, false,
+    return check_hip(isa::launch_topk_select(S, kv_len, B, Tq, L_cap, k, idx, ws, false,
                                              static_cast<hipStream_t>(stream)),
                      "topk launch");
 }
@@ -238,34 +238,18 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
     float* S = reinterpret_cast<float*>(ws + L.scores);
     void* topk_ws = ws + L.topk;
     void* attend_ws = ws + L.attend;
-    // one fill kernel zeroes the top-k counters (histograms, candidate counts)
-    if (L.need_index) {
-        isa_status st = check_hip(isa::launch_clear_u32(reinterpret_cast<uint32_t*>(topk_ws),
-                                                        L.topk_zero_bytes / 4, stream),
-                                  "group: clear launch");
-        if (st != ISA_OK) return st;
-    }
-    bool topk_clear = true;
+    // each index set: the indexer grid also zeroes the top-k counters
+    // (histograms, entry counts), then the top-k runs
     auto index = [&](int l) -> isa_status {
-        if (!topk_clear) {
-            // a second index set in the same call (per-layer indexers): clear again
-            isa_status st = check_hip(isa::launch_clear_u32(reinterpret_cast<uint32_t*>(topk_ws),
-                                                            L.topk_zero_bytes / 4, stream),
-                                      "group: clear launch");
-            if (st != ISA_OK) return st;
-        }
-        topk_clear = false;
-        // with one query per indexer workgroup the indexer also builds the
-        // top-k's first-digit histogram (the histogram leads the top-k scratch)
-        const bool fuse = isa::indexer_fuses_hist(a->H_I, a->Tq);
-        uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(topk_ws) : nullptr;
         isa_status st = check_hip(isa::launch_indexer_scores(a->qI[l], a->w[l], a->kI[l], a->kv_len,
                                                              a->B, a->Tq, a->H_I, a->D_I, a->L_cap,
-                                                             S, hist, stream),
+                                                             S, reinterpret_cast<uint32_t*>(topk_ws),
+                                                             (uint32_t)(L.topk_zero_bytes / 4),
+                                                             stream),
                                   "group: indexer launch");
         if (st != ISA_OK) return st;
         return check_hip(isa::launch_topk_select(S, a->kv_len, a->B, a->Tq, a->L_cap, a->k, a->idx,
-                                                 topk_ws, true, fuse, stream),
+                                                 topk_ws, true, stream),
                          "group: topk launch");
     };
     if (L.need_index && !per_layer) {

@@ -15,10 +15,7 @@
 // registers plus one cross-lane swap; blocks past the last visible key of
 // every query in the workgroup skip the loads and write -inf.  Each wave
 // keeps the next key block's loads in flight while it computes the current
-// one.  With one query per workgroup the kernel can also build the top-k's
-// first-digit histogram (top 12 bits of the order-preserving image of each
-// visible score) in LDS and add it to the row's global histogram, sparing
-// the top-k a pass over the scores.
+// one.
 #include "isa_internal.h"
 
 namespace isa {
@@ -32,23 +29,24 @@ constexpr int IX_KEYS_PER_WG = IX_KEYS_PER_STEP * IX_STEPS;
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
-// Order-preserving 32-bit image of a score (larger score, larger key; -0 = +0).
-__device__ __forceinline__ uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// Zeroes zero[0, zero_n) with the whole grid (the next launch's counters; it
+// saves that launch a fill kernel of its own).
+__device__ __forceinline__ void grid_clear(uint32_t* __restrict__ zero, uint32_t zero_n) {
+    if (zero_n == 0) return;
+    const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t nwg = gridDim.x * gridDim.y * gridDim.z;
+    for (uint32_t i = wg * IX_THREADS + threadIdx.x; i < zero_n; i += nwg * IX_THREADS) zero[i] = 0u;
 }
 
-template <int H_I, int D_I, bool HIST>
+template <int H_I, int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
     const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ zero, uint32_t zero_n) {
+    grid_clear(zero, zero_n);
     constexpr int QPW = IX_ROWS / H_I;             // queries per workgroup
     constexpr int KS = D_I / 32;                   // MFMA k-steps over the indexer dim
     constexpr int NQL = H_I >= 8 ? 64 / H_I : 8;   // query slots held per lane
-    static_assert(!HIST || QPW == 1, "the fused histogram needs one query per workgroup");
-    __shared__ uint32_t lh[HIST ? TOPK_HIST_BINS : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane & 31;
@@ -58,9 +56,6 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int len = clamp_len(kv_len[b], L_cap);
     const int t_last = min(t0 + QPW, Tq) - 1;
     const int pos_max = len - Tq + t_last;          // last key any query here can see
-    if (HIST) {
-        for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += IX_THREADS) lh[i] = 0;
-    }
 
     // A operands: row m = 32*rb + j is (query m / H_I, head m % H_I); k bytes 32*ks + 16*g .. +16.
     v4i a[2][KS];
@@ -91,7 +86,6 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
             wr[rb][r] = t < Tq ? w[((size_t)b * Tq + t) * H_I + (m % H_I)] : 0.0f;
         }
     }
-    if (HIST) __syncthreads();                      // histogram zeroed
 
     // B operands of one 32-key block: lane (key s0 + j, half g) holds k bytes 32*ks + 16*g .. +16
     auto load_keys = [&](int s0, v4i* bk) {
@@ -155,18 +149,8 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
                 const int t = t0 + qt;
                 if (t >= Tq) continue;
                 const int pos = len - Tq + t;
-                const bool vis = s <= pos;
-                S[((size_t)b * Tq + t) * L_cap + s] = vis ? sum[q] : -__builtin_inff();
-                if (HIST && vis) atomicAdd(&lh[score_key(sum[q]) >> (32 - TOPK_HIST_BITS)], 1u);
+                S[((size_t)b * Tq + t) * L_cap + s] = s <= pos ? sum[q] : -__builtin_inff();
             }
-        }
-    }
-    if (HIST) {
-        __syncthreads();
-        uint32_t* gh = hist + ((size_t)b * Tq + t0) * TOPK_HIST_BINS;
-        for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += IX_THREADS) {
-            const uint32_t c = lh[i];
-            if (c) atomicAdd(&gh[i], c);
         }
     }
 }
@@ -184,7 +168,9 @@ constexpr int PF_MIN_TQ = 64;             // from this many queries per sequence
 template <int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
-    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S) {
+    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
+    uint32_t* __restrict__ zero, uint32_t zero_n) {
+    grid_clear(zero, zero_n);
     constexpr int H_I = 64;
     constexpr int KS = D_I / 32;
     constexpr int RB = 2 * PF_QPWAVE;                 // 32-row blocks per wave
@@ -276,27 +262,20 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
 
 template <int H_I, int D_I>
 hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
-                     int B, int Tq, int L_cap, float* S, uint32_t* hist, hipStream_t stream) {
+                     int B, int Tq, int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
+                     hipStream_t stream) {
     constexpr int QPW = IX_ROWS / H_I;
     dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
-    if constexpr (QPW == 1) {
-        if (hist) {
-            hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I, true>), grid, dim3(IX_THREADS), 0,
-                               stream, qI, w, kI, kv_len, Tq, L_cap, S, hist);
-            return hipGetLastError();
-        }
-    }
-    if (hist) return hipErrorInvalidValue;
     if constexpr (H_I == 64) {
         if (Tq >= PF_MIN_TQ) {
             dim3 pgrid((Tq + PF_QPW - 1) / PF_QPW, B);
             hipLaunchKernelGGL((indexer_prefill_kernel<D_I>), pgrid, dim3(IX_THREADS), 0, stream, qI,
-                               w, kI, kv_len, Tq, L_cap, S);
+                               w, kI, kv_len, Tq, L_cap, S, zero, zero_n);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I, false>), grid, dim3(IX_THREADS), 0, stream,
-                       qI, w, kI, kv_len, Tq, L_cap, S, nullptr);
+    hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I>), grid, dim3(IX_THREADS), 0, stream,
+                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n);
     return hipGetLastError();
 }
 
@@ -308,15 +287,14 @@ bool indexer_shape_supported(int H_I, int D_I) {
     return h_ok && d_ok;
 }
 
-bool indexer_fuses_hist(int H_I, int Tq) { return H_I == IX_ROWS && Tq < PF_MIN_TQ; }
-
 #define ISA_IX_CASE(HH, DD)                                                              \
     if (H_I == HH && D_I == DD)                                                          \
-        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, hist, stream);
+        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, zero, zero_n, stream);
 
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
-                                 int L_cap, float* S, uint32_t* hist, hipStream_t stream) {
+                                 int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
+                                 hipStream_t stream) {
     ISA_IX_CASE(64, 128) ISA_IX_CASE(64, 64) ISA_IX_CASE(64, 32)
     ISA_IX_CASE(32, 128) ISA_IX_CASE(32, 64) ISA_IX_CASE(32, 32)
     ISA_IX_CASE(16, 128) ISA_IX_CASE(16, 64) ISA_IX_CASE(16, 32)

@@ -25,9 +25,10 @@ constexpr int TOPK_HIST_BINS = 1 << TOPK_HIST_BITS;
 constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bits
 
 struct TopkLayout {
-    size_t hist, cand_cnt, row_state, count_above, chunk_off, cand, total;
+    size_t hist, hist2, alloc, zero_bytes;   // counters: [0, zero_bytes) is cleared per call
+    size_t row_state, runs, ent, total;
     int rows, nchunks;
-    uint32_t cap;
+    uint32_t cap;                     // entries per row in the entry buffer
 };
 TopkLayout topk_layout(int rows, int L_cap);
 
@@ -43,17 +44,15 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k);
 
 // Launchers (host side; argument checking happens in the API layer).
 hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream);
-// hist != NULL: also add each row's first-digit histogram of the visible
-// scores to hist[row][TOPK_HIST_BINS] (zeroed beforehand); only when
-// indexer_fuses_hist(H_I).
+// zero[0, zero_n): words the indexer grid also sets to 0 (the top-k counters of
+// the group call that follows), or zero_n = 0
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
-                                 int L_cap, float* S, uint32_t* hist, hipStream_t stream);
-bool indexer_fuses_hist(int H_I, int Tq);
-// counters_clear: the caller already zeroed the first topk_layout().row_state bytes;
-// hist_ready: the histogram was already built (by the fused indexer)
+                                 int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
+                                 hipStream_t stream);
+// counters_clear: the caller already zeroed the first topk_layout().zero_bytes
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
-                              int k, int32_t* idx, void* ws, bool counters_clear, bool hist_ready,
+                              int k, int32_t* idx, void* ws, bool counters_clear,
                               hipStream_t stream);
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,

@@ -9,24 +9,24 @@
 // Radix select on the order-preserving 32-bit image of each score, spread
 // over many workgroups per query so one long row (up to 2^21 positions) uses
 // the whole chip:
-//   0. clear:   zero the row counters in the workspace.
-//   1. hist:    every workgroup histograms the top 12 key bits of a 4096-score
-//               chunk in LDS and adds its non-zero bins to the row's global
-//               histogram.
-//   2. classify: every workgroup finds the bin that holds the k-th key, counts
-//               its keys above that bin, and appends the keys that fall in the
-//               bin to a per-row candidate list (one atomic per workgroup).
-//   3. finish:  the exact threshold key T and the position cut-off among keys
-//               equal to T (two radix passes over the low 20 key bits, two over
-//               the position bits, on the candidates staged in LDS), and the
-//               output offset of every chunk.  With few rows every compact
-//               workgroup does this itself; with many, one workgroup per row.
-//               If the candidate list overflowed the row is re-read instead.
-//   4. compact: every workgroup re-reads its chunk and writes the selected
-//               positions, in order, at its offset.
+//   0. clear:    zero the row counters in the workspace (a fill kernel).
+//   1. hist:     every workgroup histograms the top 12 key bits of a
+//                4096-score chunk in LDS and adds its non-zero bins to the
+//                row's global histogram.
+//   2. classify: every workgroup finds the bin that holds the k-th key and
+//                keeps its chunk's keys at or above that bin as one run of
+//                (key, position) entries in ascending position.
+//   3. finish:   one workgroup per row finds the exact k-th key T and the
+//                position cut among keys equal to T (radix passes over the
+//                entries of the threshold bin), then writes the selected
+//                positions as the ordered stream compaction of the runs taken
+//                chunk by chunk.  If the entry buffer overflowed (a very flat
+//                score distribution) the row's scores are re-read instead.
 // Workgroups never wait on each other inside a kernel: on gfx950 a device-
 // scope fence writes back and invalidates the whole L2 of the XCD, so each
 // hand-over between workgroups goes through a kernel boundary instead.
+#include <type_traits>
+
 #include "isa_internal.h"
 
 namespace isa {
@@ -51,7 +51,7 @@ __device__ __forceinline__ int visible_count(const int32_t* kv_len, int row, int
 }
 
 // Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh_waves) {
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh_waves) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     uint32_t inc = v;
@@ -76,11 +76,11 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* 
 
 // Over bins h[0..nbins) (nbins = 256 * per): the largest bin B with
 // sum_{b >= B} h[b] >= need (descending) or the smallest bin B with
-// sum_{b <= B} h[b] >= need (ascending).  Returns B and the count strictly
-// beyond it (above for descending, below for ascending) to every thread.
+// sum_{b <= B} h[b] >= need (ascending).  Returns (B, the count strictly
+// beyond it: above for descending, below for ascending) to every thread.
 template <int PER, bool DESC>
-__device__ void find_bin(const uint32_t* h, uint32_t need, uint32_t* bin_out, uint32_t* beyond_out,
-                         uint32_t* sh_waves, uint32_t* sh_res) {
+__device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint32_t* sh_waves,
+                                          uint32_t* sh_res) {
     const int tid = threadIdx.x;
     // thread t owns bins [PER*t, PER*t + PER) ascending, or the mirrored range descending
     const int first = DESC ? (TOPK_THREADS - 1 - tid) * PER : tid * PER;
@@ -104,9 +104,9 @@ __device__ void find_bin(const uint32_t* h, uint32_t need, uint32_t* bin_out, ui
         }
     }
     __syncthreads();
-    *bin_out = sh_res[0];
-    *beyond_out = sh_res[1];
+    const uint2 r = make_uint2(sh_res[0], sh_res[1]);
     __syncthreads();
+    return r;
 }
 
 // Zeroes counters (histograms, candidate counts, tickets) at the start of a
@@ -147,80 +147,30 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_hist_kernel(const float* __
     }
 }
 
+// Entries the finishing workgroup stages in LDS (more are read from global).
+constexpr int ENT_LDS = 12288;
+constexpr int STAGE_PER_THREAD = ENT_LDS / TOPK_THREADS;   // all staging loads in flight at once
+constexpr int HIST2_BINS = 1024;                            // second digit: key bits [19:10]
+
 struct RowState {
-    uint32_t bin;     // first-digit bin of the k-th key
-    uint32_t T;       // exact k-th key
-    int32_t s_cut;    // last selected position among keys equal to T
-    uint32_t pad;
+    uint32_t bin1;     // first-digit bin of the k-th key
+    uint32_t above1;   // keys in the bins above it
 };
 
-// Candidates the finishing workgroup stages in LDS (more fall back to global).
-constexpr int CAND_LDS = 6144;
-
-// Calls f(key, pos) for every key in the threshold bin: from the copy of the
-// candidate list staged in LDS, from the list in global memory, or by
-// re-reading the row when the list overflowed.
-template <class F>
-__device__ __forceinline__ void for_each_candidate(int mode, const uint2* lcand, const uint2* cand,
-                                                   uint32_t nc, const float* rowp, int n,
-                                                   uint32_t bin, F f) {
-    if (mode == 0) {
-        for (uint32_t i = threadIdx.x; i < nc; i += TOPK_THREADS) {
-            const uint2 c = lcand[i];
-            f(c.x, (int)c.y);
-        }
-    } else if (mode == 1) {
-        for (uint32_t i = threadIdx.x; i < nc; i += TOPK_THREADS) {
-            const uint2 c = cand[i];
-            f(c.x, (int)c.y);
-        }
-    } else {
-        for (int s = threadIdx.x; s < n; s += TOPK_THREADS) {
-            const uint32_t key = score_key(rowp[s]);
-            if ((key >> (32 - TOPK_HIST_BITS)) == bin) f(key, s);
-        }
-    }
-}
-
-// The bin of the first digit that holds the k-th key, and the number of
-// keys in the bins above it, from the row's global histogram.
-__device__ void threshold_bin(const uint32_t* gh, int k, uint32_t* sh, uint32_t* sh_waves,
-                              uint32_t* sh_res, uint32_t* bin1, uint32_t* above1) {
-    const int tid = threadIdx.x;
-    // the histogram has 4096 bins; scan it in two halves of 2048 through LDS
-    // (each half: 8 independent loads in flight per thread)
-    auto stage_half = [&](const uint32_t* src) {
-        uint32_t v[2048 / TOPK_THREADS];
-#pragma unroll
-        for (int u = 0; u < 2048 / TOPK_THREADS; ++u) v[u] = src[u * TOPK_THREADS + tid];
-#pragma unroll
-        for (int u = 0; u < 2048 / TOPK_THREADS; ++u) sh[u * TOPK_THREADS + tid] = v[u];
-    };
-    stage_half(gh + 2048);
-    __syncthreads();
-    uint32_t hi_local = 0;
-    for (int i = tid; i < 2048; i += TOPK_THREADS) hi_local += sh[i];
-    uint32_t hi_total;
-    block_exclusive_scan(hi_local, &hi_total, sh_waves);
-    if (hi_total >= (uint32_t)k) {
-        find_bin<8, true>(sh, (uint32_t)k, bin1, above1, sh_waves, sh_res);
-        *bin1 += 2048;
-    } else {
-        __syncthreads();
-        stage_half(gh);
-        __syncthreads();
-        find_bin<8, true>(sh, (uint32_t)k - hi_total, bin1, above1, sh_waves, sh_res);
-        *above1 += hi_total;
-    }
-}
-
-// Classify: every workgroup counts its chunk's keys above the threshold bin
-// and appends the keys inside it to the row's candidate list (one atomic per
-// workgroup reserves its slots).
+// Classify: every workgroup finds the first-digit bin that holds the k-th key
+// (one pass over the row's histogram) and keeps the keys of its 4096-score
+// chunk whose first digit is at or above that bin as one run of (key,
+// position) entries in ascending position.  One atomic per workgroup reserves
+// the run in the row's entry buffer; the runs of a row tile [0, total) with no
+// gaps, and runs[row][chunk] records where each chunk's run starts and how
+// long it is.  The candidates (keys inside the threshold bin) also go into a
+// second-digit histogram of the row, and the chunk-0 workgroup records the
+// threshold bin for the finishing step.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ hist, uint32_t* __restrict__ cand_cnt,
-    uint32_t* __restrict__ count_above, uint2* __restrict__ cand, uint32_t cap, int nchunks_max) {
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ hist2, uint32_t* __restrict__ alloc,
+    RowState* __restrict__ row_state, uint2* __restrict__ runs, uint2* __restrict__ ent,
+    uint32_t cap, int nchunks_max) {
     const int row = blockIdx.y;
     const int n = visible_count(kv_len, row, Tq, L_cap);
     if (n <= k) return;
@@ -228,239 +178,336 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     const int c = blockIdx.x;
     if (c >= nch) return;
     const int tid = threadIdx.x;
-    __shared__ uint32_t sh[2048];
-    __shared__ uint32_t sh_waves[TOPK_THREADS / 64];
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    constexpr int NW = TOPK_THREADS / 64;
+    __shared__ uint32_t lh2[HIST2_BINS];
+    __shared__ uint32_t sh_waves[NW];
     __shared__ uint32_t sh_res[4];
+    __shared__ uint32_t sh_cnt[TOPK_PER_THREAD][NW];   // then the exclusive offsets
     __shared__ uint32_t sh_base;
 
-    uint32_t bin1, above1;
-    threshold_bin(hist + (size_t)row * TOPK_HIST_BINS, k, sh, sh_waves, sh_res, &bin1, &above1);
-
+    for (int i = tid; i < HIST2_BINS; i += TOPK_THREADS) lh2[i] = 0;
+    // this chunk's scores, in flight while the threshold bin is found
+    // (position = start + e * 256 + tid: ascending order is (e, wave, lane))
     const float* rowp = S + (size_t)row * L_cap;
     const int start = c * TOPK_CHUNK;
+    float sc[TOPK_PER_THREAD];
+#pragma unroll
+    for (int e = 0; e < TOPK_PER_THREAD; ++e) {
+        const int s = start + e * TOPK_THREADS + tid;
+        sc[e] = s < n ? rowp[s] : 0.0f;
+    }
+    const uint2 th =
+        find_bin<TOPK_HIST_BINS / TOPK_THREADS, true>(hist + (size_t)row * TOPK_HIST_BINS,
+                                                      (uint32_t)k, sh_waves, sh_res);
+    const uint32_t bin1 = th.x;
+    if (c == 0 && tid == 0) row_state[row] = RowState{bin1, th.y};
+
     uint32_t keys[TOPK_PER_THREAD];
-    uint32_t n_above = 0, n_cand = 0;
+    uint64_t kept[TOPK_PER_THREAD];
 #pragma unroll
     for (int e = 0; e < TOPK_PER_THREAD; ++e) {
         const int s = start + e * TOPK_THREADS + tid;
         const bool valid = s < n;
-        const uint32_t key = valid ? score_key(rowp[s]) : 0u;
-        keys[e] = key;
-        const uint32_t d = key >> (32 - TOPK_HIST_BITS);
-        n_above += (valid && d > bin1) ? 1u : 0u;
-        n_cand += (valid && d == bin1) ? 1u : 0u;
-    }
-    uint32_t above_total;
-    block_exclusive_scan(n_above, &above_total, sh_waves);
-    uint32_t cand_total;
-    const uint32_t cand_before = block_exclusive_scan(n_cand, &cand_total, sh_waves);
-    if (tid == 0) {
-        count_above[(size_t)row * nchunks_max + c] = above_total;
-        sh_base = cand_total ? atomicAdd(&cand_cnt[row], cand_total) : 0u;
+        keys[e] = valid ? score_key(sc[e]) : 0u;
+        const uint32_t d = keys[e] >> (32 - TOPK_HIST_BITS);
+        const bool keep = valid && d >= bin1;
+        if (valid && d == bin1) atomicAdd(&lh2[(keys[e] >> 10) & (HIST2_BINS - 1)], 1u);
+        kept[e] = __ballot(keep);
+        if (lane == 0) sh_cnt[e][wave] = (uint32_t)__popcll(kept[e]);
     }
     __syncthreads();
-    uint32_t slot = sh_base + cand_before;
-    uint2* rc = cand + (size_t)row * cap;
+    if (wave == 0) {
+        // exclusive scan of the 64 (e, wave) counts in ascending-position order
+        const uint32_t v = sh_cnt[lane / NW][lane % NW];
+        uint32_t inc = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += o;
+        }
+        const uint32_t total = __shfl(inc, 63, 64);
+        sh_cnt[lane / NW][lane % NW] = inc - v;
+        if (lane == 0) {
+            const uint32_t base = total ? atomicAdd(&alloc[row], total) : 0u;
+            sh_base = base;
+            runs[(size_t)row * nchunks_max + c] = make_uint2(base, total);
+        }
+    }
+    __syncthreads();
+    const uint32_t base = sh_base;
+    uint2* re = ent + (size_t)row * cap;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int e = 0; e < TOPK_PER_THREAD; ++e) {
-        const int s = start + e * TOPK_THREADS + tid;
-        if (s < n && (keys[e] >> (32 - TOPK_HIST_BITS)) == bin1) {
-            if (slot < cap) rc[slot] = make_uint2(keys[e], (uint32_t)s);
-            ++slot;
+        if ((kept[e] >> lane) & 1ull) {
+            const uint32_t slot = base + sh_cnt[e][wave] + (uint32_t)__popcll(kept[e] & below);
+            if (slot < cap) re[slot] = make_uint2(keys[e], (uint32_t)(start + e * TOPK_THREADS + tid));
         }
+    }
+    uint32_t* gh2 = hist2 + (size_t)row * HIST2_BINS;
+    for (int i = tid; i < HIST2_BINS; i += TOPK_THREADS) {
+        const uint32_t v = lh2[i];
+        if (v) atomicAdd(&gh2[i], v);
     }
 }
 
 // LDS of the finishing step.
+constexpr int COL_MAX = 512;              // entries ranked directly for the exact cut
 struct FinishShared {
-    uint32_t sh[2048 + 512];          // digit histograms, then per-chunk counts / offsets
-    uint2 lcand[CAND_LDS];            // the row's candidates
+    uint32_t sh[2048];                    // digit histograms; then per-chunk selected counts
+    uint32_t cbase[TOPK_MAX_CHUNKS];      // chunk -> first entry of its run
+    uint32_t clen[TOPK_MAX_CHUNKS];       // chunk -> run length
+    uint2 lent[ENT_LDS];                  // the row's entries, in allocation order
+    uint2 col[COL_MAX];                   // entries that share the cut's 22-bit key prefix
+    uint32_t ncol;
     uint32_t waves[TOPK_THREADS / 64];
     uint32_t res[4];
 };
 
-// Finish a row: the exact k-th key T, the last selected position s_cut
-// among keys equal to T, and the output offset of every chunk, left in
-// f.sh[0..nch).  Needs the histogram, the candidate list and count_above of
-// the classify step.
-__device__ void finish_row(int row, int n, int k, int L_cap, const float* S,
-                           const uint32_t* hist, const uint32_t* cand_cnt, const uint2* cand,
-                           uint32_t cap, const uint32_t* count_above, int nchunks_max,
-                           FinishShared& f, RowState* st_out) {
-    const int tid = threadIdx.x;
-    const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-    const float* rowp = S + (size_t)row * L_cap;
-    uint32_t bin1, above1;
-    threshold_bin(hist + (size_t)row * TOPK_HIST_BINS, k, f.sh, f.waves, f.res, &bin1, &above1);
-    const uint32_t nc = cand_cnt[row];
-    const uint2* rc = cand + (size_t)row * cap;
-    const int mode = nc <= (uint32_t)CAND_LDS ? 0 : (nc <= cap ? 1 : 2);
-    if (mode == 0) {
-        // stage the candidates: 8 independent loads in flight per thread
-        for (uint32_t base = 0; base < nc; base += 8 * TOPK_THREADS) {
-            uint2 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t i = base + u * TOPK_THREADS + tid;
-                v[u] = i < nc ? rc[i] : make_uint2(0u, 0u);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t i = base + u * TOPK_THREADS + tid;
-                if (i < nc) f.lcand[i] = v[u];
-            }
-        }
-        __syncthreads();
-    }
-    uint32_t* sh = f.sh;
-    uint32_t need = (uint32_t)k - above1;       // >= 1 keys still to take from the bin
-
-    // key bits [19:10]
-    for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
-    __syncthreads();
-    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1,
-                       [&](uint32_t key, int) { atomicAdd(&sh[(key >> 10) & 1023u], 1u); });
-    __syncthreads();
-    uint32_t d2, above2;
-    find_bin<4, true>(sh, need, &d2, &above2, f.waves, f.res);
-    need -= above2;
-    const uint32_t pre22 = (bin1 << 10) | d2;
-    // key bits [9:0]
-    for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
-    __syncthreads();
-    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int) {
-        if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
-    });
-    __syncthreads();
-    uint32_t d3, above3;
-    find_bin<4, true>(sh, need, &d3, &above3, f.waves, f.res);
-    need -= above3;                              // keys equal to T still to take (>= 1)
-    const uint32_t T = (pre22 << 10) | d3;
-    // among keys equal to T, the need-th lowest position: position bits [20:10], then [9:0]
-    for (int i = tid; i < 2048; i += TOPK_THREADS) sh[i] = 0;
-    __syncthreads();
-    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
-        if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
-    });
-    __syncthreads();
-    uint32_t p2, below2;
-    find_bin<8, false>(sh, need, &p2, &below2, f.waves, f.res);
-    need -= below2;
-    for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
-    __syncthreads();
-    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
-        if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
-    });
-    __syncthreads();
-    uint32_t p3, below3;
-    find_bin<4, false>(sh, need, &p3, &below3, f.waves, f.res);
-    const int s_cut = (int)((p2 << 10) | p3);
-
-    // selected keys of the bin per chunk, plus the keys above it: exclusive
-    // prefix over the chunks = each chunk's output offset (nch <= 512)
-    for (int i = tid; i < nch; i += TOPK_THREADS) sh[i] = 0;
-    __syncthreads();
-    for_each_candidate(mode, f.lcand, rc, nc, rowp, n, bin1, [&](uint32_t key, int s) {
-        if (key > T || (key == T && s <= s_cut)) atomicAdd(&sh[s / TOPK_CHUNK], 1u);
-    });
-    __syncthreads();
-    {
-        const uint32_t* ca = count_above + (size_t)row * nchunks_max;
-        const int c0 = 2 * tid, c1 = 2 * tid + 1;
-        const uint32_t v0 = c0 < nch ? sh[c0] + ca[c0] : 0u;
-        const uint32_t v1 = c1 < nch ? sh[c1] + ca[c1] : 0u;
-        uint32_t tot;
-        const uint32_t ex = block_exclusive_scan(v0 + v1, &tot, f.waves);   // barriers inside
-        if (c0 < nch) sh[c0] = ex;
-        if (c1 < nch) sh[c1] = ex + v0;
-    }
-    __syncthreads();
-    st_out->bin = bin1;
-    st_out->T = T;
-    st_out->s_cut = s_cut;
-    st_out->pad = 0;
-}
-
-// Finish kernel (many rows): one workgroup per row writes the row's state and
-// chunk offsets for the compact step.
+// Finish: one workgroup per row.  From the threshold bin and the candidates'
+// second-digit histogram it knows the 22-bit prefix of the k-th key; the few
+// entries with that prefix are ranked directly under (key desc, position asc)
+// to give the exact k-th key T and the last selected position s_cut among keys
+// equal to T (radix passes over key bits [9:0] and position bits [20:10],
+// [9:0] take over when very many keys share the prefix).  Then every wave
+// takes whole chunks: it counts their selected entries, the counts are
+// scanned over the chunks, and it writes each chunk's selected positions at
+// the chunk's offset in ascending order (the runs are ascending).  If the
+// entry buffer overflowed, the row's scores are re-read instead.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ cand_cnt,
-    const uint32_t* __restrict__ count_above, const uint2* __restrict__ cand, uint32_t cap,
-    int nchunks_max, RowState* __restrict__ row_state, uint32_t* __restrict__ chunk_off) {
+    const uint32_t* __restrict__ hist2, const uint32_t* __restrict__ alloc,
+    const RowState* __restrict__ row_state, const uint2* __restrict__ runs,
+    const uint2* __restrict__ ent, uint32_t cap, int nchunks_max, int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
-    const int n = visible_count(kv_len, row, Tq, L_cap);
-    if (n <= k) return;
-    __shared__ FinishShared f;
-    RowState st;
-    finish_row(row, n, k, L_cap, S, hist, cand_cnt, cand, cap, count_above, nchunks_max, f, &st);
-    const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-    for (int i = threadIdx.x; i < nch; i += TOPK_THREADS)
-        chunk_off[(size_t)row * nchunks_max + i] = f.sh[i];
-    if (threadIdx.x == 0) row_state[row] = st;
-}
-
-// Compact: every workgroup re-reads its chunk and writes the selected
-// positions, in order, at the chunk's offset.  With SELF_FINISH (few rows)
-// each workgroup first finishes the row itself instead of reading the finish
-// kernel's results, which saves a launch.
-template <bool SELF_FINISH>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_compact_kernel(
-    const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ cand_cnt,
-    const uint32_t* __restrict__ count_above, const uint2* __restrict__ cand, uint32_t cap,
-    const RowState* __restrict__ row_state, const uint32_t* __restrict__ chunk_off,
-    int nchunks_max, int32_t* __restrict__ idx) {
-    const int row = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    constexpr int NW = TOPK_THREADS / 64;
     const int n = visible_count(kv_len, row, Tq, L_cap);
     int32_t* out = idx + (size_t)row * k;
-    const int c = blockIdx.x;
-    const int tid = threadIdx.x;
     if (n <= k) {
-        // every visible position, then -1 padding (k <= 2048 < one chunk)
-        if (c == 0)
-            for (int j = tid; j < k; j += TOPK_THREADS) out[j] = j < n ? j : -1;
+        // every visible position, then -1 padding
+        for (int j = tid; j < k; j += TOPK_THREADS) out[j] = j < n ? j : -1;
         return;
     }
+    __shared__ FinishShared f;
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-    if (c >= nch) return;
-    __shared__ uint32_t sh_waves[TOPK_THREADS / 64];
-    RowState st;
-    uint32_t off;
-    if constexpr (SELF_FINISH) {
-        __shared__ FinishShared f;
-        finish_row(row, n, k, L_cap, S, hist, cand_cnt, cand, cap, count_above, nchunks_max, f, &st);
-        off = f.sh[c];
-    } else {
-        st = row_state[row];
-        off = chunk_off[(size_t)row * nchunks_max + c];
-    }
     const float* rowp = S + (size_t)row * L_cap;
-    const int first = c * TOPK_CHUNK + tid * TOPK_PER_THREAD;   // thread-contiguous run
-    uint32_t selmask = 0, cnt = 0;
+    const uint2* re = ent + (size_t)row * cap;
+    // every load of this phase is issued before any is used: the row state,
+    // the second-digit histogram, the chunk table and the entries (entries
+    // past the row's total are loaded but never used; they lie inside the
+    // row's buffer)
+    const RowState rs = row_state[row];
+    const uint32_t total = alloc[row];
+    uint32_t h2[HIST2_BINS / TOPK_THREADS];
 #pragma unroll
-    for (int e = 0; e < TOPK_PER_THREAD; ++e) {
-        const int s = first + e;
-        if (s < n) {
-            const uint32_t key = score_key(rowp[s]);
-            const uint32_t d = key >> (32 - TOPK_HIST_BITS);
-            const bool sel = d > st.bin ||
-                             (d == st.bin && (key > st.T || (key == st.T && s <= st.s_cut)));
-            if (sel) {
-                selmask |= 1u << e;
-                ++cnt;
+    for (int u = 0; u < HIST2_BINS / TOPK_THREADS; ++u)
+        h2[u] = hist2[(size_t)row * HIST2_BINS + u * TOPK_THREADS + tid];
+    const int c0 = 2 * tid, c1 = 2 * tid + 1;
+    const uint2 r0 = c0 < nch ? runs[(size_t)row * nchunks_max + c0] : make_uint2(0u, 0u);
+    const uint2 r1 = c1 < nch ? runs[(size_t)row * nchunks_max + c1] : make_uint2(0u, 0u);
+    const uint32_t nstage = cap < (uint32_t)ENT_LDS ? cap : (uint32_t)ENT_LDS;
+    uint2 v[STAGE_PER_THREAD];
+#pragma unroll
+    for (int u = 0; u < STAGE_PER_THREAD; ++u) {
+        const uint32_t i = u * TOPK_THREADS + tid;
+        v[u] = i < nstage ? re[i] : make_uint2(0u, 0u);
+    }
+    const uint32_t bin1 = rs.bin1;
+    // 0: entries staged in LDS; 1: read from the entry buffer; 2: buffer overflowed, re-read S
+    const int mode = total <= (uint32_t)ENT_LDS ? 0 : (total <= cap ? 1 : 2);
+    if (mode == 0) {
+#pragma unroll
+        for (int u = 0; u < STAGE_PER_THREAD; ++u) {
+            const uint32_t i = u * TOPK_THREADS + tid;
+            if (i < total) f.lent[i] = v[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < HIST2_BINS / TOPK_THREADS; ++u) f.sh[u * TOPK_THREADS + tid] = h2[u];
+    if (c0 < nch) { f.cbase[c0] = r0.x; f.clen[c0] = r0.y; }
+    if (c1 < nch) { f.cbase[c1] = r1.x; f.clen[c1] = r1.y; }
+    if (tid == 0) f.ncol = 0;
+    __syncthreads();
+
+    // f(key, pos) for every candidate of the threshold bin
+    auto for_each_cand = [&](auto fn) {
+        if (mode == 0) {
+            for (uint32_t i = tid; i < total; i += TOPK_THREADS) {
+                const uint2 e = f.lent[i];
+                if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
+            }
+        } else if (mode == 1) {
+            for (uint32_t i = tid; i < total; i += TOPK_THREADS) {
+                const uint2 e = re[i];
+                if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
+            }
+        } else {
+            for (int s = tid; s < n; s += TOPK_THREADS) {
+                const uint32_t key = score_key(rowp[s]);
+                if ((key >> (32 - TOPK_HIST_BITS)) == bin1) fn(key, s);
             }
         }
-    }
-    uint32_t total;
-    uint32_t pos = block_exclusive_scan(cnt, &total, sh_waves) + off;
-#pragma unroll
-    for (int e = 0; e < TOPK_PER_THREAD; ++e) {
-        if (selmask & (1u << e)) {
-            if (pos < (uint32_t)k) out[pos] = first + e;   // the offsets sum to exactly k
-            ++pos;
+    };
+
+    uint32_t* sh = f.sh;
+    uint32_t need = (uint32_t)k - rs.above1;     // >= 1 keys still to take from the bin
+    // key bits [19:10]: from the second-digit histogram the classify step built
+    const uint2 r2 = find_bin<HIST2_BINS / TOPK_THREADS, true>(sh, need, f.waves, f.res);
+    need -= r2.y;                                // >= 1 keys to take among the prefix group
+    const uint32_t pre22 = (bin1 << 10) | r2.x;
+    // the entries with that 22-bit prefix
+    for_each_cand([&](uint32_t key, int s) {
+        if ((key >> 10) == pre22) {
+            const uint32_t slot = atomicAdd(&f.ncol, 1u);
+            if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key, (uint32_t)s);
         }
+    });
+    __syncthreads();
+    const uint32_t m = f.ncol;
+    uint32_t T;
+    int s_cut;
+    if (m <= (uint32_t)COL_MAX) {
+        // rank every collected entry under (key desc, position asc); the one of
+        // rank need-1 is the last selected: its key is T, its position s_cut
+        for (uint32_t t = tid; t < m; t += TOPK_THREADS) {
+            const uint2 e = f.col[t];
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < m; ++j) {
+                const uint2 o = f.col[j];
+                rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
+            }
+            if (rank == need - 1) { f.res[2] = e.x; f.res[3] = e.y; }
+        }
+        __syncthreads();
+        T = f.res[2];
+        s_cut = (int)f.res[3];
+    } else {
+        // key bits [9:0]
+        for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int) {
+            if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
+        });
+        __syncthreads();
+        const uint2 r3 = find_bin<4, true>(sh, need, f.waves, f.res);
+        need -= r3.y;                            // keys equal to T still to take (>= 1)
+        T = (pre22 << 10) | r3.x;
+        // among keys equal to T, the need-th lowest position: position bits [20:10], then [9:0]
+        for (int i = tid; i < 2048; i += TOPK_THREADS) sh[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int s) {
+            if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
+        });
+        __syncthreads();
+        const uint2 q2 = find_bin<8, false>(sh, need, f.waves, f.res);
+        const uint32_t p2 = q2.x;
+        need -= q2.y;
+        for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int s) {
+            if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
+        });
+        __syncthreads();
+        const uint32_t p3 = find_bin<4, false>(sh, need, f.waves, f.res).x;
+        s_cut = (int)((p2 << 10) | p3);
     }
+    __syncthreads();
+
+    // selected: a key above T, or equal to T at a position <= s_cut (keys of
+    // higher first-digit bins are above T).  Evaluated without branches: the
+    // compiler lost the value of a conditionally written position on the
+    // short-circuit form of this test.
+    auto sel_of = [&](uint32_t key, uint32_t s) -> uint32_t {
+        return (uint32_t)(key > T) | ((uint32_t)(key == T) & (uint32_t)(s <= (uint32_t)s_cut));
+    };
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    if (mode == 2) {
+        // overflow: ordered stream compaction over the row's scores
+        constexpr int PER = 8;
+        constexpr int TILE = PER * TOPK_THREADS;
+        uint32_t written = 0;
+        for (uint32_t t0 = 0; t0 < (uint32_t)n; t0 += TILE) {
+            const uint32_t v0 = t0 + (uint32_t)tid * PER;
+            uint32_t selmask = 0;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const uint32_t vv = v0 + u;
+                const uint32_t in = vv < (uint32_t)n ? 1u : 0u;
+                const uint32_t key = in ? score_key(rowp[vv]) : 0u;
+                selmask |= (in & sel_of(key, vv)) << u;
+            }
+            uint32_t tile_total;
+            uint32_t o = written +
+                         block_exclusive_scan((uint32_t)__popc(selmask), &tile_total, f.waves);
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                if ((selmask >> u) & 1u) {
+                    if (o < (uint32_t)k) out[o] = (int32_t)(v0 + u);   // exactly k are selected
+                    ++o;
+                }
+            }
+            written += tile_total;
+        }
+        return;
+    }
+
+    // chunk-wise compaction: a wave per chunk; the LDS and global entry
+    // sources are separate instantiations so that no load goes through a
+    // generic pointer
+    auto compact = [&](auto source) {
+        constexpr bool LDS = decltype(source)::value;
+        auto get = [&](uint32_t a) -> uint2 {
+            if constexpr (LDS) return f.lent[a];
+            else return re[a];
+        };
+        // 1. selected entries per chunk
+        for (int c = wave; c < nch; c += NW) {
+            const uint32_t base = f.cbase[c], len = f.clen[c];
+            uint32_t cnt = 0;
+            for (uint32_t j0 = 0; j0 < len; j0 += 128) {
+                const uint32_t ja = j0 + lane, jb = j0 + 64 + lane;
+                const uint2 ea = get(base + (ja < len ? ja : 0u));
+                const uint2 eb = get(base + (jb < len ? jb : 0u));
+                const uint32_t sa = (uint32_t)(ja < len) & sel_of(ea.x, ea.y);
+                const uint32_t sb = (uint32_t)(jb < len) & sel_of(eb.x, eb.y);
+                cnt += (uint32_t)__popcll(__ballot(sa)) + (uint32_t)__popcll(__ballot(sb));
+            }
+            if (lane == 0) f.sh[c] = cnt;
+        }
+        __syncthreads();
+        // 2. offsets: exclusive scan over the chunks (two per thread, nch <= 512)
+        {
+            const uint32_t a0 = c0 < nch ? f.sh[c0] : 0u;
+            const uint32_t a1 = c1 < nch ? f.sh[c1] : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_exclusive_scan(a0 + a1, &tot, f.waves);   // barriers inside
+            if (c0 < nch) f.sh[c0] = ex;
+            if (c1 < nch) f.sh[c1] = ex + a0;
+        }
+        __syncthreads();
+        // 3. write each chunk's selected positions at its offset
+        for (int c = wave; c < nch; c += NW) {
+            const uint32_t base = f.cbase[c], len = f.clen[c];
+            uint32_t o = f.sh[c];
+            for (uint32_t j0 = 0; j0 < len; j0 += 64) {
+                const uint32_t j = j0 + lane;
+                const uint2 e = get(base + (j < len ? j : 0u));
+                const uint32_t sel = (uint32_t)(j < len) & sel_of(e.x, e.y);
+                const uint64_t b = __ballot(sel);
+                const uint32_t at = o + (uint32_t)__popcll(b & below);
+                if (sel && at < (uint32_t)k) out[at] = (int32_t)e.y;   // exactly k are selected
+                o += (uint32_t)__popcll(b);
+            }
+        }
+    };
+    if (mode == 0) compact(std::true_type{});
+    else compact(std::false_type{});
 }
 
 }  // namespace
@@ -482,12 +529,13 @@ TopkLayout topk_layout(int rows, int L_cap) {
     };
     // counters zeroed at the start of every call come first
     L.hist = take((size_t)rows * TOPK_HIST_BINS * 4);
-    L.cand_cnt = take((size_t)rows * 4);
+    L.hist2 = take((size_t)rows * HIST2_BINS * 4);
+    L.alloc = take((size_t)rows * 4);
+    L.zero_bytes = off;
     // scratch overwritten by every call
     L.row_state = take((size_t)rows * sizeof(RowState));
-    L.count_above = take((size_t)rows * L.nchunks * 4);
-    L.chunk_off = take((size_t)rows * L.nchunks * 4);
-    L.cand = take((size_t)rows * cap * 8);
+    L.runs = take((size_t)rows * L.nchunks * 8);
+    L.ent = take((size_t)rows * cap * 8);
     L.total = off;
     return L;
 }
@@ -502,41 +550,28 @@ hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream) {
 }
 
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
-                              int k, int32_t* idx, void* ws, bool counters_clear, bool hist_ready,
+                              int k, int32_t* idx, void* ws, bool counters_clear,
                               hipStream_t stream) {
     const int rows = B * Tq;
     const TopkLayout L = topk_layout(rows, L_cap);
     char* base = static_cast<char*>(ws);
     uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
-    uint32_t* cand_cnt = reinterpret_cast<uint32_t*>(base + L.cand_cnt);
+    uint32_t* hist2 = reinterpret_cast<uint32_t*>(base + L.hist2);
+    uint32_t* alloc = reinterpret_cast<uint32_t*>(base + L.alloc);
     RowState* row_state = reinterpret_cast<RowState*>(base + L.row_state);
-    uint32_t* count_above = reinterpret_cast<uint32_t*>(base + L.count_above);
-    uint32_t* chunk_off = reinterpret_cast<uint32_t*>(base + L.chunk_off);
-    uint2* cand = reinterpret_cast<uint2*>(base + L.cand);
-    if (!counters_clear) {                      // hist and cand_cnt precede row_state
-        hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.row_state / 4, stream);
+    uint2* runs = reinterpret_cast<uint2*>(base + L.runs);
+    uint2* ent = reinterpret_cast<uint2*>(base + L.ent);
+    if (!counters_clear) {
+        hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.zero_bytes / 4, stream);
         if (e != hipSuccess) return e;
     }
     dim3 grid(L.nchunks, rows);
-    if (!hist_ready)
-        hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
-                           L_cap, k, hist);
+    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq, L_cap,
+                       k, hist);
     hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
-                       L_cap, k, hist, cand_cnt, count_above, cand, L.cap, L.nchunks);
-    // few rows: every compact workgroup finishes its row itself (one launch
-    // fewer); many rows: one finish workgroup per row
-    if ((size_t)rows * L.nchunks <= 2048) {
-        hipLaunchKernelGGL(topk_compact_kernel<true>, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len,
-                           Tq, L_cap, k, hist, cand_cnt, count_above, cand, L.cap, row_state,
-                           chunk_off, L.nchunks, idx);
-    } else {
-        hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(TOPK_THREADS), 0, stream, S,
-                           kv_len, Tq, L_cap, k, hist, cand_cnt, count_above, cand, L.cap,
-                           L.nchunks, row_state, chunk_off);
-        hipLaunchKernelGGL(topk_compact_kernel<false>, grid, dim3(TOPK_THREADS), 0, stream, S,
-                           kv_len, Tq, L_cap, k, hist, cand_cnt, count_above, cand, L.cap,
-                           row_state, chunk_off, L.nchunks, idx);
-    }
+                       L_cap, k, hist, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(TOPK_THREADS), 0, stream, S, kv_len,
+                       Tq, L_cap, k, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks, idx);
     return hipGetLastError();
 }
 
