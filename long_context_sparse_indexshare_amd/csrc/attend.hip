@@ -74,7 +74,7 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
-template <int HB, int VS, int D, int DV>
+template <int HB, int VS, int D, int DV, int GR>
 struct AttendGeom {
     static constexpr int KSP = 4 / HB;              // waves sharing a head block (K split)
     static constexpr int KS = D / 16;               // k-steps of the QK product
@@ -92,35 +92,39 @@ struct AttendGeom {
     static constexpr int TILE_BYTES = TILE_ROWS * ROWB;
     static constexpr int TILE_CHUNKS = TILE_ROWS * CH;
     static constexpr int GPT = (TILE_CHUNKS + AT_THREADS - 1) / AT_THREADS;   // chunks per thread
-    // workgroups resident per CU: two where the accumulators are small
-    // enough for 256 registers per lane (one computes while the other waits
-    // on its gathers), else one
-    static constexpr int WG_PER_CU = NB <= 4 ? 2 : 1;
-    // tiles in flight in registers while one is computed
-    static constexpr int AHEAD = 1;
+    // GR groups of 4 waves per workgroup, each on its own tiles; waves per
+    // SIMD: 2 where the accumulators fit 256 registers per lane (two groups
+    // in one workgroup, or two workgroups), else 1
+    static constexpr int THREADS = AT_THREADS * GR;
+    static constexpr int WAVES_PER_SIMD = NB <= 4 ? 2 : 1;
+    static constexpr int WG_PER_CU = WAVES_PER_SIMD / GR > 0 ? WAVES_PER_SIMD / GR : 1;
     // QK accumulators per wave (two halve the dependent MFMA chain where
     // registers allow)
-    static constexpr int QK_ACC = (WG_PER_CU == 2 && NB == 4) ? 1 : 2;
+    static constexpr int QK_ACC = (WAVES_PER_SIMD == 2 && NB == 4) ? 1 : 2;
+    static_assert(GR == 1 || WAVES_PER_SIMD == 2, "two groups need the 256-register budget");
     static_assert(KS % KSP == 0, "the K split must divide the k-steps");
     static_assert(CW % 32 == 0, "value columns per wave");
 };
 
-template <int HB, int VS, int D, int DV>
-__global__ __launch_bounds__(AT_THREADS, (AttendGeom<HB, VS, D, DV>::WG_PER_CU)) void sparse_attend_kernel(
+template <int HB, int VS, int D, int DV, int GR>
+__global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
+                             (AttendGeom<HB, VS, D, DV, GR>::WG_PER_CU)) void sparse_attend_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const int32_t* __restrict__ idx,
     int Tq, int H, int L_cap, int k, float scale_log2, int slots_per_split, int splits,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float2* __restrict__ part_ml) {
-    using G = AttendGeom<HB, VS, D, DV>;
+    using G = AttendGeom<HB, VS, D, DV, GR>;
     constexpr int ROWB = G::ROWB;
 
-    __shared__ __attribute__((aligned(16))) char tile[G::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) float xbuf[4][4][64][4];   // partial S^T blocks
-    __shared__ int sidx[MAX_SPLIT_SLOTS];
+    __shared__ __attribute__((aligned(16))) char tiles[GR][G::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) float xbufs[GR][4][4][64][4];   // partial S^T blocks
+    __shared__ int sidx[MAX_SPLIT_SLOTS + TILE_ROWS * GR];
 
-    const int tid = threadIdx.x;
+    // group and wave indices are wave-uniform: keep them in scalar registers
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / AT_THREADS);   // group of 4 waves
+    const int tid = threadIdx.x % AT_THREADS;  // index within the group
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31;
     const int g = lane >> 5;
     const int hbl = wave % HB;              // head block within the workgroup
@@ -137,27 +141,34 @@ __global__ __launch_bounds__(AT_THREADS, (AttendGeom<HB, VS, D, DV>::WG_PER_CU))
     const int32_t* qidx = idx + (size_t)q * k;
     const char* Cb = reinterpret_cast<const char*>(C + (size_t)b * L_cap * D);
     const int col0 = vh * G::COLS + kp * G::CW;   // first value column of this wave
+    char* tile = tiles[grp];
+    float (*xbuf)[4][64][4] = xbufs[grp];
 
+    // tiles of the split; group grp takes tiles grp, grp + GR, ...  Every group
+    // runs the same number of iterations (a group past the last tile computes
+    // an all-invalid tile, which changes nothing), so the workgroup barriers
+    // stay uniform.
+    const int ntiles = (slot1 - slot0 + TILE_ROWS - 1) / TILE_ROWS;
+    const int iters = (ntiles + GR - 1) / GR;
     // this split's positions, once, into LDS; invalid ones and the padding up
-    // to a whole number of tiles become -1
-    const int padded = ((slot1 - slot0 + TILE_ROWS - 1) / TILE_ROWS) * TILE_ROWS;
-    for (int i = tid; i < padded; i += AT_THREADS) {
+    // to a whole number of tiles per group become -1
+    const int padded = iters * GR * TILE_ROWS;
+    for (int i = threadIdx.x; i < padded; i += G::THREADS) {
         const int s = slot0 + i < slot1 ? qidx[slot0 + i] : -1;
         sidx[i] = (s >= 0 && s < L_cap) ? s : -1;
     }
 
-    // this wave's share of Q^T: lane (head j, half g) holds dims 16*ks + 8*g .. +8
-    // for ks in [kp*KSW, (kp+1)*KSW); heads past H read head 0 and are zeroed
+    // this wave's share of Q^T (requested after the positions, which gate the
+    // first gathers): lane (head j, half g) holds
+    // dims 16*ks + 8*g .. +8 for ks in [kp*KSW, (kp+1)*KSW).  Heads past H
+    // read head 0; their results are never stored.
     v8bf qb[G::KSW];
     {
         const uint16_t* qrow = Q + ((size_t)q * H + (head_ok ? head : 0)) * D;
-        const uint32_t keep = head_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int i = 0; i < G::KSW; ++i) {
-            uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * (kp * G::KSW + i) + 8 * g);
-            v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
-            qb[i] = __builtin_bit_cast(v8bf, v);
-        }
+        for (int i = 0; i < G::KSW; ++i)
+            qb[i] = __builtin_bit_cast(
+                v8bf, *reinterpret_cast<const uint4*>(qrow + 16 * (kp * G::KSW + i) + 8 * g));
     }
 
     v16f o[G::NB];
@@ -292,49 +303,57 @@ __global__ __launch_bounds__(AT_THREADS, (AttendGeom<HB, VS, D, DV>::WG_PER_CU))
         }
     };
 
-    // software pipeline: two tiles in flight in registers (rA, rB) while the
-    // LDS tile is computed; the register sets alternate, so the loop body is
-    // unrolled by two to keep their roles static
-    const int ntiles = (slot1 - slot0 + TILE_ROWS - 1) / TILE_ROWS;
+    // software pipeline: the next tile of the group is in flight in registers
+    // while the current one is computed from LDS
+    auto tile_start = [&](int it) { return slot0 + (it * GR + grp) * TILE_ROWS; };
     lds_barrier();                          // sidx visible
-    v4u rA[G::GPT], rB[G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
-    if constexpr (G::AHEAD == 2) {
-        if (ntiles > 0) { ISA_LOAD_TILE(rA, slot0) }
-        if (ntiles > 1) { ISA_LOAD_TILE(rB, slot0 + TILE_ROWS) }
-        if (ntiles > 0) { ISA_STORE_TILE(rA) }
-        if (ntiles > 2) { ISA_LOAD_TILE(rA, slot0 + 2 * TILE_ROWS) }
+    v4u rA[G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
+    if (iters > 0) { ISA_LOAD_TILE(rA, tile_start(0)) }
+    if (iters > 0) { ISA_STORE_TILE(rA) }
+    if (iters > 1) { ISA_LOAD_TILE(rA, tile_start(1)) }
+    lds_barrier();
+    for (int it = 0; it < iters; ++it) {
+        compute_tile(tile_start(it));                        // in flight: rA = it+1
+        if (it + 1 >= iters) break;
         lds_barrier();
-        for (int it = 0; it < ntiles; it += 2) {
-            compute_tile(slot0 + it * TILE_ROWS);            // in flight: rB = it+1, rA = it+2
-            if (it + 1 >= ntiles) break;
-            lds_barrier();
-            ISA_STORE_TILE(rB)
-            if (it + 3 < ntiles) { ISA_LOAD_TILE(rB, slot0 + (it + 3) * TILE_ROWS) }
-            lds_barrier();
-            compute_tile(slot0 + (it + 1) * TILE_ROWS);      // in flight: rA = it+2, rB = it+3
-            if (it + 2 >= ntiles) break;
-            lds_barrier();
-            ISA_STORE_TILE(rA)
-            if (it + 4 < ntiles) { ISA_LOAD_TILE(rA, slot0 + (it + 4) * TILE_ROWS) }
-            lds_barrier();
-        }
-    } else {
-        (void)rB;
-        if (ntiles > 0) { ISA_LOAD_TILE(rA, slot0) }
-        if (ntiles > 0) { ISA_STORE_TILE(rA) }
-        if (ntiles > 1) { ISA_LOAD_TILE(rA, slot0 + TILE_ROWS) }
+        ISA_STORE_TILE(rA)
+        if (it + 2 < iters) { ISA_LOAD_TILE(rA, tile_start(it + 2)) }
         lds_barrier();
-        for (int it = 0; it < ntiles; ++it) {
-            compute_tile(slot0 + it * TILE_ROWS);            // in flight: rA = it+1
-            if (it + 1 >= ntiles) break;
-            lds_barrier();
-            ISA_STORE_TILE(rA)
-            if (it + 2 < ntiles) { ISA_LOAD_TILE(rA, slot0 + (it + 2) * TILE_ROWS) }
-            lds_barrier();
-        }
     }
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
+
+    if constexpr (GR == 2) {
+        // group 1 hands (o, max, sum) to group 0 through the (now free) tile
+        // LDS; group 0 combines the two online-softmax states
+        float* mb = reinterpret_cast<float*>(&tiles[0][0]);
+        constexpr int PER_LANE = G::NB * 16 + 2;
+        static_assert(4 * 64 * PER_LANE * 4 <= GR * G::TILE_BYTES, "hand-off fits the tiles");
+        lds_barrier();
+        if (grp == 1) {
+#pragma unroll
+            for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mb[((wave * PER_LANE) + nb * 16 + r) * 64 + lane] = o[nb][r];
+            mb[((wave * PER_LANE) + G::NB * 16) * 64 + lane] = m_run;
+            mb[((wave * PER_LANE) + G::NB * 16 + 1) * 64 + lane] = l_run;
+        }
+        lds_barrier();
+        if (grp == 1) return;
+        const float m1 = mb[((wave * PER_LANE) + G::NB * 16) * 64 + lane];
+        const float l1 = mb[((wave * PER_LANE) + G::NB * 16 + 1) * 64 + lane];
+        const float M = fmaxf(m_run, m1);
+        const float Mu = M == -__builtin_inff() ? 0.0f : M;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[nb][r] = o[nb][r] * a0 + mb[((wave * PER_LANE) + nb * 16 + r) * 64 + lane] * a1;
+        l_run = l_run * a0 + l1 * a1;
+        m_run = M;
+    }
 
     // softmax denominator of head j over all rows (the lane pair splits them)
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -362,48 +381,76 @@ __global__ __launch_bounds__(AT_THREADS, (AttendGeom<HB, VS, D, DV>::WG_PER_CU))
         return;
     }
 
-    // ---- split: publish the unnormalised partial and (max, sum) of this column part
-    if (head_ok) {
-        float* po = part_o + (((size_t)q * splits + sp) * H + head) * DV;
+    // ---- split: publish this split's output normalised by its own sum (bf16;
+    // the merge re-weights it by the split's (max, sum), kept in fp32).  The
+    // partial keeps the register layout, [..][wave][nb][r4][lane] x 4 bf16, so
+    // every store instruction writes 512 contiguous bytes; the merge kernel
+    // reads it in that layout.
+    {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const int n_hbg = gridDim.z / VS;
+        v2u* po = reinterpret_cast<v2u*>(part_o) +
+                  (((((size_t)q * splits + sp) * n_hbg + hbg) * VS + vh) * 4 + wave) *
+                      (G::NB * 4 * 64);
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int col = col0 + 32 * nb + 8 * r4 + 4 * g;
-                *reinterpret_cast<float4*>(po + col) =
-                    make_float4(o[nb][4 * r4], o[nb][4 * r4 + 1], o[nb][4 * r4 + 2], o[nb][4 * r4 + 3]);
+                const uint32_t lo = (uint32_t)f2bf(o[nb][4 * r4] * inv) |
+                                    ((uint32_t)f2bf(o[nb][4 * r4 + 1] * inv) << 16);
+                const uint32_t hi = (uint32_t)f2bf(o[nb][4 * r4 + 2] * inv) |
+                                    ((uint32_t)f2bf(o[nb][4 * r4 + 3] * inv) << 16);
+                // streamed past L2: the merge kernel reads the partials once
+                __builtin_nontemporal_store(v2u{lo, hi}, po + (nb * 4 + r4) * 64 + lane);
             }
         }
-        if (kp == 0 && g == 0)
+        if (head_ok && kp == 0 && g == 0)
             part_ml[(((size_t)q * splits + sp) * VS + vh) * H + head] = make_float2(m_run, l_tot);
     }
 }
 
-// Combines the splits of one (query, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// in split order; column part p uses the (max, sum) its own workgroups wrote.
-// Every split's partial is requested before any is used (the loads are
-// independent, so their latencies overlap).
-template <int DV, int VS>
-__global__ __launch_bounds__(DV / 4) void merge_splits_kernel(const float* __restrict__ part_o,
-                                                              const float2* __restrict__ part_ml,
-                                                              int H, int splits,
-                                                              uint16_t* __restrict__ out,
-                                                              float* __restrict__ lse) {
-    const int qh = blockIdx.x;             // q * H + h
-    const int q = qh / H;
-    const int h = qh - q * H;
-    const int col = threadIdx.x * 4;
-    const int vh = col / (DV / VS);
+// Combines the splits of every (query, head): with each split's output O_s
+// normalised by its own sum l_s, out = sum_s w_s O_s / sum_s w_s where
+// w_s = 2^(m_s - M) l_s, in split order; column part p uses the (max, sum)
+// its own workgroups wrote.  The partials are in the attention kernel's
+// register layout (per query, split, head-block group and column part:
+// [wave][nb][r4][lane] x 4 bf16), and a merge thread takes one lane position
+// of that layout (4 columns of one head), so its loads are contiguous across
+// threads.  Every split's partial is requested before any is used.
+constexpr int MERGE_THREADS = 256;
+template <int DV, int VS, int HB, int NB, int CW>
+__global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
+    const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml, int nq, int H,
+    int n_hbg, int splits, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    constexpr int COLS = DV / VS;
+    constexpr int BLOCK = 4 * NB * 4 * 64;         // v2u per (query, split, hbg, column part)
+    const size_t gid = (size_t)blockIdx.x * MERGE_THREADS + threadIdx.x;
+    const int lane = (int)(gid % 64);
+    size_t rest = gid / 64;
+    const int r4 = (int)(rest % 4); rest /= 4;
+    const int nb = (int)(rest % NB); rest /= NB;
+    const int wave = (int)(rest % 4); rest /= 4;
+    const int vh = (int)(rest % VS); rest /= VS;
+    const int hbg = (int)(rest % n_hbg); rest /= n_hbg;
+    const int q = (int)rest;
+    if (q >= nq) return;
+    const int hbl = wave % HB, kp = wave / HB;
+    const int head = (hbg * HB + hbl) * 32 + (lane & 31);
+    if (head >= H) return;
+    const int col = vh * COLS + kp * CW + 32 * nb + 8 * r4 + 4 * (lane >> 5);
+    const size_t within = ((size_t)wave * NB + nb) * 4 * 64 + r4 * 64 + lane;
     float2 ml[MAX_SPLITS];
-    float4 v[MAX_SPLITS];
+    v2u v[MAX_SPLITS];
 #pragma unroll
     for (int sj = 0; sj < MAX_SPLITS; ++sj) {
         if (sj < splits) {
-            ml[sj] = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + h];
-            v[sj] = *reinterpret_cast<const float4*>(part_o + (((size_t)q * splits + sj) * H + h) * DV + col);
+            ml[sj] = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + head];
+            v[sj] = __builtin_nontemporal_load(
+                reinterpret_cast<const v2u*>(part_o) +
+                ((((size_t)q * splits + sj) * n_hbg + hbg) * VS + vh) * BLOCK + within);
         } else {
             ml[sj] = make_float2(-__builtin_inff(), 0.0f);
-            v[sj] = make_float4(0.f, 0.f, 0.f, 0.f);
+            v[sj] = v2u{0u, 0u};
         }
     }
     float M = -__builtin_inff();
@@ -411,39 +458,51 @@ __global__ __launch_bounds__(DV / 4) void merge_splits_kernel(const float* __res
     for (int sj = 0; sj < MAX_SPLITS; ++sj) M = fmaxf(M, ml[sj].x);
     const float Mu = M == -__builtin_inff() ? 0.0f : M;
     float L = 0.0f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int sj = 0; sj < MAX_SPLITS; ++sj) {
         if (sj < splits) {
-            const float wgt = exp2f(ml[sj].x - Mu);
-            L += wgt * ml[sj].y;
-            acc.x += wgt * v[sj].x; acc.y += wgt * v[sj].y; acc.z += wgt * v[sj].z; acc.w += wgt * v[sj].w;
+            const float wgt = exp2f(ml[sj].x - Mu) * ml[sj].y;   // 0 for an empty split
+            L += wgt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w32 = v[sj][e / 2];
+                acc[e] += wgt * __uint_as_float((e & 1) ? (w32 & 0xFFFF0000u) : (w32 << 16));
+            }
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    ushort4 r;
-    r.x = f2bf(acc.x * inv); r.y = f2bf(acc.y * inv); r.z = f2bf(acc.z * inv); r.w = f2bf(acc.w * inv);
-    *reinterpret_cast<ushort4*>(out + (size_t)qh * DV + col) = r;
-    if (lse && threadIdx.x == 0) lse[qh] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
+    const v2u r = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
+                   (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
+    *reinterpret_cast<v2u*>(out + ((size_t)q * H + head) * DV + col) = r;
+    if (lse && vh == 0 && kp == 0 && nb == 0 && r4 == 0 && lane < 32)
+        lse[(size_t)q * H + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
 }
 
-template <int HB, int VS, int D, int DV>
+template <int HB, int VS, int D, int DV, int GR>
 hipError_t launch_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B, int Tq,
                          int H, int L_cap, int k, float sm_scale, uint16_t* out, float* lse,
                          void* partials, hipStream_t stream) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, DV, k);
     const int nq = B * Tq;
     char* base = static_cast<char*>(partials);
-    float* part_o = reinterpret_cast<float*>(base + plan.part_o_off);
+    uint16_t* part_o = reinterpret_cast<uint16_t*>(base + plan.part_o_off);
     float2* part_ml = reinterpret_cast<float2*>(base + plan.part_ml_off);
     const int n_hbg = (H + 32 * HB - 1) / (32 * HB);
     dim3 grid(plan.splits, nq, n_hbg * VS);
-    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV>), grid, dim3(AT_THREADS), 0, stream, Q,
+    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV, GR>), grid, dim3(AT_THREADS * GR), 0,
+                       stream, Q,
                        C, idx, Tq, H, L_cap, k, sm_scale * LOG2E, plan.slots_per_split,
                        plan.splits, out, lse, part_o, part_ml);
     if (plan.splits > 1)
-        hipLaunchKernelGGL((merge_splits_kernel<DV, VS>), dim3(nq * H), dim3(DV / 4), 0, stream,
-                           part_o, part_ml, H, plan.splits, out, lse);
+    {
+        using Gm = AttendGeom<HB, VS, D, DV, GR>;
+        const size_t threads = (size_t)nq * n_hbg * VS * 4 * Gm::NB * 4 * 64;
+        hipLaunchKernelGGL((merge_splits_kernel<DV, VS, HB, Gm::NB, Gm::CW>),
+                           dim3((unsigned)((threads + MERGE_THREADS - 1) / MERGE_THREADS)),
+                           dim3(MERGE_THREADS), 0, stream, part_o, part_ml, nq, H, n_hbg,
+                           plan.splits, out, lse);
+    }
     return hipGetLastError();
 }
 
@@ -462,9 +521,9 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k) {
     const int n_hbg = (H + 32 * p.head_blocks - 1) / (32 * p.head_blocks);
     const int units = nq * n_hbg * p.col_parts;
     const int tiles = (k + TILE_ROWS - 1) / TILE_ROWS;
-    // enough workgroups for every resident slot: 256 CUs, two workgroups per
-    // CU for the decode variant
-    const int target = wide ? 256 : 512;
+    // one workgroup per CU (256 CUs): the decode variant's workgroup holds two
+    // groups of 4 waves
+    const int target = 256;
     int splits = units >= target ? 1 : (target + units - 1) / units;
     if (splits > MAX_SPLITS) splits = MAX_SPLITS;
     if (splits > tiles) splits = tiles;
@@ -478,7 +537,9 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k) {
         off += (bytes + 255) & ~(size_t)255;
         return o;
     };
-    p.part_o_off = take(splits > 1 ? (size_t)nq * splits * H * D_v * 4 : 0);
+    // partial outputs cover every head slot of the workgroups (32 * head_blocks
+    // per head-block group), bf16
+    p.part_o_off = take(splits > 1 ? (size_t)nq * splits * n_hbg * 32 * p.head_blocks * D_v * 2 : 0);
     p.part_ml_off = take(splits > 1 ? (size_t)nq * splits * p.col_parts * H * 8 : 0);
     p.partial_bytes = off;
     return p;
@@ -497,14 +558,14 @@ hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const 
     const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
     if (D == 576 && D_v == 512) {
         if (plan.col_parts == 1)
-            return launch_attend<2, 1, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
-                                                 partials, stream);
-        return launch_attend<2, 2, 576, 512>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
-                                             partials, stream);
+            return launch_attend<2, 1, 576, 512, 1>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out,
+                                                    lse, partials, stream);
+        return launch_attend<2, 2, 576, 512, 2>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+                                                partials, stream);
     }
     if (D == 160 && D_v == 128)
-        return launch_attend<2, 1, 160, 128>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
-                                             partials, stream);
+        return launch_attend<2, 1, 160, 128, 1>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+                                                partials, stream);
     return hipErrorInvalidValue;
 }
 
