@@ -117,7 +117,7 @@ isa_status isa_topk_select(const float* S, const int32_t* kv_len, int B, int Tq,
  * out [B,Tq,H,D_v] bf16; lse [B,Tq,H] fp32 or NULL.
  * bf16 MFMA with fp32 accumulation and an fp32 online softmax.
  * Supported: (D, D_v) in {(576, 512), (160, 128)}, 1 <= H <= 64,
- * 1 <= k <= ISA_MAX_TOPK, sm_scale finite.
+ * 1 <= k <= ISA_MAX_TOPK, sm_scale finite and > 0 (a softmax temperature).
  */
 size_t isa_attend_workspace_bytes(int B, int Tq, int H, int D, int D_v, int k);
 isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,

@@ -90,7 +90,8 @@ isa_status check_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx
               ISA_MAX_TOPK);
     ISA_CHECK(L_cap <= ISA_MAX_LCAP, ISA_ERR_INVALID_ARG, "attend: L_cap=%d exceeds %d", L_cap,
               ISA_MAX_LCAP);
-    ISA_CHECK(std::isfinite(sm_scale), ISA_ERR_INVALID_ARG, "attend: sm_scale is not finite");
+    ISA_CHECK(std::isfinite(sm_scale) && sm_scale > 0.0f, ISA_ERR_INVALID_ARG,
+              "attend: sm_scale must be finite and positive (got %g)", (double)sm_scale);
     ISA_CHECK(isa::attend_shape_supported(H, D, D_v), ISA_ERR_UNSUPPORTED,
               "attend: (H=%d, D=%d, D_v=%d) not compiled; (D, D_v) in {(576,512), (160,128)}, "
               "H <= 64",

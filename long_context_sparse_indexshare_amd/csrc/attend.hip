@@ -45,6 +45,10 @@ constexpr int AT_THREADS = 256;
 constexpr int TILE_ROWS = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+// The running softmax reference max moves only when a tile's max exceeds it
+// by more than this (log2 units): P stays <= 2^8, and most tiles skip the
+// rescale of the output accumulators.
+constexpr float RESCALE_SLACK = 8.0f;
 
 typedef __attribute__((address_space(3))) v4bf* lds_v4bf_ptr;
 // Gathers go through global-address-space pointers: a generic (flat) load
@@ -91,7 +95,9 @@ struct AttendGeom {
     static constexpr int NB = CW / 32;              // 32-column MFMA blocks per wave
     static constexpr int TILE_BYTES = TILE_ROWS * ROWB;
     static constexpr int TILE_CHUNKS = TILE_ROWS * CH;
-    static constexpr int GPT = (TILE_CHUNKS + AT_THREADS - 1) / AT_THREADS;   // chunks per thread
+    // gather: 8 threads per row, thread (row, sub) takes chunks sub, sub + 8, ...
+    static constexpr int TPR = AT_THREADS / TILE_ROWS;
+    static constexpr int GPT = (CH + TPR - 1) / TPR;     // chunks per thread
     // GR groups of 4 waves per workgroup, each on its own tiles; waves per
     // SIMD: 2 where the accumulators fit 256 registers per lane (two groups
     // in one workgroup, or two workgroups), else 1
@@ -119,6 +125,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     __shared__ __attribute__((aligned(16))) char tiles[GR][G::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) float xbufs[GR][4][4][64][4];   // partial S^T blocks
     __shared__ int sidx[MAX_SPLIT_SLOTS + TILE_ROWS * GR];
+    __shared__ uint32_t tmask[(MAX_SPLIT_SLOTS + TILE_ROWS * GR) / TILE_ROWS + 2];   // valid rows per tile
 
     // group and wave indices are wave-uniform: keep them in scalar registers
     const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / AT_THREADS);   // group of 4 waves
@@ -155,22 +162,17 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const int padded = iters * GR * TILE_ROWS;
     for (int i = threadIdx.x; i < padded; i += G::THREADS) {
         const int s = slot0 + i < slot1 ? qidx[slot0 + i] : -1;
-        sidx[i] = (s >= 0 && s < L_cap) ? s : -1;
+        const bool ok = s >= 0 && s < L_cap;
+        sidx[i] = ok ? s : -1;
+        // a wave covers 64 consecutive slots = two tiles: one bit per row
+        const uint64_t bits = __ballot(ok);
+        if (lane == 0) {
+            tmask[i / TILE_ROWS] = (uint32_t)bits;
+            tmask[i / TILE_ROWS + 1] = (uint32_t)(bits >> 32);
+        }
     }
 
-    // this wave's share of Q^T (requested after the positions, which gate the
-    // first gathers): lane (head j, half g) holds
-    // dims 16*ks + 8*g .. +8 for ks in [kp*KSW, (kp+1)*KSW).  Heads past H
-    // read head 0; their results are never stored.
-    v8bf qb[G::KSW];
-    {
-        const uint16_t* qrow = Q + ((size_t)q * H + (head_ok ? head : 0)) * D;
-#pragma unroll
-        for (int i = 0; i < G::KSW; ++i)
-            qb[i] = __builtin_bit_cast(
-                v8bf, *reinterpret_cast<const uint4*>(qrow + 16 * (kp * G::KSW + i) + 8 * g));
-    }
-
+    v8bf qb[G::KSW];   // this wave's share of Q^T (loaded after the first gather is issued)
     v16f o[G::NB];
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb)
@@ -179,30 +181,28 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
 
-    // gather: thread tid owns chunks c = i*256 + tid of a tile (row c / CH,
-    // logical chunk c % CH); rows of -1 / out-of-range slots read a zero row.
+    // gather: thread (row tid / 8, sub tid % 8) owns chunks sub, sub + 8, ... of
+    // one tile row, so one base address and immediate offsets serve all its
+    // loads and LDS stores; rows of -1 / out-of-range slots read a zero row.
     // (Macros rather than lambdas keep the register arrays out of memory.)
     const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_row);
     const uintptr_t cbase = reinterpret_cast<uintptr_t>(Cb);
+    const int grow = tid / G::TPR;
+    const int gsub = tid % G::TPR;
+    char* const lrow = tile + grow * ROWB + gsub * 16;
 #define ISA_LOAD_TILE(R, TS)                                                                   \
-    _Pragma("unroll") for (int i_ = 0; i_ < G::GPT; ++i_) {                                   \
-        const int c_ = i_ * AT_THREADS + tid;                                                  \
-        if (G::TILE_CHUNKS % AT_THREADS == 0 || c_ < G::TILE_CHUNKS) {                         \
-            const int row_ = c_ / G::CH;                                                       \
-            const int ch_ = c_ - row_ * G::CH;                                                 \
-            const int s_ = sidx[(TS) - slot0 + row_];   /* -1 past the split (padded) */       \
-            const uintptr_t ra_ = cbase + (size_t)(s_ & ~(s_ >> 31)) * G::CROWB;               \
-            R[i_] = *(global_v4u_ptr)((s_ >= 0 ? ra_ : zero_row) + ch_ * 16);                  \
+    {                                                                                          \
+        const int s_ = sidx[(TS) - slot0 + grow];   /* -1 past the split (padded) */           \
+        const uintptr_t ra_ = (s_ >= 0 ? cbase + (size_t)s_ * G::CROWB : zero_row) + gsub * 16; \
+        _Pragma("unroll") for (int i_ = 0; i_ < G::GPT; ++i_) {                               \
+            if (G::CH % G::TPR == 0 || gsub + G::TPR * i_ < G::CH)                             \
+                R[i_] = *(global_v4u_ptr)(ra_ + i_ * G::TPR * 16);                             \
         }                                                                                      \
     }
 #define ISA_STORE_TILE(R)                                                                      \
     _Pragma("unroll") for (int i_ = 0; i_ < G::GPT; ++i_) {                                   \
-        const int c_ = i_ * AT_THREADS + tid;                                                  \
-        if (G::TILE_CHUNKS % AT_THREADS == 0 || c_ < G::TILE_CHUNKS) {                         \
-            const int row_ = c_ / G::CH;                                                       \
-            const int ch_ = c_ - row_ * G::CH;                                                 \
-            *reinterpret_cast<v4u*>(tile + row_ * ROWB + ch_ * 16) = R[i_];                    \
-        }                                                                                      \
+        if (G::CH % G::TPR == 0 || gsub + G::TPR * i_ < G::CH)                                 \
+            *reinterpret_cast<v4u*>(lrow + i_ * G::TPR * 16) = R[i_];                          \
     }
 
     // one tile of the online softmax attention, from the LDS tile
@@ -258,33 +258,41 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                 }
             }
         }
-        // register r holds tile row 8*(r/4) + 4*g + r%4, head j
-        float mloc = -__builtin_inff();
+        // register r holds tile row 8*(r/4) + 4*g + r%4, head j; rows of -1
+        // slots get -inf (tiles without such rows, the usual case, skip this)
+        const uint32_t tm = tmask[(tile_start - slot0) / TILE_ROWS];
+        if (tm != 0xFFFFFFFFu) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const bool valid = sidx[tile_start - slot0 + 8 * (r / 4) + 4 * g + (r % 4)] >= 0;
-            const float x = valid ? s[r] * scale_log2 : -__builtin_inff();
-            s[r] = x;
-            mloc = fmaxf(mloc, x);
+            for (int r = 0; r < 16; ++r)
+                if (!((tm >> (8 * (r / 4) + 4 * g + (r % 4))) & 1u)) s[r] = -__builtin_inff();
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        float mloc = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;   // scale > 0 keeps the order
+        // move the reference max only when this tile's max exceeds it by more
+        // than RESCALE_SLACK (always on the first tile with a valid row)
+        const bool move = mloc > m_run + RESCALE_SLACK;
+        if (__ballot(move)) {
+            const float m_new = move ? mloc : m_run;
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+        }
+        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
         float psum = 0.0f;
         v8bf pk[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(s[r] - m_use);
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_use));
             psum += p;
             pk[r / 8][r % 8] = (__bf16)p;
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+        l_run += psum;
 
         // ---- O^T[this wave's columns x heads] += V^T . P^T over the tile's 32 rows
         const int G16 = lane >> 4;
@@ -309,6 +317,17 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     lds_barrier();                          // sidx visible
     v4u rA[G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
     if (iters > 0) { ISA_LOAD_TILE(rA, tile_start(0)) }
+    // this wave's share of Q^T, requested after the first tile's gather (which
+    // gates everything): lane (head j, half g) holds dims 16*ks + 8*g .. +8 for
+    // ks in [kp*KSW, (kp+1)*KSW).  Heads past H read head 0; their results are
+    // never stored.
+    {
+        const uint16_t* qrow = Q + ((size_t)q * H + (head_ok ? head : 0)) * D;
+#pragma unroll
+        for (int i = 0; i < G::KSW; ++i)
+            qb[i] = __builtin_bit_cast(
+                v8bf, *reinterpret_cast<const uint4*>(qrow + 16 * (kp * G::KSW + i) + 8 * g));
+    }
     if (iters > 0) { ISA_STORE_TILE(rA) }
     if (iters > 1) { ISA_LOAD_TILE(rA, tile_start(1)) }
     lds_barrier();

@@ -105,9 +105,10 @@ def test_attend_rejects_bad_arguments(lib):
         args = list(good)
         args[5], args[6], args[7] = H, D, D_v
         assert _status(lib, "isa_sparse_mla_attend", *args)[0] == isa.ISA_ERR_UNSUPPORTED
-    args = list(good)
-    args[10] = f(float("inf"))
-    assert _status(lib, "isa_sparse_mla_attend", *args)[0] == isa.ISA_ERR_INVALID_ARG
+    for bad_scale in (float("inf"), float("nan"), 0.0, -0.5):
+        args = list(good)
+        args[10] = f(bad_scale)
+        assert _status(lib, "isa_sparse_mla_attend", *args)[0] == isa.ISA_ERR_INVALID_ARG
     args = list(good)
     args[9] = 4096
     assert _status(lib, "isa_sparse_mla_attend", *args)[0] == isa.ISA_ERR_INVALID_ARG
