@@ -240,6 +240,78 @@ def run_stage(isa, wl, stage, reps, torch):
           flush=True)
 
 
+def run_ablation(isa, torch, steps, warmup):
+    """C4 (2 x 1M context): the shared index set vs an indexer + top-k per layer
+    (the IndexShare saving), each timed over whole groups."""
+    import synth
+    wl = synth.WORKLOADS["C4"]
+    log("C4: generating inputs (shared and per-layer indexers)")
+    d = synth.group_inputs(wl, device="cuda")
+    abl = synth.ablation_indexers(wl, device="cuda")
+    ws = isa.Workspace()
+    shared = isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], d["C"], wl.k,
+                           wl.D_v, wl.sm_scale, ws=ws)
+    per_layer = isa.GroupCall([a["qI"] for a in abl], [a["w"] for a in abl], [a["kI"] for a in abl],
+                              d["kv_len"], d["Q"], d["C"], wl.k, wl.D_v, wl.sm_scale,
+                              per_layer_indexer=True, ws=ws)
+    t_sh = time_group(isa, [shared], steps, warmup, torch)
+    t_pl = time_group(isa, [per_layer], steps, warmup, torch)
+    a = algorithmic(wl)
+    ix_topk_bytes = a["ix_bytes"] + a["topk_bytes"]
+    bytes_sh = a["group_bytes"]
+    bytes_pl = bytes_sh + (wl.n_layers - 1) * ix_topk_bytes
+    # per-token FLOPs of the group, indexer (16384 per key) vs attention
+    F_I = 2 * wl.H_I * wl.D_I * wl.kv_len
+    F_A = a["at_flops_per_layer"] / wl.B
+    del shared, per_layer, d, abl
+    torch.cuda.empty_cache()
+    return {"workload": "C4: 2 sequences x 1 query, context 1048576, 4 layers",
+            "shared_us_per_group": t_sh * 1e6, "per_layer_us_per_group": t_pl * 1e6,
+            "measured_ratio": t_pl / t_sh,
+            "algorithmic_bytes_ratio": bytes_pl / bytes_sh,
+            "group_flops_ratio": (4 * F_I + 4 * F_A) / (F_I + 4 * F_A),
+            "pages_claim": "2.9x lower compute overhead (whole model, 1M context, no hardware "
+                           "stated; context, not a target)"}
+
+
+def run_mtp(isa, torch, reps):
+    """C5: 7 sequential MTP draft steps on 16 x 262144 contexts; the index set
+    is computed at step 1 and reused by steps 2-7 (every step attends in 4
+    layers with its own queries), compared with recomputing it every step."""
+    import synth
+    wl = synth.WORKLOADS["C5"]
+    log("C5: generating inputs")
+    d = synth.group_inputs(wl, device="cuda")
+    Qs = [synth.mtp_queries(wl, s, device="cuda") for s in range(1, wl.mtp_steps + 1)]
+    ws = isa.Workspace()
+    first = isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qs[0], d["C"], wl.k,
+                          wl.D_v, wl.sm_scale, ws=ws)
+    later = [isa.GroupCall(None, None, None, d["kv_len"], Qs[s], d["C"], wl.k, wl.D_v,
+                           wl.sm_scale, idx=first.idx, reuse_idx=True, ws=ws)
+             for s in range(1, wl.mtp_steps)]
+    again = [isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qs[s], d["C"], wl.k,
+                           wl.D_v, wl.sm_scale, ws=ws) for s in range(wl.mtp_steps)]
+
+    def run_reuse():
+        first()
+        for c in later:
+            c()
+
+    def run_recompute():
+        for c in again:
+            c()
+
+    t_reuse = time_group(isa, [run_reuse], reps, 2, torch)
+    t_recompute = time_group(isa, [run_recompute], reps, 2, torch)
+    tokens = wl.B * wl.mtp_steps
+    del first, later, again, d, Qs
+    torch.cuda.empty_cache()
+    return {"workload": "C5: 16 sequences x 262144 context, 7 draft steps, 4 layers",
+            "tokens_per_s": tokens / t_reuse, "ms_per_7_steps": t_reuse * 1e3,
+            "ms_per_7_steps_recomputing_index": t_recompute * 1e3,
+            "reuse_speedup": t_recompute / t_reuse}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -292,6 +364,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 1M-context ablation and the 7-step MTP measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group"],
                     help="profiling mode: run one stage of --workload --reps times and print "
@@ -370,6 +444,9 @@ def main():
                                           f"host core of {cpu_name} ({ncpu} cpus)",
                                 "seconds": o["seconds"], "idx_exact": o["idx_exact"],
                                 "max_abs_err_vs_gpu": o["max_abs_err"]}
+    if not args.no_extra:
+        line["ablation"] = run_ablation(isa, torch, steps=10, warmup=3)
+        line["mtp"] = run_mtp(isa, torch, reps=5)
     if args.prefill:
         wp = synth.WORKLOADS["C3"]
         pre = run_workload(isa, wp, max(2, min(args.steps, 5)), 2, 1, torch,

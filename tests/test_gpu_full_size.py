@@ -1,0 +1,141 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (one isa_group_forward call per group), against the oracle
+on sampled sequences / query rows it can compute one by one in seconds.
+
+Inputs are generated on the GPU by the seeded generators; the oracle gets host
+copies of the sampled slices.  Indices are compared bit for bit, outputs to
+the attention tolerance.  Covered: the 32K and 128K decode groups, sampled
+rows of the 4096-query causal prefill, the 1M-context decode group with the
+shared index set and with per-layer indexers (the ablation), and the 7-step
+MTP run that reuses the step-1 index set."""
+import pytest
+import torch
+
+import long_context_sparse_indexshare_amd as isa
+import oracle
+import synth
+from _parity import assert_attn_close, assert_idx_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _slice_b(inp, bs):
+    """Host copies of sequences bs (a slice) of every input tensor."""
+    out = {}
+    for key, v in inp.items():
+        if isinstance(v, list):
+            out[key] = [x[bs].cpu() for x in v]
+        else:
+            out[key] = v[bs].cpu()
+    return out
+
+
+def _run_group(wl, d, **kw):
+    _print_case("gpu group", wl.name, kw.get("per_layer_indexer", False))
+    idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                         d["C"], wl.k, wl.D_v, wl.sm_scale, **kw)
+    torch.cuda.synchronize()
+    return idx, outs
+
+
+def _check_sequences(wl, d, idx, outs, seqs):
+    for b in seqs:
+        h = _slice_b(d, slice(b, b + 1))
+        _print_case("oracle", wl.name, "sequence", b)
+        idx_ref, outs_ref, _ = oracle.group_forward([h["qI"]], [h["w"]], [h["kI"]], h["kv_len"],
+                                                    h["Q"], h["C"], wl.k, wl.D_v, wl.sm_scale)
+        assert_idx_equal(idx[b:b + 1], idx_ref, f"{wl.name} seq {b}")
+        for l in range(wl.n_layers):
+            assert_attn_close(outs[l][b:b + 1], outs_ref[l], f"{wl.name} seq {b} layer {l}")
+
+
+@pytest.mark.parametrize("name,seqs", [("C2", list(range(8))), ("C2_128K", [0, 7])])
+def test_decode_group_full_size(name, seqs):
+    wl = synth.WORKLOADS[name]
+    d = synth.group_inputs(wl, device="cuda")
+    idx, outs = _run_group(wl, d)
+    _check_sequences(wl, d, idx, outs, seqs)
+
+
+def test_prefill_group_full_size_sampled_rows():
+    wl = synth.WORKLOADS["C3"]
+    d = synth.group_inputs(wl, device="cuda")
+    idx, outs = _run_group(wl, d)
+    kI = d["kI"][0:1].cpu()
+    C = [x[0:1].cpu() for x in d["C"]]
+    for t in (0, 1, 1000, 2047, 4094, 4095):
+        _print_case("oracle C3 row", t)
+        kv = torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32)   # what row t sees
+        idx_ref, outs_ref, _ = oracle.group_forward(
+            [d["qI"][0:1, t:t + 1].cpu()], [d["w"][0:1, t:t + 1].cpu()], [kI], kv,
+            [x[0:1, t:t + 1].cpu() for x in d["Q"]], C, wl.k, wl.D_v, wl.sm_scale)
+        assert_idx_equal(idx[0:1, t:t + 1], idx_ref, f"C3 row {t}")
+        for l in range(wl.n_layers):
+            assert_attn_close(outs[l][0:1, t:t + 1], outs_ref[l], f"C3 row {t} layer {l}")
+
+
+def test_1m_decode_shared_and_per_layer_indexer():
+    wl = synth.WORKLOADS["C4"]
+    d = synth.group_inputs(wl, device="cuda")
+    idx, outs = _run_group(wl, d)
+    _check_sequences(wl, d, idx, outs, [1])
+    # ablation: every layer its own indexer inputs; layer l attends over its own set
+    abl = synth.ablation_indexers(wl, device="cuda")
+    _print_case("gpu group C4 per-layer indexers")
+    idx_pl, outs_pl, _ = isa.isa_group_forward([a["qI"] for a in abl], [a["w"] for a in abl],
+                                               [a["kI"] for a in abl], d["kv_len"], d["Q"], d["C"],
+                                               wl.k, wl.D_v, wl.sm_scale, per_layer_indexer=True)
+    torch.cuda.synchronize()
+    b = 0
+    h = _slice_b(d, slice(b, b + 1))
+    ha = [_slice_b(a, slice(b, b + 1)) for a in abl]
+    _print_case("oracle C4 per-layer indexers, sequence", b)
+    idx_ref, outs_ref, _ = oracle.group_forward([a["qI"] for a in ha], [a["w"] for a in ha],
+                                                [a["kI"] for a in ha], h["kv_len"], h["Q"], h["C"],
+                                                wl.k, wl.D_v, wl.sm_scale, per_layer_indexer=True)
+    assert_idx_equal(idx_pl[b:b + 1], idx_ref, "C4 per-layer: last layer's set")
+    for l in range(wl.n_layers):
+        assert_attn_close(outs_pl[l][b:b + 1], outs_ref[l], f"C4 per-layer layer {l}")
+    # the shared set differs from the last per-layer set (independent indexers)
+    assert not torch.equal(idx_pl, idx)
+
+
+def test_mtp_seven_steps_full_size():
+    wl = synth.WORKLOADS["C5"]
+    d = synth.group_inputs(wl, device="cuda")
+    seqs = [0, wl.B - 1]
+    hs = {b: _slice_b(d, slice(b, b + 1)) for b in seqs}   # host copies of the sampled sequences
+    idx = None
+    idx_ref = {}
+    for step in range(1, wl.mtp_steps + 1):
+        Qd = synth.mtp_queries(wl, step, device="cuda")
+        _print_case("gpu mtp step", step)
+        if step == 1:
+            idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qd,
+                                                 d["C"], wl.k, wl.D_v, wl.sm_scale)
+        else:
+            before = idx.clone()
+            _, outs, _ = isa.isa_group_forward(None, None, None, d["kv_len"], Qd, d["C"], wl.k,
+                                               wl.D_v, wl.sm_scale, idx=idx, reuse_idx=True)
+            torch.cuda.synchronize()
+            assert torch.equal(idx, before), "reuse must not touch idx"
+        torch.cuda.synchronize()
+        for b in seqs:
+            _print_case("oracle mtp step", step, "sequence", b)
+            h = hs[b]
+            Qh = [x[b:b + 1].cpu() for x in Qd]
+            if step == 1:
+                ir, outs_ref, _ = oracle.group_forward([h["qI"]], [h["w"]], [h["kI"]], h["kv_len"],
+                                                       Qh, h["C"], wl.k, wl.D_v, wl.sm_scale)
+                idx_ref[b] = ir
+                assert_idx_equal(idx[b:b + 1], ir, f"mtp step 1 seq {b}")
+            else:
+                _, outs_ref, _ = oracle.group_forward(None, None, None, h["kv_len"], Qh, h["C"],
+                                                      wl.k, wl.D_v, wl.sm_scale, idx=idx_ref[b],
+                                                      reuse_idx=True)
+            for l in range(wl.n_layers):
+                assert_attn_close(outs[l][b:b + 1], outs_ref[l], f"mtp step {step} seq {b} layer {l}")
