@@ -321,7 +321,42 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     // gates everything): lane (head j, half g) holds dims 16*ks + 8*g .. +8 for
     // ks in [kp*KSW, (kp+1)*KSW).  Heads past H read head 0; their results are
     // never stored.
-    {
+    if constexpr (GR == 2) {
+        // both groups need the same Q: the workgroup's 64 head rows (contiguous
+        // in HBM) are staged once in the still unused tile LDS, 64 rows of ROWB
+        // bytes, and every wave reads its share from there
+        constexpr int QROWS = HB * 32;
+        constexpr int QCH = QROWS * G::CH;
+        constexpr int QPT = (QCH + G::THREADS - 1) / G::THREADS;
+        static_assert(QROWS * ROWB <= GR * G::TILE_BYTES, "Q rows fit the tile buffers");
+        char* const qlds = &tiles[0][0];
+        const int h0 = hbg * QROWS;
+        v4u qt[QPT];
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int c = u * G::THREADS + (int)threadIdx.x;
+            if (QCH % G::THREADS == 0 || c < QCH) {
+                const int hr = c / G::CH, ch = c - (c / G::CH) * G::CH;
+                const int hh = h0 + hr < H ? h0 + hr : 0;
+                qt[u] = *(global_v4u_ptr)(Q + ((size_t)q * H + hh) * D + ch * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int c = u * G::THREADS + (int)threadIdx.x;
+            if (QCH % G::THREADS == 0 || c < QCH) {
+                const int hr = c / G::CH, ch = c - (c / G::CH) * G::CH;
+                *reinterpret_cast<v4u*>(qlds + hr * ROWB + ch * 16) = qt[u];
+            }
+        }
+        lds_barrier();
+        const char* qr = qlds + (hbl * 32 + j) * ROWB;
+#pragma unroll
+        for (int i = 0; i < G::KSW; ++i)
+            qb[i] = __builtin_bit_cast(
+                v8bf, *reinterpret_cast<const v4u*>(qr + (16 * (kp * G::KSW + i) + 8 * g) * 2));
+        lds_barrier();                      // Q read out before the tiles are written
+    } else {
         const uint16_t* qrow = Q + ((size_t)q * H + (head_ok ? head : 0)) * D;
 #pragma unroll
         for (int i = 0; i < G::KSW; ++i)
