@@ -50,7 +50,8 @@ __device__ __forceinline__ int visible_count(const int32_t* kv_len, int row, int
     return n > 0 ? n : 0;
 }
 
-// Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
+// Exclusive prefix sum over the NT threads of the workgroup; *total gets the sum.
+template <int NT = TOPK_THREADS>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh_waves) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -65,7 +66,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < TOPK_THREADS / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const uint32_t x = sh_waves[w];
         before += w < wave ? x : 0u;
         all += x;
@@ -74,21 +75,21 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
     return before + inc - v;
 }
 
-// Over bins h[0..nbins) (nbins = 256 * per): the largest bin B with
+// Over bins h[0..nbins) (nbins = NT * per): the largest bin B with
 // sum_{b >= B} h[b] >= need (descending) or the smallest bin B with
 // sum_{b <= B} h[b] >= need (ascending).  Returns (B, the count strictly
 // beyond it: above for descending, below for ascending) to every thread.
-template <int PER, bool DESC>
+template <int PER, bool DESC, int NT = TOPK_THREADS>
 __device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint32_t* sh_waves,
                                           uint32_t* sh_res) {
     const int tid = threadIdx.x;
     // thread t owns bins [PER*t, PER*t + PER) ascending, or the mirrored range descending
-    const int first = DESC ? (TOPK_THREADS - 1 - tid) * PER : tid * PER;
+    const int first = DESC ? (NT - 1 - tid) * PER : tid * PER;
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) local += h[first + i];
     uint32_t total;
-    const uint32_t before = block_exclusive_scan(local, &total, sh_waves);
+    const uint32_t before = block_exclusive_scan<NT>(local, &total, sh_waves);
     if (before < need && before + local >= need) {
         uint32_t acc = before;
 #pragma unroll
@@ -510,6 +511,233 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
     else compact(std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// Many rows of at most SEL_MAX_N positions (prefill): after the histogram
+// kernel, one workgroup of 1024 threads per row does the rest in LDS.  With
+// fewer rows than the chip has compute units (decode) the classify/finish
+// pair spreads each row over many workgroups instead: one workgroup streams
+// one row at only a fraction of the HBM rate.
+//   1. the threshold bin from the row's histogram;
+//   2. every wave streams its contiguous segment of the row in steps of 256
+//      positions and appends the keys at or above the threshold bin to an LDS
+//      entry list, one ordered run per step (recorded per wave and step), and
+//      builds the candidates' second-digit histogram;
+//   3. the exact k-th key T and position cut s_cut as in the finish kernel;
+//   4. each wave counts the selected entries of its runs, the waves' counts
+//      are scanned, and each wave writes its selected positions in order.
+// If the entry list overflows, steps 3-4 read the row's scores again.
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_STEP = 256;                                    // positions per wave step
+constexpr int SEL_MAX_N = 262144;
+constexpr int SEL_MIN_ROWS = 256;
+constexpr int SEL_MAX_STEPS = SEL_MAX_N / SEL_WAVES / SEL_STEP;  // 64
+constexpr int SEL_UNROLL = 8;                                    // steps in flight per wave
+constexpr int SEL_ENT = 12288;
+
+struct SelectShared {
+    uint2 ent[SEL_ENT];                          // (key, position) of the kept keys
+    uint2 rec[SEL_WAVES][SEL_MAX_STEPS];         // (first entry, count) of every step's run
+    uint32_t h2[HIST2_BINS];                     // candidates' second digit
+    uint32_t sh[2048];                           // radix passes when many keys share the prefix
+    uint2 col[COL_MAX];
+    uint32_t wsum[SEL_WAVES];
+    uint32_t alloc, ncol;
+    uint32_t waves[SEL_WAVES];
+    uint32_t res[4];
+};
+
+__global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
+    const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
+    const uint32_t* __restrict__ hist, int32_t* __restrict__ idx) {
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = visible_count(kv_len, row, Tq, L_cap);
+    int32_t* out = idx + (size_t)row * k;
+    if (n <= k) {
+        for (int j = tid; j < k; j += SEL_THREADS) out[j] = j < n ? j : -1;
+        return;
+    }
+    __shared__ SelectShared f;
+    const float* rowp = S + (size_t)row * L_cap;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    // 1. threshold bin
+    for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) f.h2[i] = 0;
+    if (tid == 0) { f.alloc = 0; f.ncol = 0; }
+    const uint2 th = find_bin<TOPK_HIST_BINS / SEL_THREADS, true, SEL_THREADS>(
+        hist + (size_t)row * TOPK_HIST_BINS, (uint32_t)k, f.waves, f.res);   // barriers inside
+    const uint32_t bin1 = th.x;
+
+    // 2. stream the row: wave w owns [w * seg, (w + 1) * seg); position of
+    // (step s, key e, lane) = w * seg + s * 256 + e * 64 + lane, so the order of
+    // a step's keys is (e, lane)
+    const int seg = ((n + SEL_WAVES * SEL_STEP - 1) / (SEL_WAVES * SEL_STEP)) * SEL_STEP;
+    const int p0 = wave * seg;
+    const int nsteps = p0 >= n ? 0 : (min(seg, n - p0) + SEL_STEP - 1) / SEL_STEP;
+    for (int s0 = 0; s0 < nsteps; s0 += SEL_UNROLL) {
+        float sc[SEL_UNROLL][4];
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = p0 + (s0 + u) * SEL_STEP + e * 64 + lane;
+                sc[u][e] = (s0 + u < nsteps && pos < n) ? rowp[pos] : 0.0f;
+            }
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            if (s0 + u >= nsteps) break;
+            const int sbase = p0 + (s0 + u) * SEL_STEP;
+            uint32_t key[4];
+            uint64_t b[4];
+            uint32_t c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = sbase + e * 64 + lane;
+                const bool valid = pos < n;
+                key[e] = valid ? score_key(sc[u][e]) : 0u;
+                const uint32_t d = key[e] >> (32 - TOPK_HIST_BITS);
+                if (valid && d == bin1) atomicAdd(&f.h2[(key[e] >> 10) & (HIST2_BINS - 1)], 1u);
+                b[e] = __ballot(valid && d >= bin1);
+                c[e] = (uint32_t)__popcll(b[e]);
+            }
+            const uint32_t cnt = c[0] + c[1] + c[2] + c[3];
+            uint32_t base = 0;
+            if (lane == 0 && cnt) base = atomicAdd(&f.alloc, cnt);
+            base = __builtin_amdgcn_readfirstlane(base);
+            if (lane == 0) f.rec[wave][s0 + u] = make_uint2(base, cnt);
+            uint32_t before = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if ((b[e] >> lane) & 1ull) {
+                    const uint32_t slot = base + before + (uint32_t)__popcll(b[e] & below);
+                    if (slot < (uint32_t)SEL_ENT) f.ent[slot] = make_uint2(key[e], (uint32_t)(sbase + e * 64 + lane));
+                }
+                before += c[e];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t total = f.alloc;
+    const bool overflow = total > (uint32_t)SEL_ENT;
+
+    // f(key, pos) for every candidate of the threshold bin
+    auto for_each_cand = [&](auto fn) {
+        if (!overflow) {
+            for (uint32_t i = tid; i < total; i += SEL_THREADS) {
+                const uint2 e = f.ent[i];
+                if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
+            }
+        } else {
+            for (int s = tid; s < n; s += SEL_THREADS) {
+                const uint32_t key = score_key(rowp[s]);
+                if ((key >> (32 - TOPK_HIST_BITS)) == bin1) fn(key, s);
+            }
+        }
+    };
+
+    // 3. exact cut
+    uint32_t need = (uint32_t)k - th.y;          // >= 1 keys still to take from the bin
+    const uint2 r2 = find_bin<HIST2_BINS / SEL_THREADS, true, SEL_THREADS>(f.h2, need, f.waves, f.res);
+    need -= r2.y;                                // >= 1 keys to take among the prefix group
+    const uint32_t pre22 = (bin1 << 10) | r2.x;
+    for_each_cand([&](uint32_t key, int s) {
+        if ((key >> 10) == pre22) {
+            const uint32_t slot = atomicAdd(&f.ncol, 1u);
+            if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key, (uint32_t)s);
+        }
+    });
+    __syncthreads();
+    const uint32_t m = f.ncol;
+    uint32_t T;
+    int s_cut;
+    if (m <= (uint32_t)COL_MAX) {
+        for (uint32_t t = tid; t < m; t += SEL_THREADS) {
+            const uint2 e = f.col[t];
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < m; ++j) {
+                const uint2 o = f.col[j];
+                rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
+            }
+            if (rank == need - 1) { f.res[2] = e.x; f.res[3] = e.y; }
+        }
+        __syncthreads();
+        T = f.res[2];
+        s_cut = (int)f.res[3];
+    } else {
+        uint32_t* sh = f.sh;
+        for (int i = tid; i < 1024; i += SEL_THREADS) sh[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int) {
+            if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
+        });
+        __syncthreads();
+        const uint2 r3 = find_bin<1, true, SEL_THREADS>(sh, need, f.waves, f.res);
+        need -= r3.y;
+        T = (pre22 << 10) | r3.x;
+        for (int i = tid; i < 2048; i += SEL_THREADS) sh[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int s) {
+            if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
+        });
+        __syncthreads();
+        const uint2 q2 = find_bin<2, false, SEL_THREADS>(sh, need, f.waves, f.res);
+        const uint32_t p2 = q2.x;
+        need -= q2.y;
+        for (int i = tid; i < 1024; i += SEL_THREADS) sh[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int s) {
+            if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
+        });
+        __syncthreads();
+        const uint32_t p3 = find_bin<1, false, SEL_THREADS>(sh, need, f.waves, f.res).x;
+        s_cut = (int)((p2 << 10) | p3);
+    }
+    __syncthreads();
+    // branch-free selection test (see the finish kernel)
+    auto sel_of = [&](uint32_t key, uint32_t s) -> uint32_t {
+        return (uint32_t)(key > T) | ((uint32_t)(key == T) & (uint32_t)(s <= (uint32_t)s_cut));
+    };
+
+    // 4. ordered output: per wave, its runs (or, after an overflow, its segment
+    // of the row) in order
+    auto walk = [&](auto emit) {
+        if (!overflow) {
+            for (int s = 0; s < nsteps; ++s) {
+                const uint2 r = f.rec[wave][s];
+                for (uint32_t j0 = 0; j0 < r.y; j0 += 64) {
+                    const uint32_t jj = j0 + lane;
+                    const uint2 e = f.ent[r.x + (jj < r.y ? jj : 0u)];
+                    emit((uint32_t)(jj < r.y) & sel_of(e.x, e.y), e.y);
+                }
+            }
+        } else {
+            for (int s = 0; s < nsteps; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pos = p0 + s * SEL_STEP + e * 64 + lane;
+                    const uint32_t in = pos < n ? 1u : 0u;
+                    const uint32_t key = in ? score_key(rowp[pos]) : 0u;
+                    emit(in & sel_of(key, (uint32_t)pos), (uint32_t)pos);
+                }
+        }
+    };
+    uint32_t cnt_w = 0;
+    walk([&](uint32_t sel, uint32_t) { cnt_w += (uint32_t)__popcll(__ballot(sel)); });
+    if (lane == 0) f.wsum[wave] = cnt_w;
+    __syncthreads();
+    uint32_t o = 0;
+    for (int w = 0; w < wave; ++w) o += f.wsum[w];
+    walk([&](uint32_t sel, uint32_t pos) {
+        const uint64_t bb = __ballot(sel);
+        const uint32_t at = o + (uint32_t)__popcll(bb & below);
+        if (sel && at < (uint32_t)k) out[at] = (int32_t)pos;   // exactly k are selected
+        o += (uint32_t)__popcll(bb);
+    });
+}
+
 }  // namespace
 
 TopkLayout topk_layout(int rows, int L_cap) {
@@ -568,6 +796,11 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
     dim3 grid(L.nchunks, rows);
     hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq, L_cap,
                        k, hist);
+    if (L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS) {
+        hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(SEL_THREADS), 0, stream, S,
+                           kv_len, Tq, L_cap, k, hist, idx);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
                        L_cap, k, hist, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks);
     hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(TOPK_THREADS), 0, stream, S, kv_len,

@@ -130,6 +130,47 @@ def test_topk_reuses_workspace_across_calls():
         assert_idx_equal(idx, ref, f"call {it}")
 
 
+# Many rows (a prefill chunk) take the one-workgroup-per-row path.
+
+def test_topk_many_rows_causal_ragged():
+    # rows see 1801..2100 positions: some padded (n <= k), the rest selected
+    r = np.random.default_rng(11)
+    B, Tq, L_cap = 2, 300, 2100
+    S = (r.integers(0, 3000, size=(B, Tq, L_cap)) * 0.5).astype(np.float32)
+    kv_len = torch.tensor([2100, 2090], dtype=torch.int32)
+    _topk_check(S, kv_len, 2048, "many rows ragged")
+
+
+def test_topk_many_rows_long_with_ties():
+    r = np.random.default_rng(12)
+    B, Tq, L_cap = 1, 260, 40000
+    S = (r.integers(0, 20000, size=(B, Tq, L_cap)) * 0.125).astype(np.float32)
+    S[0, 7] = 2.0                                # every score equal
+    S[0, 8, ::3] = -0.0
+    S[0, 9] = -np.inf
+    S[0, 9, 12345:12350] = 4.0
+    kv_len = torch.tensor([L_cap - 3], dtype=torch.int32)
+    _topk_check(S, kv_len, 2048, "many rows long")
+
+
+def test_topk_many_rows_entry_overflow():
+    # the threshold bin holds every score: the LDS entry list overflows and
+    # the row is read again
+    r = np.random.default_rng(13)
+    S = (1000.0 + r.integers(0, 3, size=(1, 256, 20000)) * 0.25).astype(np.float32)
+    kv_len = torch.tensor([20000], dtype=torch.int32)
+    _topk_check(S, kv_len, 2048, "many rows overflow")
+
+
+@pytest.mark.parametrize("L_cap", [262144, 262145])
+def test_topk_many_rows_size_limit(L_cap):
+    # the largest row the one-workgroup path takes, and one past it
+    r = np.random.default_rng(L_cap)
+    S = r.standard_normal((1, 256, L_cap), dtype=np.float32)
+    kv_len = torch.tensor([L_cap], dtype=torch.int32)
+    _topk_check(S, kv_len, 2048, f"many rows L_cap={L_cap}")
+
+
 # ---------------------------------------------------------------- attention ----
 
 def _attend_case(B, Tq, H, D, D_v, L_cap, k, idx_np, seed, name, want_lse=True):
