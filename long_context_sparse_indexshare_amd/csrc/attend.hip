@@ -570,8 +570,8 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k) {
     // columns per workgroup (their QK work is duplicated, their gathers meet
     // in L2), and the k slots split across workgroups
     const bool wide = nq >= 256 || D != 576;
-    p.head_blocks = 2;
-    p.col_parts = wide ? 1 : 2;
+    p.head_blocks = wide ? 2 : 1;
+    p.col_parts = 1;
     const int n_hbg = (H + 32 * p.head_blocks - 1) / (32 * p.head_blocks);
     const int units = nq * n_hbg * p.col_parts;
     const int tiles = (k + TILE_ROWS - 1) / TILE_ROWS;
@@ -611,10 +611,10 @@ hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const 
                                     hipStream_t stream) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
     if (D == 576 && D_v == 512) {
-        if (plan.col_parts == 1)
+        if (plan.head_blocks == 2)
             return launch_attend<2, 1, 576, 512, 1>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out,
                                                     lse, partials, stream);
-        return launch_attend<2, 2, 576, 512, 2>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
+        return launch_attend<1, 1, 576, 512, 2>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
                                                 partials, stream);
     }
     if (D == 160 && D_v == 128)

@@ -150,7 +150,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_hist_kernel(const float* __
 
 // Entries the finishing workgroup stages in LDS (more are read from global).
 constexpr int ENT_LDS = 12288;
-constexpr int STAGE_PER_THREAD = ENT_LDS / TOPK_THREADS;   // all staging loads in flight at once
 constexpr int HIST2_BINS = 1024;                            // second digit: key bits [19:10]
 
 struct RowState {
@@ -255,15 +254,23 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
 }
 
 // LDS of the finishing step.
+constexpr int FIN_THREADS = 1024;
+constexpr int FIN_WAVES = FIN_THREADS / 64;
+constexpr int FIN_SPEC = 6;               // entries per thread requested before the total is known
+constexpr int FIN_LDS_PER = ENT_LDS / FIN_THREADS;
+constexpr int FIN_PER = 4;                // entries per thread per compaction tile
 constexpr int COL_MAX = 512;              // entries ranked directly for the exact cut
+static_assert(HIST2_BINS == FIN_THREADS, "one second-digit bin per thread");
+static_assert(TOPK_MAX_CHUNKS <= FIN_THREADS, "one chunk per thread");
+static_assert(ENT_LDS % FIN_THREADS == 0 && FIN_SPEC <= FIN_LDS_PER, "staging geometry");
 struct FinishShared {
-    uint32_t sh[2048];                    // digit histograms; then per-chunk selected counts
+    uint32_t sh[2048];                    // digit histograms
     uint32_t cbase[TOPK_MAX_CHUNKS];      // chunk -> first entry of its run
-    uint32_t clen[TOPK_MAX_CHUNKS];       // chunk -> run length
+    uint32_t cstart[TOPK_MAX_CHUNKS + 1]; // chunk -> index of its run's first entry in chunk order
     uint2 lent[ENT_LDS];                  // the row's entries, in allocation order
     uint2 col[COL_MAX];                   // entries that share the cut's 22-bit key prefix
     uint32_t ncol;
-    uint32_t waves[TOPK_THREADS / 64];
+    uint32_t waves[FIN_WAVES];
     uint32_t res[4];
 };
 
@@ -272,26 +279,23 @@ struct FinishShared {
 // entries with that prefix are ranked directly under (key desc, position asc)
 // to give the exact k-th key T and the last selected position s_cut among keys
 // equal to T (radix passes over key bits [9:0] and position bits [20:10],
-// [9:0] take over when very many keys share the prefix).  Then every wave
-// takes whole chunks: it counts their selected entries, the counts are
-// scanned over the chunks, and it writes each chunk's selected positions at
-// the chunk's offset in ascending order (the runs are ascending).  If the
-// entry buffer overflowed, the row's scores are re-read instead.
-__global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
+// [9:0] take over when very many keys share the prefix).  The runs, taken in
+// chunk order, list the row's candidates in ascending position: every thread
+// takes FIN_PER consecutive entries of that order, and one scan of the
+// threads' selected counts gives each selected position its output slot.
+// If the entry buffer overflowed, the row's scores are re-read instead.
+__global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
     const uint32_t* __restrict__ hist2, const uint32_t* __restrict__ alloc,
     const RowState* __restrict__ row_state, const uint2* __restrict__ runs,
     const uint2* __restrict__ ent, uint32_t cap, int nchunks_max, int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    constexpr int NW = TOPK_THREADS / 64;
     const int n = visible_count(kv_len, row, Tq, L_cap);
     int32_t* out = idx + (size_t)row * k;
     if (n <= k) {
         // every visible position, then -1 padding
-        for (int j = tid; j < k; j += TOPK_THREADS) out[j] = j < n ? j : -1;
+        for (int j = tid; j < k; j += FIN_THREADS) out[j] = j < n ? j : -1;
         return;
     }
     __shared__ FinishShared f;
@@ -299,56 +303,68 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
     const float* rowp = S + (size_t)row * L_cap;
     const uint2* re = ent + (size_t)row * cap;
     // every load of this phase is issued before any is used: the row state,
-    // the second-digit histogram, the chunk table and the entries (entries
-    // past the row's total are loaded but never used; they lie inside the
-    // row's buffer)
+    // the second-digit histogram, the chunk table and the first entries
+    // (entries past the row's total are loaded but never used; they lie
+    // inside the row's buffer)
     const RowState rs = row_state[row];
     const uint32_t total = alloc[row];
-    uint32_t h2[HIST2_BINS / TOPK_THREADS];
+    const uint32_t h2 = hist2[(size_t)row * HIST2_BINS + tid];
+    const uint2 rr = tid < nch ? runs[(size_t)row * nchunks_max + tid] : make_uint2(0u, 0u);
+    const uint32_t nspec = cap < (uint32_t)(FIN_SPEC * FIN_THREADS) ? cap : (uint32_t)(FIN_SPEC * FIN_THREADS);
+    uint2 v[FIN_SPEC];
 #pragma unroll
-    for (int u = 0; u < HIST2_BINS / TOPK_THREADS; ++u)
-        h2[u] = hist2[(size_t)row * HIST2_BINS + u * TOPK_THREADS + tid];
-    const int c0 = 2 * tid, c1 = 2 * tid + 1;
-    const uint2 r0 = c0 < nch ? runs[(size_t)row * nchunks_max + c0] : make_uint2(0u, 0u);
-    const uint2 r1 = c1 < nch ? runs[(size_t)row * nchunks_max + c1] : make_uint2(0u, 0u);
-    const uint32_t nstage = cap < (uint32_t)ENT_LDS ? cap : (uint32_t)ENT_LDS;
-    uint2 v[STAGE_PER_THREAD];
-#pragma unroll
-    for (int u = 0; u < STAGE_PER_THREAD; ++u) {
-        const uint32_t i = u * TOPK_THREADS + tid;
-        v[u] = i < nstage ? re[i] : make_uint2(0u, 0u);
+    for (int u = 0; u < FIN_SPEC; ++u) {
+        const uint32_t i = u * FIN_THREADS + tid;
+        v[u] = i < nspec ? re[i] : make_uint2(0u, 0u);
     }
     const uint32_t bin1 = rs.bin1;
     // 0: entries staged in LDS; 1: read from the entry buffer; 2: buffer overflowed, re-read S
     const int mode = total <= (uint32_t)ENT_LDS ? 0 : (total <= cap ? 1 : 2);
     if (mode == 0) {
 #pragma unroll
-        for (int u = 0; u < STAGE_PER_THREAD; ++u) {
-            const uint32_t i = u * TOPK_THREADS + tid;
+        for (int u = 0; u < FIN_SPEC; ++u) {
+            const uint32_t i = u * FIN_THREADS + tid;
             if (i < total) f.lent[i] = v[u];
         }
-    }
+        if (total > (uint32_t)(FIN_SPEC * FIN_THREADS)) {
+            uint2 w[FIN_LDS_PER - FIN_SPEC];
 #pragma unroll
-    for (int u = 0; u < HIST2_BINS / TOPK_THREADS; ++u) f.sh[u * TOPK_THREADS + tid] = h2[u];
-    if (c0 < nch) { f.cbase[c0] = r0.x; f.clen[c0] = r0.y; }
-    if (c1 < nch) { f.cbase[c1] = r1.x; f.clen[c1] = r1.y; }
-    if (tid == 0) f.ncol = 0;
+            for (int u = 0; u < FIN_LDS_PER - FIN_SPEC; ++u) {
+                const uint32_t i = (FIN_SPEC + u) * FIN_THREADS + tid;
+                w[u] = i < total ? re[i] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < FIN_LDS_PER - FIN_SPEC; ++u) {
+                const uint32_t i = (FIN_SPEC + u) * FIN_THREADS + tid;
+                if (i < total) f.lent[i] = w[u];
+            }
+        }
+    }
+    f.sh[tid] = h2;
+    if (tid < nch) f.cbase[tid] = rr.x;
+    uint32_t ntot;
+    const uint32_t cs = block_exclusive_scan<FIN_THREADS>(tid < nch ? rr.y : 0u, &ntot, f.waves);
+    if (tid < nch) f.cstart[tid] = cs;
+    if (tid == 0) {
+        f.cstart[nch] = ntot;
+        f.ncol = 0;
+    }
     __syncthreads();
 
     // f(key, pos) for every candidate of the threshold bin
     auto for_each_cand = [&](auto fn) {
         if (mode == 0) {
-            for (uint32_t i = tid; i < total; i += TOPK_THREADS) {
+            for (uint32_t i = tid; i < total; i += FIN_THREADS) {
                 const uint2 e = f.lent[i];
                 if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
             }
         } else if (mode == 1) {
-            for (uint32_t i = tid; i < total; i += TOPK_THREADS) {
+            for (uint32_t i = tid; i < total; i += FIN_THREADS) {
                 const uint2 e = re[i];
                 if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
             }
         } else {
-            for (int s = tid; s < n; s += TOPK_THREADS) {
+            for (int s = tid; s < n; s += FIN_THREADS) {
                 const uint32_t key = score_key(rowp[s]);
                 if ((key >> (32 - TOPK_HIST_BITS)) == bin1) fn(key, s);
             }
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
     uint32_t* sh = f.sh;
     uint32_t need = (uint32_t)k - rs.above1;     // >= 1 keys still to take from the bin
     // key bits [19:10]: from the second-digit histogram the classify step built
-    const uint2 r2 = find_bin<HIST2_BINS / TOPK_THREADS, true>(sh, need, f.waves, f.res);
+    const uint2 r2 = find_bin<1, true, FIN_THREADS>(sh, need, f.waves, f.res);
     need -= r2.y;                                // >= 1 keys to take among the prefix group
     const uint32_t pre22 = (bin1 << 10) | r2.x;
     // the entries with that 22-bit prefix
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
     if (m <= (uint32_t)COL_MAX) {
         // rank every collected entry under (key desc, position asc); the one of
         // rank need-1 is the last selected: its key is T, its position s_cut
-        for (uint32_t t = tid; t < m; t += TOPK_THREADS) {
+        for (uint32_t t = tid; t < m; t += FIN_THREADS) {
             const uint2 e = f.col[t];
             uint32_t rank = 0;
             for (uint32_t j = 0; j < m; ++j) {
@@ -389,32 +405,32 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
         s_cut = (int)f.res[3];
     } else {
         // key bits [9:0]
-        for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
+        for (int i = tid; i < 1024; i += FIN_THREADS) sh[i] = 0;
         __syncthreads();
         for_each_cand([&](uint32_t key, int) {
             if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
         });
         __syncthreads();
-        const uint2 r3 = find_bin<4, true>(sh, need, f.waves, f.res);
+        const uint2 r3 = find_bin<1, true, FIN_THREADS>(sh, need, f.waves, f.res);
         need -= r3.y;                            // keys equal to T still to take (>= 1)
         T = (pre22 << 10) | r3.x;
         // among keys equal to T, the need-th lowest position: position bits [20:10], then [9:0]
-        for (int i = tid; i < 2048; i += TOPK_THREADS) sh[i] = 0;
+        for (int i = tid; i < 2048; i += FIN_THREADS) sh[i] = 0;
         __syncthreads();
         for_each_cand([&](uint32_t key, int s) {
             if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
         });
         __syncthreads();
-        const uint2 q2 = find_bin<8, false>(sh, need, f.waves, f.res);
+        const uint2 q2 = find_bin<2, false, FIN_THREADS>(sh, need, f.waves, f.res);
         const uint32_t p2 = q2.x;
         need -= q2.y;
-        for (int i = tid; i < 1024; i += TOPK_THREADS) sh[i] = 0;
+        for (int i = tid; i < 1024; i += FIN_THREADS) sh[i] = 0;
         __syncthreads();
         for_each_cand([&](uint32_t key, int s) {
             if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
         });
         __syncthreads();
-        const uint32_t p3 = find_bin<4, false>(sh, need, f.waves, f.res).x;
+        const uint32_t p3 = find_bin<1, false, FIN_THREADS>(sh, need, f.waves, f.res).x;
         s_cut = (int)((p2 << 10) | p3);
     }
     __syncthreads();
@@ -426,12 +442,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
     auto sel_of = [&](uint32_t key, uint32_t s) -> uint32_t {
         return (uint32_t)(key > T) | ((uint32_t)(key == T) & (uint32_t)(s <= (uint32_t)s_cut));
     };
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     if (mode == 2) {
         // overflow: ordered stream compaction over the row's scores
         constexpr int PER = 8;
-        constexpr int TILE = PER * TOPK_THREADS;
+        constexpr int TILE = PER * FIN_THREADS;
         uint32_t written = 0;
         for (uint32_t t0 = 0; t0 < (uint32_t)n; t0 += TILE) {
             const uint32_t v0 = t0 + (uint32_t)tid * PER;
@@ -444,8 +459,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
                 selmask |= (in & sel_of(key, vv)) << u;
             }
             uint32_t tile_total;
-            uint32_t o = written +
-                         block_exclusive_scan((uint32_t)__popc(selmask), &tile_total, f.waves);
+            uint32_t o = written + block_exclusive_scan<FIN_THREADS>((uint32_t)__popc(selmask),
+                                                                     &tile_total, f.waves);
 #pragma unroll
             for (int u = 0; u < PER; ++u) {
                 if ((selmask >> u) & 1u) {
@@ -458,53 +473,50 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_finish_kernel(
         return;
     }
 
-    // chunk-wise compaction: a wave per chunk; the LDS and global entry
-    // sources are separate instantiations so that no load goes through a
-    // generic pointer
+    // ordered compaction over the runs in chunk order; the LDS and global
+    // entry sources are separate instantiations so that no load goes through
+    // a generic pointer
     auto compact = [&](auto source) {
         constexpr bool LDS = decltype(source)::value;
         auto get = [&](uint32_t a) -> uint2 {
             if constexpr (LDS) return f.lent[a];
             else return re[a];
         };
-        // 1. selected entries per chunk
-        for (int c = wave; c < nch; c += NW) {
-            const uint32_t base = f.cbase[c], len = f.clen[c];
-            uint32_t cnt = 0;
-            for (uint32_t j0 = 0; j0 < len; j0 += 128) {
-                const uint32_t ja = j0 + lane, jb = j0 + 64 + lane;
-                const uint2 ea = get(base + (ja < len ? ja : 0u));
-                const uint2 eb = get(base + (jb < len ? jb : 0u));
-                const uint32_t sa = (uint32_t)(ja < len) & sel_of(ea.x, ea.y);
-                const uint32_t sb = (uint32_t)(jb < len) & sel_of(eb.x, eb.y);
-                cnt += (uint32_t)__popcll(__ballot(sa)) + (uint32_t)__popcll(__ballot(sb));
+        uint32_t written = 0;
+        for (uint32_t t0 = 0; t0 < ntot; t0 += FIN_PER * FIN_THREADS) {
+            const uint32_t i0 = t0 + (uint32_t)tid * FIN_PER;
+            // the run holding entry i0: the last chunk whose run starts at or
+            // before it (past the end: the last entry, whose result is masked)
+            const uint32_t a0 = i0 < ntot ? i0 : ntot - 1;
+            int lo = 0, hi = nch - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (f.cstart[mid] <= a0) lo = mid;
+                else hi = mid - 1;
             }
-            if (lane == 0) f.sh[c] = cnt;
-        }
-        __syncthreads();
-        // 2. offsets: exclusive scan over the chunks (two per thread, nch <= 512)
-        {
-            const uint32_t a0 = c0 < nch ? f.sh[c0] : 0u;
-            const uint32_t a1 = c1 < nch ? f.sh[c1] : 0u;
-            uint32_t tot;
-            const uint32_t ex = block_exclusive_scan(a0 + a1, &tot, f.waves);   // barriers inside
-            if (c0 < nch) f.sh[c0] = ex;
-            if (c1 < nch) f.sh[c1] = ex + a0;
-        }
-        __syncthreads();
-        // 3. write each chunk's selected positions at its offset
-        for (int c = wave; c < nch; c += NW) {
-            const uint32_t base = f.cbase[c], len = f.clen[c];
-            uint32_t o = f.sh[c];
-            for (uint32_t j0 = 0; j0 < len; j0 += 64) {
-                const uint32_t j = j0 + lane;
-                const uint2 e = get(base + (j < len ? j : 0u));
-                const uint32_t sel = (uint32_t)(j < len) & sel_of(e.x, e.y);
-                const uint64_t b = __ballot(sel);
-                const uint32_t at = o + (uint32_t)__popcll(b & below);
-                if (sel && at < (uint32_t)k) out[at] = (int32_t)e.y;   // exactly k are selected
-                o += (uint32_t)__popcll(b);
+            int c = lo;
+            uint32_t pos[FIN_PER];
+            uint32_t selmask = 0;
+#pragma unroll
+            for (int u = 0; u < FIN_PER; ++u) {
+                const uint32_t i = i0 + u;
+                const uint32_t a = i < ntot ? i : ntot - 1;
+                while (f.cstart[c + 1] <= a) ++c;
+                const uint2 e = get(f.cbase[c] + (a - f.cstart[c]));
+                pos[u] = e.y;
+                selmask |= ((uint32_t)(i < ntot) & sel_of(e.x, e.y)) << u;
             }
+            uint32_t tile_total;
+            uint32_t o = written + block_exclusive_scan<FIN_THREADS>((uint32_t)__popc(selmask),
+                                                                     &tile_total, f.waves);
+#pragma unroll
+            for (int u = 0; u < FIN_PER; ++u) {
+                if ((selmask >> u) & 1u) {
+                    if (o < (uint32_t)k) out[o] = (int32_t)pos[u];   // exactly k are selected
+                    ++o;
+                }
+            }
+            written += tile_total;
         }
     };
     if (mode == 0) compact(std::true_type{});
@@ -803,7 +815,7 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
     }
     hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
                        L_cap, k, hist, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks);
-    hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(TOPK_THREADS), 0, stream, S, kv_len,
+    hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(FIN_THREADS), 0, stream, S, kv_len,
                        Tq, L_cap, k, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks, idx);
     return hipGetLastError();
 }
