@@ -102,6 +102,19 @@ def test_topk_crafted_ties():
     _topk_check(S, kv_len, k, "crafted")
 
 
+def test_topk_crafted_ties_long_rows():
+    # rows longer than 131072 positions take the histogram / classify path
+    L_cap, k = 140000, 2048
+    kv_len = torch.tensor([L_cap] * 5, dtype=torch.int32)
+    S = np.random.default_rng(21).standard_normal((5, 1, L_cap)).astype(np.float32)
+    S[1] = 3.5                                  # all equal
+    S[2, 0, ::2] = -0.0                         # -0.0 and +0.0 tie
+    S[3, 0, :] = np.arange(L_cap) % 7           # duplicates straddle the cut
+    S[4, 0, :] = -np.inf
+    S[4, 0, 70000:70003] = 1.0
+    _topk_check(S, kv_len, k, "crafted long")
+
+
 def test_topk_all_in_one_bin_overflows_candidates():
     # every key in the first-digit bin: the candidate list overflows and the
     # last workgroup re-reads the row
