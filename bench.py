@@ -13,9 +13,10 @@ Inputs are synthetic (synth/), generated on the GPU; decode steps rotate over
 several independent input instances so the 256 MiB MALL cannot hold the
 working set between steps.  Timing: W untimed warm-up steps, then exactly K
 steps between two synchronised HIP events on the stream the library launches
-on.  The dominant kernel (the indexer for decode) is also timed per launch
-with HIP events for its roofline entry, and the CPU oracle is timed on one
-group of the same workload on the host.
+on.  Each stage (indexer, top-k, one attention layer) is also timed alone,
+back to back with HIP events, for its roofline entry; "roofline" is the stage
+that takes the largest share of a step (attention, four launches per group),
+and the CPU oracle is timed on one group of the same workload on the host.
 
 Prints one JSON line.
 """
@@ -61,12 +62,14 @@ def algorithmic(wl, n_layers=None):
     ix_bytes = keys_read * wl.D_I + rows * wl.H_I * (wl.D_I + 4)
     ix_ops = 2 * wl.H_I * wl.D_I * pairs
     topk_bytes = rows * wl.k * 4
+    topk_read_bytes = sum(ns) * 4 + topk_bytes      # the scores once, the index sets
     at_bytes = sel * wl.D * 2 + rows * wl.H * (wl.D + wl.D_v) * 2
     at_flops = sel * wl.H * 2 * (wl.D + wl.D_v)
     t_ix = max(ix_ops / PEAK_INT8, ix_bytes / PEAK_HBM)
     t_at = max(at_flops / PEAK_BF16, at_bytes / PEAK_HBM)
     t_ideal = t_ix + topk_bytes / PEAK_HBM + L * t_at
     return {"ix_bytes": ix_bytes, "ix_ops": ix_ops, "topk_bytes": topk_bytes,
+            "topk_read_bytes": topk_read_bytes,
             "at_bytes_per_layer": at_bytes, "at_flops_per_layer": at_flops,
             "group_bytes": ix_bytes + topk_bytes + L * at_bytes,
             "t_ideal_s": t_ideal, "t_ix_s": t_ix, "t_at_s": t_at,
@@ -182,7 +185,11 @@ def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
     return tokens, dt, results
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scores_C2_128K_traffic.txt")
+# committed counter summaries: stage -> (summary file, kernel source it was taken on)
+TRAFFIC = {
+    "indexer": ("indexer_scores_C2_128K_traffic.txt", "indexer.hip"),
+    "attend": ("sparse_attend_C2_128K_traffic.txt", "attend.hip"),
+}
 
 
 def source_digest(path):
@@ -191,15 +198,18 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per indexer launch from the committed counter summary, or None
-    when the summary is missing or the kernel source changed since it was taken."""
+def measured_traffic(stage):
+    """HBM bytes per launch of a stage from its committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    if stage not in TRAFFIC:
+        return None
+    fname, srcname = TRAFFIC[stage]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", fname)) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
-    src = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "csrc", "indexer.hip")
+    src = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "csrc", srcname)
     if kv.get("source_sha256", "").strip() != source_digest(src):
         return None
     return float(kv["traffic_bytes_per_launch"])
@@ -213,7 +223,7 @@ def run_stage(isa, wl, stage, reps, torch):
     idx = torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
     ws = isa.Workspace()
-    if stage == "indexer":
+    if stage in ("indexer", "attend"):
         # a 1 GiB device copy first: its counters calibrate the traffic figures
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -407,8 +417,26 @@ def main():
     alg = dec["alg"]
     t = dec["t_step"]
     tokens = wl.tokens_per_group
-    t_ix = dec["stages_us"]["indexer"] * 1e-6
-    ix_achieved = alg["ix_bytes"] / t_ix
+    st = dec["stages_us"]
+    # per stage: launches per group, algorithmic bytes per launch, kernels
+    stages = {
+        "indexer": (1, alg["ix_bytes"], "indexer_scores_kernel<64, 128>"),
+        "topk": (1, alg["topk_read_bytes"],
+                 "topk_hist_kernel + topk_classify_kernel + topk_finish_kernel"),
+        "attend": (wl.n_layers, alg["at_bytes_per_layer"],
+                   "sparse_attend_kernel<1, 1, 576, 512, 2> + merge_splits_kernel (one layer)"),
+    }
+    stage_us = {"indexer": st["indexer"], "topk": st["topk"], "attend": st["attend_per_layer"]}
+    rooflines = {}
+    for name, (per_group, nbytes, kernels) in stages.items():
+        t_launch = stage_us[name] * 1e-6
+        rooflines[name] = {"kernel": kernels, "bound": "hbm", "launches_per_group": per_group,
+                           "launch_us": stage_us[name], "algorithmic_bytes": nbytes,
+                           "achieved": nbytes / t_launch / 1e9, "peak": PEAK_HBM / 1e9,
+                           "unit": "GB/s", "frac": nbytes / t_launch / PEAK_HBM,
+                           "traffic": measured_traffic(name),
+                           "share_of_step": per_group * t_launch / t}
+    dominant = max(rooflines, key=lambda n: rooflines[n]["share_of_step"])
     cpu_name, ncpu = host_info()
     line = {
         "metric": METRIC,
@@ -426,9 +454,8 @@ def main():
         "config": {"workload": "C2_128K decode group: B=8 x 1 query, context 131072, indexer "
                                "64x128 int8, top-2048, 4 layers x 64 heads x 576 bf16 latent",
                    "input_instances": args.instances},
-        "roofline": {"kernel": "indexer_scores", "bound": "hbm",
-                     "achieved": ix_achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": ix_achieved / PEAK_HBM, "traffic": measured_traffic()},
+        "roofline": dict(rooflines[dominant], stage=dominant),
+        "stage_rooflines": rooflines,
         "group_roofline": {"t_ideal_us": alg["t_ideal_s"] * 1e6, "t_measured_us": t * 1e6,
                            "frac": alg["t_ideal_s"] / t,
                            "algorithmic_bytes": alg["group_bytes"],

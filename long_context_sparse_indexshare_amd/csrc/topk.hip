@@ -22,6 +22,8 @@
 //                positions as the ordered stream compaction of the runs taken
 //                chunk by chunk.  If the entry buffer overflowed (a very flat
 //                score distribution) the row's scores are re-read instead.
+// With at least 256 rows of at most 262144 positions (a prefill chunk) steps 2
+// and 3 are one kernel instead, a workgroup per row (topk_select_kernel).
 // Workgroups never wait on each other inside a kernel: on gfx950 a device-
 // scope fence writes back and invalidates the whole L2 of the XCD, so each
 // hand-over between workgroups goes through a kernel boundary instead.
