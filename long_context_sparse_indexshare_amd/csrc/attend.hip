@@ -248,13 +248,20 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+            // in kp order; a wave's own block comes from its registers (the
+            // same bits it stored)
 #pragma unroll
             for (int p = 0; p < G::KSP; ++p) {
-                const int w2 = p * HB + hbl;
+                if (p == kp) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
-                    s[4 * r4] += v.x; s[4 * r4 + 1] += v.y; s[4 * r4 + 2] += v.z; s[4 * r4 + 3] += v.w;
+                    for (int r = 0; r < 16; ++r) s[r] += st[r];
+                } else {
+                    const int w2 = p * HB + hbl;
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
+                        s[4 * r4] += v.x; s[4 * r4 + 1] += v.y; s[4 * r4 + 2] += v.z; s[4 * r4 + 3] += v.w;
+                    }
                 }
             }
         }
@@ -377,35 +384,51 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
 
+    // With two groups, group g finishes value blocks [g*NB/2, (g+1)*NB/2): each
+    // group hands the other the blocks it does not finish, with its (max, sum),
+    // through the (now free) tile LDS, and both combine the two online-softmax
+    // states in the same order (group 0's term first), so both hold the same
+    // sum and maximum.
+    constexpr int HALF = GR == 2 ? G::NB / 2 : G::NB;
+    auto mine_block = [&](int nb) { return GR == 1 || nb / HALF == grp; };
     if constexpr (GR == 2) {
-        // group 1 hands (o, max, sum) to group 0 through the (now free) tile
-        // LDS; group 0 combines the two online-softmax states
-        float* mb = reinterpret_cast<float*>(&tiles[0][0]);
-        constexpr int PER_LANE = G::NB * 16 + 2;
-        static_assert(4 * 64 * PER_LANE * 4 <= GR * G::TILE_BYTES, "hand-off fits the tiles");
-        lds_barrier();
-        if (grp == 1) {
+        static_assert(G::NB % 2 == 0, "value blocks split between the groups");
+        constexpr int PER_LANE = HALF * 16 + 2;
+        static_assert(GR * 4 * 64 * PER_LANE * 4 <= GR * G::TILE_BYTES, "hand-off fits the tiles");
+        float* const mb = reinterpret_cast<float*>(&tiles[0][0]);
+        float* const give = mb + (size_t)((grp * 4 + wave) * PER_LANE) * 64;
+        const float* const take = mb + (size_t)(((1 - grp) * 4 + wave) * PER_LANE) * 64;
+        lds_barrier();                      // every wave is done with the tiles
 #pragma unroll
-            for (int nb = 0; nb < G::NB; ++nb)
+        for (int nb = 0; nb < G::NB; ++nb) {
+            if (!mine_block(nb)) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mb[((wave * PER_LANE) + nb * 16 + r) * 64 + lane] = o[nb][r];
-            mb[((wave * PER_LANE) + G::NB * 16) * 64 + lane] = m_run;
-            mb[((wave * PER_LANE) + G::NB * 16 + 1) * 64 + lane] = l_run;
+                for (int r = 0; r < 16; ++r) give[((nb % HALF) * 16 + r) * 64 + lane] = o[nb][r];
+            }
         }
+        give[(HALF * 16) * 64 + lane] = m_run;
+        give[(HALF * 16 + 1) * 64 + lane] = l_run;
         lds_barrier();
-        if (grp == 1) return;
-        const float m1 = mb[((wave * PER_LANE) + G::NB * 16) * 64 + lane];
-        const float l1 = mb[((wave * PER_LANE) + G::NB * 16 + 1) * 64 + lane];
-        const float M = fmaxf(m_run, m1);
+        const float m_t = take[(HALF * 16) * 64 + lane];
+        const float l_t = take[(HALF * 16 + 1) * 64 + lane];
+        const float m0 = grp == 0 ? m_run : m_t, m1 = grp == 0 ? m_t : m_run;
+        const float l0 = grp == 0 ? l_run : l_t, l1 = grp == 0 ? l_t : l_run;
+        const float M = fmaxf(m0, m1);
         const float Mu = M == -__builtin_inff() ? 0.0f : M;
-        const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
+        const float a0 = __builtin_amdgcn_exp2f(m0 - Mu);
         const float a1 = __builtin_amdgcn_exp2f(m1 - Mu);
 #pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb)
+        for (int nb = 0; nb < G::NB; ++nb) {
+            if (mine_block(nb)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                o[nb][r] = o[nb][r] * a0 + mb[((wave * PER_LANE) + nb * 16 + r) * 64 + lane] * a1;
-        l_run = l_run * a0 + l1 * a1;
+                for (int r = 0; r < 16; ++r) {
+                    const float own = o[nb][r];
+                    const float oth = take[((nb % HALF) * 16 + r) * 64 + lane];
+                    o[nb][r] = (grp == 0 ? own : oth) * a0 + (grp == 0 ? oth : own) * a1;
+                }
+            }
+        }
+        l_run = l0 * a0 + l1 * a1;
         m_run = M;
     }
 
@@ -419,6 +442,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         uint16_t* orow = out + ((size_t)q * H + head) * DV;
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb) {
+            if (!mine_block(nb)) continue;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int col = col0 + 32 * nb + 8 * r4 + 4 * g;
@@ -430,7 +454,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                 *reinterpret_cast<ushort4*>(orow + col) = v;
             }
         }
-        if (lse && kp == 0 && vh == 0 && g == 0)
+        if (lse && grp == 0 && kp == 0 && vh == 0 && g == 0)
             lse[(size_t)q * H + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * LN2 : -__builtin_inff();
         return;
     }
@@ -448,6 +472,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                       (G::NB * 4 * 64);
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb) {
+            if (!mine_block(nb)) continue;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const uint32_t lo = (uint32_t)f2bf(o[nb][4 * r4] * inv) |
@@ -458,7 +483,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                 __builtin_nontemporal_store(v2u{lo, hi}, po + (nb * 4 + r4) * 64 + lane);
             }
         }
-        if (head_ok && kp == 0 && g == 0)
+        if (head_ok && grp == 0 && kp == 0 && g == 0)
             part_ml[(((size_t)q * splits + sp) * VS + vh) * H + head] = make_float2(m_run, l_tot);
     }
 }

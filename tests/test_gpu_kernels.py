@@ -227,6 +227,15 @@ def test_attend_576_many_queries():
     _attend_case(2, 130, 64, 576, 512, 9000, 128, idx, seed=13, name="576 wide")
 
 
+def test_attend_576_unsplit_two_groups():
+    # 160 queries: the 32-head, two-group variant with enough workgroups that
+    # the k slots are not split (each group writes its half of the columns)
+    r = np.random.default_rng(14)
+    idx = _random_sets(2, 80, 5000, 256, 256, r)
+    idx[0, 3, 100:] = -1
+    _attend_case(2, 80, 64, 576, 512, 5000, 256, idx, seed=15, name="576 unsplit")
+
+
 def test_attend_160_16_heads():
     r = np.random.default_rng(7)
     idx = _random_sets(1, 50, 1024, 64, 64, r)
