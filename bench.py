@@ -322,6 +322,41 @@ def run_mtp(isa, torch, reps):
             "reuse_speedup": t_recompute / t_reuse}
 
 
+def run_fp8_kv(isa, torch, steps, warmup, n_inst):
+    """The C2_128K decode group with FP8 latent caches (E4M3 codes, one
+    power-of-two scale byte per row, bf16 RoPE dims): whole groups and one
+    attention layer alone, against that layer's algorithmic bytes."""
+    import synth
+    wl = synth.WORKLOADS["C2_128K"]
+    log("C2_128K fp8: generating inputs")
+    insts = [synth.group_inputs(wl.scaled(seed=wl.seed + 1000 * i), device="cuda", kv8=True)
+             for i in range(n_inst)]
+    torch.cuda.synchronize()
+    ws = isa.Workspace()
+    calls = [isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], None, wl.k,
+                           wl.D_v, wl.sm_scale, ws=ws, kv8=(d["C8"], d["Ce"], d["Cr"]))
+             for d in insts]
+    t = time_group(isa, calls, steps, warmup, torch)
+    d = insts[0]
+    out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+    t_at = time_per_launch(lambda: isa.isa_sparse_mla_attend_fp8(
+        d["Q"][0], d["C8"][0], d["Ce"][0], d["Cr"][0], calls[0].idx, wl.sm_scale, out=out, ws=ws),
+        20, torch)
+    a = algorithmic(wl)
+    row_bytes = wl.D_v + 1 + (wl.D - wl.D_v) * 2          # codes, scale byte, RoPE dims
+    sel = wl.B * wl.Tq * min(wl.k, wl.kv_len)
+    at_bytes = sel * row_bytes + wl.B * wl.Tq * wl.H * (wl.D + wl.D_v) * 2
+    t_ideal = a["t_ix_s"] + a["topk_bytes"] / PEAK_HBM + wl.n_layers * at_bytes / PEAK_HBM
+    del calls, insts
+    torch.cuda.empty_cache()
+    return {"workload": "C2_128K decode group with FP8 latent caches (E4M3 + per-row "
+                        "power-of-two scale, bf16 RoPE)",
+            "tokens_per_s": wl.tokens_per_group / t, "ms_per_step": t * 1e3,
+            "attend_us_per_layer": t_at * 1e6, "attend_algorithmic_bytes": at_bytes,
+            "attend_frac_hbm": at_bytes / t_at / PEAK_HBM,
+            "group_frac_of_roofline": t_ideal / t}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -375,7 +410,8 @@ def main():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the 1M-context ablation and the 7-step MTP measurements")
+                    help="skip the 1M-context ablation, the 7-step MTP and the FP8-cache "
+                         "measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group"],
                     help="profiling mode: run one stage of --workload --reps times and print "
@@ -474,6 +510,7 @@ def main():
     if not args.no_extra:
         line["ablation"] = run_ablation(isa, torch, steps=10, warmup=3)
         line["mtp"] = run_mtp(isa, torch, reps=5)
+        line["fp8_kv"] = run_fp8_kv(isa, torch, steps=50, warmup=10, n_inst=args.instances)
     if args.prefill:
         wp = synth.WORKLOADS["C3"]
         pre = run_workload(isa, wp, max(2, min(args.steps, 5)), 2, 1, torch,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ISA_ABI_VERSION 1
+#define ISA_ABI_VERSION 2
 #define ISA_MAX_TOPK 2048            /* index_topk of [P3] */
 #define ISA_MAX_LCAP (1 << 21)       /* positions must fit 21 bits */
 
@@ -126,6 +126,29 @@ isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int
                                  size_t ws_bytes, void* stream);
 
 /*
+ * The same attention over an FP8 latent cache (the FP8 KV cache the pages
+ * name among the serving optimisations: [P1] section 4, [P4] section 3).
+ * Row s of sequence b is stored as
+ *   C8[b,s,0:D_c]  OCP FP8 E4M3 codes of the latent dims (bias 7, max 448),
+ *   Ce[b,s]        one byte e: the row's scale is 2^(e - 127) (UE8M0),
+ *   Cr[b,s,0:D_r]  the RoPE dims in bf16,
+ * and stands for the bf16 row C[b,s,d] = e4m3(C8[b,s,d]) * 2^(Ce[b,s]-127)
+ * for d < D_c and Cr[b,s,d-D_c] for D_c <= d < D_c + D_r.  The result is
+ * isa_sparse_mla_attend on that row with D = D_c + D_r and D_v = D_c (the
+ * values are the dequantized latent dims).  The kernel dequantizes to bf16,
+ * which is exact while every dequantized value is a normal bf16 number (for
+ * example e in [10, 246]); E4M3 NaN codes (0x7F, 0xFF) give unspecified
+ * values.  Supported: (D_c, D_r) in {(512, 64), (128, 32)}; other conditions
+ * and the workspace as for isa_sparse_mla_attend with D = D_c + D_r.
+ */
+size_t isa_attend_fp8_workspace_bytes(int B, int Tq, int H, int D_c, int D_r, int k);
+isa_status isa_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
+                                     const uint16_t* Cr, const int32_t* idx, int B, int Tq, int H,
+                                     int D_c, int D_r, int L_cap, int k, float sm_scale,
+                                     uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/*
  * One IndexShare layer group ([P1] section 1 table; [P4] sections 2.1 and
  * 2.2.1; index_topk_freq and index_share_for_mtp_iteration of [P3]).
  *  - reuse_idx = 0, per_layer_indexer = 0: indexer + top-k run once from
@@ -136,9 +159,11 @@ isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int
  *  - per_layer_indexer = 1: the baseline without sharing; layer l runs its
  *    own indexer + top-k from (qI[l], w[l], kI[l]) before its attention, and
  *    idx ends holding the last layer's set.
- * The pointer arrays (qI, w, kI, Q, C, out, lse) are HOST arrays read during
- * the call only; the tensors they point to are device memory.  lse may be
- * NULL, or an array whose entries may be NULL.
+ * The pointer arrays (qI, w, kI, Q, C, out, lse, C8, Ce, Cr) are HOST arrays
+ * read during the call only; the tensors they point to are device memory.
+ * lse may be NULL, or an array whose entries may be NULL.
+ * kv_fp8 = 1: the layers' latent caches are FP8 as in isa_sparse_mla_attend_fp8
+ * (D_c = D_v, D_r = D - D_v); C is ignored and C8, Ce, Cr hold n_layers entries.
  */
 typedef struct {
     int B, Tq, L_cap;
@@ -159,6 +184,10 @@ typedef struct {
     int per_layer_indexer;
     void* ws;
     size_t ws_bytes;
+    int kv_fp8;
+    const uint8_t* const* C8;          /* n_layers entries with kv_fp8 */
+    const uint8_t* const* Ce;
+    const uint16_t* const* Cr;
 } isa_group_args;
 
 size_t isa_group_workspace_bytes(const isa_group_args* args);

@@ -17,7 +17,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libisa.so")
-ISA_ABI_VERSION = 1
+ISA_ABI_VERSION = 2
 ISA_MAX_TOPK = 2048
 
 ISA_OK = 0
@@ -29,6 +29,7 @@ ISA_ERR_HIP = -4
 EXPORTED_SYMBOLS = (
     "isa_abi_version", "isa_last_error", "isa_indexer_scores", "isa_topk_workspace_bytes",
     "isa_topk_select", "isa_attend_workspace_bytes", "isa_sparse_mla_attend",
+    "isa_attend_fp8_workspace_bytes", "isa_sparse_mla_attend_fp8",
     "isa_group_workspace_bytes", "isa_group_forward",
 )
 
@@ -56,6 +57,7 @@ class GroupArgs(ctypes.Structure):
         ("Q", _P), ("C", _P), ("out", _P), ("lse", _P),
         ("idx", _P), ("reuse_idx", _I), ("per_layer_indexer", _I),
         ("ws", _P), ("ws_bytes", _Z),
+        ("kv_fp8", _I), ("C8", _P), ("Ce", _P), ("Cr", _P),
     ]
 
 
@@ -86,6 +88,11 @@ def load_library():
     lib.isa_sparse_mla_attend.restype = _I
     lib.isa_sparse_mla_attend.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P,
                                           _P, _Z, _P]
+    lib.isa_attend_fp8_workspace_bytes.restype = _Z
+    lib.isa_attend_fp8_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+    lib.isa_sparse_mla_attend_fp8.restype = _I
+    lib.isa_sparse_mla_attend_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                              _P, _P, _P, _Z, _P]
     lib.isa_group_workspace_bytes.restype = _Z
     lib.isa_group_workspace_bytes.argtypes = [ctypes.POINTER(GroupArgs)]
     lib.isa_group_forward.restype = _I
@@ -224,22 +231,67 @@ def isa_sparse_mla_attend(Q, C, idx, D_v: int, sm_scale: float, out=None, lse=No
     return out, lse
 
 
-class GroupCall:
-    """Marshals one isa_group_forward call and keeps its ctypes arrays alive."""
+def isa_attend_fp8_workspace_bytes(B: int, Tq: int, H: int, D_c: int, D_r: int, k: int) -> int:
+    return int(load_library().isa_attend_fp8_workspace_bytes(B, Tq, H, D_c, D_r, k))
 
-    def __init__(self, qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence, C: Sequence,
-                 k: int, D_v: int, sm_scale: float, idx=None, reuse_idx: bool = False,
-                 per_layer_indexer: bool = False, out: Optional[Sequence] = None,
-                 lse: Optional[Sequence] = None, ws: Optional[Workspace] = None):
+
+def isa_sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, sm_scale: float, out=None, lse=None,
+                              want_lse: bool = False, ws: Optional[Workspace] = None,
+                              stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse latent attention over an FP8 cache: C8 [B,L_cap,D_c] E4M3 codes
+    (uint8), Ce [B,L_cap] exponent bytes (uint8, scale 2^(e-127)), Cr
+    [B,L_cap,D_r] bf16 RoPE dims.  Returns (out [B,Tq,H,D_c] bf16, lse or None)."""
+    _dev(Q, torch.bfloat16, "Q"); _dev(C8, torch.uint8, "C8"); _dev(Ce, torch.uint8, "Ce")
+    _dev(Cr, torch.bfloat16, "Cr"); _dev(idx, torch.int32, "idx")
+    B, Tq, H, D = Q.shape
+    L_cap, D_c = C8.shape[1], C8.shape[2]
+    D_r = Cr.shape[2]
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, Tq, H, D_c), dtype=torch.bfloat16, device=Q.device)
+    _dev(out, torch.bfloat16, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=Q.device)
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    nbytes = isa_attend_fp8_workspace_bytes(B, Tq, H, D_c, D_r, k)
+    buf = _workspace(ws, Q.device).get(nbytes)
+    _check(load_library().isa_sparse_mla_attend_fp8(
+        _ptr(Q), _ptr(C8), _ptr(Ce), _ptr(Cr), _ptr(idx), B, Tq, H, D_c, D_r, L_cap, k,
+        float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(), _stream_ptr(stream)))
+    return out, lse
+
+
+class GroupCall:
+    """Marshals one isa_group_forward call and keeps its ctypes arrays alive.
+    With kv8 = (C8, Ce, Cr), three per-layer lists, the layers' caches are FP8
+    (as in isa_sparse_mla_attend_fp8) and C is ignored."""
+
+    def __init__(self, qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence,
+                 C: Optional[Sequence], k: int, D_v: int, sm_scale: float, idx=None,
+                 reuse_idx: bool = False, per_layer_indexer: bool = False,
+                 out: Optional[Sequence] = None, lse: Optional[Sequence] = None,
+                 ws: Optional[Workspace] = None, kv8: Optional[Tuple[Sequence, Sequence, Sequence]] = None):
         n = len(Q)
         dev = Q[0].device
         for i, x in enumerate(Q):
             _dev(x, torch.bfloat16, f"Q[{i}]")
-        for i, x in enumerate(C):
-            _dev(x, torch.bfloat16, f"C[{i}]")
+        if kv8 is not None:
+            C8, Ce, Cr = (list(x) for x in kv8)
+            if not (len(C8) == len(Ce) == len(Cr) == n):
+                raise ValueError("kv8 needs one (C8, Ce, Cr) entry per layer")
+            for i in range(n):
+                _dev(C8[i], torch.uint8, f"C8[{i}]"); _dev(Ce[i], torch.uint8, f"Ce[{i}]")
+                _dev(Cr[i], torch.bfloat16, f"Cr[{i}]")
+            C = []
+            L_cap = C8[0].shape[1]
+        else:
+            C8 = Ce = Cr = []
+            for i, x in enumerate(C):
+                _dev(x, torch.bfloat16, f"C[{i}]")
+            L_cap = C[0].shape[1]
         _dev(kv_len, torch.int32, "kv_len")
         B, Tq, H, D = Q[0].shape
-        L_cap = C[0].shape[1]
         n_ix = n if per_layer_indexer else (0 if reuse_idx else 1)
         qI = list(qI or [])[: max(n_ix, 0)]
         w = list(w or [])[: max(n_ix, 0)]
@@ -256,13 +308,14 @@ class GroupCall:
         if out is None:
             out = [torch.empty((B, Tq, H, D_v), dtype=torch.bfloat16, device=dev) for _ in range(n)]
         self.idx, self.out, self.lse = idx, list(out), (list(lse) if lse is not None else None)
-        self._keep = [qI, w, kI, Q, C, self.out, self.lse]
+        self._keep = [qI, w, kI, Q, C, self.out, self.lse, C8, Ce, Cr]
 
         def arr(ts):
             return (_P * len(ts))(*[_ptr(t) for t in ts]) if ts else None
 
         self._arrays = [arr(qI), arr(w), arr(kI), arr(list(Q)), arr(list(C)), arr(self.out),
-                        arr(self.lse) if self.lse is not None else None]
+                        arr(self.lse) if self.lse is not None else None,
+                        arr(C8), arr(Ce), arr(Cr)]
         a = GroupArgs()
         a.B, a.Tq, a.L_cap, a.H_I, a.D_I, a.k = B, Tq, L_cap, H_I, D_I, int(k)
         a.H, a.D, a.D_v, a.n_layers, a.sm_scale = H, D, int(D_v), n, float(sm_scale)
@@ -271,12 +324,17 @@ class GroupCall:
         a.kI = ctypes.cast(self._arrays[2], _P) if self._arrays[2] else None
         a.kv_len = _ptr(kv_len)
         a.Q = ctypes.cast(self._arrays[3], _P)
-        a.C = ctypes.cast(self._arrays[4], _P)
+        a.C = ctypes.cast(self._arrays[4], _P) if self._arrays[4] else None
         a.out = ctypes.cast(self._arrays[5], _P)
         a.lse = ctypes.cast(self._arrays[6], _P) if self._arrays[6] is not None else None
         a.idx = _ptr(idx)
         a.reuse_idx = int(bool(reuse_idx))
         a.per_layer_indexer = int(bool(per_layer_indexer))
+        a.kv_fp8 = int(kv8 is not None)
+        if kv8 is not None:
+            a.C8 = ctypes.cast(self._arrays[7], _P)
+            a.Ce = ctypes.cast(self._arrays[8], _P)
+            a.Cr = ctypes.cast(self._arrays[9], _P)
         self.args = a
         nbytes = int(load_library().isa_group_workspace_bytes(ctypes.byref(a)))
         self.ws_buf = _workspace(ws, dev).get(nbytes)
@@ -292,11 +350,11 @@ def isa_group_workspace_bytes(call: GroupCall) -> int:
     return int(load_library().isa_group_workspace_bytes(ctypes.byref(call.args)))
 
 
-def isa_group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence, C: Sequence,
-                      k: int, D_v: int, sm_scale: float, idx=None, reuse_idx: bool = False,
-                      per_layer_indexer: bool = False, out=None, lse=None,
-                      ws: Optional[Workspace] = None, stream=None):
+def isa_group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence,
+                      C: Optional[Sequence], k: int, D_v: int, sm_scale: float, idx=None,
+                      reuse_idx: bool = False, per_layer_indexer: bool = False, out=None, lse=None,
+                      ws: Optional[Workspace] = None, stream=None, kv8=None):
     """One IndexShare layer group: (idx, [out_l], [lse_l] or None)."""
     call = GroupCall(qI, w, kI, kv_len, Q, C, k, D_v, sm_scale, idx=idx, reuse_idx=reuse_idx,
-                     per_layer_indexer=per_layer_indexer, out=out, lse=lse, ws=ws)
+                     per_layer_indexer=per_layer_indexer, out=out, lse=lse, ws=ws, kv8=kv8)
     return call(stream)

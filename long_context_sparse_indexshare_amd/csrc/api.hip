@@ -79,6 +79,8 @@ isa_status check_topk(const float* S, const int32_t* kv_len, int B, int Tq, int 
     return ISA_OK;
 }
 
+// C: the bf16 cache, or (fp8) any non-NULL stand-in when the FP8 arrays are
+// checked separately by check_kv8
 isa_status check_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B, int Tq,
                         int H, int D, int D_v, int L_cap, int k, float sm_scale,
                         const uint16_t* out) {
@@ -101,6 +103,18 @@ isa_status check_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx
     ISA_CHECK(aligned(Q, 16) && aligned(C, 16) && aligned(out, 16) && aligned(idx, 4),
               ISA_ERR_INVALID_ARG, "attend: Q, C and out need 16-byte alignment");
     return ISA_OK;
+}
+
+isa_status check_kv8(const uint8_t* C8, const uint8_t* Ce, const uint16_t* Cr) {
+    ISA_CHECK(C8 && Ce && Cr, ISA_ERR_INVALID_ARG, "attend fp8: NULL cache pointer");
+    ISA_CHECK(aligned(C8, 16) && aligned(Cr, 16), ISA_ERR_INVALID_ARG,
+              "attend fp8: C8 and Cr need 16-byte alignment");
+    return ISA_OK;
+}
+
+// Shapes of the FP8 variant, as (D, D_v) of the bf16 one.
+bool kv8_shape_supported(int D_c, int D_r) {
+    return (D_c == 512 && D_r == 64) || (D_c == 128 && D_r == 32);
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -191,6 +205,35 @@ isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int
                      "attend launch");
 }
 
+size_t isa_attend_fp8_workspace_bytes(int B, int Tq, int H, int D_c, int D_r, int k) {
+    if (D_c <= 0 || D_r <= 0) return 0;
+    return isa_attend_workspace_bytes(B, Tq, H, D_c + D_r, D_c, k);
+}
+
+isa_status isa_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
+                                     const uint16_t* Cr, const int32_t* idx, int B, int Tq, int H,
+                                     int D_c, int D_r, int L_cap, int k, float sm_scale,
+                                     uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    ISA_CHECK(kv8_shape_supported(D_c, D_r), ISA_ERR_UNSUPPORTED,
+              "attend fp8: (D_c=%d, D_r=%d) not compiled; (512, 64) or (128, 32)", D_c, D_r);
+    isa_status st = check_kv8(C8, Ce, Cr);
+    if (st != ISA_OK) return st;
+    st = check_attend(Q, Cr, idx, B, Tq, H, D_c + D_r, D_c, L_cap, k, sm_scale, out);
+    if (st != ISA_OK) return st;
+    ISA_CHECK(!lse || aligned(lse, 4), ISA_ERR_INVALID_ARG, "attend fp8: misaligned lse");
+    const size_t need = isa_attend_fp8_workspace_bytes(B, Tq, H, D_c, D_r, k);
+    if (need) {
+        ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
+                  "attend fp8: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                  ws_bytes);
+    }
+    return check_hip(isa::launch_sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, B, Tq, H, D_c + D_r,
+                                                       D_c, L_cap, k, sm_scale, out, lse, ws,
+                                                       static_cast<hipStream_t>(stream)),
+                     "attend fp8 launch");
+}
+
 size_t isa_group_workspace_bytes(const isa_group_args* a) {
     if (!a || a->B <= 0 || a->Tq <= 0 || a->L_cap <= 0 || a->H <= 0 || a->D_v <= 0 || a->k <= 0)
         return 0;
@@ -201,8 +244,14 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
     ISA_CHECK(a, ISA_ERR_INVALID_ARG, "group: NULL args");
     ISA_CHECK(a->n_layers >= 1 && a->n_layers <= 64, ISA_ERR_INVALID_ARG,
               "group: n_layers=%d outside [1, 64]", a->n_layers);
-    ISA_CHECK(a->Q && a->C && a->out && a->idx && a->kv_len, ISA_ERR_INVALID_ARG,
-              "group: NULL pointer array or tensor");
+    const bool kv8 = a->kv_fp8 != 0;
+    ISA_CHECK(a->Q && (kv8 ? (a->C8 && a->Ce && a->Cr) : a->C != nullptr) && a->out && a->idx &&
+                  a->kv_len,
+              ISA_ERR_INVALID_ARG, "group: NULL pointer array or tensor");
+    if (kv8) {
+        ISA_CHECK(kv8_shape_supported(a->D_v, a->D - a->D_v), ISA_ERR_UNSUPPORTED,
+                  "group: FP8 cache with (D=%d, D_v=%d) not compiled", a->D, a->D_v);
+    }
     const bool per_layer = a->per_layer_indexer != 0;
     const bool need_index = !a->reuse_idx || per_layer;
     const int n_ix = per_layer ? a->n_layers : (need_index ? 1 : 0);
@@ -223,8 +272,12 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
         if (st != ISA_OK) return st;
     }
     for (int l = 0; l < a->n_layers; ++l) {
-        isa_status st = check_attend(a->Q[l], a->C[l], a->idx, a->B, a->Tq, a->H, a->D, a->D_v,
-                                     a->L_cap, a->k, a->sm_scale, a->out[l]);
+        if (kv8) {
+            isa_status st = check_kv8(a->C8[l], a->Ce[l], a->Cr[l]);
+            if (st != ISA_OK) return st;
+        }
+        isa_status st = check_attend(a->Q[l], kv8 ? a->Cr[l] : a->C[l], a->idx, a->B, a->Tq, a->H,
+                                     a->D, a->D_v, a->L_cap, a->k, a->sm_scale, a->out[l]);
         if (st != ISA_OK) return st;
         if (a->lse && a->lse[l]) {
             ISA_CHECK(aligned(a->lse[l], 4), ISA_ERR_INVALID_ARG, "group: misaligned lse[%d]", l);
@@ -263,11 +316,15 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
             if (st != ISA_OK) return st;
         }
         float* lse = a->lse ? a->lse[l] : nullptr;
-        isa_status st = check_hip(isa::launch_sparse_mla_attend(a->Q[l], a->C[l], a->idx, a->B,
-                                                                a->Tq, a->H, a->D, a->D_v,
-                                                                a->L_cap, a->k, a->sm_scale,
-                                                                a->out[l], lse, attend_ws, stream),
-                                  "group: attend launch");
+        const hipError_t e =
+            kv8 ? isa::launch_sparse_mla_attend_fp8(a->Q[l], a->C8[l], a->Ce[l], a->Cr[l], a->idx,
+                                                    a->B, a->Tq, a->H, a->D, a->D_v, a->L_cap,
+                                                    a->k, a->sm_scale, a->out[l], lse, attend_ws,
+                                                    stream)
+                : isa::launch_sparse_mla_attend(a->Q[l], a->C[l], a->idx, a->B, a->Tq, a->H, a->D,
+                                                a->D_v, a->L_cap, a->k, a->sm_scale, a->out[l],
+                                                lse, attend_ws, stream);
+        isa_status st = check_hip(e, "group: attend launch");
         if (st != ISA_OK) return st;
     }
     return ok();

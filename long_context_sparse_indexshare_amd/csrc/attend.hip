@@ -78,6 +78,16 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two E4M3 codes (the low or high 16 bits of w) times the row scale, as two
+// bf16 in one word.  The scale is a power of two, so the products are exact
+// in bf16 while they stay in its normal range.
+template <bool HI>
+__device__ __forceinline__ uint32_t kv8_dequant_pair(uint32_t w, float scale) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int HB, int VS, int D, int DV, int GR>
 struct AttendGeom {
     static constexpr int KSP = 4 / HB;              // waves sharing a head block (K split)
@@ -112,15 +122,25 @@ struct AttendGeom {
     static_assert(CW % 32 == 0, "value columns per wave");
 };
 
-template <int HB, int VS, int D, int DV, int GR>
+// KV8: the latent cache is FP8 (see kv8_dequant_pair): the gather reads the
+// E4M3 codes, the row's exponent byte and the bf16 RoPE slice, and the tile
+// store writes the dequantized bf16 row, so the LDS tile and everything that
+// reads it are the same as for a bf16 cache.
+template <int HB, int VS, int D, int DV, int GR, bool KV8>
 __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                              (AttendGeom<HB, VS, D, DV, GR>::WG_PER_CU)) void sparse_attend_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const int32_t* __restrict__ idx,
-    int Tq, int H, int L_cap, int k, float scale_log2, int slots_per_split, int splits,
-    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const uint8_t* __restrict__ C8,
+    const uint8_t* __restrict__ Ce, const uint16_t* __restrict__ Cr,
+    const int32_t* __restrict__ idx, int Tq, int H, int L_cap, int k, float scale_log2,
+    int slots_per_split, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
+    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml) {
     using G = AttendGeom<HB, VS, D, DV, GR>;
     constexpr int ROWB = G::ROWB;
+    // FP8 row: DV code bytes, the exponent byte, D - DV bf16 RoPE dims
+    constexpr int F8CH = DV / 16;                  // 16-byte code chunks per row
+    constexpr int F8PT = F8CH / G::TPR;            // code chunks per gather thread
+    constexpr int RCH = (D - DV) * 2 / 16;         // 16-byte RoPE chunks per row
+    static_assert(!KV8 || (F8CH % G::TPR == 0 && RCH <= G::TPR), "FP8 gather geometry");
 
     __shared__ __attribute__((aligned(16))) char tiles[GR][G::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) float xbufs[GR][4][4][64][4];   // partial S^T blocks
@@ -146,7 +166,10 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const int slot0 = sp * slots_per_split;
     const int slot1 = min(slot0 + slots_per_split, k);
     const int32_t* qidx = idx + (size_t)q * k;
-    const char* Cb = reinterpret_cast<const char*>(C + (size_t)b * L_cap * D);
+    const char* Cb = KV8 ? nullptr : reinterpret_cast<const char*>(C + (size_t)b * L_cap * D);
+    const char* C8b = KV8 ? reinterpret_cast<const char*>(C8 + (size_t)b * L_cap * DV) : nullptr;
+    const uint8_t* Ceb = KV8 ? Ce + (size_t)b * L_cap : nullptr;
+    const char* Crb = KV8 ? reinterpret_cast<const char*>(Cr + (size_t)b * L_cap * (D - DV)) : nullptr;
     const int col0 = vh * G::COLS + kp * G::CW;   // first value column of this wave
     char* tile = tiles[grp];
     float (*xbuf)[4][64][4] = xbufs[grp];
@@ -203,6 +226,39 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     _Pragma("unroll") for (int i_ = 0; i_ < G::GPT; ++i_) {                                   \
         if (G::CH % G::TPR == 0 || gsub + G::TPR * i_ < G::CH)                                 \
             *reinterpret_cast<v4u*>(lrow + i_ * G::TPR * 16) = R[i_];                          \
+    }
+    // FP8 rows: thread (row, sub) takes code chunks sub, sub + 8, ... (each is
+    // 16 dims, 32 bytes of the bf16 tile row), RoPE chunk sub (if any) and the
+    // row's exponent byte; an invalid slot reads zero codes with exponent 0.
+    const uintptr_t c8base = reinterpret_cast<uintptr_t>(C8b);
+    const uintptr_t crbase = reinterpret_cast<uintptr_t>(Crb);
+    char* const lrow8 = tile + grow * ROWB;
+#define ISA_LOAD_TILE8(R8, RR, SE, TS)                                                         \
+    {                                                                                          \
+        const int s_ = sidx[(TS) - slot0 + grow];                                              \
+        const uintptr_t ca_ = (s_ >= 0 ? c8base + (size_t)s_ * DV : zero_row) + gsub * 16;     \
+        _Pragma("unroll") for (int i_ = 0; i_ < F8PT; ++i_)                                    \
+            R8[i_] = *(global_v4u_ptr)(ca_ + i_ * G::TPR * 16);                                \
+        if (gsub < RCH)                                                                        \
+            RR = *(global_v4u_ptr)((s_ >= 0 ? crbase + (size_t)s_ * ((D - DV) * 2) : zero_row) \
+                                   + gsub * 16);                                               \
+        SE = s_ >= 0 ? (uint32_t)Ceb[s_] : 0u;                                                 \
+    }
+#define ISA_STORE_TILE8(R8, RR, SE)                                                            \
+    {                                                                                          \
+        const float sc_ = __uint_as_float((SE) << 23);                                         \
+        _Pragma("unroll") for (int i_ = 0; i_ < F8PT; ++i_) {                                  \
+            char* d_ = lrow8 + (gsub + i_ * G::TPR) * 32;                                      \
+            *reinterpret_cast<v4u*>(d_) = v4u{kv8_dequant_pair<false>(R8[i_][0], sc_),         \
+                                              kv8_dequant_pair<true>(R8[i_][0], sc_),          \
+                                              kv8_dequant_pair<false>(R8[i_][1], sc_),         \
+                                              kv8_dequant_pair<true>(R8[i_][1], sc_)};         \
+            *reinterpret_cast<v4u*>(d_ + 16) = v4u{kv8_dequant_pair<false>(R8[i_][2], sc_),    \
+                                                   kv8_dequant_pair<true>(R8[i_][2], sc_),     \
+                                                   kv8_dequant_pair<false>(R8[i_][3], sc_),    \
+                                                   kv8_dequant_pair<true>(R8[i_][3], sc_)};    \
+        }                                                                                      \
+        if (gsub < RCH) *reinterpret_cast<v4u*>(lrow8 + DV * 2 + gsub * 16) = RR;              \
     }
 
     // one tile of the online softmax attention, from the LDS tile
@@ -322,8 +378,14 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     // while the current one is computed from LDS
     auto tile_start = [&](int it) { return slot0 + (it * GR + grp) * TILE_ROWS; };
     lds_barrier();                          // sidx visible
-    v4u rA[G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
-    if (iters > 0) { ISA_LOAD_TILE(rA, tile_start(0)) }
+    v4u rA[KV8 ? 1 : G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
+    v4u r8A[KV8 ? F8PT : 1], rrA = v4u{0u, 0u, 0u, 0u};
+    uint32_t seA = 0;
+#define ISA_LOAD_ANY(TS)                                                                        \
+    if constexpr (KV8) { ISA_LOAD_TILE8(r8A, rrA, seA, TS) } else { ISA_LOAD_TILE(rA, TS) }
+#define ISA_STORE_ANY()                                                                         \
+    if constexpr (KV8) { ISA_STORE_TILE8(r8A, rrA, seA) } else { ISA_STORE_TILE(rA) }
+    if (iters > 0) { ISA_LOAD_ANY(tile_start(0)) }
     // this wave's share of Q^T, requested after the first tile's gather (which
     // gates everything): lane (head j, half g) holds dims 16*ks + 8*g .. +8 for
     // ks in [kp*KSW, (kp+1)*KSW).  Heads past H read head 0; their results are
@@ -370,17 +432,21 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
             qb[i] = __builtin_bit_cast(
                 v8bf, *reinterpret_cast<const uint4*>(qrow + 16 * (kp * G::KSW + i) + 8 * g));
     }
-    if (iters > 0) { ISA_STORE_TILE(rA) }
-    if (iters > 1) { ISA_LOAD_TILE(rA, tile_start(1)) }
+    if (iters > 0) { ISA_STORE_ANY() }
+    if (iters > 1) { ISA_LOAD_ANY(tile_start(1)) }
     lds_barrier();
     for (int it = 0; it < iters; ++it) {
-        compute_tile(tile_start(it));                        // in flight: rA = it+1
+        compute_tile(tile_start(it));                        // in flight: tile it+1
         if (it + 1 >= iters) break;
         lds_barrier();
-        ISA_STORE_TILE(rA)
-        if (it + 2 < iters) { ISA_LOAD_TILE(rA, tile_start(it + 2)) }
+        ISA_STORE_ANY()
+        if (it + 2 < iters) { ISA_LOAD_ANY(tile_start(it + 2)) }
         lds_barrier();
     }
+#undef ISA_LOAD_ANY
+#undef ISA_STORE_ANY
+#undef ISA_LOAD_TILE8
+#undef ISA_STORE_TILE8
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
 
@@ -558,8 +624,17 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
         lse[(size_t)q * H + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
 }
 
-template <int HB, int VS, int D, int DV, int GR>
-hipError_t launch_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx, int B, int Tq,
+// The latent cache: bf16 rows (C), or FP8 codes, exponents and bf16 RoPE
+// slices (C8, Ce, Cr).
+struct KvSrc {
+    const uint16_t* C;
+    const uint8_t* C8;
+    const uint8_t* Ce;
+    const uint16_t* Cr;
+};
+
+template <int HB, int VS, int D, int DV, int GR, bool KV8>
+hipError_t launch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B, int Tq,
                          int H, int L_cap, int k, float sm_scale, uint16_t* out, float* lse,
                          void* partials, hipStream_t stream) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, DV, k);
@@ -569,10 +644,10 @@ hipError_t launch_attend(const uint16_t* Q, const uint16_t* C, const int32_t* id
     float2* part_ml = reinterpret_cast<float2*>(base + plan.part_ml_off);
     const int n_hbg = (H + 32 * HB - 1) / (32 * HB);
     dim3 grid(plan.splits, nq, n_hbg * VS);
-    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV, GR>), grid, dim3(AT_THREADS * GR), 0,
-                       stream, Q,
-                       C, idx, Tq, H, L_cap, k, sm_scale * LOG2E, plan.slots_per_split,
-                       plan.splits, out, lse, part_o, part_ml);
+    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV, GR, KV8>), grid,
+                       dim3(AT_THREADS * GR), 0, stream, Q, kv.C, kv.C8, kv.Ce, kv.Cr, idx, Tq, H,
+                       L_cap, k, sm_scale * LOG2E, plan.slots_per_split, plan.splits, out, lse,
+                       part_o, part_ml);
     if (plan.splits > 1)
     {
         using Gm = AttendGeom<HB, VS, D, DV, GR>;
@@ -590,10 +665,10 @@ hipError_t launch_attend(const uint16_t* Q, const uint16_t* C, const int32_t* id
 AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k) {
     AttendPlan p;
     const int nq = B * Tq;
-    // many queries: one workgroup per query holds both head blocks and every
-    // value column; few queries (decode): one head block and half the value
-    // columns per workgroup (their QK work is duplicated, their gathers meet
-    // in L2), and the k slots split across workgroups
+    // many queries: one workgroup per query holds both 32-head blocks and
+    // every value column; few queries (decode): one 32-head block per
+    // workgroup, two groups of 4 waves on alternate tiles (the two blocks'
+    // gathers of a row meet in L2), and the k slots split across workgroups
     const bool wide = nq >= 256 || D != 576;
     p.head_blocks = wide ? 2 : 1;
     p.col_parts = 1;
@@ -630,22 +705,43 @@ bool attend_shape_supported(int H, int D, int D_v) {
     return false;
 }
 
+namespace {
+
+template <bool KV8>
+hipError_t dispatch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B, int Tq, int H,
+                           int D, int D_v, int L_cap, int k, float sm_scale, uint16_t* out,
+                           float* lse, void* partials, hipStream_t stream) {
+    const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
+    if (D == 576 && D_v == 512) {
+        if (plan.head_blocks == 2)
+            return launch_attend<2, 1, 576, 512, 1, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale,
+                                                         out, lse, partials, stream);
+        return launch_attend<1, 1, 576, 512, 2, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale, out,
+                                                     lse, partials, stream);
+    }
+    if (D == 160 && D_v == 128)
+        return launch_attend<2, 1, 160, 128, 1, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale, out,
+                                                     lse, partials, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,
                                     float sm_scale, uint16_t* out, float* lse, void* partials,
                                     hipStream_t stream) {
-    const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
-    if (D == 576 && D_v == 512) {
-        if (plan.head_blocks == 2)
-            return launch_attend<2, 1, 576, 512, 1>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out,
-                                                    lse, partials, stream);
-        return launch_attend<1, 1, 576, 512, 2>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
-                                                partials, stream);
-    }
-    if (D == 160 && D_v == 128)
-        return launch_attend<2, 1, 160, 128, 1>(Q, C, idx, B, Tq, H, L_cap, k, sm_scale, out, lse,
-                                                partials, stream);
-    return hipErrorInvalidValue;
+    return dispatch_attend<false>(Q, KvSrc{C, nullptr, nullptr, nullptr}, idx, B, Tq, H, D, D_v,
+                                  L_cap, k, sm_scale, out, lse, partials, stream);
+}
+
+hipError_t launch_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
+                                        const uint16_t* Cr, const int32_t* idx, int B, int Tq,
+                                        int H, int D, int D_v, int L_cap, int k, float sm_scale,
+                                        uint16_t* out, float* lse, void* partials,
+                                        hipStream_t stream) {
+    return dispatch_attend<true>(Q, KvSrc{nullptr, C8, Ce, Cr}, idx, B, Tq, H, D, D_v, L_cap, k,
+                                 sm_scale, out, lse, partials, stream);
 }
 
 }  // namespace isa

@@ -60,6 +60,14 @@ hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const 
                                     float sm_scale, uint16_t* out, float* lse, void* partials,
                                     hipStream_t stream);
 
+// FP8 latent cache: C8 [B,L_cap,D_v] E4M3 codes, Ce [B,L_cap] exponent bytes,
+// Cr [B,L_cap,D-D_v] bf16 RoPE slices; otherwise as launch_sparse_mla_attend.
+hipError_t launch_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
+                                        const uint16_t* Cr, const int32_t* idx, int B, int Tq,
+                                        int H, int D, int D_v, int L_cap, int k, float sm_scale,
+                                        uint16_t* out, float* lse, void* partials,
+                                        hipStream_t stream);
+
 bool indexer_shape_supported(int H_I, int D_I);
 bool attend_shape_supported(int H, int D, int D_v);
 

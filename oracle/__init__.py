@@ -48,6 +48,11 @@ def _load():
     lib.oracle_group_forward.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.c_float,
                                          P, P, P, P, P, P, P, P, P, I, I, P]
     lib.oracle_group_forward.restype = None
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_sparse_mla_attend_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I,
+                                                 ctypes.c_float, P, P]
+    lib.oracle_sparse_mla_attend_fp8.restype = None
     _lib = lib
     return lib
 
@@ -115,6 +120,32 @@ def sparse_mla_attend(Q, C, idx, D_v: int, sm_scale: float):
     lse = np.empty((B, Tq, H), dtype=np.float64)
     _load().oracle_sparse_mla_attend(_ptr(Q), _ptr(C), _ptr(idx), B, Tq, H, D, int(D_v), L_cap,
                                      k, ctypes.c_float(sm_scale), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def e4m3_to_double(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code."""
+    return float(_load().oracle_e4m3_to_double(int(code) & 0xFF))
+
+
+def sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, sm_scale: float):
+    """(out [B,Tq,H,D_c] float64, lse [B,Tq,H] float64) of sparse attention over
+    an FP8 latent cache (C8 codes, Ce exponent bytes, Cr bf16 RoPE dims)."""
+    Q = _np(Q, np.uint16)
+    C8 = _np(C8, np.uint8)
+    Ce = _np(Ce, np.uint8)
+    Cr = _np(Cr, np.uint16)
+    idx = _np(idx, np.int32)
+    B, Tq, H, D = Q.shape
+    L_cap, D_c = C8.shape[1], C8.shape[2]
+    D_r = Cr.shape[2]
+    k = idx.shape[2]
+    assert D == D_c + D_r and Ce.shape == (B, L_cap) and Cr.shape == (B, L_cap, D_r)
+    out = np.empty((B, Tq, H, D_c), dtype=np.float64)
+    lse = np.empty((B, Tq, H), dtype=np.float64)
+    _load().oracle_sparse_mla_attend_fp8(_ptr(Q), _ptr(C8), _ptr(Ce), _ptr(Cr), _ptr(idx), B, Tq,
+                                         H, D_c, D_r, L_cap, k, ctypes.c_float(sm_scale),
+                                         _ptr(out), _ptr(lse))
     return out, lse
 
 

@@ -176,6 +176,85 @@ void oracle_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_
     free(z);
 }
 
+/* OCP FP8 E4M3 (the "FN" variant): sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent field 0 holds the subnormals m * 2^-9; no
+ * infinities; S.1111.111 is NaN; the largest finite magnitude is 448. */
+double oracle_e4m3_to_double(uint8_t code) {
+    const int sign = code >> 7;
+    const int e = (code >> 3) & 15;
+    const int m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Attention over an FP8 latent cache: every selected row is first written
+ * out as the D = D_c + D_r values it stands for (E4M3 code times the row's
+ * power-of-two scale 2^(Ce - 127) for d < D_c, the bf16 RoPE value after
+ * that), then the attention is the same as oracle_sparse_mla_attend's. */
+void oracle_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
+                                  const uint16_t* Cr, const int32_t* idx, int B, int Tq, int H,
+                                  int D_c, int D_r, int L_cap, int k, float sm_scale,
+                                  double* out, double* lse) {
+    const int D = D_c + D_r;
+    const int D_v = D_c;
+    double code_value[256];
+    for (int c = 0; c < 256; ++c) code_value[c] = oracle_e4m3_to_double((uint8_t)c);
+    double* rows = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1) * (size_t)D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    const double scale = (double)sm_scale;
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < Tq; ++t) {
+            const int32_t* sel = idx + ((size_t)b * Tq + t) * k;
+            for (int j = 0; j < k; ++j) {
+                int32_t s = sel[j];
+                if (s < 0 || s >= L_cap) continue;
+                const size_t row = (size_t)b * L_cap + s;
+                const double row_scale = ldexp(1.0, (int)Ce[row] - 127);
+                double* r = rows + (size_t)j * D;
+                for (int d = 0; d < D_c; ++d) r[d] = code_value[C8[row * D_c + d]] * row_scale;
+                for (int d = 0; d < D_r; ++d) r[D_c + d] = bf16_to_double(Cr[row * D_r + d]);
+            }
+            for (int h = 0; h < H; ++h) {
+                const uint16_t* q = Q + (((size_t)b * Tq + t) * H + h) * D;
+                double* o = out + (((size_t)b * Tq + t) * H + h) * D_v;
+                double m = -INFINITY;
+                int n_valid = 0;
+                for (int j = 0; j < k; ++j) {
+                    int32_t s = sel[j];
+                    if (s < 0 || s >= L_cap) continue;
+                    const double* r = rows + (size_t)j * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += bf16_to_double(q[d]) * r[d];
+                    z[j] = scale * dot;
+                    if (z[j] > m) m = z[j];
+                    ++n_valid;
+                }
+                for (int v = 0; v < D_v; ++v) o[v] = 0.0;
+                if (n_valid == 0) {
+                    if (lse) lse[((size_t)b * Tq + t) * H + h] = -INFINITY;
+                    continue;
+                }
+                double denom = 0.0;
+                for (int j = 0; j < k; ++j) {
+                    int32_t s = sel[j];
+                    if (s < 0 || s >= L_cap) continue;
+                    const double* r = rows + (size_t)j * D;
+                    double e = exp(z[j] - m);
+                    denom += e;
+                    for (int v = 0; v < D_v; ++v) o[v] += e * r[v];
+                }
+                for (int v = 0; v < D_v; ++v) o[v] /= denom;
+                if (lse) lse[((size_t)b * Tq + t) * H + h] = m + log(denom);
+            }
+        }
+    }
+    free(z);
+    free(rows);
+}
+
 void oracle_group_forward(int B, int Tq, int L_cap, int H_I, int D_I, int k, int H, int D,
                           int D_v, int n_layers, float sm_scale,
                           const int8_t* const* qI, const float* const* w,

@@ -45,6 +45,19 @@ void oracle_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_
                               int B, int Tq, int H, int D, int D_v, int L_cap, int k,
                               float sm_scale, double* out, double* lse);
 
+/* Value of an OCP FP8 E4M3 code (bias 7, subnormals m * 2^-9, no infinities,
+ * S.1111.111 = NaN, largest finite 448). */
+double oracle_e4m3_to_double(uint8_t code);
+
+/* oracle_sparse_mla_attend over an FP8 latent cache: row s of sequence b
+ * stands for C[b,s,d] = e4m3(C8[b,s,d]) * 2^(Ce[b,s] - 127) for d < D_c and
+ * Cr[b,s,d-D_c] (bf16) for D_c <= d < D_c + D_r; D = D_c + D_r, D_v = D_c.
+ * C8 [B,L_cap,D_c] codes, Ce [B,L_cap] exponent bytes, Cr [B,L_cap,D_r]. */
+void oracle_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
+                                  const uint16_t* Cr, const int32_t* idx, int B, int Tq, int H,
+                                  int D_c, int D_r, int L_cap, int k, float sm_scale,
+                                  double* out, double* lse);
+
 /* One layer group.  When reuse_idx is 0 the index set is computed once from
  * (qI[0], w[0], kI[0]) and written to idx; when it is 1 idx is read as given
  * (later MTP draft steps).  When per_layer_indexer is 1 every layer l computes

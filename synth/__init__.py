@@ -17,7 +17,7 @@ RoPE slice, the 128K mid-training length and the 1M serving context, and the
 seven-step MTP draft that reuses one index set.
 
 Draw order (fixed, so a seed names one workload): qI, w, kI, then for each
-layer l: Q_l, C_l.  Per-layer indexer inputs (the per-layer-indexer
+layer l: Q_l, C_l (or, for an FP8 cache, Q_l and the layer's FP8 cache).  Per-layer indexer inputs (the per-layer-indexer
 ablation) come from their own seeds, and per-step MTP queries from seed
 ``mtp_q_seed0 + step``.
 """
@@ -107,6 +107,19 @@ def normal_bf16(shape, g: torch.Generator, device) -> torch.Tensor:
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
 
 
+def fp8_cache(B: int, L_cap: int, D_c: int, D_r: int, g: torch.Generator, device):
+    """An FP8 latent cache (C8, Ce, Cr).  Per row: an exponent byte e drawn
+    uniformly from [124, 130] (row scale 2^(e-127) in [1/8, 8]); the E4M3 codes
+    (torch's float8_e4m3fn rounding) of N(0,1) latent values divided by the
+    row scale; N(0,1) bf16 RoPE dims.  C8 [B,L_cap,D_c] uint8, Ce [B,L_cap]
+    uint8, Cr [B,L_cap,D_r] bf16."""
+    e = torch.randint(124, 131, (B, L_cap), generator=g, device=device, dtype=torch.int32)
+    x = torch.randn((B, L_cap, D_c), generator=g, device=device, dtype=torch.float32)
+    C8 = torch.ldexp(x, (127 - e)[..., None].float()).to(torch.float8_e4m3fn).view(torch.uint8)
+    Cr = normal_bf16((B, L_cap, D_r), g, device)
+    return C8.contiguous(), e.to(torch.uint8), Cr
+
+
 def indexer_inputs(wl: Workload, seed: Optional[int] = None, device="cpu") -> Dict[str, torch.Tensor]:
     """qI [B,Tq,H_I,D_I] int8, w [B,Tq,H_I] fp32, kI [B,L_cap,D_I] int8, kv_len [B] int32."""
     g = _gen(wl.seed if seed is None else seed, device)
@@ -117,8 +130,10 @@ def indexer_inputs(wl: Workload, seed: Optional[int] = None, device="cpu") -> Di
     return {"qI": qI, "w": w, "kI": kI, "kv_len": kv_len}
 
 
-def group_inputs(wl: Workload, device="cpu", layers: Optional[int] = None) -> Dict[str, object]:
-    """Indexer inputs plus, per layer, Q_l [B,Tq,H,D] and C_l [B,L_cap,D] (bf16).
+def group_inputs(wl: Workload, device="cpu", layers: Optional[int] = None,
+                 kv8: bool = False) -> Dict[str, object]:
+    """Indexer inputs plus, per layer, Q_l [B,Tq,H,D] and C_l [B,L_cap,D] (bf16),
+    or with kv8 the layer's FP8 cache (lists C8, Ce, Cr; C is then None).
 
     One generator stream in the fixed draw order, so the indexer tensors are
     identical to ``indexer_inputs(wl)`` on the same device.
@@ -130,11 +145,21 @@ def group_inputs(wl: Workload, device="cpu", layers: Optional[int] = None) -> Di
     kI = int8_uniform((wl.B, wl.L_cap, wl.D_I), g, device)
     Q: List[torch.Tensor] = []
     C: List[torch.Tensor] = []
+    C8: List[torch.Tensor] = []
+    Ce: List[torch.Tensor] = []
+    Cr: List[torch.Tensor] = []
     for _ in range(n_layers):
         Q.append(normal_bf16((wl.B, wl.Tq, wl.H, wl.D), g, device))
-        C.append(normal_bf16((wl.B, wl.L_cap, wl.D), g, device))
+        if kv8:
+            c8, ce, cr = fp8_cache(wl.B, wl.L_cap, wl.D_v, wl.D - wl.D_v, g, device)
+            C8.append(c8); Ce.append(ce); Cr.append(cr)
+        else:
+            C.append(normal_bf16((wl.B, wl.L_cap, wl.D), g, device))
     kv_len = torch.full((wl.B,), wl.kv_len, dtype=torch.int32, device=device)
-    return {"qI": qI, "w": w, "kI": kI, "kv_len": kv_len, "Q": Q, "C": C}
+    d = {"qI": qI, "w": w, "kI": kI, "kv_len": kv_len, "Q": Q, "C": None if kv8 else C}
+    if kv8:
+        d.update(C8=C8, Ce=Ce, Cr=Cr)
+    return d
 
 
 def mtp_queries(wl: Workload, step: int, device="cpu", layers: Optional[int] = None) -> List[torch.Tensor]:

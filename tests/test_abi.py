@@ -19,7 +19,7 @@ A4 = (1 << 20) + 4     # 4-byte aligned only
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(isa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(isa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version(lib):
     assert lib.isa_abi_version() == isa.ISA_ABI_VERSION
-    assert isa.isa_abi_version() == 1
+    assert isa.isa_abi_version() == 2
 
 
 def _status(lib, fn, *args):
@@ -120,6 +120,33 @@ def test_attend_rejects_bad_arguments(lib):
     assert _status(lib, "isa_sparse_mla_attend", *args)[0] == isa.ISA_ERR_INVALID_ARG
 
 
+def test_attend_fp8_rejects_bad_arguments(lib):
+    f = ctypes.c_float
+    need = lib.isa_attend_fp8_workspace_bytes(8, 1, 64, 512, 64, 2048)
+    assert need == lib.isa_attend_workspace_bytes(8, 1, 64, 576, 512, 2048) > 0
+    # Q, C8, Ce, Cr, idx, B, Tq, H, D_c, D_r, L_cap, k, scale, out, lse, ws, ws_bytes, stream
+    good = [A16, A16, A4, A16, A4, 8, 1, 64, 512, 64, 4096, 2048, f(1 / 24), A16, None, A16 << 8,
+            need, None]
+    for D_c, D_r in ((512, 32), (256, 64), (128, 64)):
+        args = list(good)
+        args[8], args[9] = D_c, D_r
+        assert _status(lib, "isa_sparse_mla_attend_fp8", *args)[0] == isa.ISA_ERR_UNSUPPORTED
+    for i in (1, 2, 3):                                   # each FP8 cache array
+        args = list(good)
+        args[i] = None
+        assert _status(lib, "isa_sparse_mla_attend_fp8", *args)[0] == isa.ISA_ERR_INVALID_ARG
+    for i in (1, 3):                                      # codes and RoPE need 16-byte rows
+        args = list(good)
+        args[i] = A4
+        assert _status(lib, "isa_sparse_mla_attend_fp8", *args)[0] == isa.ISA_ERR_INVALID_ARG
+    args = list(good)
+    args[12] = f(float("nan"))
+    assert _status(lib, "isa_sparse_mla_attend_fp8", *args)[0] == isa.ISA_ERR_INVALID_ARG
+    args = list(good)
+    args[16] = 100
+    assert _status(lib, "isa_sparse_mla_attend_fp8", *args)[0] == isa.ISA_ERR_WORKSPACE
+
+
 def test_group_rejects_bad_arguments(lib):
     P = ctypes.c_void_p
     arr1 = (P * 1)(A16)
@@ -152,6 +179,18 @@ def test_group_rejects_bad_arguments(lib):
     a.reuse_idx = 1
     assert lib.isa_group_workspace_bytes(ctypes.byref(a)) < need
     assert lib.isa_group_forward(None, None) == isa.ISA_ERR_INVALID_ARG
+    # FP8 caches: the three arrays are required, C is not; shapes as for the call
+    a.kv_fp8 = 1
+    a.C = None
+    assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_INVALID_ARG
+    a.C8 = ctypes.cast(arr4, P); a.Ce = ctypes.cast((P * 4)(A4, A4, A4, A4), P)
+    a.Cr = ctypes.cast(arr4, P)
+    a.D_v = 448
+    assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_UNSUPPORTED
+    a.D_v = 512
+    a.Cr = ctypes.cast((P * 4)(A16, A4, A16, A16), P)       # layer 1's RoPE slice misaligned
+    assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_INVALID_ARG
+    assert "fp8" in lib.isa_last_error().decode()
 
 
 def test_binding_fails_loudly_without_device():

@@ -62,6 +62,30 @@ def test_group_matches_oracle(name):
         assert torch.equal(outs2[l], outs[l])
 
 
+@pytest.mark.parametrize("name", ["C1", "C2-8K", "prefill-96"])
+def test_group_fp8_cache_matches_oracle(name):
+    # the layers' latent caches in FP8 (E4M3 codes, a power-of-two scale per
+    # row, bf16 RoPE dims); the index set is computed and shared as before
+    wl = SMALL[name]
+    _print_case("group fp8", wl)
+    inp = synth.group_inputs(wl, kv8=True)
+    S = oracle.indexer_scores(inp["qI"], inp["w"], inp["kI"], inp["kv_len"])
+    idx_ref = oracle.topk_select(S, inp["kv_len"], wl.k)
+    d = _to_dev({k: v for k, v in inp.items() if v is not None})
+    kv8 = (d["C8"], d["Ce"], d["Cr"])
+    idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], None,
+                                         wl.k, wl.D_v, wl.sm_scale, kv8=kv8)
+    torch.cuda.synchronize()
+    assert_idx_equal(idx, idx_ref, name)
+    for l in range(wl.n_layers):
+        out_ref, _ = oracle.sparse_mla_attend_fp8(inp["Q"][l], inp["C8"][l], inp["Ce"][l],
+                                                  inp["Cr"][l], idx_ref, wl.sm_scale)
+        assert_attn_close(outs[l], out_ref, f"{name} fp8 layer {l}")
+        o, _ = isa.isa_sparse_mla_attend_fp8(d["Q"][l], d["C8"][l], d["Ce"][l], d["Cr"][l], idx,
+                                             wl.sm_scale)
+        assert torch.equal(o, outs[l]), f"fp8 layer {l} differs from standalone"
+
+
 def test_group_dense_causal_when_context_fits_k():
     # context <= k: every query keeps its whole causal prefix (dense attention)
     wl = synth.WORKLOADS["C1"].scaled(Tq=60, kv_len=60, L_cap=64)

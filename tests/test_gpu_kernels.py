@@ -269,3 +269,74 @@ def test_attend_small_k():
     r = np.random.default_rng(10)
     idx = _random_sets(4, 2, 3000, 100, 100, r)
     _attend_case(4, 2, 64, 576, 512, 3000, 100, idx, seed=6, name="k100")
+
+
+# ------------------------------------------------------- FP8 latent cache ----
+
+def _attend_fp8_case(B, Tq, H, D_c, D_r, L_cap, k, idx_np, seed, name):
+    _print_case("attend fp8", name, B, Tq, H, D_c, D_r, L_cap, k)
+    g = torch.Generator().manual_seed(seed)
+    C8, Ce, Cr = synth.fp8_cache(B, L_cap, D_c, D_r, g, "cpu")
+    Q = synth.normal_bf16((B, Tq, H, D_c + D_r), g, "cpu")
+    scale = 1.0 / math.sqrt(D_c + D_r)
+    idx = torch.from_numpy(idx_np.astype(np.int32))
+    ref_out, ref_lse = oracle.sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, scale)
+    out, lse = isa.isa_sparse_mla_attend_fp8(dev(Q), dev(C8), dev(Ce), dev(Cr), dev(idx), scale,
+                                             want_lse=True)
+    torch.cuda.synchronize()
+    assert_attn_close(out, ref_out, name)
+    assert_lse_close(lse, ref_lse, name)
+    return Q, (C8, Ce, Cr), idx, out, lse
+
+
+@pytest.mark.parametrize("B,Tq,fill", [(8, 1, 2048), (2, 3, 1000), (3, 2, 77)])
+def test_attend_fp8_decode(B, Tq, fill):
+    # few queries: the 32-head two-group variant with the k slots split
+    r = np.random.default_rng(40 + fill)
+    idx = _random_sets(B, Tq, 5000, 2048, fill, r)
+    _attend_fp8_case(B, Tq, 64, 512, 64, 5000, 2048, idx, seed=41, name=f"fp8 decode fill={fill}")
+
+
+def test_attend_fp8_wide_and_unsplit():
+    r = np.random.default_rng(42)
+    idx = _random_sets(2, 130, 9000, 128, 128, r)          # >= 256 queries: 64-head variant
+    _attend_fp8_case(2, 130, 64, 512, 64, 9000, 128, idx, seed=43, name="fp8 wide")
+    idx = _random_sets(2, 80, 5000, 256, 256, r)           # 160 queries: two groups, no split
+    _attend_fp8_case(2, 80, 64, 512, 64, 5000, 256, idx, seed=44, name="fp8 unsplit")
+
+
+def test_attend_fp8_160_16_heads():
+    r = np.random.default_rng(45)
+    idx = _random_sets(1, 40, 1024, 64, 64, r)
+    _attend_fp8_case(1, 40, 16, 128, 32, 1024, 64, idx, seed=46, name="fp8 160")
+
+
+def test_attend_fp8_invalid_and_empty_slots():
+    r = np.random.default_rng(47)
+    B, Tq, L_cap, k = 2, 3, 5000, 2048
+    idx = _random_sets(B, Tq, L_cap, k, 1500, r)
+    idx[0, 0, :] = -1
+    idx[0, 1, 7] = L_cap + 3
+    idx[0, 1, 9] = -77
+    idx[1, 2, 1:] = -1
+    _, _, _, out, lse = _attend_fp8_case(B, Tq, 64, 512, 64, L_cap, k, idx, seed=48,
+                                         name="fp8 invalid")
+    assert torch.all(host(out)[0, 0] == 0) and torch.all(host(lse)[0, 0] == -math.inf)
+
+
+def test_attend_fp8_equals_bf16_kernel_on_dequantized_cache():
+    # power-of-two row scales make the dequantized rows bf16 numbers: the FP8
+    # kernel's LDS tiles then hold the bf16 kernel's, and the outputs agree bit
+    # for bit (decode and wide variants)
+    for (B, Tq, L_cap, k, seed) in ((8, 1, 4000, 2048, 50), (2, 130, 3000, 96, 51)):
+        r = np.random.default_rng(seed)
+        idx = _random_sets(B, Tq, L_cap, k, k, r)
+        Q, (C8, Ce, Cr), idx_t, out8, lse8 = _attend_fp8_case(B, Tq, 64, 512, 64, L_cap, k, idx,
+                                                              seed=seed, name=f"fp8 vs bf16 {B}x{Tq}")
+        lat = C8.view(torch.float8_e4m3fn).double() * torch.exp2(Ce.double() - 127)[..., None]
+        C = torch.cat([lat, Cr.double()], dim=-1).to(torch.bfloat16)
+        outb, lseb = isa.isa_sparse_mla_attend(dev(Q), dev(C), dev(idx_t), 512, 1.0 / 24,
+                                               want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(host(out8), host(outb))
+        assert torch.equal(host(lse8), host(lseb))

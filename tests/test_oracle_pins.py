@@ -295,6 +295,63 @@ def test_attend_closed_forms():
     np.testing.assert_allclose(lse_a, lse_b, rtol=1e-14, atol=1e-15)
 
 
+# --------------------------------------------------------- FP8 latent cache ----
+
+def test_e4m3_decoder_matches_torch_for_every_code():
+    # the oracle decodes E4M3 from its bit definition; torch's float8_e4m3fn is
+    # an independent implementation of the same OCP format
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double()
+    got = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+    nan = np.isnan(ref.numpy())
+    assert list(np.flatnonzero(nan)) == [0x7F, 0xFF]
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref.numpy()[~nan])
+    # closed forms: largest finite, smallest subnormal, smallest normal, signed zero
+    assert oracle.e4m3_to_double(0x7E) == 448.0
+    assert oracle.e4m3_to_double(0x01) == 2.0 ** -9
+    assert oracle.e4m3_to_double(0x08) == 2.0 ** -6
+    assert oracle.e4m3_to_double(0xC0) == -2.0
+    assert math.copysign(1.0, oracle.e4m3_to_double(0x80)) == -1.0
+
+
+def _fp8_case(seed, B, Tq, H, D_c, D_r, L_cap, k):
+    g = torch.Generator().manual_seed(seed)
+    r = _rng(seed)
+    C8, Ce, Cr = synth.fp8_cache(B, L_cap, D_c, D_r, g, "cpu")
+    Q = _bf16((B, Tq, H, D_c + D_r), g)
+    idx = np.full((B, Tq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            m = int(r.integers(1, min(k, L_cap) + 1))
+            idx[b, t, :m] = r.choice(L_cap, size=m, replace=False)
+    # the cache each row stands for, dequantized by torch in float64
+    lat = C8.view(torch.float8_e4m3fn).double() * torch.exp2(Ce.double() - 127)[..., None]
+    C = torch.cat([lat, Cr.double()], dim=-1)
+    return Q, C8, Ce, Cr, idx, C
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fp8_attend_matches_sdpa_on_the_dequantized_cache(seed):
+    Q, C8, Ce, Cr, idx, C = _fp8_case(300 + seed, 2, 2, 3, 16, 4, 30, 9)
+    scale = float(np.float32(1.0 / math.sqrt(20)))
+    out, lse = oracle.sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, scale)
+    ref_out, ref_lse = _sdpa_reference(Q, C, idx, 16, scale)
+    np.testing.assert_allclose(out, ref_out.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_attend_equals_bf16_attend_when_dequantization_is_exact():
+    # with power-of-two row scales every dequantized value is a bf16 number, so
+    # attention over the FP8 cache is attention over that bf16 cache, bit for bit
+    Q, C8, Ce, Cr, idx, C = _fp8_case(7, 2, 3, 4, 32, 8, 50, 12)
+    Cb = C.to(torch.bfloat16)
+    assert torch.equal(Cb.double(), C)
+    out8, lse8 = oracle.sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, 0.2)
+    outb, lseb = oracle.sparse_mla_attend(Q, Cb, idx, 32, 0.2)
+    np.testing.assert_array_equal(out8, outb)
+    np.testing.assert_array_equal(lse8, lseb)
+
+
 def test_dense_causal_when_context_fits_k():
     # When every query sees at most k keys, the sparse layer is plain causal
     # attention; checked against torch SDPA(is_causal) on a scaled-down C1.
