@@ -144,7 +144,11 @@ def stage_times(isa, inst, wl, torch, reps=20):
     t_at = time_per_launch(lambda: isa.isa_sparse_mla_attend(d["Q"][0], d["C"][0], idx, wl.D_v,
                                                              wl.sm_scale, out=outs[0], ws=ws),
                            reps, torch)
-    return t_ix, t_tk, t_at
+    # access counts of the index set (the HiSparse input; not part of the step)
+    counts = torch.zeros((wl.B, wl.L_cap), dtype=torch.int32, device="cuda")
+    t_h = time_per_launch(lambda: isa.isa_index_histogram(idx, wl.L_cap, counts=counts), reps,
+                          torch)
+    return t_ix, t_tk, t_at, t_h
 
 
 def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
@@ -373,10 +377,11 @@ def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_row
     t_step = time_group(isa, calls, steps, warmup, torch)
     alg = algorithmic(wl)
     log(f"{wl.name}: {t_step * 1e6:.1f} us/step; timing stages")
-    t_ix, t_tk, t_at = stage_times(isa, insts[0], wl, torch)
+    t_ix, t_tk, t_at, t_h = stage_times(isa, insts[0], wl, torch)
     res = {
         "t_step": t_step, "alg": alg,
         "stages_us": {"indexer": t_ix * 1e6, "topk": t_tk * 1e6, "attend_per_layer": t_at * 1e6},
+        "index_histogram_us": t_h * 1e6,
     }
     # CPU oracle on a bounded sample of the same workload, plus a parity spot check
     if baseline_seq or q_rows:
@@ -497,6 +502,7 @@ def main():
                            "algorithmic_bytes": alg["group_bytes"],
                            "achieved_GBps": alg["group_bytes"] / t / 1e9},
         "stages_us": dec["stages_us"],
+        "index_histogram_us": dec["index_histogram_us"],
         "copy_GBps_measured": copy_GBps,
     }
     if "oracle" in dec:
@@ -511,6 +517,16 @@ def main():
         line["ablation"] = run_ablation(isa, torch, steps=10, warmup=3)
         line["mtp"] = run_mtp(isa, torch, reps=5)
         line["fp8_kv"] = run_fp8_kv(isa, torch, steps=50, warmup=10, n_inst=args.instances)
+        wm = synth.WORKLOADS["C2_128K_MQ8"]
+        mq = run_workload(isa, wm, 30, 5, 2, torch)
+        am = mq["alg"]
+        line["multi_query"] = {
+            "workload": "C2_128K_MQ8 decode group: 8 sequences x 8 queries (causal among them) "
+                        "over 131072 cached tokens, one index set per query, 4 layers",
+            "tokens_per_s": wm.tokens_per_group / mq["t_step"], "ms_per_step": mq["t_step"] * 1e3,
+            "stages_us": mq["stages_us"],
+            "t_ideal_us": am["t_ideal_s"] * 1e6, "frac_of_roofline": am["t_ideal_s"] / mq["t_step"],
+            "indexer_int8_TOPS": am["ix_ops"] / (mq["stages_us"]["indexer"] * 1e-6) / 1e12}
     if args.prefill:
         wp = synth.WORKLOADS["C3"]
         pre = run_workload(isa, wp, max(2, min(args.steps, 5)), 2, 1, torch,
@@ -523,6 +539,7 @@ def main():
             "tokens_per_s": wp.tokens_per_group / tp, "ms_per_step": tp * 1e3,
             "t_ideal_ms": ap_["t_ideal_s"] * 1e3, "frac_of_roofline": ap_["t_ideal_s"] / tp,
             "stages_us": pre["stages_us"],
+            "index_histogram_us": pre["index_histogram_us"],
             "indexer_int8_TOPS": ap_["ix_ops"] / (pre["stages_us"]["indexer"] * 1e-6) / 1e12,
             "attend_bf16_TFLOPS": ap_["at_flops_per_layer"] /
                                   (pre["stages_us"]["attend_per_layer"] * 1e-6) / 1e12,

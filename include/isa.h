@@ -18,7 +18,11 @@
  *         index_share_for_mtp_iteration = true; kv_lora_rank = 512.
  *   [P1]  "GLM-5.2 技术报告解读：IndexShare 稀疏注意力与反奖励作弊强化学习",
  *         section 1, training-strategy table: the indexer sits in the first of
- *         every four sparse layers and the other three reuse its top-k.
+ *         every four sparse layers and the other three reuse its top-k;
+ *         section 4: FP8 KV cache among the serving optimisations.
+ *   [P5]  "GLM-5.2 深度技术解析：智谱百万上下文旗舰模型的架构创新与工程实践",
+ *         HiSparse memory-management section: per-position access counts of
+ *         the top-k sets drive hot/cold cache placement.
  *
  * Conventions shared by every call
  *  - Tensor pointers are DEVICE pointers to dense row-major arrays owned by
@@ -147,6 +151,21 @@ isa_status isa_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const
                                      int D_c, int D_r, int L_cap, int k, float sm_scale,
                                      uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/*
+ * Access counts of an index set, the input of hot/cold cache placement
+ * ([P5] "GLM-5.2 深度技术解析：智谱百万上下文旗舰模型的架构创新与工程实践",
+ * HiSparse memory-management section: every attention step adds one access to
+ * each position the top-k selected):
+ *   counts[b,s] += |{ (t,j) : idx[b,t,j] == s }|   for 0 <= s < L_cap.
+ * Slot values outside [0, L_cap) (the -1 padding included) are ignored.
+ * idx [B,Tq,k] int32; counts [B,L_cap] uint32, accumulated (the caller zeroes
+ * it to start a count; a uint32 count wraps after 2^32 accesses).  The result
+ * is exact and independent of the order of the additions.
+ * 1 <= k <= ISA_MAX_TOPK, L_cap <= ISA_MAX_LCAP.
+ */
+isa_status isa_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
+                               uint32_t* counts, void* stream);
 
 /*
  * One IndexShare layer group ([P1] section 1 table; [P4] sections 2.1 and

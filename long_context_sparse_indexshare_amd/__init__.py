@@ -29,7 +29,7 @@ ISA_ERR_HIP = -4
 EXPORTED_SYMBOLS = (
     "isa_abi_version", "isa_last_error", "isa_indexer_scores", "isa_topk_workspace_bytes",
     "isa_topk_select", "isa_attend_workspace_bytes", "isa_sparse_mla_attend",
-    "isa_attend_fp8_workspace_bytes", "isa_sparse_mla_attend_fp8",
+    "isa_attend_fp8_workspace_bytes", "isa_sparse_mla_attend_fp8", "isa_index_histogram",
     "isa_group_workspace_bytes", "isa_group_forward",
 )
 
@@ -93,6 +93,8 @@ def load_library():
     lib.isa_sparse_mla_attend_fp8.restype = _I
     lib.isa_sparse_mla_attend_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                               _P, _P, _P, _Z, _P]
+    lib.isa_index_histogram.restype = _I
+    lib.isa_index_histogram.argtypes = [_P, _I, _I, _I, _I, _P, _P]
     lib.isa_group_workspace_bytes.restype = _Z
     lib.isa_group_workspace_bytes.argtypes = [ctypes.POINTER(GroupArgs)]
     lib.isa_group_forward.restype = _I
@@ -260,6 +262,21 @@ def isa_sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, sm_scale: float, out=None, lse
         _ptr(Q), _ptr(C8), _ptr(Ce), _ptr(Cr), _ptr(idx), B, Tq, H, D_c, D_r, L_cap, k,
         float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(), _stream_ptr(stream)))
     return out, lse
+
+
+def isa_index_histogram(idx, L_cap: int, counts=None, stream=None) -> torch.Tensor:
+    """counts [B,L_cap] int32 (read as uint32) += the occurrences of every
+    position in idx [B,Tq,k]; a zeroed tensor is made when counts is None."""
+    _dev(idx, torch.int32, "idx")
+    B, Tq, k = idx.shape
+    if counts is None:
+        counts = torch.zeros((B, L_cap), dtype=torch.int32, device=idx.device)
+    _dev(counts, torch.int32, "counts")
+    if tuple(counts.shape) != (B, L_cap):
+        raise ValueError(f"counts must be [{B}, {L_cap}]")
+    _check(load_library().isa_index_histogram(_ptr(idx), B, Tq, k, int(L_cap), _ptr(counts),
+                                              _stream_ptr(stream)))
+    return counts
 
 
 class GroupCall:

@@ -234,6 +234,22 @@ isa_status isa_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const
                      "attend fp8 launch");
 }
 
+isa_status isa_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
+                               uint32_t* counts, void* stream) {
+    ISA_CHECK(idx && counts, ISA_ERR_INVALID_ARG, "histogram: NULL tensor pointer");
+    ISA_CHECK(B > 0 && Tq > 0 && L_cap > 0, ISA_ERR_INVALID_ARG,
+              "histogram: sizes must be positive (B=%d Tq=%d L_cap=%d)", B, Tq, L_cap);
+    ISA_CHECK(k >= 1 && k <= ISA_MAX_TOPK, ISA_ERR_INVALID_ARG, "histogram: k=%d outside [1, %d]",
+              k, ISA_MAX_TOPK);
+    ISA_CHECK(L_cap <= ISA_MAX_LCAP, ISA_ERR_INVALID_ARG, "histogram: L_cap=%d exceeds %d", L_cap,
+              ISA_MAX_LCAP);
+    ISA_CHECK(aligned(idx, 16) && aligned(counts, 4), ISA_ERR_INVALID_ARG,
+              "histogram: idx needs 16-byte alignment, counts 4-byte");
+    return check_hip(isa::launch_index_histogram(idx, B, Tq, k, L_cap, counts,
+                                                 static_cast<hipStream_t>(stream)),
+                     "histogram launch");
+}
+
 size_t isa_group_workspace_bytes(const isa_group_args* a) {
     if (!a || a->B <= 0 || a->Tq <= 0 || a->L_cap <= 0 || a->H <= 0 || a->D_v <= 0 || a->k <= 0)
         return 0;

@@ -155,20 +155,25 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     }
 }
 
-// Many queries per sequence (prefill): every wave owns two queries (their
-// 2 x 64 head rows, four 32-row MFMA blocks, stay in registers) and streams
-// every key block up to its last visible key; the four waves of a workgroup
-// read the same key blocks at about the same time, so each key block comes
-// from HBM / L2 once per workgroup and from L1 for the other waves.  The
-// epilogue (ReLU, head weight, head sum) is the same as above.
+// Two or more queries per sequence (prefill, multi-query decode): every wave
+// owns two queries (their 2 x 64 head rows, four 32-row MFMA blocks, stay in
+// registers) and streams the key blocks of its workgroup's key range up to
+// its last visible key; the four waves of a workgroup read the same key
+// blocks at about the same time, so each key block comes from HBM / L2 once
+// per workgroup and from L1 for the other waves.  The keys are split across
+// workgroups too (blockIdx.z takes keys [z * chunk, (z+1) * chunk)), so few
+// queries still fill the chip while every key block serves all the queries
+// of its workgroup; waves without a query return at once.  The epilogue
+// (ReLU, head weight, head sum) is the same as above.
 constexpr int PF_QPWAVE = 2;
 constexpr int PF_QPW = 4 * PF_QPWAVE;     // queries per workgroup
-constexpr int PF_MIN_TQ = 64;             // from this many queries per sequence on
+constexpr int PF_MIN_TQ = 2;              // from this many queries per sequence on
+constexpr int PF_TARGET_WGS = 1024;       // key splits aim at this many workgroups
 
 template <int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
-    const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
+    const int32_t* __restrict__ kv_len, int Tq, int L_cap, int chunk, float* __restrict__ S,
     uint32_t* __restrict__ zero, uint32_t zero_n) {
     grid_clear(zero, zero_n);
     constexpr int H_I = 64;
@@ -180,6 +185,9 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
     const int g = lane >> 5;
     const int b = blockIdx.y;
     const int tw = blockIdx.x * PF_QPW + wave * PF_QPWAVE;   // first query of this wave
+    if (tw >= Tq) return;                  // no query here (no workgroup barrier follows)
+    const int s_lo = blockIdx.z * chunk;                      // this workgroup's keys
+    const int s_hi = min(s_lo + chunk, L_cap);
     const int len = clamp_len(kv_len[b], L_cap);
 
     // A operands: block rb holds heads 32*(rb%2) .. +32 of query tw + rb/2
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
 
     auto load_keys = [&](int s0, v4i* bk) {
         const int s = s0 + j;
-        const bool live = s0 <= pos_max && s < L_cap;
+        const bool live = s0 <= pos_max && s0 < s_hi && s < L_cap;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + ((size_t)b * L_cap + s) * D_I +
@@ -251,12 +259,12 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
 
     // two key buffers in turn: the next block is in flight while one is used
     v4i k0[KS], k1[KS];
-    load_keys(0, k0);
-    for (int s0 = 0; s0 < L_cap; s0 += 64) {
-        load_keys(s0 + 32, k1);       // load_keys returns zeros past L_cap
+    load_keys(s_lo, k0);
+    for (int s0 = s_lo; s0 < s_hi; s0 += 64) {
+        load_keys(s0 + 32, k1);       // load_keys returns zeros past s_hi
         step(s0, k0);
         load_keys(s0 + 64, k0);
-        if (s0 + 32 < L_cap) step(s0 + 32, k1);
+        if (s0 + 32 < s_hi) step(s0 + 32, k1);
     }
 }
 
@@ -268,9 +276,18 @@ hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const i
     dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
     if constexpr (H_I == 64) {
         if (Tq >= PF_MIN_TQ) {
-            dim3 pgrid((Tq + PF_QPW - 1) / PF_QPW, B);
+            // key splits: enough workgroups to fill the chip, chunks of whole
+            // 64-key steps
+            const int rows = (Tq + PF_QPW - 1) / PF_QPW * B;
+            const int steps = (L_cap + 63) / 64;
+            int splits = (PF_TARGET_WGS + rows - 1) / rows;
+            if (splits > steps) splits = steps;
+            if (splits < 1) splits = 1;
+            const int chunk = (steps + splits - 1) / splits * 64;
+            splits = (L_cap + chunk - 1) / chunk;
+            dim3 pgrid((Tq + PF_QPW - 1) / PF_QPW, B, splits);
             hipLaunchKernelGGL((indexer_prefill_kernel<D_I>), pgrid, dim3(IX_THREADS), 0, stream, qI,
-                               w, kI, kv_len, Tq, L_cap, S, zero, zero_n);
+                               w, kI, kv_len, Tq, L_cap, chunk, S, zero, zero_n);
             return hipGetLastError();
         }
     }

@@ -68,6 +68,10 @@ hipError_t launch_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, co
                                         uint16_t* out, float* lse, void* partials,
                                         hipStream_t stream);
 
+// counts [B,L_cap] += occurrences of each position in idx [B,Tq,k]
+hipError_t launch_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
+                                  uint32_t* counts, hipStream_t stream);
+
 bool indexer_shape_supported(int H_I, int D_I);
 bool attend_shape_supported(int H, int D, int D_v);
 

@@ -48,6 +48,8 @@ def _load():
     lib.oracle_group_forward.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.c_float,
                                          P, P, P, P, P, P, P, P, P, I, I, P]
     lib.oracle_group_forward.restype = None
+    lib.oracle_index_histogram.argtypes = [P, I, I, I, I, P]
+    lib.oracle_index_histogram.restype = None
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_to_double.restype = ctypes.c_double
     lib.oracle_sparse_mla_attend_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I,
@@ -121,6 +123,17 @@ def sparse_mla_attend(Q, C, idx, D_v: int, sm_scale: float):
     _load().oracle_sparse_mla_attend(_ptr(Q), _ptr(C), _ptr(idx), B, Tq, H, D, int(D_v), L_cap,
                                      k, ctypes.c_float(sm_scale), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def index_histogram(idx, L_cap: int, counts=None) -> np.ndarray:
+    """counts [B,L_cap] uint32 += occurrences of each position in idx [B,Tq,k]."""
+    idx = _np(idx, np.int32)
+    B, Tq, k = idx.shape
+    if counts is None:
+        counts = np.zeros((B, L_cap), dtype=np.uint32)
+    counts = np.ascontiguousarray(counts, dtype=np.uint32)
+    _load().oracle_index_histogram(_ptr(idx), B, Tq, k, int(L_cap), _ptr(counts))
+    return counts
 
 
 def e4m3_to_double(code: int) -> float:

@@ -255,6 +255,19 @@ void oracle_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const ui
     free(rows);
 }
 
+/* Access counts of an index set (the per-position access frequency that
+ * hot/cold cache placement reads): counts[b,s] += the number of slots of
+ * idx[b,:,:] equal to s, for 0 <= s < L_cap; other slot values are ignored. */
+void oracle_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
+                            uint32_t* counts) {
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < Tq; ++t)
+            for (int j = 0; j < k; ++j) {
+                const int32_t s = idx[((size_t)b * Tq + t) * k + j];
+                if (s >= 0 && s < L_cap) counts[(size_t)b * L_cap + s] += 1u;
+            }
+}
+
 void oracle_group_forward(int B, int Tq, int L_cap, int H_I, int D_I, int k, int H, int D,
                           int D_v, int n_layers, float sm_scale,
                           const int8_t* const* qI, const float* const* w,

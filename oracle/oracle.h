@@ -58,6 +58,11 @@ void oracle_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const ui
                                   int D_c, int D_r, int L_cap, int k, float sm_scale,
                                   double* out, double* lse);
 
+/* counts [B,L_cap] += occurrences of each position s in [0, L_cap) among the
+ * slots of idx [B,Tq,k]; other slot values are ignored. */
+void oracle_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
+                            uint32_t* counts);
+
 /* One layer group.  When reuse_idx is 0 the index set is computed once from
  * (qI[0], w[0], kI[0]) and written to idx; when it is 1 idx is read as given
  * (later MTP draft steps).  When per_layer_indexer is 1 every layer l computes

@@ -84,6 +84,10 @@ WORKLOADS: Dict[str, Workload] = {
     # MTP draft: batch 16 at 256K, 7 steps reusing the step-1 index set
     "C5": Workload("C5", B=16, Tq=1, kv_len=262144, L_cap=262144, H_I=64, D_I=128, k=2048,
                    H=64, D=576, D_v=512, n_layers=4, seed=5, mtp_steps=7, mtp_q_seed0=5000),
+    # multi-query decode (e.g. verifying 8 draft tokens): batch 8 x 8 queries
+    # at 128K, each query with its own index set, causal among the 8
+    "C2_128K_MQ8": Workload("C2_128K_MQ8", B=8, Tq=8, kv_len=131072, L_cap=131072, H_I=64,
+                            D_I=128, k=2048, H=64, D=576, D_v=512, n_layers=4, seed=7),
 }
 
 

@@ -147,6 +147,18 @@ def test_attend_fp8_rejects_bad_arguments(lib):
     assert _status(lib, "isa_sparse_mla_attend_fp8", *args)[0] == isa.ISA_ERR_WORKSPACE
 
 
+def test_histogram_rejects_bad_arguments(lib):
+    good = [A16, 2, 1, 2048, 4096, A4, None]
+    assert _status(lib, "isa_index_histogram", None, *good[1:])[0] == isa.ISA_ERR_INVALID_ARG
+    for i, bad in ((1, 0), (3, 0), (3, 4096), (4, (1 << 21) + 1)):
+        args = list(good)
+        args[i] = bad
+        assert _status(lib, "isa_index_histogram", *args)[0] == isa.ISA_ERR_INVALID_ARG
+    args = list(good)
+    args[0] = A4                                          # idx rows are read 16 bytes at a time
+    assert _status(lib, "isa_index_histogram", *args)[0] == isa.ISA_ERR_INVALID_ARG
+
+
 def test_group_rejects_bad_arguments(lib):
     P = ctypes.c_void_p
     arr1 = (P * 1)(A16)

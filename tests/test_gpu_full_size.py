@@ -61,6 +61,15 @@ def test_decode_group_full_size(name, seqs):
     _check_sequences(wl, d, idx, outs, seqs)
 
 
+def test_multi_query_decode_group_full_size():
+    # 8 sequences x 8 queries at 128K: the indexer streams each key block once
+    # for all 8 queries of a sequence
+    wl = synth.WORKLOADS["C2_128K_MQ8"]
+    d = synth.group_inputs(wl, device="cuda")
+    idx, outs = _run_group(wl, d)
+    _check_sequences(wl, d, idx, outs, [0, 7])
+
+
 def test_prefill_group_full_size_sampled_rows():
     wl = synth.WORKLOADS["C3"]
     d = synth.group_inputs(wl, device="cuda")

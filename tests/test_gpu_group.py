@@ -28,6 +28,9 @@ SMALL = {
     "decode-B3-Tq2": synth.WORKLOADS["C2"].scaled(name="decode-B3-Tq2", B=3, Tq=2, kv_len=6000,
                                                   L_cap=6100),
     "prefill-96": synth.WORKLOADS["C3"].scaled(name="prefill-96", Tq=96, kv_len=5000, L_cap=5000),
+    # multi-query decode: 8 queries per sequence share each streamed key block
+    "mq-decode-B2-Tq8": synth.WORKLOADS["C2_128K_MQ8"].scaled(name="mq-decode-B2-Tq8", B=2,
+                                                             kv_len=7000, L_cap=7200),
 }
 
 

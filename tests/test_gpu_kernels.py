@@ -37,6 +37,9 @@ INDEXER_CASES = [
     ("prefill-kv<Tq", 2, 65, [40, 1000], 1100, 64, 128),
     ("prefill-d64", 1, 101, [3000], 3000, 64, 64),
     ("prefill-d32", 2, 64, [64, 333], 350, 64, 32),
+    # multi-query decode: few queries, the keys split across workgroups
+    ("mq-Tq8-split", 2, 8, [20000, 9000], 20100, 64, 128),
+    ("mq-Tq5-split", 3, 5, [4097, 1, 70000], 70000, 64, 128),
 ]
 
 
@@ -340,3 +343,19 @@ def test_attend_fp8_equals_bf16_kernel_on_dequantized_cache():
         torch.cuda.synchronize()
         assert torch.equal(host(out8), host(outb))
         assert torch.equal(host(lse8), host(lseb))
+
+
+# ------------------------------------------------------ index access counts ----
+
+@pytest.mark.parametrize("B,Tq,k,L_cap", [(2, 300, 2048, 9000), (3, 5, 17, 60), (1, 1, 2048, 2048)])
+def test_index_histogram_bitwise(B, Tq, k, L_cap):
+    _print_case("histogram", B, Tq, k, L_cap)
+    r = np.random.default_rng(B * 1000 + k)
+    idx = r.integers(-2, L_cap + 2, size=(B, Tq, k)).astype(np.int32)
+    idx[0, 0, : min(k, 40)] = 7                    # a hot position
+    start = r.integers(0, 5, size=(B, L_cap)).astype(np.uint32)
+    ref = oracle.index_histogram(idx, L_cap, counts=start.copy())
+    counts = dev(torch.from_numpy(start.view(np.int32).copy()))
+    isa.isa_index_histogram(dev(torch.from_numpy(idx)), L_cap, counts=counts)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(counts).numpy().view(np.uint32), ref)

@@ -352,6 +352,24 @@ def test_fp8_attend_equals_bf16_attend_when_dequantization_is_exact():
     np.testing.assert_array_equal(lse8, lseb)
 
 
+# ------------------------------------------------------ index access counts ----
+
+@pytest.mark.parametrize("seed", range(3))
+def test_index_histogram_matches_bincount(seed):
+    r = _rng(500 + seed)
+    B, Tq, k, L_cap = 3, 5, 17, 60
+    idx = r.integers(-3, L_cap + 4, size=(B, Tq, k)).astype(np.int32)   # invalid values too
+    counts = oracle.index_histogram(idx, L_cap)
+    for b in range(B):
+        v = idx[b].ravel()
+        v = v[(v >= 0) & (v < L_cap)]
+        np.testing.assert_array_equal(counts[b], np.bincount(v, minlength=L_cap))
+    assert int(counts.sum()) == int(((idx >= 0) & (idx < L_cap)).sum())
+    # counts accumulate: a second call adds the same counts again
+    twice = oracle.index_histogram(idx, L_cap, counts=counts.copy())
+    np.testing.assert_array_equal(twice, 2 * counts)
+
+
 def test_dense_causal_when_context_fits_k():
     # When every query sees at most k keys, the sparse layer is plain causal
     # attention; checked against torch SDPA(is_causal) on a scaled-down C1.
