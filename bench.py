@@ -361,6 +361,37 @@ def run_fp8_kv(isa, torch, steps, warmup, n_inst):
             "group_frac_of_roofline": t_ideal / t}
 
 
+def run_paged(isa, torch, steps, warmup, n_inst, block_size=64):
+    """The C2_128K decode group over paged caches: kI and every layer's
+    latent cache in pools of block_size-token pages, placed in a random
+    order through one block table per instance."""
+    import synth
+    wl = synth.WORKLOADS["C2_128K"]
+    log(f"C2_128K paged ({block_size}-token pages): generating inputs")
+    calls, keep = [], []
+    ws = isa.Workspace()
+    for i in range(n_inst):
+        d = synth.group_inputs(wl.scaled(seed=wl.seed + 1000 * i), device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(900 + i)
+        table = synth.page_layout(wl.B, wl.L_cap, block_size, g, "cuda", extra_pages=64)
+        n_pages = wl.B * (wl.L_cap // block_size) + 64
+        kI = synth.to_pages(d["kI"], table, block_size, n_pages)
+        C = [synth.to_pages(x, table, block_size, n_pages) for x in d["C"]]
+        del d["kI"], d["C"]
+        keep.append((d, kI, C, table))
+        calls.append(isa.GroupCall([d["qI"]], [d["w"]], [kI], d["kv_len"], d["Q"], C, wl.k,
+                                   wl.D_v, wl.sm_scale, ws=ws, block_table=table))
+    torch.cuda.synchronize()
+    t = time_group(isa, calls, steps, warmup, torch)
+    a = algorithmic(wl)
+    del calls, keep
+    torch.cuda.empty_cache()
+    return {"workload": f"C2_128K decode group, caches in {block_size}-token pages placed in a "
+                        "random order",
+            "tokens_per_s": wl.tokens_per_group / t, "ms_per_step": t * 1e3,
+            "frac_of_roofline": a["t_ideal_s"] / t}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -415,8 +446,8 @@ def main():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the 1M-context ablation, the 7-step MTP and the FP8-cache "
-                         "measurements")
+                    help="skip the 1M-context ablation, the 7-step MTP, the FP8-cache, the "
+                         "paged-cache and the multi-query measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group"],
                     help="profiling mode: run one stage of --workload --reps times and print "
@@ -517,6 +548,7 @@ def main():
         line["ablation"] = run_ablation(isa, torch, steps=10, warmup=3)
         line["mtp"] = run_mtp(isa, torch, reps=5)
         line["fp8_kv"] = run_fp8_kv(isa, torch, steps=50, warmup=10, n_inst=args.instances)
+        line["paged"] = run_paged(isa, torch, steps=50, warmup=10, n_inst=args.instances)
         wm = synth.WORKLOADS["C2_128K_MQ8"]
         mq = run_workload(isa, wm, 30, 5, 2, torch)
         am = mq["alg"]

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ISA_ABI_VERSION 2
+#define ISA_ABI_VERSION 3
 #define ISA_MAX_TOPK 2048            /* index_topk of [P3] */
 #define ISA_MAX_LCAP (1 << 21)       /* positions must fit 21 bits */
 
@@ -153,6 +153,30 @@ isa_status isa_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const
                                      void* stream);
 
 /*
+ * Paged caches (the paged KV memory of serving engines, [P4] sections 3 and
+ * 5).  A cache of rows (kI: D_I int8; C: D bf16) is split into pages of
+ * block_size consecutive positions held in a pool [n_pages, block_size, row];
+ * block_table [B, max_blocks] int32 maps logical block j of sequence b (its
+ * positions j*block_size .. +block_size-1) to a pool page.  Entries outside
+ * [0, n_pages) mark unallocated blocks: their positions score -inf in the
+ * indexer and are skipped by attention.  The logical capacity is
+ * L_cap = max_blocks * block_size; everything else (S, idx, out, positions)
+ * is as for the contiguous calls, which these equal on the same logical
+ * cache.  block_size is a power of two in [32, 65536];
+ * n_pages * block_size < 2^31; L_cap <= ISA_MAX_LCAP.
+ */
+isa_status isa_indexer_scores_paged(const int8_t* qI, const float* w, const int8_t* kI_pages,
+                                    const int32_t* block_table, int max_blocks, int block_size,
+                                    int n_pages, const int32_t* kv_len, int B, int Tq, int H_I,
+                                    int D_I, float* S, void* stream);
+isa_status isa_sparse_mla_attend_paged(const uint16_t* Q, const uint16_t* C_pages,
+                                       const int32_t* block_table, int max_blocks,
+                                       int block_size, int n_pages, const int32_t* idx, int B,
+                                       int Tq, int H, int D, int D_v, int k, float sm_scale,
+                                       uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                       void* stream);
+
+/*
  * Access counts of an index set, the input of hot/cold cache placement
  * ([P5] "GLM-5.2 深度技术解析：智谱百万上下文旗舰模型的架构创新与工程实践",
  * HiSparse memory-management section: every attention step adds one access to
@@ -183,6 +207,9 @@ isa_status isa_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_c
  * lse may be NULL, or an array whose entries may be NULL.
  * kv_fp8 = 1: the layers' latent caches are FP8 as in isa_sparse_mla_attend_fp8
  * (D_c = D_v, D_r = D - D_v); C is ignored and C8, Ce, Cr hold n_layers entries.
+ * paged = 1: kI and every layer's cache (C, or C8/Ce/Cr) are page pools of
+ * n_pages pages sharing block_table (as in isa_sparse_mla_attend_paged), and
+ * L_cap must equal max_blocks * block_size.
  */
 typedef struct {
     int B, Tq, L_cap;
@@ -207,6 +234,9 @@ typedef struct {
     const uint8_t* const* C8;          /* n_layers entries with kv_fp8 */
     const uint8_t* const* Ce;
     const uint16_t* const* Cr;
+    int paged;
+    const int32_t* block_table;        /* device [B, max_blocks] with paged */
+    int max_blocks, block_size, n_pages;
 } isa_group_args;
 
 size_t isa_group_workspace_bytes(const isa_group_args* args);

@@ -17,7 +17,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libisa.so")
-ISA_ABI_VERSION = 2
+ISA_ABI_VERSION = 3
 ISA_MAX_TOPK = 2048
 
 ISA_OK = 0
@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "isa_abi_version", "isa_last_error", "isa_indexer_scores", "isa_topk_workspace_bytes",
     "isa_topk_select", "isa_attend_workspace_bytes", "isa_sparse_mla_attend",
     "isa_attend_fp8_workspace_bytes", "isa_sparse_mla_attend_fp8", "isa_index_histogram",
+    "isa_indexer_scores_paged", "isa_sparse_mla_attend_paged",
     "isa_group_workspace_bytes", "isa_group_forward",
 )
 
@@ -58,6 +59,8 @@ class GroupArgs(ctypes.Structure):
         ("idx", _P), ("reuse_idx", _I), ("per_layer_indexer", _I),
         ("ws", _P), ("ws_bytes", _Z),
         ("kv_fp8", _I), ("C8", _P), ("Ce", _P), ("Cr", _P),
+        ("paged", _I), ("block_table", _P), ("max_blocks", _I), ("block_size", _I),
+        ("n_pages", _I),
     ]
 
 
@@ -93,6 +96,12 @@ def load_library():
     lib.isa_sparse_mla_attend_fp8.restype = _I
     lib.isa_sparse_mla_attend_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                               _P, _P, _P, _Z, _P]
+    lib.isa_indexer_scores_paged.restype = _I
+    lib.isa_indexer_scores_paged.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _P,
+                                             _P]
+    lib.isa_sparse_mla_attend_paged.restype = _I
+    lib.isa_sparse_mla_attend_paged.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _I,
+                                                _I, _F, _P, _P, _P, _Z, _P]
     lib.isa_index_histogram.restype = _I
     lib.isa_index_histogram.argtypes = [_P, _I, _I, _I, _I, _P, _P]
     lib.isa_group_workspace_bytes.restype = _Z
@@ -264,6 +273,51 @@ def isa_sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, sm_scale: float, out=None, lse
     return out, lse
 
 
+def isa_indexer_scores_paged(qI, w, kI_pages, block_table, kv_len, S=None,
+                             stream=None) -> torch.Tensor:
+    """Indexer scores over a paged key cache: kI_pages [n_pages, block_size,
+    D_I] int8, block_table [B, max_blocks] int32.  S [B,Tq,max_blocks*block_size]."""
+    _dev(qI, torch.int8, "qI"); _dev(w, torch.float32, "w"); _dev(kI_pages, torch.int8, "kI_pages")
+    _dev(block_table, torch.int32, "block_table"); _dev(kv_len, torch.int32, "kv_len")
+    B, Tq, H_I, D_I = qI.shape
+    n_pages, bs = kI_pages.shape[0], kI_pages.shape[1]
+    max_blocks = block_table.shape[1]
+    if S is None:
+        S = torch.empty((B, Tq, max_blocks * bs), dtype=torch.float32, device=qI.device)
+    _dev(S, torch.float32, "S")
+    _check(load_library().isa_indexer_scores_paged(
+        _ptr(qI), _ptr(w), _ptr(kI_pages), _ptr(block_table), max_blocks, bs, n_pages,
+        _ptr(kv_len), B, Tq, H_I, D_I, _ptr(S), _stream_ptr(stream)))
+    return S
+
+
+def isa_sparse_mla_attend_paged(Q, C_pages, block_table, idx, D_v: int, sm_scale: float,
+                                out=None, lse=None, want_lse: bool = False,
+                                ws: Optional[Workspace] = None, stream=None):
+    """Sparse latent attention over a paged cache: C_pages [n_pages, block_size,
+    D] bf16, block_table [B, max_blocks] int32; idx holds logical positions."""
+    _dev(Q, torch.bfloat16, "Q"); _dev(C_pages, torch.bfloat16, "C_pages")
+    _dev(block_table, torch.int32, "block_table"); _dev(idx, torch.int32, "idx")
+    B, Tq, H, D = Q.shape
+    n_pages, bs = C_pages.shape[0], C_pages.shape[1]
+    max_blocks = block_table.shape[1]
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, Tq, H, D_v), dtype=torch.bfloat16, device=Q.device)
+    _dev(out, torch.bfloat16, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=Q.device)
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    nbytes = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k)
+    buf = _workspace(ws, Q.device).get(nbytes)
+    _check(load_library().isa_sparse_mla_attend_paged(
+        _ptr(Q), _ptr(C_pages), _ptr(block_table), max_blocks, bs, n_pages, _ptr(idx), B, Tq, H,
+        D, int(D_v), k, float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(),
+        _stream_ptr(stream)))
+    return out, lse
+
+
 def isa_index_histogram(idx, L_cap: int, counts=None, stream=None) -> torch.Tensor:
     """counts [B,L_cap] int32 (read as uint32) += the occurrences of every
     position in idx [B,Tq,k]; a zeroed tensor is made when counts is None."""
@@ -282,13 +336,16 @@ def isa_index_histogram(idx, L_cap: int, counts=None, stream=None) -> torch.Tens
 class GroupCall:
     """Marshals one isa_group_forward call and keeps its ctypes arrays alive.
     With kv8 = (C8, Ce, Cr), three per-layer lists, the layers' caches are FP8
-    (as in isa_sparse_mla_attend_fp8) and C is ignored."""
+    (as in isa_sparse_mla_attend_fp8) and C is ignored.  With block_table
+    [B, max_blocks] int32, kI and the layers' caches are page pools
+    [n_pages, block_size, row] sharing that table."""
 
     def __init__(self, qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence,
                  C: Optional[Sequence], k: int, D_v: int, sm_scale: float, idx=None,
                  reuse_idx: bool = False, per_layer_indexer: bool = False,
                  out: Optional[Sequence] = None, lse: Optional[Sequence] = None,
-                 ws: Optional[Workspace] = None, kv8: Optional[Tuple[Sequence, Sequence, Sequence]] = None):
+                 ws: Optional[Workspace] = None, kv8: Optional[Tuple[Sequence, Sequence, Sequence]] = None,
+                 block_table: Optional[torch.Tensor] = None):
         n = len(Q)
         dev = Q[0].device
         for i, x in enumerate(Q):
@@ -309,6 +366,11 @@ class GroupCall:
             L_cap = C[0].shape[1]
         _dev(kv_len, torch.int32, "kv_len")
         B, Tq, H, D = Q[0].shape
+        pool = (C8[0] if kv8 is not None else C[0])
+        if block_table is not None:
+            _dev(block_table, torch.int32, "block_table")
+            n_pages, bs = pool.shape[0], pool.shape[1]
+            L_cap = block_table.shape[1] * bs
         n_ix = n if per_layer_indexer else (0 if reuse_idx else 1)
         qI = list(qI or [])[: max(n_ix, 0)]
         w = list(w or [])[: max(n_ix, 0)]
@@ -325,7 +387,7 @@ class GroupCall:
         if out is None:
             out = [torch.empty((B, Tq, H, D_v), dtype=torch.bfloat16, device=dev) for _ in range(n)]
         self.idx, self.out, self.lse = idx, list(out), (list(lse) if lse is not None else None)
-        self._keep = [qI, w, kI, Q, C, self.out, self.lse, C8, Ce, Cr]
+        self._keep = [qI, w, kI, Q, C, self.out, self.lse, C8, Ce, Cr, block_table]
 
         def arr(ts):
             return (_P * len(ts))(*[_ptr(t) for t in ts]) if ts else None
@@ -348,6 +410,9 @@ class GroupCall:
         a.reuse_idx = int(bool(reuse_idx))
         a.per_layer_indexer = int(bool(per_layer_indexer))
         a.kv_fp8 = int(kv8 is not None)
+        if block_table is not None:
+            a.paged, a.block_table = 1, _ptr(block_table)
+            a.max_blocks, a.block_size, a.n_pages = block_table.shape[1], bs, n_pages
         if kv8 is not None:
             a.C8 = ctypes.cast(self._arrays[7], _P)
             a.Ce = ctypes.cast(self._arrays[8], _P)
@@ -370,8 +435,9 @@ def isa_group_workspace_bytes(call: GroupCall) -> int:
 def isa_group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence,
                       C: Optional[Sequence], k: int, D_v: int, sm_scale: float, idx=None,
                       reuse_idx: bool = False, per_layer_indexer: bool = False, out=None, lse=None,
-                      ws: Optional[Workspace] = None, stream=None, kv8=None):
+                      ws: Optional[Workspace] = None, stream=None, kv8=None, block_table=None):
     """One IndexShare layer group: (idx, [out_l], [lse_l] or None)."""
     call = GroupCall(qI, w, kI, kv_len, Q, C, k, D_v, sm_scale, idx=idx, reuse_idx=reuse_idx,
-                     per_layer_indexer=per_layer_indexer, out=out, lse=lse, ws=ws, kv8=kv8)
+                     per_layer_indexer=per_layer_indexer, out=out, lse=lse, ws=ws, kv8=kv8,
+                     block_table=block_table)
     return call(stream)

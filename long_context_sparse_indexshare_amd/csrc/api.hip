@@ -117,6 +117,24 @@ bool kv8_shape_supported(int D_c, int D_r) {
     return (D_c == 512 && D_r == 64) || (D_c == 128 && D_r == 32);
 }
 
+// Page geometry of the paged calls; on success *pm describes it.
+isa_status check_pages(const int32_t* table, int max_blocks, int block_size, int n_pages,
+                       isa::PageMap* pm) {
+    ISA_CHECK(table && aligned(table, 4), ISA_ERR_INVALID_ARG, "paged: NULL or misaligned table");
+    ISA_CHECK(max_blocks > 0 && n_pages > 0, ISA_ERR_INVALID_ARG,
+              "paged: max_blocks=%d and n_pages=%d must be positive", max_blocks, n_pages);
+    int shift = 5;
+    while (shift < 16 && (1 << shift) < block_size) ++shift;
+    ISA_CHECK(block_size == (1 << shift), ISA_ERR_INVALID_ARG,
+              "paged: block_size=%d is not a power of two in [32, 65536]", block_size);
+    ISA_CHECK((long long)n_pages * block_size < (1LL << 31), ISA_ERR_INVALID_ARG,
+              "paged: n_pages * block_size must stay below 2^31");
+    ISA_CHECK((long long)max_blocks * block_size <= ISA_MAX_LCAP, ISA_ERR_INVALID_ARG,
+              "paged: max_blocks * block_size exceeds %d", ISA_MAX_LCAP);
+    *pm = isa::PageMap{table, max_blocks, shift, n_pages};
+    return ISA_OK;
+}
+
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Group workspace: [top-k counters | top-k scratch | scores S | attention
@@ -165,6 +183,21 @@ isa_status isa_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI
                      "indexer launch");
 }
 
+isa_status isa_indexer_scores_paged(const int8_t* qI, const float* w, const int8_t* kI_pages,
+                                    const int32_t* block_table, int max_blocks, int block_size,
+                                    int n_pages, const int32_t* kv_len, int B, int Tq, int H_I,
+                                    int D_I, float* S, void* stream) {
+    isa::PageMap pm;
+    isa_status st = check_pages(block_table, max_blocks, block_size, n_pages, &pm);
+    if (st != ISA_OK) return st;
+    const int L_cap = max_blocks * block_size;
+    st = check_indexer(qI, w, kI_pages, kv_len, B, Tq, H_I, D_I, L_cap, S);
+    if (st != ISA_OK) return st;
+    return check_hip(isa::launch_indexer_scores(qI, w, kI_pages, kv_len, B, Tq, H_I, D_I, L_cap, S,
+                                                nullptr, 0, static_cast<hipStream_t>(stream), pm),
+                     "indexer launch");
+}
+
 size_t isa_topk_workspace_bytes(int B, int Tq, int L_cap, int k) {
     (void)k;
     if (B <= 0 || Tq <= 0 || L_cap <= 0) return 0;
@@ -202,6 +235,30 @@ isa_status isa_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int
     }
     return check_hip(isa::launch_sparse_mla_attend(Q, C, idx, B, Tq, H, D, D_v, L_cap, k, sm_scale,
                                                    out, lse, ws, static_cast<hipStream_t>(stream)),
+                     "attend launch");
+}
+
+isa_status isa_sparse_mla_attend_paged(const uint16_t* Q, const uint16_t* C_pages,
+                                       const int32_t* block_table, int max_blocks,
+                                       int block_size, int n_pages, const int32_t* idx, int B,
+                                       int Tq, int H, int D, int D_v, int k, float sm_scale,
+                                       uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                       void* stream) {
+    isa::PageMap pm;
+    isa_status st = check_pages(block_table, max_blocks, block_size, n_pages, &pm);
+    if (st != ISA_OK) return st;
+    const int L_cap = max_blocks * block_size;
+    st = check_attend(Q, C_pages, idx, B, Tq, H, D, D_v, L_cap, k, sm_scale, out);
+    if (st != ISA_OK) return st;
+    ISA_CHECK(!lse || aligned(lse, 4), ISA_ERR_INVALID_ARG, "attend: misaligned lse");
+    const size_t need = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k);
+    if (need) {
+        ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
+                  "attend: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+    }
+    return check_hip(isa::launch_sparse_mla_attend(Q, C_pages, idx, B, Tq, H, D, D_v, L_cap, k,
+                                                   sm_scale, out, lse, ws,
+                                                   static_cast<hipStream_t>(stream), pm),
                      "attend launch");
 }
 
@@ -268,6 +325,14 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
         ISA_CHECK(kv8_shape_supported(a->D_v, a->D - a->D_v), ISA_ERR_UNSUPPORTED,
                   "group: FP8 cache with (D=%d, D_v=%d) not compiled", a->D, a->D_v);
     }
+    isa::PageMap pm{nullptr, 0, 0, 0};
+    if (a->paged) {
+        isa_status st = check_pages(a->block_table, a->max_blocks, a->block_size, a->n_pages, &pm);
+        if (st != ISA_OK) return st;
+        ISA_CHECK((long long)a->max_blocks * a->block_size == a->L_cap, ISA_ERR_INVALID_ARG,
+                  "group: paged caches need L_cap = max_blocks * block_size (%d != %d * %d)",
+                  a->L_cap, a->max_blocks, a->block_size);
+    }
     const bool per_layer = a->per_layer_indexer != 0;
     const bool need_index = !a->reuse_idx || per_layer;
     const int n_ix = per_layer ? a->n_layers : (need_index ? 1 : 0);
@@ -315,7 +380,7 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
                                                              a->B, a->Tq, a->H_I, a->D_I, a->L_cap,
                                                              S, reinterpret_cast<uint32_t*>(topk_ws),
                                                              (uint32_t)(L.topk_zero_bytes / 4),
-                                                             stream),
+                                                             stream, pm),
                                   "group: indexer launch");
         if (st != ISA_OK) return st;
         return check_hip(isa::launch_topk_select(S, a->kv_len, a->B, a->Tq, a->L_cap, a->k, a->idx,
@@ -336,10 +401,10 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
             kv8 ? isa::launch_sparse_mla_attend_fp8(a->Q[l], a->C8[l], a->Ce[l], a->Cr[l], a->idx,
                                                     a->B, a->Tq, a->H, a->D, a->D_v, a->L_cap,
                                                     a->k, a->sm_scale, a->out[l], lse, attend_ws,
-                                                    stream)
+                                                    stream, pm)
                 : isa::launch_sparse_mla_attend(a->Q[l], a->C[l], a->idx, a->B, a->Tq, a->H, a->D,
                                                 a->D_v, a->L_cap, a->k, a->sm_scale, a->out[l],
-                                                lse, attend_ws, stream);
+                                                lse, attend_ws, stream, pm);
         isa_status st = check_hip(e, "group: attend launch");
         if (st != ISA_OK) return st;
     }

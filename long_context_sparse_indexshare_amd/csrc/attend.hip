@@ -133,7 +133,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const uint8_t* __restrict__ Ce, const uint16_t* __restrict__ Cr,
     const int32_t* __restrict__ idx, int Tq, int H, int L_cap, int k, float scale_log2,
     int slots_per_split, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml) {
+    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml, PageMap pm) {
     using G = AttendGeom<HB, VS, D, DV, GR>;
     constexpr int ROWB = G::ROWB;
     // FP8 row: DV code bytes, the exponent byte, D - DV bf16 RoPE dims
@@ -166,10 +166,13 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const int slot0 = sp * slots_per_split;
     const int slot1 = min(slot0 + slots_per_split, k);
     const int32_t* qidx = idx + (size_t)q * k;
-    const char* Cb = KV8 ? nullptr : reinterpret_cast<const char*>(C + (size_t)b * L_cap * D);
-    const char* C8b = KV8 ? reinterpret_cast<const char*>(C8 + (size_t)b * L_cap * DV) : nullptr;
-    const uint8_t* Ceb = KV8 ? Ce + (size_t)b * L_cap : nullptr;
-    const char* Crb = KV8 ? reinterpret_cast<const char*>(Cr + (size_t)b * L_cap * (D - DV)) : nullptr;
+    // cache rows of this sequence: [b*L_cap, (b+1)*L_cap) of a contiguous
+    // cache, or the page pool (slots are translated to pool rows below)
+    const size_t row0 = pm.table ? 0 : (size_t)b * L_cap;
+    const char* Cb = KV8 ? nullptr : reinterpret_cast<const char*>(C + row0 * D);
+    const char* C8b = KV8 ? reinterpret_cast<const char*>(C8 + row0 * DV) : nullptr;
+    const uint8_t* Ceb = KV8 ? Ce + row0 : nullptr;
+    const char* Crb = KV8 ? reinterpret_cast<const char*>(Cr + row0 * (D - DV)) : nullptr;
     const int col0 = vh * G::COLS + kp * G::CW;   // first value column of this wave
     char* tile = tiles[grp];
     float (*xbuf)[4][64][4] = xbufs[grp];
@@ -184,8 +187,14 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     // to a whole number of tiles per group become -1
     const int padded = iters * GR * TILE_ROWS;
     for (int i = threadIdx.x; i < padded; i += G::THREADS) {
-        const int s = slot0 + i < slot1 ? qidx[slot0 + i] : -1;
-        const bool ok = s >= 0 && s < L_cap;
+        int s = slot0 + i < slot1 ? qidx[slot0 + i] : -1;
+        bool ok = s >= 0 && s < L_cap;
+        if (pm.table != nullptr && ok) {
+            // logical position -> row of the page pool; unallocated pages are skipped
+            const int page = pm.table[(size_t)b * pm.max_blocks + (s >> pm.shift)];
+            ok = page >= 0 && page < pm.n_pages;
+            s = (page << pm.shift) + (s & ((1 << pm.shift) - 1));
+        }
         sidx[i] = ok ? s : -1;
         // a wave covers 64 consecutive slots = two tiles: one bit per row
         const uint64_t bits = __ballot(ok);
@@ -636,7 +645,7 @@ struct KvSrc {
 template <int HB, int VS, int D, int DV, int GR, bool KV8>
 hipError_t launch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B, int Tq,
                          int H, int L_cap, int k, float sm_scale, uint16_t* out, float* lse,
-                         void* partials, hipStream_t stream) {
+                         void* partials, hipStream_t stream, PageMap pm) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, DV, k);
     const int nq = B * Tq;
     char* base = static_cast<char*>(partials);
@@ -647,7 +656,7 @@ hipError_t launch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B,
     hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV, GR, KV8>), grid,
                        dim3(AT_THREADS * GR), 0, stream, Q, kv.C, kv.C8, kv.Ce, kv.Cr, idx, Tq, H,
                        L_cap, k, sm_scale * LOG2E, plan.slots_per_split, plan.splits, out, lse,
-                       part_o, part_ml);
+                       part_o, part_ml, pm);
     if (plan.splits > 1)
     {
         using Gm = AttendGeom<HB, VS, D, DV, GR>;
@@ -710,18 +719,18 @@ namespace {
 template <bool KV8>
 hipError_t dispatch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B, int Tq, int H,
                            int D, int D_v, int L_cap, int k, float sm_scale, uint16_t* out,
-                           float* lse, void* partials, hipStream_t stream) {
+                           float* lse, void* partials, hipStream_t stream, PageMap pm) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
     if (D == 576 && D_v == 512) {
         if (plan.head_blocks == 2)
             return launch_attend<2, 1, 576, 512, 1, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale,
-                                                         out, lse, partials, stream);
+                                                         out, lse, partials, stream, pm);
         return launch_attend<1, 1, 576, 512, 2, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale, out,
-                                                     lse, partials, stream);
+                                                     lse, partials, stream, pm);
     }
     if (D == 160 && D_v == 128)
         return launch_attend<2, 1, 160, 128, 1, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale, out,
-                                                     lse, partials, stream);
+                                                     lse, partials, stream, pm);
     return hipErrorInvalidValue;
 }
 
@@ -730,18 +739,18 @@ hipError_t dispatch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int 
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,
                                     float sm_scale, uint16_t* out, float* lse, void* partials,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, PageMap pm) {
     return dispatch_attend<false>(Q, KvSrc{C, nullptr, nullptr, nullptr}, idx, B, Tq, H, D, D_v,
-                                  L_cap, k, sm_scale, out, lse, partials, stream);
+                                  L_cap, k, sm_scale, out, lse, partials, stream, pm);
 }
 
 hipError_t launch_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const uint8_t* Ce,
                                         const uint16_t* Cr, const int32_t* idx, int B, int Tq,
                                         int H, int D, int D_v, int L_cap, int k, float sm_scale,
                                         uint16_t* out, float* lse, void* partials,
-                                        hipStream_t stream) {
+                                        hipStream_t stream, PageMap pm) {
     return dispatch_attend<true>(Q, KvSrc{nullptr, C8, Ce, Cr}, idx, B, Tq, H, D, D_v, L_cap, k,
-                                 sm_scale, out, lse, partials, stream);
+                                 sm_scale, out, lse, partials, stream, pm);
 }
 
 }  // namespace isa

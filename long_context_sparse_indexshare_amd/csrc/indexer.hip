@@ -38,17 +38,29 @@ __device__ __forceinline__ void grid_clear(uint32_t* __restrict__ zero, uint32_t
     for (uint32_t i = wg * IX_THREADS + threadIdx.x; i < zero_n; i += nwg * IX_THREADS) zero[i] = 0u;
 }
 
+// First cache row of the 32-key block at logical position s0 (a multiple of
+// 32) of sequence b, or -1 when its page is unallocated.  A page holds a
+// power-of-two number (>= 32) of keys, so a block never straddles pages;
+// s0 is wave-uniform, so the table read is a scalar load.
+__device__ __forceinline__ long long key_block_row(const PageMap& pm, int b, int L_cap, int s0) {
+    if (pm.table == nullptr) return (long long)b * L_cap + s0;
+    const int blk = __builtin_amdgcn_readfirstlane(s0 >> pm.shift);
+    const int page = pm.table[(size_t)b * pm.max_blocks + blk];
+    if (page < 0 || page >= pm.n_pages) return -1;
+    return ((long long)page << pm.shift) + (s0 & ((1 << pm.shift) - 1));
+}
+
 template <int H_I, int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
     const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
-    uint32_t* __restrict__ zero, uint32_t zero_n) {
+    uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm) {
     grid_clear(zero, zero_n);
     constexpr int QPW = IX_ROWS / H_I;             // queries per workgroup
     constexpr int KS = D_I / 32;                   // MFMA k-steps over the indexer dim
     constexpr int NQL = H_I >= 8 ? 64 / H_I : 8;   // query slots held per lane
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31;
     const int g = lane >> 5;
     const int b = blockIdx.z;
@@ -90,10 +102,11 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     // B operands of one 32-key block: lane (key s0 + j, half g) holds k bytes 32*ks + 16*g .. +16
     auto load_keys = [&](int s0, v4i* bk) {
         const int s = s0 + j;
-        const bool live = s0 <= pos_max && s < L_cap;
+        const long long r0 = s0 <= pos_max && s0 < L_cap ? key_block_row(pm, b, L_cap, s0) : -1;
+        const bool live = r0 >= 0 && s < L_cap;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + ((size_t)b * L_cap + s) * D_I +
+            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + (size_t)(r0 + j) * D_I +
                                                           32 * ks + 16 * g)
                           : v4i{0, 0, 0, 0};
         }
@@ -110,6 +123,8 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
         for (int ks = 0; ks < KS; ++ks) bk[ks] = bk_next[ks];
         if (step + 1 < IX_STEPS) load_keys(s0 + IX_KEYS_PER_STEP, bk_next);   // next block in flight
         const int s = s0 + j;
+        // positions on an unallocated page score -inf
+        const bool page_ok = pm.table == nullptr || key_block_row(pm, b, L_cap, s0) >= 0;
         float sum[NQL];
 #pragma unroll
         for (int q = 0; q < NQL; ++q) sum[q] = 0.0f;
@@ -149,7 +164,8 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
                 const int t = t0 + qt;
                 if (t >= Tq) continue;
                 const int pos = len - Tq + t;
-                S[((size_t)b * Tq + t) * L_cap + s] = s <= pos ? sum[q] : -__builtin_inff();
+                S[((size_t)b * Tq + t) * L_cap + s] =
+                    s <= pos && page_ok ? sum[q] : -__builtin_inff();
             }
         }
     }
@@ -174,13 +190,13 @@ template <int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
     const int32_t* __restrict__ kv_len, int Tq, int L_cap, int chunk, float* __restrict__ S,
-    uint32_t* __restrict__ zero, uint32_t zero_n) {
+    uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm) {
     grid_clear(zero, zero_n);
     constexpr int H_I = 64;
     constexpr int KS = D_I / 32;
     constexpr int RB = 2 * PF_QPWAVE;                 // 32-row blocks per wave
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31;
     const int g = lane >> 5;
     const int b = blockIdx.y;
@@ -217,10 +233,12 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
 
     auto load_keys = [&](int s0, v4i* bk) {
         const int s = s0 + j;
-        const bool live = s0 <= pos_max && s0 < s_hi && s < L_cap;
+        const long long r0 =
+            s0 <= pos_max && s0 < s_hi && s0 < L_cap ? key_block_row(pm, b, L_cap, s0) : -1;
+        const bool live = r0 >= 0 && s < L_cap;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + ((size_t)b * L_cap + s) * D_I +
+            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + (size_t)(r0 + j) * D_I +
                                                           32 * ks + 16 * g)
                           : v4i{0, 0, 0, 0};
         }
@@ -249,10 +267,13 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
             for (int q = 0; q < PF_QPWAVE; ++q) sum[q] += __shfl_xor(sum[q], 32);
         }
         if (g == 0 && s < L_cap) {
+            // positions on an unallocated page score -inf
+            const bool page_ok = pm.table == nullptr || key_block_row(pm, b, L_cap, s0) >= 0;
 #pragma unroll
             for (int q = 0; q < PF_QPWAVE; ++q) {
                 if (tw + q >= Tq) continue;                   // past the last query
-                S[((size_t)b * Tq + tw + q) * L_cap + s] = s <= pos[q] ? sum[q] : -__builtin_inff();
+                S[((size_t)b * Tq + tw + q) * L_cap + s] =
+                    s <= pos[q] && page_ok ? sum[q] : -__builtin_inff();
             }
         }
     };
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
 template <int H_I, int D_I>
 hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
                      int B, int Tq, int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                     hipStream_t stream) {
+                     hipStream_t stream, PageMap pm) {
     constexpr int QPW = IX_ROWS / H_I;
     dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
     if constexpr (H_I == 64) {
@@ -287,12 +308,12 @@ hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const i
             splits = (L_cap + chunk - 1) / chunk;
             dim3 pgrid((Tq + PF_QPW - 1) / PF_QPW, B, splits);
             hipLaunchKernelGGL((indexer_prefill_kernel<D_I>), pgrid, dim3(IX_THREADS), 0, stream, qI,
-                               w, kI, kv_len, Tq, L_cap, chunk, S, zero, zero_n);
+                               w, kI, kv_len, Tq, L_cap, chunk, S, zero, zero_n, pm);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I>), grid, dim3(IX_THREADS), 0, stream,
-                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n);
+                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n, pm);
     return hipGetLastError();
 }
 
@@ -306,12 +327,12 @@ bool indexer_shape_supported(int H_I, int D_I) {
 
 #define ISA_IX_CASE(HH, DD)                                                              \
     if (H_I == HH && D_I == DD)                                                          \
-        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, zero, zero_n, stream);
+        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, zero, zero_n, stream, pm);
 
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, PageMap pm) {
     ISA_IX_CASE(64, 128) ISA_IX_CASE(64, 64) ISA_IX_CASE(64, 32)
     ISA_IX_CASE(32, 128) ISA_IX_CASE(32, 64) ISA_IX_CASE(32, 32)
     ISA_IX_CASE(16, 128) ISA_IX_CASE(16, 64) ISA_IX_CASE(16, 32)

@@ -17,6 +17,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
+// Paged caches: logical position s of sequence b lives in row
+// (page << shift) + (s & ((1 << shift) - 1)) of the page pool, where page =
+// table[b * max_blocks + (s >> shift)]; pages outside [0, n_pages) are
+// unallocated.  table == nullptr: the cache is contiguous, [B, L_cap, row].
+struct PageMap {
+    const int32_t* table;
+    int max_blocks;
+    int shift;                        // log2 of the page size (>= 5)
+    int n_pages;
+};
+
 // Top-k geometry (shared by the host sizing code and the kernels).
 constexpr int TOPK_THREADS = 256;
 constexpr int TOPK_CHUNK = 4096;            // scores per workgroup
@@ -50,7 +61,7 @@ hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                                 hipStream_t stream);
+                                 hipStream_t stream, PageMap pm = PageMap{nullptr, 0, 0, 0});
 // counters_clear: the caller already zeroed the first topk_layout().zero_bytes
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
                               int k, int32_t* idx, void* ws, bool counters_clear,
@@ -58,7 +69,7 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,
                                     float sm_scale, uint16_t* out, float* lse, void* partials,
-                                    hipStream_t stream);
+                                    hipStream_t stream, PageMap pm = PageMap{nullptr, 0, 0, 0});
 
 // FP8 latent cache: C8 [B,L_cap,D_v] E4M3 codes, Ce [B,L_cap] exponent bytes,
 // Cr [B,L_cap,D-D_v] bf16 RoPE slices; otherwise as launch_sparse_mla_attend.
@@ -66,7 +77,7 @@ hipError_t launch_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, co
                                         const uint16_t* Cr, const int32_t* idx, int B, int Tq,
                                         int H, int D, int D_v, int L_cap, int k, float sm_scale,
                                         uint16_t* out, float* lse, void* partials,
-                                        hipStream_t stream);
+                                        hipStream_t stream, PageMap pm = PageMap{nullptr, 0, 0, 0});
 
 // counts [B,L_cap] += occurrences of each position in idx [B,Tq,k]
 hipError_t launch_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,

@@ -48,6 +48,11 @@ def _load():
     lib.oracle_group_forward.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.c_float,
                                          P, P, P, P, P, P, P, P, P, I, I, P]
     lib.oracle_group_forward.restype = None
+    lib.oracle_indexer_scores_paged.argtypes = [P, P, P, P, I, I, I, P, I, I, I, I, P]
+    lib.oracle_indexer_scores_paged.restype = None
+    lib.oracle_sparse_mla_attend_paged.argtypes = [P, P, P, I, I, I, P, I, I, I, I, I, I,
+                                                   ctypes.c_float, P, P]
+    lib.oracle_sparse_mla_attend_paged.restype = None
     lib.oracle_index_histogram.argtypes = [P, I, I, I, I, P]
     lib.oracle_index_histogram.restype = None
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
@@ -122,6 +127,42 @@ def sparse_mla_attend(Q, C, idx, D_v: int, sm_scale: float):
     lse = np.empty((B, Tq, H), dtype=np.float64)
     _load().oracle_sparse_mla_attend(_ptr(Q), _ptr(C), _ptr(idx), B, Tq, H, D, int(D_v), L_cap,
                                      k, ctypes.c_float(sm_scale), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def indexer_scores_paged(qI, w, kI_pages, table, kv_len) -> np.ndarray:
+    """S [B,Tq,max_blocks*block_size] float32 over a paged key cache
+    (kI_pages [n_pages, block_size, D_I] int8, table [B, max_blocks] int32)."""
+    qI = _np(qI, np.int8)
+    w = _np(w, np.float32)
+    kI_pages = _np(kI_pages, np.int8)
+    table = _np(table, np.int32)
+    kv_len = _np(kv_len, np.int32)
+    B, Tq, H_I, D_I = qI.shape
+    n_pages, bs, _ = kI_pages.shape
+    max_blocks = table.shape[1]
+    S = np.empty((B, Tq, max_blocks * bs), dtype=np.float32)
+    _load().oracle_indexer_scores_paged(_ptr(qI), _ptr(w), _ptr(kI_pages), _ptr(table), max_blocks,
+                                        bs, n_pages, _ptr(kv_len), B, Tq, H_I, D_I, _ptr(S))
+    return S
+
+
+def sparse_mla_attend_paged(Q, C_pages, table, idx, D_v: int, sm_scale: float):
+    """(out, lse) of sparse attention over a paged latent cache
+    (C_pages [n_pages, block_size, D] bf16, table [B, max_blocks] int32)."""
+    Q = _np(Q, np.uint16)
+    C_pages = _np(C_pages, np.uint16)
+    table = _np(table, np.int32)
+    idx = _np(idx, np.int32)
+    B, Tq, H, D = Q.shape
+    n_pages, bs, _ = C_pages.shape
+    max_blocks = table.shape[1]
+    k = idx.shape[2]
+    out = np.empty((B, Tq, H, D_v), dtype=np.float64)
+    lse = np.empty((B, Tq, H), dtype=np.float64)
+    _load().oracle_sparse_mla_attend_paged(_ptr(Q), _ptr(C_pages), _ptr(table), max_blocks, bs,
+                                           n_pages, _ptr(idx), B, Tq, H, D, int(D_v), k,
+                                           ctypes.c_float(sm_scale), _ptr(out), _ptr(lse))
     return out, lse
 
 

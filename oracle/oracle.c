@@ -268,6 +268,73 @@ void oracle_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
             }
 }
 
+/* Paged caches: the logical row s of sequence b is row
+ * table[b][s / block_size] * block_size + s % block_size of the page pool
+ * when that table entry is a page in [0, n_pages); otherwise the row is
+ * unallocated.  Copies the logical cache out of the pool (unallocated rows
+ * zero) and marks which logical rows exist. */
+static void unpage_rows(const void* pool, size_t row_bytes, const int32_t* table, int B,
+                        int max_blocks, int block_size, int n_pages, unsigned char* out,
+                        unsigned char* valid) {
+    const long L = (long)max_blocks * block_size;
+    for (int b = 0; b < B; ++b)
+        for (long s = 0; s < L; ++s) {
+            const int32_t page = table[(size_t)b * max_blocks + s / block_size];
+            unsigned char* dst = out + ((size_t)b * L + s) * row_bytes;
+            const int ok = page >= 0 && page < n_pages;
+            valid[(size_t)b * L + s] = (unsigned char)ok;
+            if (ok)
+                memcpy(dst, (const unsigned char*)pool +
+                                ((size_t)page * block_size + s % block_size) * row_bytes,
+                       row_bytes);
+            else
+                memset(dst, 0, row_bytes);
+        }
+}
+
+void oracle_indexer_scores_paged(const int8_t* qI, const float* w, const int8_t* kI_pages,
+                                 const int32_t* table, int max_blocks, int block_size,
+                                 int n_pages, const int32_t* kv_len, int B, int Tq, int H_I,
+                                 int D_I, float* S) {
+    const long L = (long)max_blocks * block_size;
+    int8_t* kI = (int8_t*)malloc((size_t)B * L * D_I);
+    unsigned char* valid = (unsigned char*)malloc((size_t)B * L);
+    unpage_rows(kI_pages, (size_t)D_I, table, B, max_blocks, block_size, n_pages,
+                (unsigned char*)kI, valid);
+    oracle_indexer_scores(qI, w, kI, kv_len, B, Tq, H_I, D_I, (int)L, S);
+    /* positions on unallocated pages score -inf */
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < Tq; ++t)
+            for (long s = 0; s < L; ++s)
+                if (!valid[(size_t)b * L + s]) S[((size_t)b * Tq + t) * L + s] = -INFINITY;
+    free(valid);
+    free(kI);
+}
+
+void oracle_sparse_mla_attend_paged(const uint16_t* Q, const uint16_t* C_pages,
+                                    const int32_t* table, int max_blocks, int block_size,
+                                    int n_pages, const int32_t* idx, int B, int Tq, int H, int D,
+                                    int D_v, int k, float sm_scale, double* out, double* lse) {
+    const long L = (long)max_blocks * block_size;
+    uint16_t* C = (uint16_t*)malloc((size_t)B * L * D * sizeof(uint16_t));
+    unsigned char* valid = (unsigned char*)malloc((size_t)B * L);
+    int32_t* idx2 = (int32_t*)malloc((size_t)B * Tq * k * sizeof(int32_t));
+    unpage_rows(C_pages, (size_t)D * sizeof(uint16_t), table, B, max_blocks, block_size, n_pages,
+                (unsigned char*)C, valid);
+    /* slots on unallocated pages are skipped like -1 */
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < Tq; ++t)
+            for (int j = 0; j < k; ++j) {
+                const size_t o = ((size_t)b * Tq + t) * k + j;
+                const int32_t s = idx[o];
+                idx2[o] = (s >= 0 && s < L && valid[(size_t)b * L + s]) ? s : -1;
+            }
+    oracle_sparse_mla_attend(Q, C, idx2, B, Tq, H, D, D_v, (int)L, k, sm_scale, out, lse);
+    free(idx2);
+    free(valid);
+    free(C);
+}
+
 void oracle_group_forward(int B, int Tq, int L_cap, int H_I, int D_I, int k, int H, int D,
                           int D_v, int n_layers, float sm_scale,
                           const int8_t* const* qI, const float* const* w,

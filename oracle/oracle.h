@@ -63,6 +63,22 @@ void oracle_sparse_mla_attend_fp8(const uint16_t* Q, const uint8_t* C8, const ui
 void oracle_index_histogram(const int32_t* idx, int B, int Tq, int k, int L_cap,
                             uint32_t* counts);
 
+/* Paged caches: logical row s of sequence b is row
+ * table[b][s / block_size] * block_size + s % block_size of the page pool
+ * ([n_pages, block_size, row]) when that entry is in [0, n_pages), else
+ * unallocated.  L_cap = max_blocks * block_size.  The scores equal
+ * oracle_indexer_scores on the logical cache, with -inf at unallocated
+ * positions; attention equals oracle_sparse_mla_attend on the logical cache
+ * with slots at unallocated positions skipped. */
+void oracle_indexer_scores_paged(const int8_t* qI, const float* w, const int8_t* kI_pages,
+                                 const int32_t* table, int max_blocks, int block_size,
+                                 int n_pages, const int32_t* kv_len, int B, int Tq, int H_I,
+                                 int D_I, float* S);
+void oracle_sparse_mla_attend_paged(const uint16_t* Q, const uint16_t* C_pages,
+                                    const int32_t* table, int max_blocks, int block_size,
+                                    int n_pages, const int32_t* idx, int B, int Tq, int H, int D,
+                                    int D_v, int k, float sm_scale, double* out, double* lse);
+
 /* One layer group.  When reuse_idx is 0 the index set is computed once from
  * (qI[0], w[0], kI[0]) and written to idx; when it is 1 idx is read as given
  * (later MTP draft steps).  When per_layer_indexer is 1 every layer l computes

@@ -124,6 +124,27 @@ def fp8_cache(B: int, L_cap: int, D_c: int, D_r: int, g: torch.Generator, device
     return C8.contiguous(), e.to(torch.uint8), Cr
 
 
+def page_layout(B: int, L_cap: int, block_size: int, g: torch.Generator, device,
+                extra_pages: int = 0) -> torch.Tensor:
+    """A block table [B, L_cap / block_size] int32 that places the logical
+    blocks of every sequence on distinct pages of a pool of
+    B * L_cap / block_size + extra_pages pages, in a random order."""
+    nb = L_cap // block_size
+    perm = torch.randperm(B * nb + extra_pages, generator=g, device=device)[: B * nb]
+    return perm.view(B, nb).to(torch.int32).contiguous()
+
+
+def to_pages(cache: torch.Tensor, table: torch.Tensor, block_size: int, n_pages: int) -> torch.Tensor:
+    """The page pool [n_pages, block_size, row...] holding cache [B, L_cap, row...]
+    at the pages the table names (pages no block uses stay zero)."""
+    B, L = cache.shape[0], cache.shape[1]
+    nb = L // block_size
+    pool = torch.zeros((n_pages, block_size) + tuple(cache.shape[2:]), dtype=cache.dtype,
+                       device=cache.device)
+    pool[table.reshape(-1).long()] = cache.reshape((B * nb, block_size) + tuple(cache.shape[2:]))
+    return pool
+
+
 def indexer_inputs(wl: Workload, seed: Optional[int] = None, device="cpu") -> Dict[str, torch.Tensor]:
     """qI [B,Tq,H_I,D_I] int8, w [B,Tq,H_I] fp32, kI [B,L_cap,D_I] int8, kv_len [B] int32."""
     g = _gen(wl.seed if seed is None else seed, device)

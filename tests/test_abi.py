@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version(lib):
     assert lib.isa_abi_version() == isa.ISA_ABI_VERSION
-    assert isa.isa_abi_version() == 2
+    assert isa.isa_abi_version() == 3
 
 
 def _status(lib, fn, *args):
@@ -159,6 +159,29 @@ def test_histogram_rejects_bad_arguments(lib):
     assert _status(lib, "isa_index_histogram", *args)[0] == isa.ISA_ERR_INVALID_ARG
 
 
+def test_paged_calls_reject_bad_page_geometry(lib):
+    f = ctypes.c_float
+    # qI, w, kI_pages, table, max_blocks, block_size, n_pages, kv_len, B, Tq, H_I, D_I, S, stream
+    good = [A16, A4, A16, A4, 64, 64, 600, A4, 8, 1, 64, 128, A4, None]
+    for i, bad in ((3, None), (4, 0), (6, 0), (5, 48), (5, 16), (5, 1 << 17), (6, 1 << 26),
+                   (4, (1 << 21) // 64 + 1)):
+        args = list(good)
+        args[i] = bad
+        assert _status(lib, "isa_indexer_scores_paged", *args)[0] == isa.ISA_ERR_INVALID_ARG, (i, bad)
+    need = lib.isa_attend_workspace_bytes(8, 1, 64, 576, 512, 2048)
+    # Q, C_pages, table, max_blocks, block_size, n_pages, idx, B, Tq, H, D, D_v, k, scale, out,
+    # lse, ws, ws_bytes, stream
+    gooda = [A16, A16, A4, 64, 64, 600, A4, 8, 1, 64, 576, 512, 2048, f(1 / 24), A16, None,
+             A16 << 8, need, None]
+    for i, bad in ((2, A4 + 1), (4, 100), (5, -1)):
+        args = list(gooda)
+        args[i] = bad
+        assert _status(lib, "isa_sparse_mla_attend_paged", *args)[0] == isa.ISA_ERR_INVALID_ARG
+    args = list(gooda)
+    args[10] = 512
+    assert _status(lib, "isa_sparse_mla_attend_paged", *args)[0] == isa.ISA_ERR_UNSUPPORTED
+
+
 def test_group_rejects_bad_arguments(lib):
     P = ctypes.c_void_p
     arr1 = (P * 1)(A16)
@@ -203,6 +226,13 @@ def test_group_rejects_bad_arguments(lib):
     a.Cr = ctypes.cast((P * 4)(A16, A4, A16, A16), P)       # layer 1's RoPE slice misaligned
     assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_INVALID_ARG
     assert "fp8" in lib.isa_last_error().decode()
+    # paged caches: the logical capacity must be max_blocks * block_size
+    a.Cr = ctypes.cast(arr4, P)
+    a.paged, a.block_table, a.max_blocks, a.block_size, a.n_pages = 1, A4, 32, 64, 600
+    assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_INVALID_ARG
+    assert "L_cap" in lib.isa_last_error().decode()
+    a.block_size = 96
+    assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_device():

@@ -89,6 +89,34 @@ def test_group_fp8_cache_matches_oracle(name):
         assert torch.equal(o, outs[l]), f"fp8 layer {l} differs from standalone"
 
 
+@pytest.mark.parametrize("kv8", [False, True])
+def test_group_paged_caches_equal_contiguous(kv8):
+    # kI and every layer's cache in page pools (random page order, one table):
+    # the same index set and the same outputs, bit for bit, as the contiguous
+    # group on the logical caches
+    wl = SMALL["C2-8K"]
+    bs = 64
+    _print_case("group paged", wl, bs, kv8)
+    d = _to_dev({k: v for k, v in synth.group_inputs(wl, kv8=kv8).items() if v is not None})
+    g = torch.Generator(device="cuda").manual_seed(77)
+    table = synth.page_layout(wl.B, wl.L_cap, bs, g, "cuda", extra_pages=9)
+    n_pages = wl.B * (wl.L_cap // bs) + 9
+    pg = lambda x: synth.to_pages(x, table, bs, n_pages)
+    kv = (d["C8"], d["Ce"], d["Cr"]) if kv8 else None
+    kv_p = tuple([pg(x) for x in arr] for arr in kv) if kv8 else None
+    idx_c, outs_c, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                             None if kv8 else d["C"], wl.k, wl.D_v, wl.sm_scale,
+                                             kv8=kv)
+    idx_p, outs_p, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [pg(d["kI"])], d["kv_len"],
+                                             d["Q"], None if kv8 else [pg(x) for x in d["C"]],
+                                             wl.k, wl.D_v, wl.sm_scale, kv8=kv_p,
+                                             block_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_c)
+    for l in range(wl.n_layers):
+        assert torch.equal(outs_p[l], outs_c[l]), f"layer {l}"
+
+
 def test_group_dense_causal_when_context_fits_k():
     # context <= k: every query keeps its whole causal prefix (dense attention)
     wl = synth.WORKLOADS["C1"].scaled(Tq=60, kv_len=60, L_cap=64)

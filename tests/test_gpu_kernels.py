@@ -359,3 +359,63 @@ def test_index_histogram_bitwise(B, Tq, k, L_cap):
     isa.isa_index_histogram(dev(torch.from_numpy(idx)), L_cap, counts=counts)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(counts).numpy().view(np.uint32), ref)
+
+
+# ------------------------------------------------------------ paged caches ----
+
+def _pages(cache, bs, seed, extra=5):
+    g = torch.Generator().manual_seed(seed)
+    B, L = cache.shape[0], cache.shape[1]
+    table = synth.page_layout(B, L, bs, g, "cpu", extra_pages=extra)
+    return synth.to_pages(cache, table, bs, B * (L // bs) + extra), table
+
+
+@pytest.mark.parametrize("Tq,bs", [(1, 64), (8, 32), (70, 256)])
+def test_indexer_paged_bitwise(Tq, bs):
+    # decode kernel (Tq 1) and the key-split kernel (Tq 8, 70); one block unallocated
+    _print_case("indexer paged", Tq, bs)
+    B, L = 2, 4096
+    g = torch.Generator().manual_seed(Tq * 100 + bs)
+    qI = synth.int8_uniform((B, Tq, 64, 128), g, "cpu")
+    w = synth.pow2_weights((B, Tq, 64), g, "cpu")
+    kI = synth.int8_uniform((B, L, 128), g, "cpu")
+    kv_len = torch.tensor([L, 3000], dtype=torch.int32)
+    pool, table = _pages(kI, bs, Tq + bs)
+    table[1, 2] = -1
+    ref = oracle.indexer_scores_paged(qI, w, pool, table, kv_len)
+    S = isa.isa_indexer_scores_paged(dev(qI), dev(w), dev(pool), dev(table), dev(kv_len))
+    torch.cuda.synchronize()
+    assert_scores_bitwise(S, ref, f"paged Tq={Tq} bs={bs}")
+    # the contiguous kernel on the logical cache gives the same bits where allocated
+    Sc = isa.isa_indexer_scores(dev(qI), dev(w), dev(kI), dev(kv_len))
+    torch.cuda.synchronize()
+    live = torch.ones(L, dtype=torch.bool)
+    live[2 * bs:3 * bs] = False
+    assert torch.equal(host(S)[0], host(Sc)[0])
+    assert torch.equal(host(S)[1][:, live], host(Sc)[1][:, live])
+
+
+@pytest.mark.parametrize("B,Tq,bs", [(8, 1, 64), (2, 130, 128)])
+def test_attend_paged(B, Tq, bs):
+    _print_case("attend paged", B, Tq, bs)
+    r = np.random.default_rng(B + Tq + bs)
+    L, k = 4096, (2048 if Tq == 1 else 128)
+    g = torch.Generator().manual_seed(60 + B)
+    Q = synth.normal_bf16((B, Tq, 64, 576), g, "cpu")
+    C = synth.normal_bf16((B, L, 576), g, "cpu")
+    idx = torch.from_numpy(_random_sets(B, Tq, L, k, k, r).astype(np.int32))
+    pool, table = _pages(C, bs, B * 7 + bs)
+    table[0, 3] = -1                                  # its slots are skipped
+    ref_out, ref_lse = oracle.sparse_mla_attend_paged(Q, pool, table, idx, 512, 1.0 / 24)
+    out, lse = isa.isa_sparse_mla_attend_paged(dev(Q), dev(pool), dev(table), dev(idx), 512,
+                                               1.0 / 24, want_lse=True)
+    torch.cuda.synchronize()
+    assert_attn_close(out, ref_out, "paged")
+    assert_lse_close(lse, ref_lse, "paged")
+    # with every block allocated, the paged and contiguous kernels agree bit for bit
+    pool, table = _pages(C, bs, B * 11 + bs)
+    out_p, _ = isa.isa_sparse_mla_attend_paged(dev(Q), dev(pool), dev(table), dev(idx), 512,
+                                               1.0 / 24)
+    out_c, _ = isa.isa_sparse_mla_attend(dev(Q), dev(C), dev(idx), 512, 1.0 / 24)
+    torch.cuda.synchronize()
+    assert torch.equal(host(out_p), host(out_c))

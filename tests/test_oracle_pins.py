@@ -352,6 +352,68 @@ def test_fp8_attend_equals_bf16_attend_when_dequantization_is_exact():
     np.testing.assert_array_equal(lse8, lseb)
 
 
+# ------------------------------------------------------------ paged caches ----
+
+def _paged(cache, bs, seed, extra=3):
+    g = torch.Generator().manual_seed(seed)
+    B, L = cache.shape[0], cache.shape[1]
+    table = synth.page_layout(B, L, bs, g, "cpu", extra_pages=extra)
+    n_pages = B * (L // bs) + extra
+    return synth.to_pages(cache, table, bs, n_pages), table
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_paged_oracle_is_the_contiguous_one_under_any_page_placement(bs):
+    # pages placed in a random order (plus unused pages) give the results of
+    # the logical, contiguous cache
+    r = _rng(600 + bs)
+    B, Tq, H_I, D_I, L = 2, 3, 4, 32, 256
+    g = torch.Generator().manual_seed(bs)
+    qI = synth.int8_uniform((B, Tq, H_I, D_I), g, "cpu")
+    w = synth.pow2_weights((B, Tq, H_I), g, "cpu")
+    kI = synth.int8_uniform((B, L, D_I), g, "cpu")
+    kv_len = torch.tensor([L, 150], dtype=torch.int32)
+    pool, table = _paged(kI, bs, bs)
+    np.testing.assert_array_equal(oracle.indexer_scores_paged(qI, w, pool, table, kv_len),
+                                  oracle.indexer_scores(qI, w, kI, kv_len))
+    H, D, D_v, k = 2, 20, 16, 9
+    Q, C = _bf16((B, Tq, H, D), g), _bf16((B, L, D), g)
+    idx = r.integers(-1, L, size=(B, Tq, k)).astype(np.int32)
+    cpool, ctable = _paged(C, bs, bs + 1)
+    o1, l1 = oracle.sparse_mla_attend_paged(Q, cpool, ctable, idx, D_v, 0.3)
+    o2, l2 = oracle.sparse_mla_attend(Q, C, idx, D_v, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_paged_oracle_unallocated_blocks():
+    # an unallocated block (-1, or a page id past the pool) scores -inf and
+    # its slots are skipped: attention equals dropping those slots
+    bs, B, Tq, L = 32, 1, 2, 128
+    g = torch.Generator().manual_seed(5)
+    qI = synth.int8_uniform((B, Tq, 4, 32), g, "cpu")
+    w = synth.pow2_weights((B, Tq, 4), g, "cpu")
+    kI = synth.int8_uniform((B, L, 32), g, "cpu")
+    kv_len = torch.tensor([L], dtype=torch.int32)
+    pool, table = _paged(kI, bs, 9, extra=0)
+    table[0, 1] = -1
+    table[0, 3] = 1000
+    S = oracle.indexer_scores_paged(qI, w, pool, table, kv_len)
+    ref = oracle.indexer_scores(qI, w, kI, kv_len)
+    dead = np.zeros(L, dtype=bool)
+    dead[32:64] = dead[96:128] = True
+    assert np.all(np.isneginf(S[:, :, dead]))
+    np.testing.assert_array_equal(S[:, :, ~dead], ref[:, :, ~dead])
+    Q, C = _bf16((B, Tq, 2, 12), g), _bf16((B, L, 12), g)
+    cpool, _ = _paged(C, bs, 9, extra=0)          # same seed: same placement as the keys
+    idx = np.array([[[0, 40, 70, 100, -1], [33, 34, 35, 5, 64]]], dtype=np.int32)
+    out, lse = oracle.sparse_mla_attend_paged(Q, cpool, table, idx, 8, 0.5)
+    idx_live = np.where(dead[np.clip(idx, 0, L - 1)] | (idx < 0), -1, idx).astype(np.int32)
+    out2, lse2 = oracle.sparse_mla_attend(Q, C, idx_live, 8, 0.5)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
 # ------------------------------------------------------ index access counts ----
 
 @pytest.mark.parametrize("seed", range(3))
