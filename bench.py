@@ -496,7 +496,7 @@ def main():
         "topk": (1, alg["topk_read_bytes"],
                  "topk_hist_kernel + topk_classify_kernel + topk_finish_kernel"),
         "attend": (wl.n_layers, alg["at_bytes_per_layer"],
-                   "sparse_attend_kernel<1, 1, 576, 512, 2> + merge_splits_kernel (one layer)"),
+                   "sparse_attend_kernel<1, 1, 576, 512, 2, false> + merge_splits_kernel (one layer)"),
     }
     stage_us = {"indexer": st["indexer"], "topk": st["topk"], "attend": st["attend_per_layer"]}
     rooflines = {}

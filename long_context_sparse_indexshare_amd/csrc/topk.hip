@@ -124,27 +124,41 @@ __global__ __launch_bounds__(256) void clear_u32_kernel(uint32_t* __restrict__ p
         p[i] = 0u;
 }
 
-__global__ __launch_bounds__(TOPK_THREADS) void topk_hist_kernel(const float* __restrict__ S,
+// The histogram kernel takes larger chunks than the classify kernel: fewer
+// workgroups per row add their bins into the row's histogram, so a bin that
+// many scores share takes fewer contending global atomics.
+constexpr int HIST_THREADS = 1024;
+constexpr int HIST_PER = 16;
+constexpr int HIST_CHUNK = HIST_THREADS * HIST_PER;
+
+__global__ __launch_bounds__(HIST_THREADS) void topk_hist_kernel(const float* __restrict__ S,
                                                                  const int32_t* __restrict__ kv_len,
                                                                  int Tq, int L_cap, int k,
                                                                  uint32_t* __restrict__ hist) {
     const int row = blockIdx.y;
     const int n = visible_count(kv_len, row, Tq, L_cap);
     if (n <= k) return;
-    const int start = blockIdx.x * TOPK_CHUNK;
+    const int start = blockIdx.x * HIST_CHUNK;
     if (start >= n) return;
     __shared__ uint32_t lh[TOPK_HIST_BINS];
-    for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += TOPK_THREADS) lh[i] = 0;
-    __syncthreads();
+    for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += HIST_THREADS) lh[i] = 0;
+    // every score of the thread in flight before the first is used
     const float* rowp = S + (size_t)row * L_cap;
-#pragma unroll 4
-    for (int e = 0; e < TOPK_PER_THREAD; ++e) {
-        const int s = start + e * TOPK_THREADS + threadIdx.x;
-        if (s < n) atomicAdd(&lh[score_key(rowp[s]) >> (32 - TOPK_HIST_BITS)], 1u);
+    float v[HIST_PER];
+#pragma unroll
+    for (int e = 0; e < HIST_PER; ++e) {
+        const int s = start + e * HIST_THREADS + threadIdx.x;
+        v[e] = s < n ? rowp[s] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < HIST_PER; ++e) {
+        const int s = start + e * HIST_THREADS + threadIdx.x;
+        if (s < n) atomicAdd(&lh[score_key(v[e]) >> (32 - TOPK_HIST_BITS)], 1u);
     }
     __syncthreads();
     uint32_t* gh = hist + (size_t)row * TOPK_HIST_BINS;
-    for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += TOPK_THREADS) {
+    for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += HIST_THREADS) {
         const uint32_t c = lh[i];
         if (c) atomicAdd(&gh[i], c);
     }
@@ -808,8 +822,8 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
         if (e != hipSuccess) return e;
     }
     dim3 grid(L.nchunks, rows);
-    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq, L_cap,
-                       k, hist);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3((L_cap + HIST_CHUNK - 1) / HIST_CHUNK, rows),
+                       dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
     if (L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS) {
         hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(SEL_THREADS), 0, stream, S,
                            kv_len, Tq, L_cap, k, hist, idx);
