@@ -78,6 +78,16 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Workgroup blockIdx.x runs on XCD blockIdx.x % 8 (the dispatcher deals
+// workgroups round robin over the 8 XCDs).  Work items are numbered so that a
+// query's items are consecutive; giving every XCD one contiguous range of
+// per_xcd items keeps a query's splits and head blocks (and, in the merge, its
+// partials) on as few XCDs as the balance allows, sharing their L2.  Items
+// past the end belong to no work.
+__device__ __forceinline__ int xcd_item(int wg, int per_xcd) {
+    return (wg % 8) * per_xcd + wg / 8;
+}
+
 // Two E4M3 codes (the low or high 16 bits of w) times the row scale, as two
 // bf16 in one word.  The scale is a power of two, so the products are exact
 // in bf16 while they stay in its normal range.
@@ -132,8 +142,9 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const uint8_t* __restrict__ C8,
     const uint8_t* __restrict__ Ce, const uint16_t* __restrict__ Cr,
     const int32_t* __restrict__ idx, int Tq, int H, int L_cap, int k, float scale_log2,
-    int slots_per_split, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml, PageMap pm) {
+    int slots_per_split, int splits, int nq, int nz, int per_xcd, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ part_o, float2* __restrict__ part_ml,
+    PageMap pm) {
     using G = AttendGeom<HB, VS, D, DV, GR>;
     constexpr int ROWB = G::ROWB;
     // FP8 row: DV code bytes, the exponent byte, D - DV bf16 RoPE dims
@@ -156,10 +167,16 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const int g = lane >> 5;
     const int hbl = wave % HB;              // head block within the workgroup
     const int kp = wave / HB;               // this wave's share of the K and column split
-    const int q = blockIdx.y;               // b * Tq + t
-    const int sp = blockIdx.x;
-    const int hbg = blockIdx.z / VS;        // head-block group of the workgroup
-    const int vh = blockIdx.z - hbg * VS;   // column part
+    // work item (query, split, head-block group x column part), numbered in
+    // that order, from the workgroup's place in the XCD round robin (see
+    // xcd_item)
+    const int item = xcd_item(blockIdx.x, per_xcd);
+    if (item >= nq * splits * nz) return;
+    const int q = item / (splits * nz);     // b * Tq + t
+    const int sp = (item / nz) % splits;
+    const int zz = item % nz;
+    const int hbg = zz / VS;                // head-block group of the workgroup
+    const int vh = zz - hbg * VS;           // column part
     const int b = q / Tq;
     const int head = (hbg * HB + hbl) * 32 + j;
     const bool head_ok = head < H;
@@ -541,7 +558,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     // reads it in that layout.
     {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const int n_hbg = gridDim.z / VS;
+        const int n_hbg = nz / VS;
         v2u* po = reinterpret_cast<v2u*>(part_o) +
                   (((((size_t)q * splits + sp) * n_hbg + hbg) * VS + vh) * 4 + wave) *
                       (G::NB * 4 * 64);
@@ -554,8 +571,8 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                                     ((uint32_t)f2bf(o[nb][4 * r4 + 1] * inv) << 16);
                 const uint32_t hi = (uint32_t)f2bf(o[nb][4 * r4 + 2] * inv) |
                                     ((uint32_t)f2bf(o[nb][4 * r4 + 3] * inv) << 16);
-                // streamed past L2: the merge kernel reads the partials once
-                __builtin_nontemporal_store(v2u{lo, hi}, po + (nb * 4 + r4) * 64 + lane);
+                // plain stores: the merge reads them on the same XCD, from L2
+                po[(nb * 4 + r4) * 64 + lane] = v2u{lo, hi};
             }
         }
         if (head_ok && grp == 0 && kp == 0 && g == 0)
@@ -575,10 +592,10 @@ constexpr int MERGE_THREADS = 256;
 template <int DV, int VS, int HB, int NB, int CW>
 __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml, int nq, int H,
-    int n_hbg, int splits, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int n_hbg, int splits, int per_xcd, uint16_t* __restrict__ out, float* __restrict__ lse) {
     constexpr int COLS = DV / VS;
     constexpr int BLOCK = 4 * NB * 4 * 64;         // v2u per (query, split, hbg, column part)
-    const size_t gid = (size_t)blockIdx.x * MERGE_THREADS + threadIdx.x;
+    const size_t gid = (size_t)xcd_item(blockIdx.x, per_xcd) * MERGE_THREADS + threadIdx.x;
     const int lane = (int)(gid % 64);
     size_t rest = gid / 64;
     const int r4 = (int)(rest % 4); rest /= 4;
@@ -599,9 +616,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
     for (int sj = 0; sj < MAX_SPLITS; ++sj) {
         if (sj < splits) {
             ml[sj] = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + head];
-            v[sj] = __builtin_nontemporal_load(
-                reinterpret_cast<const v2u*>(part_o) +
-                ((((size_t)q * splits + sj) * n_hbg + hbg) * VS + vh) * BLOCK + within);
+            v[sj] = reinterpret_cast<const v2u*>(part_o)[
+                ((((size_t)q * splits + sj) * n_hbg + hbg) * VS + vh) * BLOCK + within];
         } else {
             ml[sj] = make_float2(-__builtin_inff(), 0.0f);
             v[sj] = v2u{0u, 0u};
@@ -652,19 +668,22 @@ hipError_t launch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B,
     uint16_t* part_o = reinterpret_cast<uint16_t*>(base + plan.part_o_off);
     float2* part_ml = reinterpret_cast<float2*>(base + plan.part_ml_off);
     const int n_hbg = (H + 32 * HB - 1) / (32 * HB);
-    dim3 grid(plan.splits, nq, n_hbg * VS);
-    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV, GR, KV8>), grid,
+    const int nz = n_hbg * VS;
+    const int items = nq * plan.splits * nz;
+    const int per_xcd = (items + 7) / 8;
+    hipLaunchKernelGGL((sparse_attend_kernel<HB, VS, D, DV, GR, KV8>), dim3(8 * per_xcd),
                        dim3(AT_THREADS * GR), 0, stream, Q, kv.C, kv.C8, kv.Ce, kv.Cr, idx, Tq, H,
-                       L_cap, k, sm_scale * LOG2E, plan.slots_per_split, plan.splits, out, lse,
-                       part_o, part_ml, pm);
+                       L_cap, k, sm_scale * LOG2E, plan.slots_per_split, plan.splits, nq, nz,
+                       per_xcd, out, lse, part_o, part_ml, pm);
     if (plan.splits > 1)
     {
         using Gm = AttendGeom<HB, VS, D, DV, GR>;
         const size_t threads = (size_t)nq * n_hbg * VS * 4 * Gm::NB * 4 * 64;
-        hipLaunchKernelGGL((merge_splits_kernel<DV, VS, HB, Gm::NB, Gm::CW>),
-                           dim3((unsigned)((threads + MERGE_THREADS - 1) / MERGE_THREADS)),
+        const int mwg = (int)((threads + MERGE_THREADS - 1) / MERGE_THREADS);
+        const int mper = (mwg + 7) / 8;
+        hipLaunchKernelGGL((merge_splits_kernel<DV, VS, HB, Gm::NB, Gm::CW>), dim3(8 * mper),
                            dim3(MERGE_THREADS), 0, stream, part_o, part_ml, nq, H, n_hbg,
-                           plan.splits, out, lse);
+                           plan.splits, mper, out, lse);
     }
     return hipGetLastError();
 }
