@@ -14,7 +14,8 @@ several independent input instances so the 256 MiB MALL cannot hold the
 working set between steps.  Timing: W untimed warm-up steps, then exactly K
 steps between two synchronised HIP events on the stream the library launches
 on.  Each stage (indexer, top-k, one attention layer) is also timed alone,
-back to back with HIP events, for its roofline entry; "roofline" is the stage
+back to back with HIP events and taking the input instances in turn, for its
+roofline entry; "roofline" is the stage
 that takes the largest share of a step (attention, four launches per group),
 and the CPU oracle is timed on one group of the same workload on the host.
 
@@ -116,37 +117,52 @@ def time_group(isa, calls, steps, warmup, torch):
 def time_per_launch(fn, n, torch):
     """Average device duration of fn's launches: n launches back to back on the
     launch stream between one pair of HIP events (the events' own overhead is
-    spread over the n launches)."""
-    fn()
+    spread over the n launches).  fn may be a list of callables, taken in turn
+    (independent input instances, so that caches do not carry one launch's
+    inputs to the next)."""
+    fns = fn if isinstance(fn, (list, tuple)) else [fn]
+    for f in fns:
+        f()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(n):
-        fn()
+    for i in range(n):
+        fns[i % len(fns)]()
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / 1e3 / n
 
 
-def stage_times(isa, inst, wl, torch, reps=20):
-    """Per-stage device time of one group, each stage timed alone."""
-    d = inst
-    S = torch.empty((wl.B, wl.Tq, wl.L_cap), dtype=torch.float32, device="cuda")
-    idx = torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda")
+def stage_times(isa, insts, wl, torch, reps=20):
+    """Per-stage device time of one group, each stage timed alone, launches
+    taking the input instances in turn (as the group steps do)."""
+    S = [torch.empty((wl.B, wl.Tq, wl.L_cap), dtype=torch.float32, device="cuda")
+         for _ in insts]
+    idx = [torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda") for _ in insts]
     ws = isa.Workspace()
-    t_ix = time_per_launch(lambda: isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"],
-                                                          S=S), reps, torch)
-    t_tk = time_per_launch(lambda: isa.isa_topk_select(S, d["kv_len"], wl.k, idx=idx, ws=ws),
-                           reps, torch)
-    outs = [torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
-            for _ in range(wl.n_layers)]
-    t_at = time_per_launch(lambda: isa.isa_sparse_mla_attend(d["Q"][0], d["C"][0], idx, wl.D_v,
-                                                             wl.sm_scale, out=outs[0], ws=ws),
-                           reps, torch)
+
+    def ix(i):
+        d = insts[i]
+        return lambda: isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"], S=S[i])
+
+    def tk(i):
+        return lambda: isa.isa_topk_select(S[i], insts[i]["kv_len"], wl.k, idx=idx[i], ws=ws)
+
+    out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+
+    def at(i):
+        d = insts[i]
+        return lambda: isa.isa_sparse_mla_attend(d["Q"][0], d["C"][0], idx[i], wl.D_v,
+                                                 wl.sm_scale, out=out, ws=ws)
+
+    n = range(len(insts))
+    t_ix = time_per_launch([ix(i) for i in n], reps, torch)    # also fills S
+    t_tk = time_per_launch([tk(i) for i in n], reps, torch)    # also fills idx
+    t_at = time_per_launch([at(i) for i in n], reps, torch)
     # access counts of the index set (the HiSparse input; not part of the step)
     counts = torch.zeros((wl.B, wl.L_cap), dtype=torch.int32, device="cuda")
-    t_h = time_per_launch(lambda: isa.isa_index_histogram(idx, wl.L_cap, counts=counts), reps,
+    t_h = time_per_launch(lambda: isa.isa_index_histogram(idx[0], wl.L_cap, counts=counts), reps,
                           torch)
     return t_ix, t_tk, t_at, t_h
 
@@ -341,11 +357,13 @@ def run_fp8_kv(isa, torch, steps, warmup, n_inst):
                            wl.D_v, wl.sm_scale, ws=ws, kv8=(d["C8"], d["Ce"], d["Cr"]))
              for d in insts]
     t = time_group(isa, calls, steps, warmup, torch)
-    d = insts[0]
     out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
-    t_at = time_per_launch(lambda: isa.isa_sparse_mla_attend_fp8(
-        d["Q"][0], d["C8"][0], d["Ce"][0], d["Cr"][0], calls[0].idx, wl.sm_scale, out=out, ws=ws),
-        20, torch)
+
+    def at(d, c):
+        return lambda: isa.isa_sparse_mla_attend_fp8(d["Q"][0], d["C8"][0], d["Ce"][0], d["Cr"][0],
+                                                     c.idx, wl.sm_scale, out=out, ws=ws)
+
+    t_at = time_per_launch([at(d, c) for d, c in zip(insts, calls)], 20, torch)
     a = algorithmic(wl)
     row_bytes = wl.D_v + 1 + (wl.D - wl.D_v) * 2          # codes, scale byte, RoPE dims
     sel = wl.B * wl.Tq * min(wl.k, wl.kv_len)
@@ -408,7 +426,7 @@ def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_row
     t_step = time_group(isa, calls, steps, warmup, torch)
     alg = algorithmic(wl)
     log(f"{wl.name}: {t_step * 1e6:.1f} us/step; timing stages")
-    t_ix, t_tk, t_at, t_h = stage_times(isa, insts[0], wl, torch)
+    t_ix, t_tk, t_at, t_h = stage_times(isa, insts, wl, torch)
     res = {
         "t_step": t_step, "alg": alg,
         "stages_us": {"indexer": t_ix * 1e6, "topk": t_tk * 1e6, "attend_per_layer": t_at * 1e6},

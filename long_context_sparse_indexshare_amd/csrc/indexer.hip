@@ -14,8 +14,8 @@
 // ReLU and the head weight in fp32 and reduces the heads of a query in
 // registers plus one cross-lane swap; blocks past the last visible key of
 // every query in the workgroup skip the loads and write -inf.  Each wave
-// keeps the next key block's loads in flight while it computes the current
-// one.
+// keeps the next two key blocks' loads in flight while it computes the
+// current one.
 #include "isa_internal.h"
 
 namespace isa {
@@ -26,8 +26,13 @@ constexpr int IX_ROWS = 64;              // (query, head) rows per workgroup
 constexpr int IX_KEYS_PER_STEP = 128;    // 4 waves x 32 keys
 constexpr int IX_STEPS = 8;
 constexpr int IX_KEYS_PER_WG = IX_KEYS_PER_STEP * IX_STEPS;
+constexpr int IX_DEPTH = 3;              // key blocks per wave: 1 computed + 2 in flight
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
+
+// Key bytes read by lanes that have no live key (the largest D_I is 128).
+__device__ __attribute__((aligned(16))) int8_t g_zero_keys[128];
+typedef const __attribute__((address_space(1))) v4i* global_v4i_ptr;
 
 // Zeroes zero[0, zero_n) with the whole grid (the next launch's counters; it
 // saves that launch a fill kernel of its own).
@@ -99,29 +104,36 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
         }
     }
 
-    // B operands of one 32-key block: lane (key s0 + j, half g) holds k bytes 32*ks + 16*g .. +16
+    // B operands of one 32-key block: lane (key s0 + j, half g) holds k bytes
+    // 32*ks + 16*g .. +16.  Lanes without a live key read the zero row instead:
+    // the loads are unconditional, so the compiler can count them and wait
+    // only for the block about to be used, not for the ones behind it.
+    const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_keys);
     auto load_keys = [&](int s0, v4i* bk) {
         const int s = s0 + j;
         const long long r0 = s0 <= pos_max && s0 < L_cap ? key_block_row(pm, b, L_cap, s0) : -1;
         const bool live = r0 >= 0 && s < L_cap;
+        const uintptr_t src =
+            (live ? reinterpret_cast<uintptr_t>(kI + (size_t)(r0 + j) * D_I) : zero_row) + 16 * g;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + (size_t)(r0 + j) * D_I +
-                                                          32 * ks + 16 * g)
-                          : v4i{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = *(global_v4i_ptr)(src + 32 * ks);
     };
 
+    // ring of IX_DEPTH key blocks per wave: the one being computed and the
+    // next IX_DEPTH - 1 in flight (the loop is unrolled, so the ring indices
+    // are constants and the blocks stay in registers)
     const int key_base = blockIdx.x * IX_KEYS_PER_WG + wave * 32;
-    v4i bk_next[KS];
-    load_keys(key_base, bk_next);
+    v4i ring[IX_DEPTH][KS];
+#pragma unroll
+    for (int p = 0; p < IX_DEPTH - 1; ++p) load_keys(key_base + p * IX_KEYS_PER_STEP, ring[p]);
+    // (blocks at or past L_cap load zeros and store nothing; no early exit, so
+    // the loop unrolls fully)
+#pragma unroll
     for (int step = 0; step < IX_STEPS; ++step) {
         const int s0 = key_base + step * IX_KEYS_PER_STEP;
-        if (s0 >= L_cap) break;
-        v4i bk[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bk[ks] = bk_next[ks];
-        if (step + 1 < IX_STEPS) load_keys(s0 + IX_KEYS_PER_STEP, bk_next);   // next block in flight
+        if (step + IX_DEPTH - 1 < IX_STEPS)
+            load_keys(s0 + (IX_DEPTH - 1) * IX_KEYS_PER_STEP, ring[(step + IX_DEPTH - 1) % IX_DEPTH]);
+        const v4i* bk = ring[step % IX_DEPTH];
         const int s = s0 + j;
         // positions on an unallocated page score -inf
         const bool page_ok = pm.table == nullptr || key_block_row(pm, b, L_cap, s0) >= 0;
@@ -231,17 +243,17 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
         }
     }
 
+    // as in the decode kernel: unconditional loads, dead lanes read the zero row
+    const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_keys);
     auto load_keys = [&](int s0, v4i* bk) {
         const int s = s0 + j;
         const long long r0 =
             s0 <= pos_max && s0 < s_hi && s0 < L_cap ? key_block_row(pm, b, L_cap, s0) : -1;
         const bool live = r0 >= 0 && s < L_cap;
+        const uintptr_t src =
+            (live ? reinterpret_cast<uintptr_t>(kI + (size_t)(r0 + j) * D_I) : zero_row) + 16 * g;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bk[ks] = live ? *reinterpret_cast<const v4i*>(kI + (size_t)(r0 + j) * D_I +
-                                                          32 * ks + 16 * g)
-                          : v4i{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = *(global_v4i_ptr)(src + 32 * ks);
     };
 
     // scores of the 32 keys s0 .. s0+31 against both queries, from keys in bk
