@@ -7,8 +7,9 @@
 // the whole latent row and the value its first D_v entries):
 //   z_j = sm_scale * Q[h] . C[idx_j];  out[h] = sum_j softmax(z)_j * C[idx_j, :D_v].
 //
-// A workgroup (4 waves) owns one query, HB blocks of 32 heads, 1/VS of the
-// value columns, and a range (split) of the query's k slots.  Per tile of 32
+// A group of 4 waves owns one query, HB blocks of 32 heads, 1/VS of the
+// value columns, and a range (split) of the query's k slots; a workgroup
+// holds GR such groups on alternate tiles of the same range.  Per tile of 32
 // gathered latent rows (each row is read from HBM once and shared by all the
 // workgroup's heads):
 //   * gather: each thread loads 16-byte chunks of the tile's rows straight
@@ -18,9 +19,9 @@
 //     need tens of KiB in flight per CU to approach HBM bandwidth; the
 //     direct-to-LDS load path measured ~3x slower for this pattern);
 //     slots that are -1 or out of range load a zero row;
-//   * LDS rows are unpadded; the 16-byte chunks of every aligned group of
-//     eight are XOR-swizzled by (row/2)%8, so the 16 rows one ds_read_b128
-//     quarter-wave touches fall in 16 distinct bank groups;
+//   * LDS rows carry one 16-byte pad, so the 16 rows one ds_read_b128
+//     quarter-wave touches (same chunk, consecutive rows) fall in 16
+//     distinct bank groups;
 //   * S^T = C_rows . Q^T on v_mfma_f32_32x32x16_bf16, a 32-row x 32-head
 //     block per head block, with the contraction over the latent dims split
 //     between the 4/HB waves of the head block (each holds only its share of
@@ -86,6 +87,18 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 // past the end belong to no work.
 __device__ __forceinline__ int xcd_item(int wg, int per_xcd) {
     return (wg % 8) * per_xcd + wg / 8;
+}
+
+// LDS slot of tile row r: within each 16-row half the rows are stored as a
+// 4 x 4 transpose (slot 4*(r%4) + (r/4)%4).  With an odd number of 16-byte
+// bank groups per row stride (stride = 4 mod 8 words, 64 banks), both read
+// patterns of a tile hit distinct banks: the QK operand reads (16
+// consecutive rows, one 16-byte chunk: any 16 distinct slots of a half) and
+// the transposing PV reads (rows 4i..4i+3, 64 contiguous bytes each, whose
+// slots 4*(r%4) + i start 64 bytes apart in bank order).  Rows keep their
+// tile order everywhere else.
+__device__ __forceinline__ int tile_slot(int r) {
+    return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 // Two E4M3 codes (the low or high 16 bits of w) times the row scale, as two
@@ -238,7 +251,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const uintptr_t cbase = reinterpret_cast<uintptr_t>(Cb);
     const int grow = tid / G::TPR;
     const int gsub = tid % G::TPR;
-    char* const lrow = tile + grow * ROWB + gsub * 16;
+    char* const lrow = tile + tile_slot(grow) * ROWB + gsub * 16;
 #define ISA_LOAD_TILE(R, TS)                                                                   \
     {                                                                                          \
         const int s_ = sidx[(TS) - slot0 + grow];   /* -1 past the split (padded) */           \
@@ -258,7 +271,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     // row's exponent byte; an invalid slot reads zero codes with exponent 0.
     const uintptr_t c8base = reinterpret_cast<uintptr_t>(C8b);
     const uintptr_t crbase = reinterpret_cast<uintptr_t>(Crb);
-    char* const lrow8 = tile + grow * ROWB;
+    char* const lrow8 = tile + tile_slot(grow) * ROWB;
 #define ISA_LOAD_TILE8(R8, RR, SE, TS)                                                         \
     {                                                                                          \
         const int s_ = sidx[(TS) - slot0 + grow];                                              \
@@ -294,7 +307,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         v16f st, st2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = st2[r] = 0.0f;
-        const char* arow = tile + j * ROWB;
+        const char* arow = tile + tile_slot(j) * ROWB;
 #pragma unroll
         for (int i = 0; i < G::KSW; ++i) {
             const int ch = 2 * (kp * G::KSW + i) + g;
@@ -392,8 +405,8 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
 #pragma unroll
             for (int nb = 0; nb < G::NB; ++nb) {
                 const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
-                const v4bf lo = lds_read_tr(tile, row * ROWB + col * 2);
-                const v4bf hi = lds_read_tr(tile, (row + 8) * ROWB + col * 2);
+                const v4bf lo = lds_read_tr(tile, tile_slot(row) * ROWB + col * 2);
+                const v4bf hi = lds_read_tr(tile, tile_slot(row + 8) * ROWB + col * 2);
                 const v8bf a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[nb], 0, 0, 0);
             }

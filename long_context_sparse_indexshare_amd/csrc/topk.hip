@@ -85,23 +85,38 @@ template <int PER, bool DESC, int NT = TOPK_THREADS>
 __device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint32_t* sh_waves,
                                           uint32_t* sh_res) {
     const int tid = threadIdx.x;
-    // thread t owns bins [PER*t, PER*t + PER) ascending, or the mirrored range descending
+    // thread t owns bins [PER*t, PER*t + PER) ascending, or the mirrored range
+    // descending; it keeps them in registers for the walk below (16-byte loads
+    // where PER allows)
     const int first = DESC ? (NT - 1 - tid) * PER : tid * PER;
+    uint32_t hv[PER];
+    if constexpr (PER % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < PER; i += 4) {
+            const uint4 q = *reinterpret_cast<const uint4*>(h + first + i);
+            hv[i] = q.x; hv[i + 1] = q.y; hv[i + 2] = q.z; hv[i + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) hv[i] = h[first + i];
+    }
     uint32_t local = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) local += h[first + i];
+    for (int i = 0; i < PER; ++i) local += hv[i];
     uint32_t total;
     const uint32_t before = block_exclusive_scan<NT>(local, &total, sh_waves);
     if (before < need && before + local >= need) {
+        // the bin where the running count (in this thread's direction) reaches need
         uint32_t acc = before;
+        bool found = false;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int bin = DESC ? first + PER - 1 - i : first + i;
-            const uint32_t c = h[bin];
-            if (acc + c >= need) {
-                sh_res[0] = (uint32_t)bin;
+            const int o = DESC ? PER - 1 - i : i;
+            const uint32_t c = hv[o];
+            if (!found && acc + c >= need) {
+                sh_res[0] = (uint32_t)(first + o);
                 sh_res[1] = acc;
-                break;
+                found = true;
             }
             acc += c;
         }
