@@ -29,7 +29,7 @@ struct PageMap {
 };
 
 // Top-k geometry (shared by the host sizing code and the kernels).
-constexpr int TOPK_THREADS = 256;
+constexpr int TOPK_THREADS = 1024;          // classify workgroup: 4 scores per thread
 constexpr int TOPK_CHUNK = 4096;            // scores per workgroup
 constexpr int TOPK_PER_THREAD = TOPK_CHUNK / TOPK_THREADS;
 constexpr int TOPK_HIST_BITS = 12;          // first radix digit: key bits [31:20]

@@ -11,8 +11,9 @@
 // the whole chip:
 //   0. clear:    zero the row counters in the workspace (a fill kernel).
 //   1. hist:     every workgroup histograms the top 12 key bits of a
-//                4096-score chunk in LDS and adds its non-zero bins to the
-//                row's global histogram.
+//                chunk of the row (16384 scores, or 4096 when few rows give
+//                few chunks) in LDS and adds its non-zero bins to the row's
+//                global histogram.
 //   2. classify: every workgroup finds the bin that holds the k-th key and
 //                keeps its chunk's keys at or above that bin as one run of
 //                (key, position) entries in ascending position.
@@ -139,17 +140,25 @@ __global__ __launch_bounds__(256) void clear_u32_kernel(uint32_t* __restrict__ p
         p[i] = 0u;
 }
 
-// The histogram kernel takes larger chunks than the classify kernel: fewer
+// The histogram kernel takes HIST_PER scores per thread.  With many rows it
+// takes larger chunks than the classify kernel (16 per thread): fewer
 // workgroups per row add their bins into the row's histogram, so a bin that
-// many scores share takes fewer contending global atomics.
+// many scores share takes fewer contending global atomics.  With few rows
+// (decode) it takes the classify kernel's 4096-score chunks (4 per thread),
+// so that enough workgroups stream the scores, as long as a row's hot bins
+// do not collect the atomics of too many workgroups.
 constexpr int HIST_THREADS = 1024;
-constexpr int HIST_PER = 16;
-constexpr int HIST_CHUNK = HIST_THREADS * HIST_PER;
+constexpr int HIST_PER_MANY = 16;
+constexpr int HIST_PER_FEW = 4;
+constexpr int HIST_MIN_WGS = 256;          // below this many 16-per-thread chunks: 4 per thread,
+constexpr int HIST_MAX_FEW_CHUNKS = 64;    // unless a row would take more chunks than this
 
+template <int HIST_PER>
 __global__ __launch_bounds__(HIST_THREADS) void topk_hist_kernel(const float* __restrict__ S,
                                                                  const int32_t* __restrict__ kv_len,
                                                                  int Tq, int L_cap, int k,
                                                                  uint32_t* __restrict__ hist) {
+    constexpr int HIST_CHUNK = HIST_THREADS * HIST_PER;
     const int row = blockIdx.y;
     const int n = visible_count(kv_len, row, Tq, L_cap);
     if (n <= k) return;
@@ -212,6 +221,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     constexpr int NW = TOPK_THREADS / 64;
+    static_assert(TOPK_PER_THREAD * NW == 64, "one wave scans the (e, wave) counts");
     __shared__ uint32_t lh2[HIST2_BINS];
     __shared__ uint32_t sh_waves[NW];
     __shared__ uint32_t sh_res[4];
@@ -837,8 +847,14 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
         if (e != hipSuccess) return e;
     }
     dim3 grid(L.nchunks, rows);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3((L_cap + HIST_CHUNK - 1) / HIST_CHUNK, rows),
-                       dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
+    constexpr int CH_MANY = HIST_THREADS * HIST_PER_MANY, CH_FEW = HIST_THREADS * HIST_PER_FEW;
+    const size_t wgs_many = (size_t)rows * ((L_cap + CH_MANY - 1) / CH_MANY);
+    if (wgs_many >= (size_t)HIST_MIN_WGS || (L_cap + CH_FEW - 1) / CH_FEW > HIST_MAX_FEW_CHUNKS)
+        hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_MANY>, dim3((L_cap + CH_MANY - 1) / CH_MANY, rows),
+                           dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
+    else
+        hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_FEW>, dim3((L_cap + CH_FEW - 1) / CH_FEW, rows),
+                           dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
     if (L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS) {
         hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(SEL_THREADS), 0, stream, S,
                            kv_len, Tq, L_cap, k, hist, idx);
