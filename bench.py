@@ -15,7 +15,8 @@ working set between steps.  Timing: W untimed warm-up steps, then exactly K
 steps between two synchronised HIP events on the stream the library launches
 on.  Each stage (indexer, top-k, one attention layer) is also timed alone,
 back to back with HIP events and taking the input instances in turn, for its
-roofline entry; "roofline" is the stage
+roofline entry, and the headline groups are also captured once in a HIP
+graph and replayed ("hip_graph"); "roofline" is the stage
 that takes the largest share of a step (attention, four launches per group),
 and the CPU oracle is timed on one group of the same workload on the host.
 
@@ -112,6 +113,35 @@ def time_group(isa, calls, steps, warmup, torch):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / 1e3 / steps
+
+
+def time_group_graph(calls, reps, torch):
+    """The same groups captured once in a HIP graph (one replay runs every
+    call in turn) and replayed reps times: time per group, and whether the
+    replays rewrite the eager results bit for bit."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ref = [(c.idx.clone(), [o.clone() for o in c.out]) for c in calls]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for c in calls:
+        c.idx.fill_(-7)
+    g.replay()
+    torch.cuda.synchronize()
+    equal = all(torch.equal(ri, c.idx) and all(torch.equal(a, b) for a, b in zip(ro, c.out))
+                for (ri, ro), c in zip(ref, calls))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / 1e3 / (reps * len(calls)), equal
 
 
 def time_per_launch(fn, n, torch):
@@ -414,7 +444,8 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_rows=None):
+def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_rows=None,
+                 graph=False):
     import numpy as np
     log(f"{wl.name}: generating {n_inst} input instance(s) on the GPU")
     insts = make_instances(wl, n_inst, "cuda")
@@ -424,11 +455,13 @@ def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_row
     calls = [isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], d["C"], wl.k,
                            wl.D_v, wl.sm_scale, ws=ws) for d in insts]
     t_step = time_group(isa, calls, steps, warmup, torch)
+    t_graph, graph_equal = (time_group_graph(calls, max(1, steps // len(calls)), torch)
+                            if graph else (None, None))
     alg = algorithmic(wl)
     log(f"{wl.name}: {t_step * 1e6:.1f} us/step; timing stages")
     t_ix, t_tk, t_at, t_h = stage_times(isa, insts, wl, torch)
     res = {
-        "t_step": t_step, "alg": alg,
+        "t_step": t_step, "alg": alg, "t_graph": t_graph, "graph_equal": graph_equal,
         "stages_us": {"indexer": t_ix * 1e6, "topk": t_tk * 1e6, "attend_per_layer": t_at * 1e6},
         "index_histogram_us": t_h * 1e6,
     }
@@ -503,7 +536,7 @@ def main():
 
     wl = synth.WORKLOADS["C2_128K"]
     dec = run_workload(isa, wl, args.steps, args.warmup, args.instances, torch,
-                       baseline_seq=None if args.no_cpu_baseline else wl.B)
+                       baseline_seq=None if args.no_cpu_baseline else wl.B, graph=True)
     alg = dec["alg"]
     t = dec["t_step"]
     tokens = wl.tokens_per_group
@@ -552,6 +585,10 @@ def main():
                            "achieved_GBps": alg["group_bytes"] / t / 1e9},
         "stages_us": dec["stages_us"],
         "index_histogram_us": dec["index_histogram_us"],
+        "hip_graph": {"us_per_group": dec["t_graph"] * 1e6,
+                      "replay_equals_eager": dec["graph_equal"],
+                      "note": "the same groups captured once and replayed; value uses eager "
+                              "launches"},
         "copy_GBps_measured": copy_GBps,
     }
     if "oracle" in dec:
