@@ -6,8 +6,9 @@ Inputs are generated on the GPU by the seeded generators; the oracle gets host
 copies of the sampled slices.  Indices are compared bit for bit, outputs to
 the attention tolerance.  Covered: the 32K and 128K decode groups, sampled
 rows of the 4096-query causal prefill, the 1M-context decode group with the
-shared index set and with per-layer indexers (the ablation), and the 7-step
-MTP run that reuses the step-1 index set."""
+shared index set and with per-layer indexers (the ablation), the 7-step MTP
+run that reuses the step-1 index set, and the 128K decode group with FP8
+caches and with paged caches."""
 import pytest
 import torch
 
@@ -148,3 +149,49 @@ def test_mtp_seven_steps_full_size():
                                                       reuse_idx=True)
             for l in range(wl.n_layers):
                 assert_attn_close(outs[l][b:b + 1], outs_ref[l], f"mtp step {step} seq {b} layer {l}")
+
+
+def test_fp8_cache_decode_group_full_size():
+    # the 128K decode group with FP8 latent caches (as bench.py times it),
+    # sampled sequences against the oracle's indexer, top-k and FP8 attention
+    wl = synth.WORKLOADS["C2_128K"]
+    d = synth.group_inputs(wl, device="cuda", kv8=True)
+    _print_case("gpu group fp8", wl.name)
+    idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                         None, wl.k, wl.D_v, wl.sm_scale,
+                                         kv8=(d["C8"], d["Ce"], d["Cr"]))
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        _print_case("oracle fp8", wl.name, "sequence", b)
+        sl = slice(b, b + 1)
+        S = oracle.indexer_scores(d["qI"][sl].cpu(), d["w"][sl].cpu(), d["kI"][sl].cpu(),
+                                  d["kv_len"][sl].cpu())
+        idx_ref = oracle.topk_select(S, d["kv_len"][sl].cpu(), wl.k)
+        assert_idx_equal(idx[sl], idx_ref, f"fp8 seq {b}")
+        for l in range(wl.n_layers):
+            out_ref, _ = oracle.sparse_mla_attend_fp8(
+                d["Q"][l][sl].cpu(), d["C8"][l][sl].cpu(), d["Ce"][l][sl].cpu(),
+                d["Cr"][l][sl].cpu(), idx_ref, wl.sm_scale)
+            assert_attn_close(outs[l][sl], out_ref, f"fp8 seq {b} layer {l}")
+
+
+def test_paged_decode_group_full_size_equals_contiguous():
+    # the 128K decode group over 64-token pages in a random order (as bench.py
+    # times it) gives the contiguous group's bits; the contiguous group is
+    # pinned to the oracle by test_decode_group_full_size
+    wl = synth.WORKLOADS["C2_128K"]
+    bs = 64
+    d = synth.group_inputs(wl, device="cuda")
+    idx, outs = _run_group(wl, d)
+    g = torch.Generator(device="cuda").manual_seed(900)
+    table = synth.page_layout(wl.B, wl.L_cap, bs, g, "cuda", extra_pages=64)
+    n_pages = wl.B * (wl.L_cap // bs) + 64
+    kI = synth.to_pages(d["kI"], table, bs, n_pages)
+    C = [synth.to_pages(x, table, bs, n_pages) for x in d["C"]]
+    _print_case("gpu group paged", wl.name, bs)
+    idx_p, outs_p, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [kI], d["kv_len"], d["Q"], C,
+                                             wl.k, wl.D_v, wl.sm_scale, block_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx), "paged index set differs"
+    for l in range(wl.n_layers):
+        assert torch.equal(outs_p[l], outs[l]), f"paged layer {l} differs"
