@@ -15,7 +15,8 @@
 // registers plus one cross-lane swap; blocks past the last visible key of
 // every query in the workgroup skip the loads and write -inf.  Each wave
 // keeps the next two key blocks' loads in flight while it computes the
-// current one.
+// current one; with one query per workgroup the scores are staged in LDS and
+// written after the last block, four contiguous floats per thread.
 #include "isa_internal.h"
 
 namespace isa {
@@ -119,6 +120,13 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
         for (int ks = 0; ks < KS; ++ks) bk[ks] = *(global_v4i_ptr)(src + 32 * ks);
     };
 
+    // With one query per workgroup (H_I = 64) each step's scores wait in
+    // registers and are written once after the loop: stores and loads share
+    // one in-order counter, so a store between the key blocks would make the
+    // wait for each later block also wait for the store.
+    float res[IX_STEPS];
+#pragma unroll
+    for (int st = 0; st < IX_STEPS; ++st) res[st] = -__builtin_inff();
     // ring of IX_DEPTH key blocks per wave: the one being computed and the
     // next IX_DEPTH - 1 in flight (the loop is unrolled, so the ring indices
     // are constants and the blocks stay in registers)
@@ -176,8 +184,37 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
                 const int t = t0 + qt;
                 if (t >= Tq) continue;
                 const int pos = len - Tq + t;
-                S[((size_t)b * Tq + t) * L_cap + s] =
-                    s <= pos && page_ok ? sum[q] : -__builtin_inff();
+                if constexpr (NQL == 1) {
+                    res[step] = s <= pos && page_ok ? sum[q] : -__builtin_inff();
+                } else {
+                    S[((size_t)b * Tq + t) * L_cap + s] =
+                        s <= pos && page_ok ? sum[q] : -__builtin_inff();
+                }
+            }
+        }
+    }
+    if constexpr (NQL == 1) {
+        // the workgroup's IX_KEYS_PER_WG scores are contiguous in S: stage them
+        // in LDS in key order, then one 16-byte streaming store per thread
+        static_assert(IX_KEYS_PER_WG == 4 * IX_THREADS, "4 scores per thread");
+        __shared__ __attribute__((aligned(16))) float sres[IX_KEYS_PER_WG];
+        if (g == 0) {
+#pragma unroll
+            for (int step = 0; step < IX_STEPS; ++step)
+                sres[step * IX_KEYS_PER_STEP + wave * 32 + j] = res[step];
+        }
+        __syncthreads();
+        const int t = t0;
+        const int k0 = blockIdx.x * IX_KEYS_PER_WG;
+        float* srow = S + ((size_t)b * Tq + t) * L_cap + k0;
+        const int e = threadIdx.x * (IX_KEYS_PER_WG / IX_THREADS);
+        const v4f v = *reinterpret_cast<const v4f*>(&sres[e]);
+        if (t < Tq) {
+            if (k0 + e + 3 < L_cap && (reinterpret_cast<uintptr_t>(srow + e) & 15) == 0) {
+                __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(srow + e));
+            } else {
+                for (int u = 0; u < 4; ++u)
+                    if (k0 + e + u < L_cap) srow[e + u] = v[u];
             }
         }
     }
