@@ -196,7 +196,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     if constexpr (NQL == 1) {
         // the workgroup's IX_KEYS_PER_WG scores are contiguous in S: stage them
         // in LDS in key order, then one 16-byte streaming store per thread
-        static_assert(IX_KEYS_PER_WG == 4 * IX_THREADS, "4 scores per thread");
+        static_assert(IX_KEYS_PER_WG % (4 * IX_THREADS) == 0, "whole 16-byte stores");
         __shared__ __attribute__((aligned(16))) float sres[IX_KEYS_PER_WG];
         if (g == 0) {
 #pragma unroll
@@ -207,14 +207,18 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
         const int t = t0;
         const int k0 = blockIdx.x * IX_KEYS_PER_WG;
         float* srow = S + ((size_t)b * Tq + t) * L_cap + k0;
-        const int e = threadIdx.x * (IX_KEYS_PER_WG / IX_THREADS);
-        const v4f v = *reinterpret_cast<const v4f*>(&sres[e]);
-        if (t < Tq) {
-            if (k0 + e + 3 < L_cap && (reinterpret_cast<uintptr_t>(srow + e) & 15) == 0) {
-                __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(srow + e));
-            } else {
-                for (int u = 0; u < 4; ++u)
-                    if (k0 + e + u < L_cap) srow[e + u] = v[u];
+        const bool a16 = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+#pragma unroll
+        for (int c = 0; c < IX_KEYS_PER_WG / (4 * IX_THREADS); ++c) {
+            const int e = (c * IX_THREADS + threadIdx.x) * 4;
+            const v4f v = *reinterpret_cast<const v4f*>(&sres[e]);
+            if (t < Tq) {
+                if (k0 + e + 3 < L_cap && a16) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(srow + e));
+                } else {
+                    for (int u = 0; u < 4; ++u)
+                        if (k0 + e + u < L_cap) srow[e + u] = v[u];
+                }
             }
         }
     }

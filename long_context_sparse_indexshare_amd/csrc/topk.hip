@@ -727,7 +727,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
             if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
         });
         __syncthreads();
-        const uint2 r3 = find_bin<1, true, SEL_THREADS>(sh, need, f.waves, f.res);
+        const uint2 r3 = find_bin<1024 / SEL_THREADS, true, SEL_THREADS>(sh, need, f.waves, f.res);
         need -= r3.y;
         T = (pre22 << 10) | r3.x;
         for (int i = tid; i < 2048; i += SEL_THREADS) sh[i] = 0;
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
             if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
         });
         __syncthreads();
-        const uint2 q2 = find_bin<2, false, SEL_THREADS>(sh, need, f.waves, f.res);
+        const uint2 q2 = find_bin<2048 / SEL_THREADS, false, SEL_THREADS>(sh, need, f.waves, f.res);
         const uint32_t p2 = q2.x;
         need -= q2.y;
         for (int i = tid; i < 1024; i += SEL_THREADS) sh[i] = 0;
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
             if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
         });
         __syncthreads();
-        const uint32_t p3 = find_bin<1, false, SEL_THREADS>(sh, need, f.waves, f.res).x;
+        const uint32_t p3 = find_bin<1024 / SEL_THREADS, false, SEL_THREADS>(sh, need, f.waves, f.res).x;
         s_cut = (int)((p2 << 10) | p3);
     }
     __syncthreads();
