@@ -371,7 +371,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         float mloc = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;   // scale > 0 keeps the order
+        mloc = xor32_max(mloc) * scale_log2;   // scale > 0 keeps the order
         // move the reference max only when this tile's max exceeds it by more
         // than RESCALE_SLACK (always on the first tile with a valid row)
         const bool move = mloc > m_run + RESCALE_SLACK;
@@ -538,7 +538,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     }
 
     // softmax denominator of head j over all rows (the lane pair splits them)
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = xor32_sum(l_run);
 
     // o[nb] register r holds value column col0 + 32*nb + 8*(r/4) + 4*g + r%4 of head j
     if (splits == 1) {

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
             }
             if (H_I >= 8) {
 #pragma unroll
-                for (int q = 0; q < NQL; ++q) sum[q] += __shfl_xor(sum[q], 32);
+                for (int q = 0; q < NQL; ++q) sum[q] = xor32_sum(sum[q]);
             }
         }
         if (s < L_cap) {
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
                 }
             }
 #pragma unroll
-            for (int q = 0; q < PF_QPWAVE; ++q) sum[q] += __shfl_xor(sum[q], 32);
+            for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = xor32_sum(sum[q]);
         }
         if (g == 0 && s < L_cap) {
             // positions on an unallocated page score -inf

@@ -17,6 +17,22 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
+// Sum and maximum of x over lanes i and i ^ 32 of a wave, the same bits in
+// both halves (the low half's value is always the left operand).
+// v_permlane32_swap exchanges the two 32-lane halves in registers; a
+// __shfl_xor(x, 32) goes through the LDS crossbar (ds_bpermute) and waits
+// for it.
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Paged caches: logical position s of sequence b lives in row
 // (page << shift) + (s & ((1 << shift) - 1)) of the page pool, where page =
 // table[b * max_blocks + (s >> shift)]; pages outside [0, n_pages) are
