@@ -12,16 +12,15 @@
 // holds GR such groups on alternate tiles of the same range.  Per tile of 32
 // gathered latent rows (each row is read from HBM once and shared by all the
 // workgroup's heads):
-//   * gather: each thread loads 16-byte chunks of the tile's rows straight
-//     into registers (thread t owns chunks t, t+256, ... of the tile) and
-//     stores them to LDS once they land; one or two tiles are in flight in
-//     registers while another is computed from LDS (random 1152-byte rows
-//     need tens of KiB in flight per CU to approach HBM bandwidth; the
-//     direct-to-LDS load path measured ~3x slower for this pattern);
-//     slots that are -1 or out of range load a zero row;
-//   * LDS rows carry one 16-byte pad, so the 16 rows one ds_read_b128
-//     quarter-wave touches (same chunk, consecutive rows) fall in 16
-//     distinct bank groups;
+//   * gather: eight threads per tile row load its 16-byte chunks straight
+//     into registers (thread (row, sub) owns chunks sub, sub + 8, ...) and
+//     store them to LDS once they land; each group has its next tile in
+//     flight in registers while it computes the current one from LDS (the
+//     direct-to-LDS load path measured ~3x slower for this pattern); slots
+//     that are -1 or out of range load a zero row;
+//   * LDS rows carry one 16-byte pad and each 16-row half of a tile is
+//     stored as a 4 x 4 transpose of its rows (tile_slot), so both the QK
+//     operand reads and the transposing PV reads hit distinct banks;
 //   * S^T = C_rows . Q^T on v_mfma_f32_32x32x16_bf16, a 32-row x 32-head
 //     block per head block, with the contraction over the latent dims split
 //     between the 4/HB waves of the head block (each holds only its share of

@@ -13,7 +13,8 @@
 // v_mfma_i32_32x32x32_i8 (exact int32 dot products).  The epilogue applies
 // ReLU and the head weight in fp32 and reduces the heads of a query in
 // registers plus one cross-lane swap; blocks past the last visible key of
-// every query in the workgroup skip the loads and write -inf.  Each wave
+// every query in the workgroup read a zero row instead of keys (no HBM
+// traffic, no MFMA) and write -inf.  Each wave
 // keeps the next two key blocks' loads in flight while it computes the
 // current one; with one query per workgroup the scores are staged in LDS and
 // written after the last block, four contiguous floats per thread.
