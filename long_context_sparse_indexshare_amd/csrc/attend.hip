@@ -644,7 +644,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
 #pragma unroll
     for (int sj = 0; sj < MAX_SPLITS; ++sj) {
         if (sj < splits) {
-            const float wgt = exp2f(ml[sj].x - Mu) * ml[sj].y;   // 0 for an empty split
+            // 0 for an empty split; weights below 2^-126 (flushed by
+            // v_exp_f32) are far below the fp32 resolution of the sum, whose
+            // largest term has weight 1
+            const float wgt = __builtin_amdgcn_exp2f(ml[sj].x - Mu) * ml[sj].y;
             L += wgt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
