@@ -607,33 +607,38 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
     int n_hbg, int splits, int per_xcd, uint16_t* __restrict__ out, float* __restrict__ lse) {
     constexpr int COLS = DV / VS;
     constexpr int BLOCK = 4 * NB * 4 * 64;         // v2u per (query, split, hbg, column part)
-    const size_t gid = (size_t)xcd_item(blockIdx.x, per_xcd) * MERGE_THREADS + threadIdx.x;
-    const int lane = (int)(gid % 64);
-    size_t rest = gid / 64;
-    const int r4 = (int)(rest % 4); rest /= 4;
-    const int nb = (int)(rest % NB); rest /= NB;
-    const int wave = (int)(rest % 4); rest /= 4;
-    const int vh = (int)(rest % VS); rest /= VS;
-    const int hbg = (int)(rest % n_hbg); rest /= n_hbg;
-    const int q = (int)rest;
+    static_assert(MERGE_THREADS == 4 * 64, "a workgroup covers the 4 r4 rows of one (wave, nb)");
+    // The workgroup's 256 threads are lane x r4 of one (query, head-block
+    // group, column part, wave, nb) of the layout: those are uniform, and a
+    // split's partials are one contiguous 2 KiB run at a uniform address.
+    int rest = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, per_xcd));
+    const int nb = rest % NB; rest /= NB;
+    const int wave = rest % 4; rest /= 4;
+    const int vh = rest % VS; rest /= VS;
+    const int hbg = rest % n_hbg; rest /= n_hbg;
+    const int q = rest;
     if (q >= nq) return;
+    const int lane = threadIdx.x & 63;
+    const int r4 = threadIdx.x >> 6;
     const int hbl = wave % HB, kp = wave / HB;
     const int head = (hbg * HB + hbl) * 32 + (lane & 31);
-    if (head >= H) return;
+    const int head_c = head < H ? head : H - 1;     // heads past H load head H-1, store nothing
     const int col = vh * COLS + kp * CW + 32 * nb + 8 * r4 + 4 * (lane >> 5);
-    const size_t within = ((size_t)wave * NB + nb) * 4 * 64 + r4 * 64 + lane;
+    const v2u* pb = reinterpret_cast<const v2u*>(part_o) +
+                    ((((size_t)q * splits) * n_hbg + hbg) * VS + vh) * BLOCK +
+                    ((size_t)wave * NB + nb) * 4 * 64;
+    const size_t pstride = (size_t)n_hbg * VS * BLOCK;       // v2u between splits
+    const float2* mb = part_ml + ((size_t)q * splits * VS + vh) * H;
+    const size_t mstride = (size_t)VS * H;                   // float2 between splits
+    // every load is issued before any is used, unconditionally: splits past
+    // the last one read the last one again and get weight 0 below
     float2 ml[MAX_SPLITS];
     v2u v[MAX_SPLITS];
 #pragma unroll
     for (int sj = 0; sj < MAX_SPLITS; ++sj) {
-        if (sj < splits) {
-            ml[sj] = part_ml[(((size_t)q * splits + sj) * VS + vh) * H + head];
-            v[sj] = reinterpret_cast<const v2u*>(part_o)[
-                ((((size_t)q * splits + sj) * n_hbg + hbg) * VS + vh) * BLOCK + within];
-        } else {
-            ml[sj] = make_float2(-__builtin_inff(), 0.0f);
-            v[sj] = v2u{0u, 0u};
-        }
+        const int sc = sj < splits ? sj : splits - 1;
+        ml[sj] = mb[sc * mstride + head_c];
+        v[sj] = pb[sc * pstride + threadIdx.x];
     }
     float M = -__builtin_inff();
 #pragma unroll
@@ -643,22 +648,21 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int sj = 0; sj < MAX_SPLITS; ++sj) {
-        if (sj < splits) {
-            // 0 for an empty split; weights below 2^-126 (flushed by
-            // v_exp_f32) are far below the fp32 resolution of the sum, whose
-            // largest term has weight 1
-            const float wgt = __builtin_amdgcn_exp2f(ml[sj].x - Mu) * ml[sj].y;
-            L += wgt;
+        // 0 for an empty split or one past the last; weights below 2^-126
+        // (flushed by v_exp_f32) are far below the fp32 resolution of the
+        // sum, whose largest term has weight 1
+        const float wgt = sj < splits ? __builtin_amdgcn_exp2f(ml[sj].x - Mu) * ml[sj].y : 0.0f;
+        L += wgt;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w32 = v[sj][e / 2];
-                acc[e] += wgt * __uint_as_float((e & 1) ? (w32 & 0xFFFF0000u) : (w32 << 16));
-            }
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w32 = v[sj][e / 2];
+            acc[e] += wgt * __uint_as_float((e & 1) ? (w32 & 0xFFFF0000u) : (w32 << 16));
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const v2u r = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
                    (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
+    if (head >= H) return;
     *reinterpret_cast<v2u*>(out + ((size_t)q * H + head) * DV + col) = r;
     if (lse && vh == 0 && kp == 0 && nb == 0 && r4 == 0 && lane < 32)
         lse[(size_t)q * H + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
