@@ -42,6 +42,12 @@ def test_algorithmic_counts_causal_prefill():
     assert a["ix_bound"] == "mfma"
     # every prefill query sees more than k keys: 2048 rows each
     assert a["at_bytes_per_layer"] == 4096 * 2048 * 1152 + 4096 * 64 * 1088 * 2
+    # counting each cache row once: at most the 135168-row cache
+    assert a["at_bytes_once_per_layer"] == 135168 * 1152 + 4096 * 64 * 1088 * 2
+    # then the layer is bound by its bf16 MFMA work and the group's ideal time
+    # is the indexer's int8 ops plus four such layers (plus the index sets)
+    t_at = a["at_flops_per_layer"] / bench.PEAK_BF16
+    assert abs(a["t_ideal_once_s"] - (a["t_ix_s"] + a["topk_bytes"] / bench.PEAK_HBM + 4 * t_at)) < 1e-12
 
 
 def test_traffic_is_null_for_another_kernel_source(tmp_path, monkeypatch):
