@@ -53,17 +53,28 @@ __device__ __forceinline__ int visible_count(const int32_t* kv_len, int row, int
     return n > 0 ? n : 0;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active), in
+// registers: DPP row shifts by 1, 2, 4 and 8 scan each 16-lane row, then
+// row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the total of lanes 0-31 to rows 2 and 3.  (A __shfl_up
+// ladder goes through the LDS crossbar, six dependent round trips.)
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    uint32_t v = x;
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
 // Exclusive prefix sum over the NT threads of the workgroup; *total gets the sum.
 template <int NT = TOPK_THREADS>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh_waves) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    uint32_t inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += o;
-    }
+    const uint32_t inc = wave_inclusive_scan(v);
     __syncthreads();
     if (lane == 63) sh_waves[wave] = inc;
     __syncthreads();
@@ -262,13 +273,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     if (wave == 0) {
         // exclusive scan of the 64 (e, wave) counts in ascending-position order
         const uint32_t v = sh_cnt[lane / NW][lane % NW];
-        uint32_t inc = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(inc, off, 64);
-            if (lane >= off) inc += o;
-        }
-        const uint32_t total = __shfl(inc, 63, 64);
+        const uint32_t inc = wave_inclusive_scan(v);
+        const uint32_t total = __builtin_amdgcn_readlane(inc, 63);
         sh_cnt[lane / NW][lane % NW] = inc - v;
         if (lane == 0) {
             const uint32_t base = total ? atomicAdd(&alloc[row], total) : 0u;
