@@ -93,15 +93,13 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
 // sum_{b >= B} h[b] >= need (descending) or the smallest bin B with
 // sum_{b <= B} h[b] >= need (ascending).  Returns (B, the count strictly
 // beyond it: above for descending, below for ascending) to every thread.
+// Thread t owns bins [PER*t, PER*t + PER) ascending, or the mirrored range
+// descending, and keeps them in registers (16-byte loads where PER allows):
+// find_bin_load requests them, find_bin_regs does the rest, so a caller can
+// have them in flight across other waits.
 template <int PER, bool DESC, int NT = TOPK_THREADS>
-__device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint32_t* sh_waves,
-                                          uint32_t* sh_res) {
-    const int tid = threadIdx.x;
-    // thread t owns bins [PER*t, PER*t + PER) ascending, or the mirrored range
-    // descending; it keeps them in registers for the walk below (16-byte loads
-    // where PER allows)
-    const int first = DESC ? (NT - 1 - tid) * PER : tid * PER;
-    uint32_t hv[PER];
+__device__ __forceinline__ void find_bin_load(const uint32_t* h, uint32_t (&hv)[PER]) {
+    const int first = DESC ? (NT - 1 - (int)threadIdx.x) * PER : (int)threadIdx.x * PER;
     if constexpr (PER % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < PER; i += 4) {
@@ -112,6 +110,12 @@ __device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint
 #pragma unroll
         for (int i = 0; i < PER; ++i) hv[i] = h[first + i];
     }
+}
+
+template <int PER, bool DESC, int NT = TOPK_THREADS>
+__device__ __forceinline__ uint2 find_bin_regs(const uint32_t (&hv)[PER], uint32_t need,
+                                               uint32_t* sh_waves, uint32_t* sh_res) {
+    const int first = DESC ? (NT - 1 - (int)threadIdx.x) * PER : (int)threadIdx.x * PER;
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) local += hv[i];
@@ -137,6 +141,14 @@ __device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint
     const uint2 r = make_uint2(sh_res[0], sh_res[1]);
     __syncthreads();
     return r;
+}
+
+template <int PER, bool DESC, int NT = TOPK_THREADS>
+__device__ __forceinline__ uint2 find_bin(const uint32_t* h, uint32_t need, uint32_t* sh_waves,
+                                          uint32_t* sh_res) {
+    uint32_t hv[PER];
+    find_bin_load<PER, DESC, NT>(h, hv);
+    return find_bin_regs<PER, DESC, NT>(hv, need, sh_waves, sh_res);
 }
 
 // Zeroes counters (histograms, candidate counts, tickets) at the start of a
@@ -171,20 +183,22 @@ __global__ __launch_bounds__(HIST_THREADS) void topk_hist_kernel(const float* __
                                                                  uint32_t* __restrict__ hist) {
     constexpr int HIST_CHUNK = HIST_THREADS * HIST_PER;
     const int row = blockIdx.y;
-    const int n = visible_count(kv_len, row, Tq, L_cap);
-    if (n <= k) return;
     const int start = blockIdx.x * HIST_CHUNK;
-    if (start >= n) return;
-    __shared__ uint32_t lh[TOPK_HIST_BINS];
-    for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += HIST_THREADS) lh[i] = 0;
-    // every score of the thread in flight before the first is used
+    // every score of the thread in flight before the first is used, and before
+    // the row's visible length arrives (the loads stay inside the row; those
+    // past the length are not counted)
     const float* rowp = S + (size_t)row * L_cap;
     float v[HIST_PER];
 #pragma unroll
     for (int e = 0; e < HIST_PER; ++e) {
         const int s = start + e * HIST_THREADS + threadIdx.x;
-        v[e] = s < n ? rowp[s] : 0.0f;
+        v[e] = s < L_cap ? rowp[s] : 0.0f;
     }
+    const int n = visible_count(kv_len, row, Tq, L_cap);
+    if (n <= k) return;
+    if (start >= n) return;
+    __shared__ uint32_t lh[TOPK_HIST_BINS];
+    for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += HIST_THREADS) lh[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < HIST_PER; ++e) {
@@ -223,11 +237,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     RowState* __restrict__ row_state, uint2* __restrict__ runs, uint2* __restrict__ ent,
     uint32_t cap, int nchunks_max) {
     const int row = blockIdx.y;
-    const int n = visible_count(kv_len, row, Tq, L_cap);
-    if (n <= k) return;
-    const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
     const int c = blockIdx.x;
-    if (c >= nch) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -239,20 +249,27 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     __shared__ uint32_t sh_cnt[TOPK_PER_THREAD][NW];   // then the exclusive offsets
     __shared__ uint32_t sh_base;
 
-    for (int i = tid; i < HIST2_BINS; i += TOPK_THREADS) lh2[i] = 0;
-    // this chunk's scores, in flight while the threshold bin is found
-    // (position = start + e * 256 + tid: ascending order is (e, wave, lane))
+    // this chunk's scores, in flight while the threshold bin is found and
+    // requested before the row's visible length arrives (they stay inside the
+    // row; the ones past the length are masked below)
+    // (position = start + e * TOPK_THREADS + tid: ascending order is (e, wave, lane))
     const float* rowp = S + (size_t)row * L_cap;
     const int start = c * TOPK_CHUNK;
     float sc[TOPK_PER_THREAD];
 #pragma unroll
     for (int e = 0; e < TOPK_PER_THREAD; ++e) {
         const int s = start + e * TOPK_THREADS + tid;
-        sc[e] = s < n ? rowp[s] : 0.0f;
+        sc[e] = s < L_cap ? rowp[s] : 0.0f;
     }
-    const uint2 th =
-        find_bin<TOPK_HIST_BINS / TOPK_THREADS, true>(hist + (size_t)row * TOPK_HIST_BINS,
-                                                      (uint32_t)k, sh_waves, sh_res);
+    constexpr int HPER = TOPK_HIST_BINS / TOPK_THREADS;
+    uint32_t hv[HPER];
+    find_bin_load<HPER, true>(hist + (size_t)row * TOPK_HIST_BINS, hv);
+    const int n = visible_count(kv_len, row, Tq, L_cap);
+    if (n <= k) return;
+    const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+    if (c >= nch) return;
+    for (int i = tid; i < HIST2_BINS; i += TOPK_THREADS) lh2[i] = 0;
+    const uint2 th = find_bin_regs<HPER, true>(hv, (uint32_t)k, sh_waves, sh_res);
     const uint32_t bin1 = th.x;
     if (c == 0 && tid == 0) row_state[row] = RowState{bin1, th.y};
 
@@ -305,7 +322,7 @@ constexpr int FIN_THREADS = 1024;
 constexpr int FIN_WAVES = FIN_THREADS / 64;
 constexpr int FIN_SPEC = 6;               // entries per thread requested before the total is known
 constexpr int FIN_LDS_PER = ENT_LDS / FIN_THREADS;
-constexpr int FIN_PER = 4;                // entries per thread per compaction tile
+constexpr int FIN_PER = 8;                // entries per thread per compaction tile
 constexpr int COL_MAX = 512;              // entries ranked directly for the exact cut
 static_assert(HIST2_BINS == FIN_THREADS, "one second-digit bin per thread");
 static_assert(TOPK_MAX_CHUNKS <= FIN_THREADS, "one chunk per thread");
@@ -338,6 +355,23 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
     const uint2* __restrict__ ent, uint32_t cap, int nchunks_max, int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
+    const uint2* re = ent + (size_t)row * cap;
+    // every load of this phase is issued before any is used, and before the
+    // row's visible length arrives: the row state, the second-digit
+    // histogram, the chunk table and the first entries (all inside the row's
+    // workspace; entries past the row's total, chunks past its length and the
+    // whole lot for a row that needs no selection are loaded but never used)
+    const RowState rs = row_state[row];
+    const uint32_t total = alloc[row];
+    const uint32_t h2 = hist2[(size_t)row * HIST2_BINS + tid];
+    const uint2 rr_all = tid < nchunks_max ? runs[(size_t)row * nchunks_max + tid] : make_uint2(0u, 0u);
+    const uint32_t nspec = cap < (uint32_t)(FIN_SPEC * FIN_THREADS) ? cap : (uint32_t)(FIN_SPEC * FIN_THREADS);
+    uint2 v[FIN_SPEC];
+#pragma unroll
+    for (int u = 0; u < FIN_SPEC; ++u) {
+        const uint32_t i = u * FIN_THREADS + tid;
+        v[u] = i < nspec ? re[i] : make_uint2(0u, 0u);
+    }
     const int n = visible_count(kv_len, row, Tq, L_cap);
     int32_t* out = idx + (size_t)row * k;
     if (n <= k) {
@@ -348,22 +382,7 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
     __shared__ FinishShared f;
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
     const float* rowp = S + (size_t)row * L_cap;
-    const uint2* re = ent + (size_t)row * cap;
-    // every load of this phase is issued before any is used: the row state,
-    // the second-digit histogram, the chunk table and the first entries
-    // (entries past the row's total are loaded but never used; they lie
-    // inside the row's buffer)
-    const RowState rs = row_state[row];
-    const uint32_t total = alloc[row];
-    const uint32_t h2 = hist2[(size_t)row * HIST2_BINS + tid];
-    const uint2 rr = tid < nch ? runs[(size_t)row * nchunks_max + tid] : make_uint2(0u, 0u);
-    const uint32_t nspec = cap < (uint32_t)(FIN_SPEC * FIN_THREADS) ? cap : (uint32_t)(FIN_SPEC * FIN_THREADS);
-    uint2 v[FIN_SPEC];
-#pragma unroll
-    for (int u = 0; u < FIN_SPEC; ++u) {
-        const uint32_t i = u * FIN_THREADS + tid;
-        v[u] = i < nspec ? re[i] : make_uint2(0u, 0u);
-    }
+    const uint2 rr = tid < nch ? rr_all : make_uint2(0u, 0u);
     const uint32_t bin1 = rs.bin1;
     // 0: entries staged in LDS; 1: read from the entry buffer; 2: buffer overflowed, re-read S
     const int mode = total <= (uint32_t)ENT_LDS ? 0 : (total <= cap ? 1 : 2);
@@ -542,14 +561,22 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
                 else hi = mid - 1;
             }
             int c = lo;
+            // the thread's entries usually lie in one run: its bounds stay in
+            // registers, and only a run boundary inside the range reads more
+            uint32_t run_s = f.cstart[c], run_e = f.cstart[c + 1], run_b = f.cbase[c];
             uint32_t pos[FIN_PER];
             uint32_t selmask = 0;
 #pragma unroll
             for (int u = 0; u < FIN_PER; ++u) {
                 const uint32_t i = i0 + u;
                 const uint32_t a = i < ntot ? i : ntot - 1;
-                while (f.cstart[c + 1] <= a) ++c;
-                const uint2 e = get(f.cbase[c] + (a - f.cstart[c]));
+                while (run_e <= a) {
+                    ++c;
+                    run_s = run_e;
+                    run_e = f.cstart[c + 1];
+                    run_b = f.cbase[c];
+                }
+                const uint2 e = get(run_b + (a - run_s));
                 pos[u] = e.y;
                 selmask |= ((uint32_t)(i < ntot) & sel_of(e.x, e.y)) << u;
             }
