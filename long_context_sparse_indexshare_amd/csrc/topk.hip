@@ -560,23 +560,34 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
                 if (f.cstart[mid] <= a0) lo = mid;
                 else hi = mid - 1;
             }
-            int c = lo;
-            // the thread's entries usually lie in one run: its bounds stay in
-            // registers, and only a run boundary inside the range reads more
-            uint32_t run_s = f.cstart[c], run_e = f.cstart[c + 1], run_b = f.cbase[c];
+            const int c = lo;
+            // The thread's entries lie in run c and, past one boundary, in run
+            // c + 1: both runs' bounds are read at once (clamped indices; run
+            // c + 1 is only used when it exists).  The 64 lanes of a wave span
+            // several boundaries, so a per-entry walk would cost a dependent
+            // LDS read at nearly every step.  Entries past run c + 1 (runs
+            // shorter than FIN_PER entries) take the walk.
+            const int c1 = c + 1 < nch ? c + 1 : nch - 1;
+            const int c2 = c + 2 <= nch ? c + 2 : nch;
+            const uint32_t run_s = f.cstart[c], run_e = f.cstart[c + 1], run_b = f.cbase[c];
+            const uint32_t run_e2 = f.cstart[c2], run_b2 = f.cbase[c1];
             uint32_t pos[FIN_PER];
             uint32_t selmask = 0;
 #pragma unroll
             for (int u = 0; u < FIN_PER; ++u) {
                 const uint32_t i = i0 + u;
                 const uint32_t a = i < ntot ? i : ntot - 1;
-                while (run_e <= a) {
-                    ++c;
-                    run_s = run_e;
-                    run_e = f.cstart[c + 1];
-                    run_b = f.cbase[c];
+                uint32_t slot;
+                if (a < run_e) {
+                    slot = run_b + (a - run_s);
+                } else if (a < run_e2) {
+                    slot = run_b2 + (a - run_e);
+                } else {
+                    int cc = c + 1;
+                    while (f.cstart[cc + 1] <= a) ++cc;
+                    slot = f.cbase[cc] + (a - f.cstart[cc]);
                 }
-                const uint2 e = get(run_b + (a - run_s));
+                const uint2 e = get(slot);
                 pos[u] = e.y;
                 selmask |= ((uint32_t)(i < ntot) & sel_of(e.x, e.y)) << u;
             }
