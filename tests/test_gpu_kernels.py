@@ -118,6 +118,25 @@ def test_topk_crafted_ties_long_rows():
     _topk_check(S, kv_len, k, "crafted long")
 
 
+def test_topk_short_and_empty_runs_across_chunks():
+    # Rows of 2^21 positions (512 chunks of 4096) whose candidates are a few
+    # spikes per chunk, so most runs are shorter than the 8 consecutive
+    # entries a finishing thread compacts (its range crosses two or more run
+    # boundaries), or are packed into three chunks with every other run empty.
+    L_cap, k = 1 << 21, 2048
+    r = np.random.default_rng(23)
+    S = (r.standard_normal((3, 1, L_cap)) * 0.01).astype(np.float32)
+    spread = np.linspace(0, L_cap - 1, 2100).astype(np.int64)            # ~4 per chunk
+    S[0, 0, spread] = 100.0 + r.integers(0, 40, size=spread.size) * 0.25  # ties at the cut
+    packed = np.concatenate([c * 4096 + r.choice(4096, 800, replace=False) for c in (5, 200, 511)])
+    S[1, 0, packed] = 50.0 + r.integers(0, 64, size=packed.size) * 0.5
+    varied = np.concatenate([c * 4096 + r.choice(4096, int(n), replace=False)
+                             for c, n in enumerate(r.integers(2, 8, size=512))])
+    S[2, 0, varied] = 7.0 + r.integers(0, 16, size=varied.size) * 0.125
+    kv_len = torch.tensor([L_cap] * 3, dtype=torch.int32)
+    _topk_check(S, kv_len, k, "short runs")
+
+
 def test_topk_all_in_one_bin_overflows_candidates():
     # every key in the first-digit bin: the candidate list overflows and the
     # last workgroup re-reads the row
