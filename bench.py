@@ -271,21 +271,63 @@ def measured_traffic(stage):
     return float(kv["traffic_bytes_per_launch"])
 
 
+def mtp_calls(isa, wl, d, Qs, ws):
+    """The 7-step MTP run: step 1 a whole group (indexer, top-k, 4 layers),
+    steps 2-7 the 4 layers alone on the same index set."""
+    first = isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qs[0], d["C"], wl.k,
+                          wl.D_v, wl.sm_scale, ws=ws)
+    later = [isa.GroupCall(None, None, None, d["kv_len"], Qs[s], d["C"], wl.k, wl.D_v,
+                           wl.sm_scale, idx=first.idx, reuse_idx=True, ws=ws)
+             for s in range(1, wl.mtp_steps)]
+
+    def run():
+        first()
+        for c in later:
+            c()
+    return run
+
+
+def mtp_roofline(wl):
+    """(algorithmic bytes, ideal seconds) of the 7-step MTP run: one indexer +
+    top-k, then 7 x 4 attention layers on the same index set.  Rows that stay
+    in the 256 MB MALL between steps can make the measured fraction exceed 1."""
+    a = algorithmic(wl)
+    later_layers = (wl.mtp_steps - 1) * wl.n_layers
+    return (a["group_bytes"] + later_layers * a["at_bytes_per_layer"],
+            a["t_ideal_s"] + later_layers * a["t_at_s"])
+
+
+def calibration_copy(torch):
+    """A 1 GiB device copy: its counters calibrate the traffic figures."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_stage(isa, wl, stage, reps, torch):
-    """One stage alone on one input instance, for profiler runs (one JSON line)."""
+    """One stage alone on one input instance, for profiler runs (one JSON line).
+    "mtp" runs the whole 7-step sequence of the C5 workload (one warm-up run,
+    then reps timed runs)."""
     import synth
     d = synth.group_inputs(wl, device="cuda")
+    if stage == "mtp":
+        Qs = [synth.mtp_queries(wl, s, device="cuda") for s in range(1, wl.mtp_steps + 1)]
+        run = mtp_calls(isa, wl, d, Qs, isa.Workspace())
+        calibration_copy(torch)
+        run()
+        torch.cuda.synchronize()
+        t = time_per_launch(run, reps, torch)
+        print(json.dumps({"stage": stage, "workload": wl.name, "reps": reps,
+                          "avg_us_per_7_steps": t * 1e6}), flush=True)
+        return
     S = torch.empty((wl.B, wl.Tq, wl.L_cap), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
     ws = isa.Workspace()
     if stage in ("indexer", "attend"):
-        # a 1 GiB device copy first: its counters calibrate the traffic figures
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch)
     isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"], S=S)
     isa.isa_topk_select(S, d["kv_len"], wl.k, idx=idx, ws=ws)
     torch.cuda.synchronize()
@@ -350,18 +392,9 @@ def run_mtp(isa, torch, reps):
     d = synth.group_inputs(wl, device="cuda")
     Qs = [synth.mtp_queries(wl, s, device="cuda") for s in range(1, wl.mtp_steps + 1)]
     ws = isa.Workspace()
-    first = isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qs[0], d["C"], wl.k,
-                          wl.D_v, wl.sm_scale, ws=ws)
-    later = [isa.GroupCall(None, None, None, d["kv_len"], Qs[s], d["C"], wl.k, wl.D_v,
-                           wl.sm_scale, idx=first.idx, reuse_idx=True, ws=ws)
-             for s in range(1, wl.mtp_steps)]
+    run_reuse = mtp_calls(isa, wl, d, Qs, ws)
     again = [isa.GroupCall([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], Qs[s], d["C"], wl.k,
                            wl.D_v, wl.sm_scale, ws=ws) for s in range(wl.mtp_steps)]
-
-    def run_reuse():
-        first()
-        for c in later:
-            c()
 
     def run_recompute():
         for c in again:
@@ -370,12 +403,15 @@ def run_mtp(isa, torch, reps):
     t_reuse = time_group(isa, [run_reuse], reps, 2, torch)
     t_recompute = time_group(isa, [run_recompute], reps, 2, torch)
     tokens = wl.B * wl.mtp_steps
-    del first, later, again, d, Qs
+    del run_reuse, again, d, Qs
     torch.cuda.empty_cache()
+    alg_bytes, t_ideal = mtp_roofline(wl)
     return {"workload": "C5: 16 sequences x 262144 context, 7 draft steps, 4 layers",
             "tokens_per_s": tokens / t_reuse, "ms_per_7_steps": t_reuse * 1e3,
             "ms_per_7_steps_recomputing_index": t_recompute * 1e3,
-            "reuse_speedup": t_recompute / t_reuse}
+            "reuse_speedup": t_recompute / t_reuse,
+            "algorithmic_bytes_per_7_steps": alg_bytes, "t_ideal_us": t_ideal * 1e6,
+            "frac_of_roofline": t_ideal / t_reuse}
 
 
 def run_fp8_kv(isa, torch, steps, warmup, n_inst):
@@ -506,9 +542,10 @@ def main():
                     help="skip the 1M-context ablation, the 7-step MTP, the FP8-cache, the "
                          "paged-cache and the multi-query measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group"],
+    ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group", "mtp"],
                     help="profiling mode: run one stage of --workload --reps times and print "
-                         "its average launch time instead of the benchmark line")
+                         "its average launch time instead of the benchmark line (mtp: the "
+                         "7-step run of C5)")
     ap.add_argument("--workload", default="C2_128K")
     ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
@@ -527,7 +564,8 @@ def main():
     isa.load_library()
     torch.cuda.set_device(0)
     if args.stage:
-        run_stage(isa, synth.WORKLOADS[args.workload], args.stage, args.reps, torch)
+        name = "C5" if args.stage == "mtp" else args.workload
+        run_stage(isa, synth.WORKLOADS[name], args.stage, args.reps, torch)
         return
 
     # reference: what a plain device copy reaches on this machine (context for the

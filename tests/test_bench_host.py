@@ -50,6 +50,17 @@ def test_algorithmic_counts_causal_prefill():
     assert abs(a["t_ideal_once_s"] - (a["t_ix_s"] + a["topk_bytes"] / bench.PEAK_HBM + 4 * t_at)) < 1e-12
 
 
+def test_mtp_seven_step_roofline():
+    wl = synth.WORKLOADS["C5"]
+    nbytes, t_ideal = bench.mtp_roofline(wl)
+    ix = 16 * 262144 * 128 + 16 * 64 * (128 + 4)       # keys once, qI and w of step 1
+    at = 16 * 2048 * 576 * 2 + 16 * 64 * (576 + 512) * 2  # one layer of one step
+    assert nbytes == ix + 16 * 2048 * 4 + 7 * 4 * at
+    # every stage of C5 is bound by HBM bytes at 8 TB/s
+    assert abs(t_ideal - nbytes / bench.PEAK_HBM) < 1e-12
+    assert abs(t_ideal * 1e6 - 207.06) < 0.01
+
+
 def test_traffic_is_null_for_another_kernel_source(tmp_path, monkeypatch):
     # a tree of its own: ROOT/profiles/<summary>, ROOT/<package>/csrc/attend.hip
     src = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "csrc", "attend.hip")
