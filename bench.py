@@ -371,10 +371,15 @@ def run_ablation(isa, torch, steps, warmup):
     # per-token FLOPs of the group, indexer (16384 per key) vs attention
     F_I = 2 * wl.H_I * wl.D_I * wl.kv_len
     F_A = a["at_flops_per_layer"] / wl.B
+    # ideal times: the shared group's, and the same with an indexer + top-k per layer
+    t_ideal_sh = a["t_ideal_s"]
+    t_ideal_pl = t_ideal_sh + (wl.n_layers - 1) * (a["t_ix_s"] + a["topk_bytes"] / PEAK_HBM)
     del shared, per_layer, d, abl
     torch.cuda.empty_cache()
     return {"workload": "C4: 2 sequences x 1 query, context 1048576, 4 layers",
             "shared_us_per_group": t_sh * 1e6, "per_layer_us_per_group": t_pl * 1e6,
+            "t_ideal_us_shared": t_ideal_sh * 1e6, "frac_of_roofline_shared": t_ideal_sh / t_sh,
+            "t_ideal_us_per_layer": t_ideal_pl * 1e6, "frac_of_roofline_per_layer": t_ideal_pl / t_pl,
             "measured_ratio": t_pl / t_sh,
             "algorithmic_bytes_ratio": bytes_pl / bytes_sh,
             "group_flops_ratio": (4 * F_I + 4 * F_A) / (F_I + 4 * F_A),
@@ -540,7 +545,7 @@ def main():
     ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 1M-context ablation, the 7-step MTP, the FP8-cache, the "
-                         "paged-cache and the multi-query measurements")
+                         "paged-cache, the 32K-context decode and the multi-query measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", choices=["indexer", "topk", "attend", "group", "mtp"],
                     help="profiling mode: run one stage of --workload --reps times and print "
@@ -648,6 +653,13 @@ def main():
         line["mtp"] = run_mtp(isa, torch, reps=5)
         line["fp8_kv"] = run_fp8_kv(isa, torch, steps=50, warmup=10, n_inst=args.instances)
         line["paged"] = run_paged(isa, torch, steps=50, warmup=10, n_inst=args.instances)
+        w32 = synth.WORKLOADS["C2"]
+        d32 = run_workload(isa, w32, 50, 10, args.instances, torch)
+        line["decode_32k"] = {
+            "workload": "C2 decode group: 8 sequences x 1 query over 32768 cached tokens, 4 layers",
+            "tokens_per_s": w32.tokens_per_group / d32["t_step"], "ms_per_step": d32["t_step"] * 1e3,
+            "stages_us": d32["stages_us"], "t_ideal_us": d32["alg"]["t_ideal_s"] * 1e6,
+            "frac_of_roofline": d32["alg"]["t_ideal_s"] / d32["t_step"]}
         wm = synth.WORKLOADS["C2_128K_MQ8"]
         mq = run_workload(isa, wm, 30, 5, 2, torch)
         am = mq["alg"]
