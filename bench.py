@@ -95,7 +95,16 @@ def host_info():
                     break
     except OSError:
         pass
-    return cpu, os.cpu_count()
+    ram_gib = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    ram_gib = round(int(line.split()[1]) / (1 << 20), 1)
+                    break
+    except OSError:
+        pass
+    return cpu, os.cpu_count(), ram_gib
 
 
 def make_instances(wl, n_inst, device):
@@ -609,7 +618,7 @@ def main():
                            "traffic": measured_traffic(name),
                            "share_of_step": per_group * t_launch / t}
     dominant = max(rooflines, key=lambda n: rooflines[n]["share_of_step"])
-    cpu_name, ncpu = host_info()
+    cpu_name, ncpu, ram_gib = host_info()
     line = {
         "metric": METRIC,
         "value": tokens / t,
@@ -647,7 +656,8 @@ def main():
                                 "sample": f"one whole C2_128K group ({o['tokens']} tokens) on one "
                                           f"host core of {cpu_name} ({ncpu} cpus)",
                                 "seconds": o["seconds"], "idx_exact": o["idx_exact"],
-                                "max_abs_err_vs_gpu": o["max_abs_err"]}
+                                "max_abs_err_vs_gpu": o["max_abs_err"],
+                                "host": {"cpu": cpu_name, "nproc": ncpu, "ram_GiB": ram_gib}}
     if not args.no_extra:
         line["ablation"] = run_ablation(isa, torch, steps=10, warmup=3)
         line["mtp"] = run_mtp(isa, torch, reps=5)
