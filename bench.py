@@ -254,6 +254,7 @@ def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
 TRAFFIC = {
     "indexer": ("indexer_scores_C2_128K_traffic.txt", "indexer.hip"),
     "attend": ("sparse_attend_C2_128K_traffic.txt", "attend.hip"),
+    "topk": ("topk_C2_128K_traffic.txt", "topk.hip"),
 }
 
 
@@ -335,7 +336,7 @@ def run_stage(isa, wl, stage, reps, torch):
     idx = torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
     ws = isa.Workspace()
-    if stage in ("indexer", "attend"):
+    if stage in ("indexer", "attend", "topk"):
         calibration_copy(torch)
     isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"], S=S)
     isa.isa_topk_select(S, d["kv_len"], wl.k, idx=idx, ws=ws)
