@@ -83,25 +83,54 @@ def test_scores_closed_form_constant_inputs(a, c):
                 assert S[b, t, s] == (want if s <= pos else -np.inf)
 
 
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
 def test_scores_hand_worked_example():
-    # Worked by hand from the definition (two heads of dim 2, four keys, the
-    # second query one position later than the first):
-    #  t=0 (sees s<=2): s0: 0.5*3 + 2*2 = 5.5; s1: 0.5*0 + 2*ReLU(-5) = 0;
-    #                   s2: 0.5*ReLU(-1) + 2*6 = 12; s3 hidden.
-    #  t=1 (sees s<=3): s0: 1*2 + 0.25*ReLU(-1) = 2; s1: 1*4 + 0.25*1 = 4.25;
-    #                   s2: 0; s3: 0.
-    qI = np.array([[[[1, 2], [-1, 3]], [[2, 0], [0, -1]]]], dtype=np.int8)
-    w = np.array([[[0.5, 2.0], [1.0, 0.25]]], dtype=np.float32)
-    kI = np.array([[[1, 1], [2, -1], [-3, 1], [0, 2]]], dtype=np.int8)
-    kv_len = np.array([4], dtype=np.int32)
+    # tests/golden/indexer_hand_worked.json: a two-head example worked by hand
+    # from the definition, with a tie at 0.0 between s2 and s3 for query 1.
+    # The per-head dot products the fixture lists are first checked against
+    # the inputs (plain integer arithmetic here), then the stated sums.
+    g = _golden("indexer_hand_worked.json")
+    qI = np.array(g["qI"], dtype=np.int8)
+    w = np.array(g["w"], dtype=np.float32)
+    kI = np.array(g["kI"], dtype=np.int8)
+    kv_len = np.array(g["kv_len"], dtype=np.int32)
+    for t, key in ((0, "t0"), (1, "t1")):
+        for s, dots in enumerate(g["dots"][key]):
+            assert dots == [int(np.dot(qI[0, t, h].astype(int), kI[0, s].astype(int)))
+                            for h in range(2)]
+    want = np.array([[[-np.inf if v == "-inf" else v for v in row] for row in b]
+                     for b in g["S"]], dtype=np.float32)
     S = oracle.indexer_scores(qI, w, kI, kv_len)
-    np.testing.assert_array_equal(S[0, 0], [5.5, 0.0, 12.0, -np.inf])
-    np.testing.assert_array_equal(S[0, 1], [2.0, 4.25, 0.0, 0.0])
-    np.testing.assert_array_equal(oracle.topk_select(S, kv_len, 2)[0], [[0, 2], [0, 1]])
-    # the tie at 0.0 between s2 and s3 goes to the lower position
-    np.testing.assert_array_equal(oracle.topk_select(S, kv_len, 3)[0], [[0, 1, 2], [0, 1, 2]])
-    np.testing.assert_array_equal(oracle.topk_select(S, kv_len, 5)[0],
-                                  [[0, 1, 2, -1, -1], [0, 1, 2, 3, -1]])
+    np.testing.assert_array_equal(S, want)
+    for k, idx in g["topk"].items():
+        np.testing.assert_array_equal(oracle.topk_select(S, kv_len, int(k)), idx)
+
+
+def test_scores_zero_weights_closed_form():
+    # w == 0 gives 0.0 (not -0.0) on every visible key whatever q and k are,
+    # so the set is the first min(k, pos+1) positions (all scores tie)
+    r = _rng(11)
+    B, Tq, L_cap, H_I, D_I, k = 2, 5, 40, 6, 16, 7
+    qI = r.integers(-128, 128, size=(B, Tq, H_I, D_I), dtype=np.int8)
+    kI = r.integers(-128, 128, size=(B, L_cap, D_I), dtype=np.int8)
+    w = np.zeros((B, Tq, H_I), dtype=np.float32)
+    kv_len = np.array([L_cap, 3], dtype=np.int32)
+    S = oracle.indexer_scores(qI, w, kI, kv_len)
+    idx = oracle.topk_select(S, kv_len, k)
+    for b in range(B):
+        for t in range(Tq):
+            pos = _positions(kv_len, L_cap, Tq, b, t)
+            vis = S[b, t, : max(pos + 1, 0)]
+            assert np.all(vis.view(np.uint32) == 0)
+            assert np.all(S[b, t, max(pos + 1, 0):] == -np.inf)
+            n = max(min(k, pos + 1), 0)
+            assert idx[b, t].tolist() == list(range(n)) + [-1] * (k - n)
 
 
 def test_power_of_two_weights_make_every_fp32_order_exact():
@@ -483,3 +512,100 @@ def test_group_shares_one_index_set_and_composes():
     np.testing.assert_array_equal(idx3, idx)
     for l in range(n):
         np.testing.assert_array_equal(outs3[l], outs[l])
+
+
+def _numpy_scores(qI, w, kI, kv_len):
+    """S by exact int64 dot products, ReLU, the weighted head sum in float64
+    rounded once to float32; -inf past each query's position (numpy only)."""
+    B, Tq, H_I, D_I = qI.shape
+    L_cap = kI.shape[1]
+    S = np.full((B, Tq, L_cap), -np.inf, dtype=np.float32)
+    for b in range(B):
+        dots = qI[b].astype(np.int64).reshape(Tq * H_I, D_I) @ kI[b].astype(np.int64).T
+        relu = np.maximum(dots, 0).reshape(Tq, H_I, L_cap).astype(np.float64)
+        tot = np.einsum("th,thl->tl", w[b].astype(np.float64), relu)
+        for t in range(Tq):
+            pos = _positions(kv_len, L_cap, Tq, b, t)
+            if pos >= 0:
+                S[b, t, : pos + 1] = tot[t, : pos + 1].astype(np.float32)
+    return S
+
+
+def _numpy_topk(S, kv_len, k):
+    """Ascending positions of the best min(k, pos+1) keys under (score desc,
+    position asc), -1 padded (numpy lexsort)."""
+    B, Tq, L_cap = S.shape
+    idx = np.full((B, Tq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            n = max(_positions(kv_len, L_cap, Tq, b, t) + 1, 0)
+            if n == 0:
+                continue
+            v = S[b, t, :n].astype(np.float64) + 0.0          # -0.0 ranks as +0.0
+            order = np.lexsort((np.arange(n), -v))
+            sel = np.sort(order[: min(k, n)])
+            idx[b, t, : len(sel)] = sel
+    return idx
+
+
+def _sdpa_selected(Q, C, idx, D_v, sm_scale):
+    """out [B,Tq,H,D_v] float64: torch float64 SDPA of each query over its
+    selected rows (V = the first D_v columns)."""
+    Qd = Q.double()
+    Cd = C.double()
+    B, Tq, H, D = Q.shape
+    out = np.zeros((B, Tq, H, D_v))
+    for b in range(B):
+        for t in range(Tq):
+            sel = [int(s) for s in idx[b, t] if s >= 0]
+            if not sel:
+                continue
+            rows = Cd[b, sel]                                   # [n, D]
+            q = Qd[b, t].unsqueeze(1)                           # [H, 1, D]
+            K = rows.unsqueeze(0).expand(H, -1, -1)
+            V = rows[:, :D_v].unsqueeze(0).expand(H, -1, -1)
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q, K, V, scale=float(np.float32(sm_scale)))
+            out[b, t] = o[:, 0].numpy()
+    return out
+
+
+def test_group_per_layer_indexer_distinct_inputs():
+    # The ablation without sharing ("GLM-5.2核心技术解析", the per-layer vs
+    # shared-indexer comparison table): layer l runs its own indexer + top-k
+    # from its own (qI, w, kI).  Expected values come from numpy integer
+    # scores, a lexsort top-k and float64 SDPA per layer, and also from the
+    # single-layer oracle calls composed by hand.  The per-layer inputs are
+    # drawn so that every layer's index set differs from every other layer's,
+    # so reading layer 0's indexer inputs for every layer cannot pass.
+    wl = synth.WORKLOADS["C1"].scaled(B=2, Tq=24, kv_len=90, L_cap=100, k=12,
+                                      ablation_seeds=(40, 41, 42, 43))
+    inp = synth.group_inputs(wl)
+    abl = synth.ablation_indexers(wl)
+    n = wl.n_layers
+    idx, outs, lses = oracle.group_forward([a["qI"] for a in abl], [a["w"] for a in abl],
+                                           [a["kI"] for a in abl], inp["kv_len"], inp["Q"],
+                                           inp["C"], wl.k, wl.D_v, wl.sm_scale,
+                                           per_layer_indexer=True)
+    kv = inp["kv_len"].numpy()
+    sets = []
+    for l in range(n):
+        a = abl[l]
+        S_np = _numpy_scores(a["qI"].numpy(), a["w"].numpy(), a["kI"].numpy(), kv)
+        idx_np = _numpy_topk(S_np, kv, wl.k)
+        sets.append(idx_np)
+        out_np = _sdpa_selected(inp["Q"][l], inp["C"][l], idx_np, wl.D_v, wl.sm_scale)
+        np.testing.assert_allclose(outs[l], out_np, rtol=1e-10, atol=1e-12)
+        # the same composed from the single-layer oracle calls
+        S_o = oracle.indexer_scores(a["qI"], a["w"], a["kI"], inp["kv_len"])
+        assert S_o.tobytes() == S_np.tobytes()
+        idx_o = oracle.topk_select(S_o, inp["kv_len"], wl.k)
+        np.testing.assert_array_equal(idx_o, idx_np)
+        o_o, l_o = oracle.sparse_mla_attend(inp["Q"][l], inp["C"][l], idx_o, wl.D_v, wl.sm_scale)
+        np.testing.assert_array_equal(outs[l], o_o)
+        np.testing.assert_array_equal(lses[l], l_o)
+    # idx ends holding the last layer's set
+    np.testing.assert_array_equal(idx, sets[-1])
+    for i in range(n):
+        for j in range(i + 1, n):
+            assert not np.array_equal(sets[i], sets[j]), (i, j)
