@@ -9,13 +9,15 @@ rows of the 4096-query causal prefill, the 1M-context decode group with the
 shared index set and with per-layer indexers (the ablation), the 7-step MTP
 run that reuses the step-1 index set, and the 128K decode group with FP8
 caches and with paged caches."""
+import os
+
 import pytest
 import torch
 
 import long_context_sparse_indexshare_amd as isa
 import oracle
 import synth
-from _parity import assert_attn_close, assert_idx_equal
+from _parity import assert_attn_close, assert_idx_equal, assert_scores_bitwise
 
 pytestmark = pytest.mark.gpu
 
@@ -43,12 +45,21 @@ def _run_group(wl, d, **kw):
     return idx, outs
 
 
+def _parallel(fn, items):
+    """fn over items in host threads (the oracle's C loops run outside the
+    interpreter lock); results in item order."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1, len(items)))) as ex:
+        return list(ex.map(fn, items))
+
+
 def _check_sequences(wl, d, idx, outs, seqs):
-    for b in seqs:
-        h = _slice_b(d, slice(b, b + 1))
-        _print_case("oracle", wl.name, "sequence", b)
-        idx_ref, outs_ref, _ = oracle.group_forward([h["qI"]], [h["w"]], [h["kI"]], h["kv_len"],
-                                                    h["Q"], h["C"], wl.k, wl.D_v, wl.sm_scale)
+    hs = {b: _slice_b(d, slice(b, b + 1)) for b in seqs}
+    _print_case("oracle", wl.name, "sequences", seqs)
+    refs = _parallel(lambda b: oracle.group_forward(
+        [hs[b]["qI"]], [hs[b]["w"]], [hs[b]["kI"]], hs[b]["kv_len"], hs[b]["Q"], hs[b]["C"], wl.k,
+        wl.D_v, wl.sm_scale), seqs)
+    for b, (idx_ref, outs_ref, _) in zip(seqs, refs):
         assert_idx_equal(idx[b:b + 1], idx_ref, f"{wl.name} seq {b}")
         for l in range(wl.n_layers):
             assert_attn_close(outs[l][b:b + 1], outs_ref[l], f"{wl.name} seq {b} layer {l}")
@@ -71,28 +82,64 @@ def test_multi_query_decode_group_full_size():
     _check_sequences(wl, d, idx, outs, [0, 7])
 
 
+# rows of the 4096-query chunk checked against the oracle: 0, every 65th
+# and 4095 (64 rows spread over the causal ramp)
+C3_ROWS = sorted(set(range(0, 4096, 65)) | {4095})
+
+
+def _oracle_rows(wl, d, rows, C):
+    """Oracle group results of single query rows of sequence 0 (each over the
+    keys it sees), computed in parallel host threads (the oracle's C loops run
+    outside the interpreter lock)."""
+    kI = d["kI"][0:1].cpu()
+    inputs = {t: (torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32),
+                  d["qI"][0:1, t:t + 1].cpu(), d["w"][0:1, t:t + 1].cpu(),
+                  [x[0:1, t:t + 1].cpu() for x in d["Q"]]) for t in rows}
+
+    def one(t):
+        kv, qI, w, Q = inputs[t]
+        return t, oracle.group_forward([qI], [w], [kI], kv, Q, C, wl.k, wl.D_v, wl.sm_scale)
+
+    return dict(_parallel(one, rows))
+
+
 def test_prefill_group_full_size_sampled_rows():
     wl = synth.WORKLOADS["C3"]
     d = synth.group_inputs(wl, device="cuda")
     idx, outs = _run_group(wl, d)
-    kI = d["kI"][0:1].cpu()
     C = [x[0:1].cpu() for x in d["C"]]
-    for t in (0, 1, 1000, 2047, 4094, 4095):
-        _print_case("oracle C3 row", t)
-        kv = torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32)   # what row t sees
-        idx_ref, outs_ref, _ = oracle.group_forward(
-            [d["qI"][0:1, t:t + 1].cpu()], [d["w"][0:1, t:t + 1].cpu()], [kI], kv,
-            [x[0:1, t:t + 1].cpu() for x in d["Q"]], C, wl.k, wl.D_v, wl.sm_scale)
+    assert len(C3_ROWS) == 64
+    _print_case("oracle C3 rows", C3_ROWS[:4], "...", len(C3_ROWS))
+    refs = _oracle_rows(wl, d, C3_ROWS, C)
+    for t in C3_ROWS:
+        idx_ref, outs_ref, _ = refs[t]
         assert_idx_equal(idx[0:1, t:t + 1], idx_ref, f"C3 row {t}")
         for l in range(wl.n_layers):
             assert_attn_close(outs[l][0:1, t:t + 1], outs_ref[l], f"C3 row {t} layer {l}")
+
+
+def test_prefill_scores_full_size_whole_rows_bitwise():
+    # the indexer alone at the full prefill size (the launch the group call
+    # makes): whole score rows, the -inf tail included, bit for bit
+    wl = synth.WORKLOADS["C3"]
+    d = synth.indexer_inputs(wl, device="cuda")
+    _print_case("gpu indexer C3 full size")
+    S = isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"])
+    torch.cuda.synchronize()
+    kI = d["kI"].cpu()
+    for t in (0, 2047, 4095):
+        _print_case("oracle C3 scores row", t)
+        # as a single query over the full-length buffer: same position, same row
+        kv = torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32)
+        ref = oracle.indexer_scores(d["qI"][:, t:t + 1].cpu(), d["w"][:, t:t + 1].cpu(), kI, kv)
+        assert_scores_bitwise(S[:, t:t + 1], ref, f"C3 scores row {t}")
 
 
 def test_1m_decode_shared_and_per_layer_indexer():
     wl = synth.WORKLOADS["C4"]
     d = synth.group_inputs(wl, device="cuda")
     idx, outs = _run_group(wl, d)
-    _check_sequences(wl, d, idx, outs, [1])
+    _check_sequences(wl, d, idx, outs, [0, 1])
     # ablation: every layer its own indexer inputs; layer l attends over its own set
     abl = synth.ablation_indexers(wl, device="cuda")
     _print_case("gpu group C4 per-layer indexers")
@@ -100,16 +147,21 @@ def test_1m_decode_shared_and_per_layer_indexer():
                                                [a["kI"] for a in abl], d["kv_len"], d["Q"], d["C"],
                                                wl.k, wl.D_v, wl.sm_scale, per_layer_indexer=True)
     torch.cuda.synchronize()
-    b = 0
-    h = _slice_b(d, slice(b, b + 1))
-    ha = [_slice_b(a, slice(b, b + 1)) for a in abl]
-    _print_case("oracle C4 per-layer indexers, sequence", b)
-    idx_ref, outs_ref, _ = oracle.group_forward([a["qI"] for a in ha], [a["w"] for a in ha],
-                                                [a["kI"] for a in ha], h["kv_len"], h["Q"], h["C"],
-                                                wl.k, wl.D_v, wl.sm_scale, per_layer_indexer=True)
-    assert_idx_equal(idx_pl[b:b + 1], idx_ref, "C4 per-layer: last layer's set")
-    for l in range(wl.n_layers):
-        assert_attn_close(outs_pl[l][b:b + 1], outs_ref[l], f"C4 per-layer layer {l}")
+    _print_case("oracle C4 per-layer indexers, sequences 0 and 1")
+
+    host_in = {b: (_slice_b(d, slice(b, b + 1)), [_slice_b(a, slice(b, b + 1)) for a in abl])
+               for b in (0, 1)}
+
+    def per_layer_ref(b):
+        h, ha = host_in[b]
+        return oracle.group_forward([a["qI"] for a in ha], [a["w"] for a in ha],
+                                    [a["kI"] for a in ha], h["kv_len"], h["Q"], h["C"], wl.k,
+                                    wl.D_v, wl.sm_scale, per_layer_indexer=True)
+
+    for b, (idx_ref, outs_ref, _) in zip((0, 1), _parallel(per_layer_ref, [0, 1])):
+        assert_idx_equal(idx_pl[b:b + 1], idx_ref, f"C4 per-layer seq {b}: last layer's set")
+        for l in range(wl.n_layers):
+            assert_attn_close(outs_pl[l][b:b + 1], outs_ref[l], f"C4 per-layer seq {b} layer {l}")
     # the shared set differs from the last per-layer set (independent indexers)
     assert not torch.equal(idx_pl, idx)
 

@@ -9,7 +9,7 @@ import torch
 import long_context_sparse_indexshare_amd as isa
 import oracle
 import synth
-from _parity import assert_attn_close, assert_idx_equal, dev, host
+from _parity import assert_attn_close, assert_idx_equal, assert_lse_close, dev, guarded, host
 
 pytestmark = pytest.mark.gpu
 
@@ -43,15 +43,23 @@ def test_group_matches_oracle(name):
                                                        inp["kv_len"], inp["Q"], inp["C"], wl.k,
                                                        wl.D_v, wl.sm_scale)
     d = _to_dev(inp)
-    lse = [torch.empty(wl.B, wl.Tq, wl.H, device="cuda") for _ in range(wl.n_layers)]
+    # every output between canary pads
+    idx_g, g_idx = guarded((wl.B, wl.Tq, wl.k), torch.int32)
+    outs_g = [guarded((wl.B, wl.Tq, wl.H, wl.D_v), torch.bfloat16) for _ in range(wl.n_layers)]
+    lse_g = [guarded((wl.B, wl.Tq, wl.H), torch.float32) for _ in range(wl.n_layers)]
+    lse = [t for t, _ in lse_g]
     idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
-                                         d["C"], wl.k, wl.D_v, wl.sm_scale, lse=lse)
+                                         d["C"], wl.k, wl.D_v, wl.sm_scale, idx=idx_g,
+                                         out=[t for t, _ in outs_g], lse=lse)
     torch.cuda.synchronize()
+    g_idx.check(f"{name} idx")
+    for l in range(wl.n_layers):
+        outs_g[l][1].check(f"{name} out {l}")
+        lse_g[l][1].check(f"{name} lse {l}")
     assert_idx_equal(idx, idx_ref, name)
     for l in range(wl.n_layers):
         assert_attn_close(outs[l], outs_ref[l], f"{name} layer {l}")
-        g = host(lse[l]).double().numpy()
-        assert np.nanmax(np.abs(np.where(np.isneginf(lses_ref[l]), 0, g - lses_ref[l]))) < 1e-3
+        assert_lse_close(lse[l], lses_ref[l], f"{name} layer {l}")
 
     # each layer equals a standalone sparse layer fed the same index set, bit for bit
     for l in range(wl.n_layers):
@@ -190,3 +198,30 @@ def test_per_layer_indexer_ablation():
     assert torch.equal(idx_a, idx_s)
     for l in range(n):
         assert torch.equal(outs_a[l], outs_s[l])
+
+
+def test_groups_on_two_streams_use_separate_workspaces():
+    # two groups launched at the same time on two streams with the default
+    # workspaces (one per stream), against the same groups run one after the
+    # other on the current stream: the bits must be equal
+    wls = [SMALL["C2-8K"], SMALL["decode-B3-Tq2"]]
+    ds = [_to_dev(synth.group_inputs(wl)) for wl in wls]
+
+    def run(i, stream=None):
+        wl, d = wls[i], ds[i]
+        return isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"], d["C"],
+                                     wl.k, wl.D_v, wl.sm_scale, stream=stream)
+
+    ref = [run(0), run(1)]
+    torch.cuda.synchronize()
+    ref = [(i.clone(), [o.clone() for o in outs]) for i, outs, _ in ref]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        got = [run(0, streams[0]), run(1, streams[1])]
+        torch.cuda.synchronize()
+        for (ri, ro), (gi, go, _) in zip(ref, got):
+            assert torch.equal(ri, gi), f"rep {rep}: idx differs"
+            for l in range(len(ro)):
+                assert torch.equal(ro[l], go[l]), f"rep {rep}: layer {l} differs"
