@@ -132,8 +132,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _stream_ptr(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return _stream_of(stream).cuda_stream
 
 
 def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
@@ -153,31 +152,57 @@ class Workspace:
 
     The library clears whatever counters it needs at the start of each call,
     so the buffer needs no initialisation and may be shared by different
-    entry points that run one after another on one stream.
+    entry points that run one after another on one stream.  Calls that may
+    overlap (different streams) need different workspaces; the default
+    workspace of the entry points is kept per device and stream.
     """
 
     def __init__(self, device=None):
         self.device = torch.device("cuda" if device is None else device)
         self.buf: Optional[torch.Tensor] = None
+        self._streams = {}        # streams the current buffer was used on
 
-    def get(self, nbytes: int) -> torch.Tensor:
+    def get(self, nbytes: int, stream=None) -> torch.Tensor:
         if nbytes <= 0:
             nbytes = 256
         if self.buf is None or self.buf.numel() < nbytes:
+            if self.buf is not None:
+                # work already queued on those streams may still use the old
+                # buffer: the allocator must not hand it out before it ends
+                for st in self._streams.values():
+                    self.buf.record_stream(st)
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._streams = {}
+        if stream is not None:
+            self._streams[stream.cuda_stream] = stream
         return self.buf
 
 
 _default_ws = {}
 
 
-def _workspace(ws: Optional[Workspace], device) -> Workspace:
+def _stream_of(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _workspace(ws: Optional[Workspace], device, stream=None) -> Workspace:
     if ws is not None:
         return ws
-    key = str(device)
+    key = (str(device), _stream_of(stream).cuda_stream)
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
+
+
+def _on_stream(stream, *tensors):
+    """Marks tensors allocated on the current stream as used by `stream` too,
+    so that the caching allocator does not reuse them while work queued there
+    may still touch them."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 # -------------------------------------------------------------- entry points ----
@@ -191,6 +216,7 @@ def isa_indexer_scores(qI, w, kI, kv_len, S=None, stream=None) -> torch.Tensor:
     if S is None:
         S = torch.empty((B, Tq, L_cap), dtype=torch.float32, device=qI.device)
     _dev(S, torch.float32, "S")
+    _on_stream(stream, S)
     _check(load_library().isa_indexer_scores(_ptr(qI), _ptr(w), _ptr(kI), _ptr(kv_len), B, Tq, H_I,
                                              D_I, L_cap, _ptr(S), _stream_ptr(stream)))
     return S
@@ -209,7 +235,8 @@ def isa_topk_select(S, kv_len, k: int, idx=None, ws: Optional[Workspace] = None,
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=S.device)
     _dev(idx, torch.int32, "idx")
     nbytes = isa_topk_workspace_bytes(B, Tq, L_cap, k)
-    buf = _workspace(ws, S.device).get(nbytes)
+    buf = _workspace(ws, S.device, stream).get(nbytes, _stream_of(stream))
+    _on_stream(stream, idx, buf)
     _check(load_library().isa_topk_select(_ptr(S), _ptr(kv_len), B, Tq, L_cap, int(k), _ptr(idx),
                                           _ptr(buf), buf.numel(), _stream_ptr(stream)))
     return idx
@@ -235,7 +262,8 @@ def isa_sparse_mla_attend(Q, C, idx, D_v: int, sm_scale: float, out=None, lse=No
     if lse is not None:
         _dev(lse, torch.float32, "lse")
     nbytes = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k)
-    buf = _workspace(ws, Q.device).get(nbytes)
+    buf = _workspace(ws, Q.device, stream).get(nbytes, _stream_of(stream))
+    _on_stream(stream, out, lse, buf)
     _check(load_library().isa_sparse_mla_attend(
         _ptr(Q), _ptr(C), _ptr(idx), B, Tq, H, D, int(D_v), L_cap, k, float(sm_scale), _ptr(out),
         _ptr(lse), _ptr(buf), buf.numel(), _stream_ptr(stream)))
@@ -266,7 +294,8 @@ def isa_sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, sm_scale: float, out=None, lse
     if lse is not None:
         _dev(lse, torch.float32, "lse")
     nbytes = isa_attend_fp8_workspace_bytes(B, Tq, H, D_c, D_r, k)
-    buf = _workspace(ws, Q.device).get(nbytes)
+    buf = _workspace(ws, Q.device, stream).get(nbytes, _stream_of(stream))
+    _on_stream(stream, out, lse, buf)
     _check(load_library().isa_sparse_mla_attend_fp8(
         _ptr(Q), _ptr(C8), _ptr(Ce), _ptr(Cr), _ptr(idx), B, Tq, H, D_c, D_r, L_cap, k,
         float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(), _stream_ptr(stream)))
@@ -285,6 +314,7 @@ def isa_indexer_scores_paged(qI, w, kI_pages, block_table, kv_len, S=None,
     if S is None:
         S = torch.empty((B, Tq, max_blocks * bs), dtype=torch.float32, device=qI.device)
     _dev(S, torch.float32, "S")
+    _on_stream(stream, S)
     _check(load_library().isa_indexer_scores_paged(
         _ptr(qI), _ptr(w), _ptr(kI_pages), _ptr(block_table), max_blocks, bs, n_pages,
         _ptr(kv_len), B, Tq, H_I, D_I, _ptr(S), _stream_ptr(stream)))
@@ -310,7 +340,8 @@ def isa_sparse_mla_attend_paged(Q, C_pages, block_table, idx, D_v: int, sm_scale
     if lse is not None:
         _dev(lse, torch.float32, "lse")
     nbytes = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k)
-    buf = _workspace(ws, Q.device).get(nbytes)
+    buf = _workspace(ws, Q.device, stream).get(nbytes, _stream_of(stream))
+    _on_stream(stream, out, lse, buf)
     _check(load_library().isa_sparse_mla_attend_paged(
         _ptr(Q), _ptr(C_pages), _ptr(block_table), max_blocks, bs, n_pages, _ptr(idx), B, Tq, H,
         D, int(D_v), k, float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(),
@@ -328,6 +359,7 @@ def isa_index_histogram(idx, L_cap: int, counts=None, stream=None) -> torch.Tens
     _dev(counts, torch.int32, "counts")
     if tuple(counts.shape) != (B, L_cap):
         raise ValueError(f"counts must be [{B}, {L_cap}]")
+    _on_stream(stream, counts)
     _check(load_library().isa_index_histogram(_ptr(idx), B, Tq, k, int(L_cap), _ptr(counts),
                                               _stream_ptr(stream)))
     return counts
@@ -418,12 +450,17 @@ class GroupCall:
             a.Ce = ctypes.cast(self._arrays[8], _P)
             a.Cr = ctypes.cast(self._arrays[9], _P)
         self.args = a
-        nbytes = int(load_library().isa_group_workspace_bytes(ctypes.byref(a)))
-        self.ws_buf = _workspace(ws, dev).get(nbytes)
-        a.ws = _ptr(self.ws_buf)
-        a.ws_bytes = self.ws_buf.numel()
+        self._nbytes = int(load_library().isa_group_workspace_bytes(ctypes.byref(a)))
+        self._ws, self._dev = ws, dev
 
     def __call__(self, stream=None):
+        # the workspace is taken at call time (the given one, or the default
+        # one of this device and stream), so calls on different streams never
+        # share scratch memory and a workspace grown by another call is seen
+        buf = _workspace(self._ws, self._dev, stream).get(self._nbytes, _stream_of(stream))
+        self.args.ws = _ptr(buf)
+        self.args.ws_bytes = buf.numel()
+        _on_stream(stream, buf, self.idx, *self.out, *(self.lse or []))
         _check(load_library().isa_group_forward(ctypes.byref(self.args), _stream_ptr(stream)))
         return self.idx, self.out, self.lse
 
