@@ -59,6 +59,8 @@ struct TopkLayout {
     uint32_t cap;                     // entries per row in the entry buffer
 };
 TopkLayout topk_layout(int rows, int L_cap);
+// true when the one-workgroup-per-row select kernel serves (rows, L_cap)
+bool topk_uses_select(int rows, int L_cap);
 
 // Attention split geometry; the workspace of one call holds the partials.
 struct AttendPlan {

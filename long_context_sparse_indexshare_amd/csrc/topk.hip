@@ -837,6 +837,10 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_kernel(
 
 }  // namespace
 
+bool topk_uses_select(int rows, int L_cap) {
+    return L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS;
+}
+
 TopkLayout topk_layout(int rows, int L_cap) {
     TopkLayout L;
     L.rows = rows;
@@ -846,6 +850,10 @@ TopkLayout topk_layout(int rows, int L_cap) {
     if (cap < lo) cap = lo;
     cap = (cap + 63u) & ~63u;
     L.cap = cap;
+    // the one-workgroup-per-row select kernel needs only the first-digit
+    // histograms; the classify/finish pair also needs the second-digit
+    // histograms, the entry counters and its scratch
+    const bool sel = topk_uses_select(rows, L_cap);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -854,13 +862,13 @@ TopkLayout topk_layout(int rows, int L_cap) {
     };
     // counters zeroed at the start of every call come first
     L.hist = take((size_t)rows * TOPK_HIST_BINS * 4);
-    L.hist2 = take((size_t)rows * HIST2_BINS * 4);
-    L.alloc = take((size_t)rows * 4);
+    L.hist2 = take(sel ? 0 : (size_t)rows * HIST2_BINS * 4);
+    L.alloc = take(sel ? 0 : (size_t)rows * 4);
     L.zero_bytes = off;
     // scratch overwritten by every call
-    L.row_state = take((size_t)rows * sizeof(RowState));
-    L.runs = take((size_t)rows * L.nchunks * 8);
-    L.ent = take((size_t)rows * cap * 8);
+    L.row_state = take(sel ? 0 : (size_t)rows * sizeof(RowState));
+    L.runs = take(sel ? 0 : (size_t)rows * L.nchunks * 8);
+    L.ent = take(sel ? 0 : (size_t)rows * cap * 8);
     L.total = off;
     return L;
 }
@@ -899,7 +907,7 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
     else
         hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_FEW>, dim3((L_cap + CH_FEW - 1) / CH_FEW, rows),
                            dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
-    if (L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS) {
+    if (topk_uses_select(rows, L_cap)) {
         hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(SEL_THREADS), 0, stream, S,
                            kv_len, Tq, L_cap, k, hist, idx);
         return hipGetLastError();
