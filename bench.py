@@ -5,9 +5,9 @@ A step is one IndexShare layer group: lightning indexer + top-k once, then
 sparse latent attention in each of the 4 layers that share the index set.
 The headline workload is the 128K-context decode group (batch 8, one query
 token per sequence, 131072 cached tokens, 64x128 int8 indexer, top-2048,
-4 layers of 64-head 576-wide bf16 latent attention).  With --prefill the
-4096-token prefill chunk over a 131072-token cache is measured as well and
-reported under "prefill".
+4 layers of 64-head 576-wide bf16 latent attention).  The 4096-token
+prefill chunk over a 131072-token cache (MFMA-bound) is measured as well and
+reported under "prefill" (--no-prefill skips it).
 
 Inputs are synthetic (synth/), generated on the GPU; decode steps rotate over
 several independent input instances so the 256 MiB MALL cannot hold the
@@ -212,6 +212,19 @@ def stage_times(isa, insts, wl, torch, reps=20):
     return t_ix, t_tk, t_at, t_h
 
 
+def pin_one_core():
+    """Pins the calling thread (the one that runs the single-threaded oracle)
+    to one host core, as taskset -c would; returns (core, previous mask)."""
+    prev = os.sched_getaffinity(0)
+    core = max(prev)
+    os.sched_setaffinity(0, {core})
+    return core, prev
+
+
+def unpin(core):
+    os.sched_setaffinity(0, core[1])
+
+
 def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
     """Times the CPU oracle on one group over a bounded sample of the workload."""
     import numpy as np
@@ -232,6 +245,12 @@ def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
         tokens = len(q_rows)
     sub["kI"] = inst["kI"][bs].cpu()
     sub["C"] = [x[bs].cpu() for x in inst["C"]]
+    if q_rows is not None:
+        # host copies of the sampled rows' inputs, made before the timed region
+        rows_in = [(torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32),
+                    inst["qI"][0:1, t:t + 1].cpu(), inst["w"][0:1, t:t + 1].cpu(),
+                    [x[0:1, t:t + 1].cpu() for x in inst["Q"]]) for t in q_rows]
+    core = pin_one_core()
     t0 = time.perf_counter()
     if q_rows is None:
         idx, outs, _ = oracle.group_forward([sub["qI"]], [sub["w"]], [sub["kI"]], sub["kv_len"],
@@ -239,15 +258,12 @@ def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
         results = (idx, outs)
     else:
         results = []
-        for t in q_rows:
-            kv = torch.tensor([wl.kv_len - wl.Tq + t + 1], dtype=torch.int32)
-            qI = inst["qI"][0:1, t:t + 1].cpu()
-            w = inst["w"][0:1, t:t + 1].cpu()
-            Q = [x[0:1, t:t + 1].cpu() for x in inst["Q"]]
+        for kv, qI, w, Q in rows_in:
             results.append(oracle.group_forward([qI], [w], [sub["kI"]], kv, Q, sub["C"], wl.k,
                                                 wl.D_v, wl.sm_scale))
     dt = time.perf_counter() - t0
-    return tokens, dt, results
+    unpin(core)
+    return tokens, dt, results, core[0]
 
 
 # committed counter summaries: stage -> (summary file, kernel source it was taken on)
@@ -497,6 +513,121 @@ def run_paged(isa, torch, steps, warmup, n_inst, block_size=64):
             "frac_of_roofline": a["t_ideal_s"] / t}
 
 
+def run_prefill(isa, torch, args, cpu_name, ncpu):
+    """C3: 4096 queries appended to a 131072-token cache (causal), 64x128 int8
+    indexer, top-2048, 4 layers.  The bound is MFMA: T_ideal counts the
+    indexer's int8 ops at the int8 peak and the attention's bf16 FLOP at the
+    bf16 peak, each cache row read once (a layer's 156 MB cache is gathered
+    about 62 times over by the 4096 queries and stays in the 256 MB MALL);
+    the same with every query's gathered rows charged to HBM is reported
+    too."""
+    import synth
+    wp = synth.WORKLOADS["C3"]
+    # stratified sample of the chunk's rows for the oracle: first, last and
+    # evenly spaced ones (bounded to keep the CPU leg near 20 s)
+    q_rows = None if args.no_cpu_baseline else [0, 4095] + list(range(455, 4095, 455))
+    pre = run_workload(isa, wp, max(2, min(args.steps, 5)), 2, 1, torch, q_rows=q_rows)
+    a = pre["alg"]
+    tp = pre["t_step"]
+    st = pre["stages_us"]
+    t_ix, t_tk, t_at = st["indexer"] * 1e-6, st["topk"] * 1e-6, st["attend_per_layer"] * 1e-6
+    # per-stage MFMA fractions against the dense peaks
+    ix_frac = a["ix_ops"] / t_ix / PEAK_INT8
+    at_frac = a["at_flops_per_layer"] / t_at / PEAK_BF16
+    t_ideal_mfma = a["ix_ops"] / PEAK_INT8 + wp.n_layers * a["at_flops_per_layer"] / PEAK_BF16
+    res = {
+        "workload": "C3 prefill group: 4096 queries over a 135168-token cache (causal), "
+                    "64x128 int8 indexer, top-2048, 4 layers x 64 heads x 576 bf16 latent",
+        "tokens_per_s": wp.tokens_per_group / tp, "ms_per_step": tp * 1e3,
+        # primary: MFMA-bound, each cache row counted once
+        "t_ideal_ms": a["t_ideal_once_s"] * 1e3, "frac_of_roofline": a["t_ideal_once_s"] / tp,
+        "t_ideal_mfma_only_ms": t_ideal_mfma * 1e3,
+        "roofline": {"bound": "mfma", "achieved": (a["ix_ops"] + wp.n_layers *
+                                                   a["at_flops_per_layer"]) / tp / 1e12,
+                     "unit": "TOP/s (int8 + bf16)",
+                     "note": "frac = T_ideal / T_measured, T_ideal = int8 ops / 5.0 POP/s + "
+                             "top-k index bytes / 8 TB/s + 4 x bf16 FLOP / 2.5 PFLOP/s"},
+        # secondary: every query's gathered rows charged to HBM
+        "t_ideal_ms_rows_per_query": a["t_ideal_s"] * 1e3,
+        "frac_of_roofline_rows_per_query": a["t_ideal_s"] / tp,
+        "stages_us": st,
+        "stage_rooflines": {
+            "indexer": {"bound": "mfma", "dtype": "int8", "launch_us": st["indexer"],
+                        "ops": a["ix_ops"], "achieved_TOPS": a["ix_ops"] / t_ix / 1e12,
+                        "peak_TOPS": PEAK_INT8 / 1e12, "frac": ix_frac},
+            "topk": {"bound": "hbm", "launch_us": st["topk"],
+                     "algorithmic_bytes": a["topk_read_bytes"],
+                     "achieved_GBps": a["topk_read_bytes"] / t_tk / 1e9,
+                     "frac": a["topk_read_bytes"] / t_tk / PEAK_HBM},
+            "attend": {"bound": "mfma", "dtype": "bf16", "launch_us": st["attend_per_layer"],
+                       "flops": a["at_flops_per_layer"],
+                       "achieved_TFLOPS": a["at_flops_per_layer"] / t_at / 1e12,
+                       "peak_TFLOPS": PEAK_BF16 / 1e12, "frac": at_frac,
+                       "gathered_bytes": a["at_bytes_per_layer"],
+                       "gathered_GBps": a["at_bytes_per_layer"] / t_at / 1e9},
+        },
+        "index_histogram_us": pre["index_histogram_us"],
+    }
+    if "oracle" in pre:
+        o = pre["oracle"]
+        res["cpu_baseline"] = {
+            "value": o["tokens"] / o["seconds"], "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(q_rows)} query rows of the chunk (0, 4095 and every 455th), each "
+                      f"over the keys it sees, on one host core (core {o['core']}, pinned) of "
+                      f"{cpu_name} ({ncpu} cpus)",
+            "seconds": o["seconds"], "idx_exact": o["idx_exact"],
+            "max_abs_err_vs_gpu": o["max_abs_err"]}
+    return res
+
+
+def measured_peaks(torch):
+    """Attainable rates on this GPU from the probe kernels of
+    long_context_sparse_indexshare_amd/peaks/peaks.hip (dense MFMA loops,
+    an LDS read loop, a streaming HBM read), each timed with HIP events on
+    the launch stream after one warm-up launch.  Context for the roofline
+    fractions, which use the published peaks."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "peaks", "libisa_peaks.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    for name in ("peaks_mfma_bf16", "peaks_mfma_fp8", "peaks_mfma_i8", "peaks_lds_read"):
+        getattr(lib, name).argtypes = [P, I, I, P]
+        getattr(lib, name).restype = I
+    lib.peaks_hbm_read.argtypes = [P, Z, P, I, P]
+    lib.peaks_hbm_read.restype = I
+    grid = 1024
+    sink = torch.empty(grid * 1024, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        return time_per_launch(fn, 3, torch)
+
+    out = {}
+    # (probe, iterations, work per (wave, iteration, chain) MFMA)
+    for name, iters, per in (("bf16", 2000, 32768), ("fp8", 1000, 131072), ("int8", 2000, 65536)):
+        fn = getattr(lib, f"peaks_mfma_{name if name != 'int8' else 'i8'}")
+        t = timed(lambda: fn(sink.data_ptr(), grid, iters, stream))
+        out[f"mfma_{name}_TFLOPS"] = grid * 8 * iters * 4 * per / t / 1e12
+    t = timed(lambda: lib.peaks_lds_read(sink.data_ptr(), grid, 2000, stream))
+    lds = grid * 1024 * 2000 * 8 * 16 / t
+    out["lds_read_TBps"] = lds / 1e12
+    out["lds_read_bytes_per_clk_per_cu"] = lds / 256 / 2.4e9
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    t = timed(lambda: lib.peaks_hbm_read(buf.data_ptr(), buf.numel() // 16, sink.data_ptr(),
+                                         256 * 8, stream))
+    out["hbm_read_GBps"] = buf.numel() / t / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    out["note"] = ("probe kernels in long_context_sparse_indexshare_amd/peaks/peaks.hip; "
+                   "2.4 GHz and 256 CUs assumed for the per-CU LDS figure")
+    return out
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -529,8 +660,8 @@ def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_row
         gidx = calls[0].idx.cpu().numpy()
         gout = [o.double().cpu().numpy() for o in calls[0].out]
         log(f"{wl.name}: timing the CPU oracle on a sample")
-        tokens, dt, results = oracle_baseline(wl, insts[0], baseline_seq or 1, torch, q_rows)
-        log(f"{wl.name}: oracle {dt:.1f} s for {tokens} token(s)")
+        tokens, dt, results, core = oracle_baseline(wl, insts[0], baseline_seq or 1, torch, q_rows)
+        log(f"{wl.name}: oracle {dt:.1f} s for {tokens} token(s) on core {core}")
         if q_rows is None:
             idx, outs = results
             exact = bool(np.array_equal(gidx[: baseline_seq], idx))
@@ -540,7 +671,7 @@ def run_workload(isa, wl, steps, warmup, n_inst, torch, baseline_seq=None, q_row
             errs = [max(float(np.abs(gout[l][0, t] - r[1][l][0, 0]).max())
                         for t, r in zip(q_rows, results)) for l in range(wl.n_layers)]
         res["oracle"] = {"tokens": tokens, "seconds": dt, "idx_exact": exact,
-                         "max_abs_err": max(errs)}
+                         "max_abs_err": max(errs), "core": core}
     del calls, insts
     torch.cuda.empty_cache()
     return res
@@ -552,7 +683,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--instances", type=int, default=4)
-    ap.add_argument("--prefill", action="store_true", help="also measure the 4K x 128K prefill")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 4K x 128K prefill group (measured by default)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 1M-context ablation, the 7-step MTP, the FP8-cache, the "
                          "paged-cache, the 32K-context decode and the multi-query measurements")
@@ -592,6 +724,8 @@ def main():
     t_copy = time_per_launch(lambda: dst.copy_(src), 10, torch)
     copy_GBps = 2 * src.numel() / t_copy / 1e9
     del src, dst
+
+    peaks = measured_peaks(torch)
 
     wl = synth.WORKLOADS["C2_128K"]
     dec = run_workload(isa, wl, args.steps, args.warmup, args.instances, torch,
@@ -649,13 +783,15 @@ def main():
                       "note": "the same groups captured once and replayed; value uses eager "
                               "launches"},
         "copy_GBps_measured": copy_GBps,
+        "measured_peaks": peaks,
     }
     if "oracle" in dec:
         o = dec["oracle"]
         line["cpu_baseline"] = {"value": o["tokens"] / o["seconds"], "unit": "tokens/s",
                                 "cores": 1, "kind": "oracle",
                                 "sample": f"one whole C2_128K group ({o['tokens']} tokens) on one "
-                                          f"host core of {cpu_name} ({ncpu} cpus)",
+                                          f"host core (core {o['core']}, pinned) of {cpu_name} "
+                                          f"({ncpu} cpus)",
                                 "seconds": o["seconds"], "idx_exact": o["idx_exact"],
                                 "max_abs_err_vs_gpu": o["max_abs_err"],
                                 "host": {"cpu": cpu_name, "nproc": ncpu, "ram_GiB": ram_gib}}
@@ -681,34 +817,8 @@ def main():
             "stages_us": mq["stages_us"],
             "t_ideal_us": am["t_ideal_s"] * 1e6, "frac_of_roofline": am["t_ideal_s"] / mq["t_step"],
             "indexer_int8_TOPS": am["ix_ops"] / (mq["stages_us"]["indexer"] * 1e-6) / 1e12}
-    if args.prefill:
-        wp = synth.WORKLOADS["C3"]
-        pre = run_workload(isa, wp, max(2, min(args.steps, 5)), 2, 1, torch,
-                           q_rows=None if args.no_cpu_baseline else [0, 1, 2047, 4095])
-        ap_ = pre["alg"]
-        tp = pre["t_step"]
-        line["prefill"] = {
-            "workload": "C3 prefill group: 4096 queries over a 135168-token cache (causal), "
-                        "64x128 int8 indexer, top-2048, 4 layers",
-            "tokens_per_s": wp.tokens_per_group / tp, "ms_per_step": tp * 1e3,
-            "t_ideal_ms": ap_["t_ideal_s"] * 1e3, "frac_of_roofline": ap_["t_ideal_s"] / tp,
-            # a cache row gathered by several queries counted once (the 156 MB
-            # cache of a layer is gathered about 62 times over): attention
-            # then bound by its MFMA work
-            "t_ideal_ms_rows_once": ap_["t_ideal_once_s"] * 1e3,
-            "frac_of_roofline_rows_once": ap_["t_ideal_once_s"] / tp,
-            "stages_us": pre["stages_us"],
-            "index_histogram_us": pre["index_histogram_us"],
-            "indexer_int8_TOPS": ap_["ix_ops"] / (pre["stages_us"]["indexer"] * 1e-6) / 1e12,
-            "attend_bf16_TFLOPS": ap_["at_flops_per_layer"] /
-                                  (pre["stages_us"]["attend_per_layer"] * 1e-6) / 1e12,
-        }
-        if "oracle" in pre:
-            o = pre["oracle"]
-            line["prefill"]["cpu_baseline"] = {
-                "value": o["tokens"] / o["seconds"], "unit": "tokens/s", "cores": 1,
-                "kind": "oracle", "sample": f"query rows 0, 1, 2047, 4095 of the chunk",
-                "idx_exact": o["idx_exact"], "max_abs_err_vs_gpu": o["max_abs_err"]}
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(isa, torch, args, cpu_name, ncpu)
     print(json.dumps(line), flush=True)
 
 
