@@ -179,36 +179,57 @@ def time_per_launch(fn, n, torch):
     return a.elapsed_time(b) / 1e3 / n
 
 
+def _raw(lib_fn, *args):
+    """A prepared C-ABI call: the arguments are marshalled once, so the timed
+    launches cost the host a few microseconds each and the host stays ahead of
+    the GPU even for kernels of a few microseconds (the binding's per-call
+    checks would otherwise be timed along with short launches)."""
+    def call():
+        st = lib_fn(*args)
+        if st != 0:
+            raise RuntimeError(f"isa call failed with status {st}")
+    return call
+
+
 def stage_times(isa, insts, wl, torch, reps=20):
     """Per-stage device time of one group, each stage timed alone, launches
     taking the input instances in turn (as the group steps do)."""
     S = [torch.empty((wl.B, wl.Tq, wl.L_cap), dtype=torch.float32, device="cuda")
          for _ in insts]
     idx = [torch.empty((wl.B, wl.Tq, wl.k), dtype=torch.int32, device="cuda") for _ in insts]
-    ws = isa.Workspace()
+    lib = isa.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    B, Tq, L_cap, k = wl.B, wl.Tq, wl.L_cap, wl.k
+    tk_ws = torch.empty(max(isa.isa_topk_workspace_bytes(B, Tq, L_cap, k), 256), dtype=torch.uint8,
+                        device="cuda")
+    at_ws = torch.empty(max(isa.isa_attend_workspace_bytes(B, Tq, wl.H, wl.D, wl.D_v, k), 256),
+                        dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
 
     def ix(i):
         d = insts[i]
-        return lambda: isa.isa_indexer_scores(d["qI"], d["w"], d["kI"], d["kv_len"], S=S[i])
+        return _raw(lib.isa_indexer_scores, d["qI"].data_ptr(), d["w"].data_ptr(),
+                    d["kI"].data_ptr(), d["kv_len"].data_ptr(), B, Tq, wl.H_I, wl.D_I, L_cap,
+                    S[i].data_ptr(), stream)
 
     def tk(i):
-        return lambda: isa.isa_topk_select(S[i], insts[i]["kv_len"], wl.k, idx=idx[i], ws=ws)
-
-    out = torch.empty((wl.B, wl.Tq, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+        return _raw(lib.isa_topk_select, S[i].data_ptr(), insts[i]["kv_len"].data_ptr(), B, Tq,
+                    L_cap, k, idx[i].data_ptr(), tk_ws.data_ptr(), tk_ws.numel(), stream)
 
     def at(i):
         d = insts[i]
-        return lambda: isa.isa_sparse_mla_attend(d["Q"][0], d["C"][0], idx[i], wl.D_v,
-                                                 wl.sm_scale, out=out, ws=ws)
+        return _raw(lib.isa_sparse_mla_attend, d["Q"][0].data_ptr(), d["C"][0].data_ptr(),
+                    idx[i].data_ptr(), B, Tq, wl.H, wl.D, wl.D_v, L_cap, k, float(wl.sm_scale),
+                    out.data_ptr(), None, at_ws.data_ptr(), at_ws.numel(), stream)
 
     n = range(len(insts))
     t_ix = time_per_launch([ix(i) for i in n], reps, torch)    # also fills S
     t_tk = time_per_launch([tk(i) for i in n], reps, torch)    # also fills idx
     t_at = time_per_launch([at(i) for i in n], reps, torch)
     # access counts of the index set (the HiSparse input; not part of the step)
-    counts = torch.zeros((wl.B, wl.L_cap), dtype=torch.int32, device="cuda")
-    t_h = time_per_launch(lambda: isa.isa_index_histogram(idx[0], wl.L_cap, counts=counts), reps,
-                          torch)
+    counts = torch.zeros((B, L_cap), dtype=torch.int32, device="cuda")
+    t_h = time_per_launch(_raw(lib.isa_index_histogram, idx[0].data_ptr(), B, Tq, k, L_cap,
+                               counts.data_ptr(), stream), reps, torch)
     return t_ix, t_tk, t_at, t_h
 
 

@@ -185,19 +185,20 @@ def _stream_of(stream):
     return torch.cuda.current_stream() if stream is None else stream
 
 
-def _workspace(ws: Optional[Workspace], device, stream=None) -> Workspace:
+def _workspace(ws: Optional[Workspace], device, st) -> Workspace:
+    """ws, or the default workspace of (device, st); st is a resolved stream."""
     if ws is not None:
         return ws
-    key = (str(device), _stream_of(stream).cuda_stream)
+    key = (str(device), st.cuda_stream)
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
 
 
 def _on_stream(stream, *tensors):
-    """Marks tensors allocated on the current stream as used by `stream` too,
-    so that the caching allocator does not reuse them while work queued there
-    may still touch them."""
+    """Marks tensors allocated on the current stream as used by `stream` too
+    (an explicitly given stream), so that the caching allocator does not
+    reuse them while work queued there may still touch them."""
     if stream is None or stream == torch.cuda.current_stream():
         return
     for t in tensors:
@@ -235,10 +236,11 @@ def isa_topk_select(S, kv_len, k: int, idx=None, ws: Optional[Workspace] = None,
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=S.device)
     _dev(idx, torch.int32, "idx")
     nbytes = isa_topk_workspace_bytes(B, Tq, L_cap, k)
-    buf = _workspace(ws, S.device, stream).get(nbytes, _stream_of(stream))
+    st = _stream_of(stream)
+    buf = _workspace(ws, S.device, st).get(nbytes, st)
     _on_stream(stream, idx, buf)
     _check(load_library().isa_topk_select(_ptr(S), _ptr(kv_len), B, Tq, L_cap, int(k), _ptr(idx),
-                                          _ptr(buf), buf.numel(), _stream_ptr(stream)))
+                                          _ptr(buf), buf.numel(), st.cuda_stream))
     return idx
 
 
@@ -262,11 +264,12 @@ def isa_sparse_mla_attend(Q, C, idx, D_v: int, sm_scale: float, out=None, lse=No
     if lse is not None:
         _dev(lse, torch.float32, "lse")
     nbytes = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k)
-    buf = _workspace(ws, Q.device, stream).get(nbytes, _stream_of(stream))
+    st = _stream_of(stream)
+    buf = _workspace(ws, Q.device, st).get(nbytes, st)
     _on_stream(stream, out, lse, buf)
     _check(load_library().isa_sparse_mla_attend(
         _ptr(Q), _ptr(C), _ptr(idx), B, Tq, H, D, int(D_v), L_cap, k, float(sm_scale), _ptr(out),
-        _ptr(lse), _ptr(buf), buf.numel(), _stream_ptr(stream)))
+        _ptr(lse), _ptr(buf), buf.numel(), st.cuda_stream))
     return out, lse
 
 
@@ -294,11 +297,12 @@ def isa_sparse_mla_attend_fp8(Q, C8, Ce, Cr, idx, sm_scale: float, out=None, lse
     if lse is not None:
         _dev(lse, torch.float32, "lse")
     nbytes = isa_attend_fp8_workspace_bytes(B, Tq, H, D_c, D_r, k)
-    buf = _workspace(ws, Q.device, stream).get(nbytes, _stream_of(stream))
+    st = _stream_of(stream)
+    buf = _workspace(ws, Q.device, st).get(nbytes, st)
     _on_stream(stream, out, lse, buf)
     _check(load_library().isa_sparse_mla_attend_fp8(
         _ptr(Q), _ptr(C8), _ptr(Ce), _ptr(Cr), _ptr(idx), B, Tq, H, D_c, D_r, L_cap, k,
-        float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(), _stream_ptr(stream)))
+        float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(), st.cuda_stream))
     return out, lse
 
 
@@ -340,12 +344,13 @@ def isa_sparse_mla_attend_paged(Q, C_pages, block_table, idx, D_v: int, sm_scale
     if lse is not None:
         _dev(lse, torch.float32, "lse")
     nbytes = isa_attend_workspace_bytes(B, Tq, H, D, D_v, k)
-    buf = _workspace(ws, Q.device, stream).get(nbytes, _stream_of(stream))
+    st = _stream_of(stream)
+    buf = _workspace(ws, Q.device, st).get(nbytes, st)
     _on_stream(stream, out, lse, buf)
     _check(load_library().isa_sparse_mla_attend_paged(
         _ptr(Q), _ptr(C_pages), _ptr(block_table), max_blocks, bs, n_pages, _ptr(idx), B, Tq, H,
         D, int(D_v), k, float(sm_scale), _ptr(out), _ptr(lse), _ptr(buf), buf.numel(),
-        _stream_ptr(stream)))
+        st.cuda_stream))
     return out, lse
 
 
@@ -457,11 +462,12 @@ class GroupCall:
         # the workspace is taken at call time (the given one, or the default
         # one of this device and stream), so calls on different streams never
         # share scratch memory and a workspace grown by another call is seen
-        buf = _workspace(self._ws, self._dev, stream).get(self._nbytes, _stream_of(stream))
+        st = _stream_of(stream)
+        buf = _workspace(self._ws, self._dev, st).get(self._nbytes, st)
         self.args.ws = _ptr(buf)
         self.args.ws_bytes = buf.numel()
         _on_stream(stream, buf, self.idx, *self.out, *(self.lse or []))
-        _check(load_library().isa_group_forward(ctypes.byref(self.args), _stream_ptr(stream)))
+        _check(load_library().isa_group_forward(ctypes.byref(self.args), st.cuda_stream))
         return self.idx, self.out, self.lse
 
 
@@ -478,3 +484,4 @@ def isa_group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequen
                      per_layer_indexer=per_layer_indexer, out=out, lse=lse, ws=ws, kv8=kv8,
                      block_table=block_table)
     return call(stream)
+

@@ -90,11 +90,13 @@ __global__ __launch_bounds__(1024) void lds_read_kernel(float* sink, int iters) 
     v4u acc = {0u, 0u, 0u, 0u};
     int p = threadIdx.x;
     for (int it = 0; it < iters; ++it) {
+        // eight distinct 16-byte words per thread per step (offsets 512 words
+        // apart inside the 4096-word array), a new set every step
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            acc ^= lds[(p + u * 1024) & (LDS_BYTES / 16 - 1)];
+            acc ^= lds[(p + u * 512) & (LDS_BYTES / 16 - 1)];
         }
-        p += 64;
+        p += 64 + (acc[0] & 0);
     }
     sink[blockIdx.x * 1024 + threadIdx.x] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
 }
