@@ -242,6 +242,29 @@ typedef struct {
 size_t isa_group_workspace_bytes(const isa_group_args* args);
 isa_status isa_group_forward(const isa_group_args* args, void* stream);
 
+/*
+ * isa_group_forward for callers that cannot allocate memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call takes its scratch memory from a fixed array of
+ * ISA_NOALLOC_SCRATCH_BYTES inside the library (one copy per GPU, held until
+ * the process ends) instead of args->ws, which is ignored (ws and ws_bytes
+ * may be 0); everything else, results included, is as for isa_group_forward.
+ * It calls no hipMalloc, hipFree or other allocating routine.
+ *  - A call whose isa_group_workspace_bytes(args) exceeds
+ *    ISA_NOALLOC_SCRATCH_BYTES returns ISA_ERR_WORKSPACE and launches
+ *    nothing (the decode shapes of up to 64 queries x 128K positions fit;
+ *    a 4096-query prefill does not).
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last
+ *    call's contents (each call clears what it needs first): calls that may
+ *    overlap on one GPU (other streams, other threads) race with each other
+ *    and must not be issued concurrently.
+ *  - The first call on a device looks up the device address of the array
+ *    (a failure there returns ISA_ERR_HIP).
+ */
+#define ISA_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t isa_group_noalloc_max_bytes(void);
+isa_status isa_group_forward_noalloc(const isa_group_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "isa_attend_fp8_workspace_bytes", "isa_sparse_mla_attend_fp8", "isa_index_histogram",
     "isa_indexer_scores_paged", "isa_sparse_mla_attend_paged",
     "isa_group_workspace_bytes", "isa_group_forward",
+    "isa_group_noalloc_max_bytes", "isa_group_forward_noalloc",
 )
 
 
@@ -108,6 +109,10 @@ def load_library():
     lib.isa_group_workspace_bytes.argtypes = [ctypes.POINTER(GroupArgs)]
     lib.isa_group_forward.restype = _I
     lib.isa_group_forward.argtypes = [ctypes.POINTER(GroupArgs), _P]
+    lib.isa_group_noalloc_max_bytes.restype = _Z
+    lib.isa_group_noalloc_max_bytes.argtypes = []
+    lib.isa_group_forward_noalloc.restype = _I
+    lib.isa_group_forward_noalloc.argtypes = [ctypes.POINTER(GroupArgs), _P]
     if lib.isa_abi_version() != ISA_ABI_VERSION:
         raise RuntimeError(f"libisa ABI {lib.isa_abi_version()} != {ISA_ABI_VERSION}")
     _lib = lib
@@ -382,7 +387,7 @@ class GroupCall:
                  reuse_idx: bool = False, per_layer_indexer: bool = False,
                  out: Optional[Sequence] = None, lse: Optional[Sequence] = None,
                  ws: Optional[Workspace] = None, kv8: Optional[Tuple[Sequence, Sequence, Sequence]] = None,
-                 block_table: Optional[torch.Tensor] = None):
+                 block_table: Optional[torch.Tensor] = None, noalloc: bool = False):
         n = len(Q)
         dev = Q[0].device
         for i, x in enumerate(Q):
@@ -457,8 +462,16 @@ class GroupCall:
         self.args = a
         self._nbytes = int(load_library().isa_group_workspace_bytes(ctypes.byref(a)))
         self._ws, self._dev = ws, dev
+        self._noalloc = bool(noalloc)
 
     def __call__(self, stream=None):
+        if self._noalloc:
+            # the library's own fixed scratch memory (isa_group_forward_noalloc)
+            st = _stream_of(stream)
+            self.args.ws, self.args.ws_bytes = None, 0
+            _on_stream(stream, self.idx, *self.out, *(self.lse or []))
+            _check(load_library().isa_group_forward_noalloc(ctypes.byref(self.args), st.cuda_stream))
+            return self.idx, self.out, self.lse
         # the workspace is taken at call time (the given one, or the default
         # one of this device and stream), so calls on different streams never
         # share scratch memory and a workspace grown by another call is seen
@@ -485,3 +498,19 @@ def isa_group_forward(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequen
                      block_table=block_table)
     return call(stream)
 
+
+def isa_group_noalloc_max_bytes() -> int:
+    return int(load_library().isa_group_noalloc_max_bytes())
+
+
+def isa_group_forward_noalloc(qI: Sequence, w: Sequence, kI: Sequence, kv_len, Q: Sequence,
+                              C: Optional[Sequence], k: int, D_v: int, sm_scale: float, idx=None,
+                              reuse_idx: bool = False, per_layer_indexer: bool = False, out=None,
+                              lse=None, stream=None, kv8=None, block_table=None):
+    """isa_group_forward on the library's fixed scratch memory (no workspace
+    is allocated): (idx, [out_l], [lse_l] or None).  Calls that may overlap on
+    one GPU share that memory and must not be issued concurrently."""
+    call = GroupCall(qI, w, kI, kv_len, Q, C, k, D_v, sm_scale, idx=idx, reuse_idx=reuse_idx,
+                     per_layer_indexer=per_layer_indexer, out=out, lse=lse, kv8=kv8,
+                     block_table=block_table, noalloc=True)
+    return call(stream)

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/isa.h"
@@ -167,6 +168,43 @@ GroupLayout group_layout(const isa_group_args* a) {
 
 }  // namespace
 
+// Scratch memory of isa_group_forward_noalloc: one fixed array in the code
+// object, so the call allocates nothing.  Every GPU the library runs on holds
+// its own copy of it (until the process ends), at its own address.  In host
+// code the name `scratch` is only a host-side stand-in: the device address of
+// the current GPU's copy comes from hipGetSymbolAddress, once per device, and
+// only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[ISA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device), or an error status.
+isa_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ISA_ERR_HIP, "noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    ISA_CHECK(dev >= 0 && dev < MAX_DEVICES, ISA_ERR_UNSUPPORTED, "noalloc: device %d beyond %d",
+              dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(ISA_ERR_HIP, "noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ISA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int isa_abi_version(void) { return ISA_ABI_VERSION; }
@@ -313,7 +351,9 @@ size_t isa_group_workspace_bytes(const isa_group_args* a) {
     return group_layout(a).total;
 }
 
-isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
+// Checks every argument of a group call except the workspace; on success
+// *pm describes the page geometry (or none) and *L the workspace layout.
+static isa_status check_group(const isa_group_args* a, isa::PageMap* pm, GroupLayout* L) {
     ISA_CHECK(a, ISA_ERR_INVALID_ARG, "group: NULL args");
     ISA_CHECK(a->n_layers >= 1 && a->n_layers <= 64, ISA_ERR_INVALID_ARG,
               "group: n_layers=%d outside [1, 64]", a->n_layers);
@@ -325,9 +365,9 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
         ISA_CHECK(kv8_shape_supported(a->D_v, a->D - a->D_v), ISA_ERR_UNSUPPORTED,
                   "group: FP8 cache with (D=%d, D_v=%d) not compiled", a->D, a->D_v);
     }
-    isa::PageMap pm{nullptr, 0, 0, 0};
+    *pm = isa::PageMap{nullptr, 0, 0, 0};
     if (a->paged) {
-        isa_status st = check_pages(a->block_table, a->max_blocks, a->block_size, a->n_pages, &pm);
+        isa_status st = check_pages(a->block_table, a->max_blocks, a->block_size, a->n_pages, pm);
         if (st != ISA_OK) return st;
         ISA_CHECK((long long)a->max_blocks * a->block_size == a->L_cap, ISA_ERR_INVALID_ARG,
                   "group: paged caches need L_cap = max_blocks * block_size (%d != %d * %d)",
@@ -364,12 +404,16 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
             ISA_CHECK(aligned(a->lse[l], 4), ISA_ERR_INVALID_ARG, "group: misaligned lse[%d]", l);
         }
     }
-    const GroupLayout L = group_layout(a);
-    ISA_CHECK(a->ws && a->ws_bytes >= L.total && aligned(a->ws, 256), ISA_ERR_WORKSPACE,
-              "group: workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, a->ws_bytes);
+    *L = group_layout(a);
+    return ISA_OK;
+}
 
-    hipStream_t stream = static_cast<hipStream_t>(stream_v);
-    char* ws = static_cast<char*>(a->ws);
+// The launches of one group call on `stream`, with scratch memory at ws
+// (L.total bytes, 256-byte aligned).
+static isa_status launch_group(const isa_group_args* a, const isa::PageMap& pm,
+                               const GroupLayout& L, char* ws, hipStream_t stream) {
+    const bool kv8 = a->kv_fp8 != 0;
+    const bool per_layer = a->per_layer_indexer != 0;
     float* S = reinterpret_cast<float*>(ws + L.scores);
     void* topk_ws = ws + L.topk;
     void* attend_ws = ws + L.attend;
@@ -409,6 +453,32 @@ isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
         if (st != ISA_OK) return st;
     }
     return ok();
+}
+
+isa_status isa_group_forward(const isa_group_args* a, void* stream_v) {
+    isa::PageMap pm;
+    GroupLayout L;
+    isa_status st = check_group(a, &pm, &L);
+    if (st != ISA_OK) return st;
+    ISA_CHECK(a->ws && a->ws_bytes >= L.total && aligned(a->ws, 256), ISA_ERR_WORKSPACE,
+              "group: workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, a->ws_bytes);
+    return launch_group(a, pm, L, static_cast<char*>(a->ws), static_cast<hipStream_t>(stream_v));
+}
+
+size_t isa_group_noalloc_max_bytes(void) { return ISA_NOALLOC_SCRATCH_BYTES; }
+
+isa_status isa_group_forward_noalloc(const isa_group_args* a, void* stream_v) {
+    isa::PageMap pm;
+    GroupLayout L;
+    isa_status st = check_group(a, &pm, &L);
+    if (st != ISA_OK) return st;
+    ISA_CHECK(L.total <= (size_t)ISA_NOALLOC_SCRATCH_BYTES, ISA_ERR_WORKSPACE,
+              "group noalloc: the call needs %zu bytes of scratch, above the fixed %zu",
+              L.total, (size_t)ISA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != ISA_OK) return st;
+    return launch_group(a, pm, L, static_cast<char*>(ws), static_cast<hipStream_t>(stream_v));
 }
 
 }  // extern "C"

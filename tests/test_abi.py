@@ -235,6 +235,29 @@ def test_group_rejects_bad_arguments(lib):
     assert lib.isa_group_forward(ctypes.byref(a), None) == isa.ISA_ERR_INVALID_ARG
 
 
+def test_group_noalloc_rejects_calls_beyond_its_scratch(lib):
+    # the 4096-query prefill's score buffer alone is 2.2 GB: far above the
+    # fixed scratch, so the call stops at the host check (nothing launched)
+    P = ctypes.c_void_p
+    arr1 = (P * 1)(A16)
+    arr4 = (P * 4)(A16, A16, A16, A16)
+    a = isa.GroupArgs()
+    a.B, a.Tq, a.L_cap, a.H_I, a.D_I, a.k = 1, 4096, 135168, 64, 128, 2048
+    a.H, a.D, a.D_v, a.n_layers, a.sm_scale = 64, 576, 512, 4, 1 / 24
+    a.qI = ctypes.cast(arr1, P); a.w = ctypes.cast((P * 1)(A4), P); a.kI = ctypes.cast(arr1, P)
+    a.kv_len = A4
+    a.Q = ctypes.cast(arr4, P); a.C = ctypes.cast(arr4, P); a.out = ctypes.cast(arr4, P)
+    a.idx = A4
+    assert lib.isa_group_noalloc_max_bytes() == 64 << 20
+    assert lib.isa_group_workspace_bytes(ctypes.byref(a)) > lib.isa_group_noalloc_max_bytes()
+    st, msg = _status(lib, "isa_group_forward_noalloc", ctypes.byref(a), None)
+    assert st == isa.ISA_ERR_WORKSPACE and "scratch" in msg
+    # argument errors are reported before the size check, as for isa_group_forward
+    a.k = 0
+    st, _ = _status(lib, "isa_group_forward_noalloc", ctypes.byref(a), None)
+    assert st == isa.ISA_ERR_INVALID_ARG
+
+
 def test_binding_fails_loudly_without_device():
     import torch
     x = torch.zeros(4, dtype=torch.int8)
