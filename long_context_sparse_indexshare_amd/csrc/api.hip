@@ -154,7 +154,7 @@ GroupLayout group_layout(const isa_group_args* a) {
     L.topk = off;
     L.topk_zero_bytes = 0;
     if (L.need_index) {
-        const isa::TopkLayout tl = isa::topk_layout((int)rows, a->L_cap);
+        const isa::TopkLayout tl = isa::topk_layout((int)rows, a->L_cap, a->k);
         L.topk_zero_bytes = tl.zero_bytes;           // the counters come first
         off += round_up(tl.total);
     }
@@ -237,9 +237,8 @@ isa_status isa_indexer_scores_paged(const int8_t* qI, const float* w, const int8
 }
 
 size_t isa_topk_workspace_bytes(int B, int Tq, int L_cap, int k) {
-    (void)k;
-    if (B <= 0 || Tq <= 0 || L_cap <= 0) return 0;
-    return isa::topk_layout(B * Tq, L_cap).total;
+    if (B <= 0 || Tq <= 0 || L_cap <= 0 || k <= 0) return 0;
+    return isa::topk_layout(B * Tq, L_cap, k).total;
 }
 
 isa_status isa_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap, int k,
@@ -415,8 +414,12 @@ static isa_status launch_group(const isa_group_args* a, const isa::PageMap& pm,
     const bool kv8 = a->kv_fp8 != 0;
     const bool per_layer = a->per_layer_indexer != 0;
     float* S = reinterpret_cast<float*>(ws + L.scores);
-    void* topk_ws = ws + L.topk;
+    char* topk_ws = ws + L.topk;
     void* attend_ws = ws + L.attend;
+    // with one query per sequence the indexer also writes the top-k summary
+    const isa::TopkLayout tl = isa::topk_layout(a->B * a->Tq, a->L_cap, a->k);
+    const bool fused_summary = L.need_index && !tl.select && isa::indexer_writes_summary(a->Tq, a->H_I);
+    uint32_t* summary = fused_summary ? reinterpret_cast<uint32_t*>(topk_ws + tl.summary) : nullptr;
     // each index set: the indexer grid also zeroes the top-k counters
     // (histograms, entry counts), then the top-k runs
     auto index = [&](int l) -> isa_status {
@@ -424,11 +427,11 @@ static isa_status launch_group(const isa_group_args* a, const isa::PageMap& pm,
                                                              a->B, a->Tq, a->H_I, a->D_I, a->L_cap,
                                                              S, reinterpret_cast<uint32_t*>(topk_ws),
                                                              (uint32_t)(L.topk_zero_bytes / 4),
-                                                             stream, pm),
+                                                             stream, pm, summary, tl.M),
                                   "group: indexer launch");
         if (st != ISA_OK) return st;
         return check_hip(isa::launch_topk_select(S, a->kv_len, a->B, a->Tq, a->L_cap, a->k, a->idx,
-                                                 topk_ws, true, stream),
+                                                 topk_ws, true, stream, fused_summary),
                          "group: topk launch");
     };
     if (L.need_index && !per_layer) {

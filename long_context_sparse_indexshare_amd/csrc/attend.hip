@@ -301,62 +301,57 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
 
     // one tile of the online softmax attention, from the LDS tile
     auto compute_tile = [&](int tile_start) {
-        // ---- partial S^T (32 rows x 32 heads) over this wave's k-steps
-        // two accumulators halve the dependent MFMA chain
-        v16f st, st2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = st2[r] = 0.0f;
+        // ---- partial S^T (32 rows x 32 heads) over this wave's k-steps: every
+        // A operand is requested from LDS first, then the MFMAs run in two
+        // independent accumulator chains (even and odd k-steps)
         const char* arow = tile + tile_slot(j) * ROWB;
+        v8bf a[G::KSW];
 #pragma unroll
         for (int i = 0; i < G::KSW; ++i) {
             const int ch = 2 * (kp * G::KSW + i) + g;
-            const v8bf a = __builtin_bit_cast(
-                v8bf, *reinterpret_cast<const uint4*>(arow + ch * 16));
-            if ((i & 1) && G::QK_ACC == 2)
-                st2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i], st2, 0, 0, 0);
+            a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(arow + ch * 16));
+        }
+        // keep the scheduler from sinking the reads between the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        v16f st, st2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = st2[r] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G::KSW; ++i) {
+            if (i & 1)
+                st2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qb[i], st2, 0, 0, 0);
             else
-                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[i], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qb[i], st, 0, 0, 0);
         }
-        if (G::QK_ACC == 2) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] += st2[r];
-        }
-        // ---- sum the K-split partials of this head block, in kp order
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            *reinterpret_cast<float4*>(&xbuf[wave][r4][lane][0]) =
-                make_float4(st[4 * r4], st[4 * r4 + 1], st[4 * r4 + 2], st[4 * r4 + 3]);
-        lds_barrier();
+        for (int r = 0; r < 16; ++r) st[r] += st2[r];
+        // ---- sum the K-split partials of this head block: every wave adds
+        // all of them, its own included, from LDS in kp order, so every wave
+        // of the block holds identical bits (no branch on the wave's place)
         v16f s;
-        if constexpr (G::KSP == 2) {
-            // own + partner: a sum of two is the same bits in either order
-            const int w2 = (1 - kp) * HB + hbl;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
-                s[4 * r4] = st[4 * r4] + v.x;
-                s[4 * r4 + 1] = st[4 * r4 + 1] + v.y;
-                s[4 * r4 + 2] = st[4 * r4 + 2] + v.z;
-                s[4 * r4 + 3] = st[4 * r4 + 3] + v.w;
-            }
+        if constexpr (G::KSP == 1) {
+            s = st;
         } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-            // in kp order; a wave's own block comes from its registers (the
-            // same bits it stored)
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4*>(&xbuf[wave][r4][lane][0]) =
+                    make_float4(st[4 * r4], st[4 * r4 + 1], st[4 * r4 + 2], st[4 * r4 + 3]);
+            lds_barrier();
+            float4 part[G::KSP][4];
 #pragma unroll
-            for (int p = 0; p < G::KSP; ++p) {
-                if (p == kp) {
+            for (int p = 0; p < G::KSP; ++p)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s[r] += st[r];
-                } else {
-                    const int w2 = p * HB + hbl;
+                for (int r4 = 0; r4 < 4; ++r4)
+                    part[p][r4] = *reinterpret_cast<const float4*>(&xbuf[p * HB + hbl][r4][lane][0]);
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const float4 v = *reinterpret_cast<const float4*>(&xbuf[w2][r4][lane][0]);
-                        s[4 * r4] += v.x; s[4 * r4 + 1] += v.y; s[4 * r4 + 2] += v.z; s[4 * r4 + 3] += v.w;
-                    }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float4 acc = part[0][r4];
+#pragma unroll
+                for (int p = 1; p < G::KSP; ++p) {
+                    acc.x += part[p][r4].x; acc.y += part[p][r4].y;
+                    acc.z += part[p][r4].z; acc.w += part[p][r4].w;
                 }
+                s[4 * r4] = acc.x; s[4 * r4 + 1] = acc.y; s[4 * r4 + 2] = acc.z; s[4 * r4 + 3] = acc.w;
             }
         }
         // register r holds tile row 8*(r/4) + 4*g + r%4, head j; rows of -1
@@ -385,6 +380,21 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                 for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
         }
         const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+        // ---- the V^T operands of the PV product are requested before the
+        // softmax arithmetic, so their LDS latency overlaps it
+        const int G16 = lane >> 4;
+        const int i16 = lane & 15;
+        v4bf vlo[2][G::NB], vhi[2][G::NB];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int row = 16 * kk + 4 * (G16 >> 1) + (i16 >> 2);
+#pragma unroll
+            for (int nb = 0; nb < G::NB; ++nb) {
+                const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
+                vlo[kk][nb] = lds_read_tr(tile, tile_slot(row) * ROWB + col * 2);
+                vhi[kk][nb] = lds_read_tr(tile, tile_slot(row + 8) * ROWB + col * 2);
+            }
+        }
         float psum = 0.0f;
         v8bf pk[2];
 #pragma unroll
@@ -396,18 +406,13 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         l_run += psum;
 
         // ---- O^T[this wave's columns x heads] += V^T . P^T over the tile's 32 rows
-        const int G16 = lane >> 4;
-        const int i16 = lane & 15;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const int row = 16 * kk + 4 * (G16 >> 1) + (i16 >> 2);
 #pragma unroll
             for (int nb = 0; nb < G::NB; ++nb) {
-                const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
-                const v4bf lo = lds_read_tr(tile, tile_slot(row) * ROWB + col * 2);
-                const v4bf hi = lds_read_tr(tile, tile_slot(row + 8) * ROWB + col * 2);
-                const v8bf a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[nb], 0, 0, 0);
+                const v4bf lo = vlo[kk][nb], hi = vhi[kk][nb];
+                const v8bf av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[kk], o[nb], 0, 0, 0);
             }
         }
     };

@@ -18,6 +18,8 @@
 // keeps the next two key blocks' loads in flight while it computes the
 // current one; with one query per workgroup the scores are staged in LDS and
 // written after the last block, four contiguous floats per thread.
+#include <type_traits>
+
 #include "isa_internal.h"
 
 namespace isa {
@@ -61,7 +63,8 @@ template <int H_I, int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
     const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
-    uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm) {
+    uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm, uint32_t* __restrict__ summary,
+    int M) {
     grid_clear(zero, zero_n);
     constexpr int QPW = IX_ROWS / H_I;             // queries per workgroup
     constexpr int KS = D_I / 32;                   // MFMA k-steps over the indexer dim
@@ -126,6 +129,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     // one in-order counter, so a store between the key blocks would make the
     // wait for each later block also wait for the store.
     float res[IX_STEPS];
+    uint32_t visb = 0;                 // which of res[] are visible scores (lanes with g == 0)
 #pragma unroll
     for (int st = 0; st < IX_STEPS; ++st) res[st] = -__builtin_inff();
     // ring of IX_DEPTH key blocks per wave: the one being computed and the
@@ -186,7 +190,9 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
                 if (t >= Tq) continue;
                 const int pos = len - Tq + t;
                 if constexpr (NQL == 1) {
-                    res[step] = s <= pos && page_ok ? sum[q] : -__builtin_inff();
+                    const bool vis = s <= pos && page_ok;
+                    res[step] = vis ? sum[q] : -__builtin_inff();
+                    visb |= (uint32_t)vis << step;
                 } else {
                     S[((size_t)b * Tq + t) * L_cap + s] =
                         s <= pos && page_ok ? sum[q] : -__builtin_inff();
@@ -195,6 +201,17 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
         }
     }
     if constexpr (NQL == 1) {
+        // the top-k summary of this wave's 256 keys (wave chunk 4 * blockIdx.x
+        // + wave of the query's row): their M largest score keys, invisible
+        // positions counting as none
+        if (summary != nullptr) {
+            uint32_t key[IX_STEPS];
+#pragma unroll
+            for (int st = 0; st < IX_STEPS; ++st) key[st] = (visb >> st) & 1u ? score_key(res[st]) : 0u;
+            const size_t row = (size_t)b * Tq + t0;
+            wave_top_m<IX_STEPS>(key, M,
+                                 summary + (row * (gridDim.x * 4) + blockIdx.x * 4 + wave) * M);
+        }
         // the workgroup's IX_KEYS_PER_WG scores are contiguous in S: stage them
         // in LDS in key order, then one 16-byte streaming store per thread
         static_assert(IX_KEYS_PER_WG % (4 * IX_THREADS) == 0, "whole 16-byte stores");
@@ -285,6 +302,7 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
         }
     }
 
+    const bool fast = false;
     // as in the decode kernel: unconditional loads, dead lanes read the zero row
     const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_keys);
     auto load_keys = [&](int s0, v4i* bk) {
@@ -298,55 +316,84 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
         for (int ks = 0; ks < KS; ++ks) bk[ks] = *(global_v4i_ptr)(src + 32 * ks);
     };
 
-    // scores of the 32 keys s0 .. s0+31 against both queries, from keys in bk
-    auto step = [&](int s0, const v4i* bk) {
-        const int s = s0 + j;
-        float sum[PF_QPWAVE];
+    auto run = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        // scores of the 32 keys s0 .. s0+31 against both queries, from keys in bk
+        auto step = [&](int s0, const v4i* bk) {
+            const int s = s0 + j;
+            float sum[PF_QPWAVE];
 #pragma unroll
-        for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = 0.0f;
-        if (s0 <= pos_max) {
+            for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = 0.0f;
+            if (s0 <= pos_max) {
+                if constexpr (FAST) {
+                    // integer ReLU sums; pairs of ReLUs go into one three-input add
+                    int tot[PF_QPWAVE];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                v16i acc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                    for (int q = 0; q < PF_QPWAVE; ++q) tot[q] = 0;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc, 0, 0, 0);
+                    for (int rb = 0; rb < RB; ++rb) {
+                        v16i acc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dot = acc[r];
-                    sum[rb / 2] += wr[rb][r] * (float)(dot > 0 ? dot : 0);
+                        for (int ks = 0; ks < KS; ++ks)
+                            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; r += 2)
+                            tot[rb / 2] += max(acc[r], 0) + max(acc[r + 1], 0);
+                    }
+#pragma unroll
+                    for (int q = 0; q < PF_QPWAVE; ++q) {
+                        // the other half of the heads sits in lane j ^ 32
+                        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)tot[q],
+                                                                        (uint32_t)tot[q], false, false);
+                        sum[q] = (float)((int)r[0] + (int)r[1]) * 0.25f;
+                    }
+                } else {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        v16i acc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks)
+                            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int dot = acc[r];
+                            sum[rb / 2] += wr[rb][r] * (float)(dot > 0 ? dot : 0);
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = xor32_sum(sum[q]);
                 }
             }
+            if (g == 0 && s < L_cap) {
+                // positions on an unallocated page score -inf
+                const bool page_ok = pm.table == nullptr || key_block_row(pm, b, L_cap, s0) >= 0;
 #pragma unroll
-            for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = xor32_sum(sum[q]);
-        }
-        if (g == 0 && s < L_cap) {
-            // positions on an unallocated page score -inf
-            const bool page_ok = pm.table == nullptr || key_block_row(pm, b, L_cap, s0) >= 0;
-#pragma unroll
-            for (int q = 0; q < PF_QPWAVE; ++q) {
-                if (tw + q >= Tq) continue;                   // past the last query
-                S[((size_t)b * Tq + tw + q) * L_cap + s] =
-                    s <= pos[q] && page_ok ? sum[q] : -__builtin_inff();
+                for (int q = 0; q < PF_QPWAVE; ++q) {
+                    if (tw + q >= Tq) continue;                   // past the last query
+                    S[((size_t)b * Tq + tw + q) * L_cap + s] =
+                        s <= pos[q] && page_ok ? sum[q] : -__builtin_inff();
+                }
             }
+        };
+
+        // two key buffers in turn: the next block is in flight while one is used
+        v4i k0[KS], k1[KS];
+        load_keys(s_lo, k0);
+        for (int s0 = s_lo; s0 < s_hi; s0 += 64) {
+            load_keys(s0 + 32, k1);       // load_keys returns zeros past s_hi
+            step(s0, k0);
+            load_keys(s0 + 64, k0);
+            if (s0 + 32 < s_hi) step(s0 + 32, k1);
         }
     };
-
-    // two key buffers in turn: the next block is in flight while one is used
-    v4i k0[KS], k1[KS];
-    load_keys(s_lo, k0);
-    for (int s0 = s_lo; s0 < s_hi; s0 += 64) {
-        load_keys(s0 + 32, k1);       // load_keys returns zeros past s_hi
-        step(s0, k0);
-        load_keys(s0 + 64, k0);
-        if (s0 + 32 < s_hi) step(s0 + 32, k1);
-    }
+    if (fast) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 template <int H_I, int D_I>
 hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
                      int B, int Tq, int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                     hipStream_t stream, PageMap pm) {
+                     hipStream_t stream, PageMap pm, uint32_t* summary, int M) {
     constexpr int QPW = IX_ROWS / H_I;
     dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
     if constexpr (H_I == 64) {
@@ -366,12 +413,15 @@ hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const i
             return hipGetLastError();
         }
     }
+    if (QPW != 1) summary = nullptr;      // only the one-query workgroups write it
     hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I>), grid, dim3(IX_THREADS), 0, stream,
-                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n, pm);
+                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n, pm, summary, M);
     return hipGetLastError();
 }
 
 }  // namespace
+
+bool indexer_writes_summary(int Tq, int H_I) { return H_I == 64 && Tq < PF_MIN_TQ; }
 
 bool indexer_shape_supported(int H_I, int D_I) {
     const bool h_ok = H_I == 4 || H_I == 8 || H_I == 16 || H_I == 32 || H_I == 64;
@@ -381,12 +431,13 @@ bool indexer_shape_supported(int H_I, int D_I) {
 
 #define ISA_IX_CASE(HH, DD)                                                              \
     if (H_I == HH && D_I == DD)                                                          \
-        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, zero, zero_n, stream, pm);
+        return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, zero, zero_n, stream, pm, \
+                                 summary, M);
 
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                                 hipStream_t stream, PageMap pm) {
+                                 hipStream_t stream, PageMap pm, uint32_t* summary, int M) {
     ISA_IX_CASE(64, 128) ISA_IX_CASE(64, 64) ISA_IX_CASE(64, 32)
     ISA_IX_CASE(32, 128) ISA_IX_CASE(32, 64) ISA_IX_CASE(32, 32)
     ISA_IX_CASE(16, 128) ISA_IX_CASE(16, 64) ISA_IX_CASE(16, 32)

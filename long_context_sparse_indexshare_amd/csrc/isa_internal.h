@@ -33,6 +33,73 @@ __device__ __forceinline__ float xor32_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Order-preserving 32-bit image of an fp32 score (larger score, larger
+// key; -0.0 ranks as +0.0).  Key 0 is below every score's key (-inf maps
+// to 0x007FFFFF) and marks "no value" in the top-k summaries.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Maximum of an unsigned value over the 64 lanes of a wave (every lane
+// active), in registers: DPP row shifts take each 16-lane row's maximum to
+// its lane 15, two row broadcasts carry it to lane 63.  0 is the identity.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    uint32_t v = x;
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k summary of a wave's values: the M largest keys (with multiplicity)
+// among the NV keys each lane holds, in descending order, written by lane 0
+// to dst[0, M); key 0 (no value) pads the list when the wave holds fewer.
+// Every lane first sorts its own keys (a small sorting network), then each of
+// the M rounds takes the wave maximum of the lanes' heads and advances the
+// head of the lowest lane holding it.  All 64 lanes must be active.
+template <int NV>
+__device__ __forceinline__ void sort_keys_desc(uint32_t (&k)[NV]) {
+    auto cas = [&](int i, int j) {
+        const uint32_t a = k[i], b = k[j];
+        k[i] = max(a, b);
+        k[j] = min(a, b);
+    };
+    if constexpr (NV == 4) {
+        cas(0, 1); cas(2, 3); cas(0, 2); cas(1, 3); cas(1, 2);
+    } else if constexpr (NV == 8) {
+        cas(0, 2); cas(1, 3); cas(4, 6); cas(5, 7);
+        cas(0, 4); cas(1, 5); cas(2, 6); cas(3, 7);
+        cas(0, 1); cas(2, 3); cas(4, 5); cas(6, 7);
+        cas(2, 4); cas(3, 5);
+        cas(1, 4); cas(3, 6);
+        cas(1, 2); cas(3, 4); cas(5, 6);
+    } else {
+        static_assert(NV == 4 || NV == 8, "summary lanes hold 4 or 8 keys");
+    }
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_top_m(uint32_t (&k)[NV], int M, uint32_t* __restrict__ dst) {
+    sort_keys_desc<NV>(k);
+    const int lane = threadIdx.x & 63;
+    for (int r = 0; r < M; ++r) {
+        const uint32_t m = wave_max_u32(k[0]);
+        const uint64_t hit = __ballot(k[0] == m);
+        const int winner = (int)__builtin_ctzll(hit);
+        if (lane == 0) dst[r] = m;
+        if (lane == winner) {
+#pragma unroll
+            for (int i = 0; i + 1 < NV; ++i) k[i] = k[i + 1];
+            k[NV - 1] = 0u;
+        }
+    }
+}
+
 // Paged caches: logical position s of sequence b lives in row
 // (page << shift) + (s & ((1 << shift) - 1)) of the page pool, where page =
 // table[b * max_blocks + (s >> shift)]; pages outside [0, n_pages) are
@@ -45,20 +112,29 @@ struct PageMap {
 };
 
 // Top-k geometry (shared by the host sizing code and the kernels).
-constexpr int TOPK_THREADS = 1024;          // classify workgroup: 4 scores per thread
-constexpr int TOPK_CHUNK = 4096;            // scores per workgroup
+constexpr int TOPK_THREADS = 1024;          // filter workgroup: 4 scores per thread
+constexpr int TOPK_CHUNK = 4096;            // scores per filter workgroup
 constexpr int TOPK_PER_THREAD = TOPK_CHUNK / TOPK_THREADS;
-constexpr int TOPK_HIST_BITS = 12;          // first radix digit: key bits [31:20]
+constexpr int TOPK_HIST_BITS = 12;          // first radix digit of the prefill path: key bits [31:20]
 constexpr int TOPK_HIST_BINS = 1 << TOPK_HIST_BITS;
 constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bits
+// The summary: for every run of 256 positions (a "wave chunk"; the indexer's
+// decode workgroup covers 1024 positions with 4 waves), its TOPK_M largest
+// keys.  TOPK_M is chosen per call so the row's summary holds about 2k keys.
+constexpr int TOPK_WAVE_CHUNK = 256;
+constexpr int TOPK_MAX_M = 16;
+constexpr int TOPK_MAX_SUMMARY = 8192;      // summary keys per row at most (8 per filter thread)
 
 struct TopkLayout {
-    size_t hist, hist2, alloc, zero_bytes;   // counters: [0, zero_bytes) is cleared per call
-    size_t row_state, runs, ent, total;
-    int rows, nchunks;
+    size_t alloc, zero_bytes;         // counters: [0, zero_bytes) is cleared per call
+    size_t hist;                      // first-digit histograms (prefill select path)
+    size_t row_state, summary, runs, ent, total;
+    int rows, nchunks;                // filter chunks of TOPK_CHUNK positions per row
+    int nwchunks, M;                  // wave chunks per row, summary keys per wave chunk
     uint32_t cap;                     // entries per row in the entry buffer
+    bool select;                      // one-workgroup-per-row select path (prefill)
 };
-TopkLayout topk_layout(int rows, int L_cap);
+TopkLayout topk_layout(int rows, int L_cap, int k);
 // true when the one-workgroup-per-row select kernel serves (rows, L_cap)
 bool topk_uses_select(int rows, int L_cap);
 
@@ -75,15 +151,20 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k);
 // Launchers (host side; argument checking happens in the API layer).
 hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream);
 // zero[0, zero_n): words the indexer grid also sets to 0 (the top-k counters of
-// the group call that follows), or zero_n = 0
+// the group call that follows), or zero_n = 0.  summary != nullptr: the
+// indexer also writes the top-k summary (M keys per 256-position wave chunk)
+// when it can (indexer_writes_summary); the caller checks that first.
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                                 hipStream_t stream, PageMap pm = PageMap{nullptr, 0, 0, 0});
-// counters_clear: the caller already zeroed the first topk_layout().zero_bytes
+                                 hipStream_t stream, PageMap pm = PageMap{nullptr, 0, 0, 0},
+                                 uint32_t* summary = nullptr, int M = 0);
+bool indexer_writes_summary(int Tq, int H_I);
+// counters_clear: the caller already zeroed the first topk_layout().zero_bytes;
+// summary_ready: the summary in the workspace was written by the indexer
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
                               int k, int32_t* idx, void* ws, bool counters_clear,
-                              hipStream_t stream);
+                              hipStream_t stream, bool summary_ready = false);
 hipError_t launch_sparse_mla_attend(const uint16_t* Q, const uint16_t* C, const int32_t* idx,
                                     int B, int Tq, int H, int D, int D_v, int L_cap, int k,
                                     float sm_scale, uint16_t* out, float* lse, void* partials,

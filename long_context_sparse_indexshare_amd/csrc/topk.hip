@@ -6,25 +6,29 @@
 // that come first under (score descending, position ascending), listed in
 // ascending position and padded with -1.
 //
-// Radix select on the order-preserving 32-bit image of each score, spread
-// over many workgroups per query so one long row (up to 2^21 positions) uses
-// the whole chip:
-//   0. clear:    zero the row counters in the workspace (a fill kernel).
-//   1. hist:     every workgroup histograms the top 12 key bits of a
-//                chunk of the row (16384 scores, or 4096 when few rows give
-//                few chunks) in LDS and adds its non-zero bins to the row's
-//                global histogram.
-//   2. classify: every workgroup finds the bin that holds the k-th key and
-//                keeps its chunk's keys at or above that bin as one run of
-//                (key, position) entries in ascending position.
-//   3. finish:   one workgroup per row finds the exact k-th key T and the
-//                position cut among keys equal to T (radix passes over the
-//                entries of the threshold bin), then writes the selected
+// Scores are compared as order-preserving 32-bit keys.  Few rows of up to
+// 2^21 positions (decode) are spread over many workgroups per row:
+//   0. summary:  for every run of 256 positions, its M largest keys (written
+//                by the indexer's epilogue in the group call, else by a
+//                summary kernel).  M is chosen so the row's summary holds
+//                about 2k keys.
+//   1. filter:   every workgroup derives from the row's summary a threshold L
+//                with at least k summary keys >= L (the summary's keys are
+//                scores of distinct visible positions, so at least k scores
+//                are >= L: the k-th largest is >= L), then keeps its chunk's
+//                scores >= L as one run of (key, position) entries in
+//                ascending position.  On random scores L sits a few percent
+//                below the k-th largest, so a row keeps little more than k
+//                entries.
+//   2. finish:   one workgroup per row finds the exact k-th key T and the
+//                position cut among keys equal to T by radix passes over the
+//                bits the candidates do not share, then writes the selected
 //                positions as the ordered stream compaction of the runs taken
 //                chunk by chunk.  If the entry buffer overflowed (a very flat
-//                score distribution) the row's scores are re-read instead.
-// With at least 256 rows of at most 262144 positions (a prefill chunk) steps 2
-// and 3 are one kernel instead, a workgroup per row (topk_select_kernel).
+//                score distribution) the row's scores are read again.
+// With at least 256 rows of at most 262144 positions (a prefill chunk) a
+// first-digit histogram kernel and one workgroup per row
+// (topk_select_kernel) do the work instead.
 // Workgroups never wait on each other inside a kernel: on gfx950 a device-
 // scope fence writes back and invalidates the whole L2 of the XCD, so each
 // hand-over between workgroups goes through a kernel boundary instead.
@@ -37,12 +41,6 @@ namespace isa {
 namespace {
 
 constexpr int CAND_MIN = 16384;
-
-__device__ __forceinline__ uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;                       // -0.0 ranks as +0.0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // monotone in the float order
-}
 
 __device__ __forceinline__ int visible_count(const int32_t* kv_len, int row, int Tq, int L_cap) {
     const int b = row / Tq;
@@ -215,27 +213,145 @@ __global__ __launch_bounds__(HIST_THREADS) void topk_hist_kernel(const float* __
 
 // Entries the finishing workgroup stages in LDS (more are read from global).
 constexpr int ENT_LDS = 12288;
-constexpr int HIST2_BINS = 1024;                            // second digit: key bits [19:10]
+constexpr int HIST2_BINS = 1024;          // prefill select path: second digit, key bits [19:10]
+constexpr int COL_MAX = 512;              // entries ranked directly for the exact cut
 
-struct RowState {
-    uint32_t bin1;     // first-digit bin of the k-th key
-    uint32_t above1;   // keys in the bins above it
+// ---------------------------------------------------------------------------
+// Summary, for calls whose indexer did not write it: wave w of workgroup c
+// covers positions c*1024 + w*256 + e*64 + lane (e < 4), wave chunk c*4 + w,
+// and writes that chunk's M largest keys; invisible positions take key 0.
+// Chunk 0 also zeroes the row's entry counter for the filter that follows.
+constexpr int SUM_THREADS = 256;
+__global__ __launch_bounds__(SUM_THREADS) void topk_summary_kernel(
+    const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int M,
+    int nwchunks, uint32_t* __restrict__ summary, uint32_t* __restrict__ alloc) {
+    const int row = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int base = blockIdx.x * (4 * TOPK_WAVE_CHUNK) + wave * TOPK_WAVE_CHUNK;
+    const float* rowp = S + (size_t)row * L_cap;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int s = base + e * 64 + lane;
+        v[e] = s < L_cap ? rowp[s] : 0.0f;
+    }
+    const int n = visible_count(kv_len, row, Tq, L_cap);
+    uint32_t key[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[e] = base + e * 64 + lane < n ? score_key(v[e]) : 0u;
+    wave_top_m<4>(key, M, summary + ((size_t)row * nwchunks + blockIdx.x * 4 + wave) * M);
+    if (blockIdx.x == 0 && threadIdx.x == 0) alloc[row] = 0u;
+}
+
+// Threshold of a row from its summary (nsum keys, SUM_PER per thread, key 0
+// = none): with P the bits every summary key shares, two 8-bit digits of the
+// bits below them are fixed in turn, each the largest digit that still has
+// at least k summary keys at or above it; the threshold is P with those two
+// digits and zeros below (0 when the summary holds fewer than k keys).  The
+// summary keys are scores of distinct visible positions, so at least k of
+// the row's scores are >= the threshold.  Every thread returns the same value.
+constexpr int SUM_PER = TOPK_MAX_SUMMARY / TOPK_THREADS;
+struct ThresholdShared {
+    uint32_t red[3][TOPK_THREADS / 64];   // per wave: count, max, ~min
+    uint32_t h[256];
+    uint32_t res[2];                      // digit, count in the bins above it
 };
 
-// Classify: every workgroup finds the first-digit bin that holds the k-th key
-// (one pass over the row's histogram) and keeps the keys of its 4096-score
-// chunk whose first digit is at or above that bin as one run of (key,
-// position) entries in ascending position.  One atomic per workgroup reserves
-// the run in the row's entry buffer; the runs of a row tile [0, total) with no
-// gaps, and runs[row][chunk] records where each chunk's run starts and how
-// long it is.  The candidates (keys inside the threshold bin) also go into a
-// second-digit histogram of the row, and the chunk-0 workgroup records the
-// threshold bin for the finishing step.
-__global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
+__device__ __forceinline__ uint32_t summary_threshold(const uint32_t (&u)[SUM_PER], uint32_t k,
+                                                      ThresholdShared& t) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t cnt = 0, mx = 0, nmn = 0;                  // nmn = ~(minimum nonzero key)
+#pragma unroll
+    for (int i = 0; i < SUM_PER; ++i) {
+        cnt += u[i] != 0u;
+        mx = max(mx, u[i]);
+        nmn = max(nmn, u[i] ? ~u[i] : 0u);
+    }
+    cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(cnt), 63);
+    mx = wave_max_u32(mx);
+    nmn = wave_max_u32(nmn);
+    if (lane == 0) {
+        t.red[0][wave] = cnt;
+        t.red[1][wave] = mx;
+        t.red[2][wave] = nmn;
+    }
+    __syncthreads();
+    uint32_t C = 0, MX = 0, NMN = 0;
+#pragma unroll
+    for (int w = 0; w < TOPK_THREADS / 64; ++w) {
+        C += t.red[0][w];
+        MX = max(MX, t.red[1][w]);
+        NMN = max(NMN, t.red[2][w]);
+    }
+    if (C < k) return 0u;
+    const uint32_t MN = ~NMN;
+    const uint32_t x = MX ^ MN;
+    if (x == 0u) return MN;                             // every summary key equal
+    int hb = 31 - __builtin_clz(x);                     // highest bit the keys differ in
+    uint32_t fval = hb >= 31 ? 0u : (MX >> (hb + 1)) << (hb + 1);
+    uint32_t fmask = hb >= 31 ? 0u : ~((1u << (hb + 1)) - 1u);
+    uint32_t need = k;
+    for (int pass = 0; pass < 2 && hb >= 0; ++pass) {
+        const int nb = hb + 1 < 8 ? hb + 1 : 8;
+        const int sh = hb - nb + 1;
+        const uint32_t bm = (1u << nb) - 1u;
+        if (threadIdx.x < 256) t.h[threadIdx.x] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < SUM_PER; ++i)
+            if (u[i] && (u[i] & fmask) == fval) atomicAdd(&t.h[(u[i] >> sh) & bm], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            // bins in descending order: lane l holds bins 255-4l .. 252-4l
+            uint32_t hv[4], local = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hv[j] = t.h[255 - 4 * lane - j];
+                local += hv[j];
+            }
+            const uint32_t inc = wave_inclusive_scan(local);
+            const uint32_t before = inc - local;
+            if (before < need && inc >= need) {
+                uint32_t acc = before;
+                int d = 0;
+                uint32_t above = 0;
+                bool found = false;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (!found && acc + hv[j] >= need) {
+                        d = 255 - 4 * lane - j;
+                        above = acc;
+                        found = true;
+                    }
+                    acc += hv[j];
+                }
+                t.res[0] = (uint32_t)d;
+                t.res[1] = above;
+            }
+        }
+        __syncthreads();
+        fval |= t.res[0] << sh;
+        fmask |= bm << sh;
+        need -= t.res[1];
+        hb = sh - 1;
+        __syncthreads();                                // t.h and t.res read before the next pass
+    }
+    return fval;
+}
+
+// Filter: every workgroup (4096 positions of one row) derives the row's
+// threshold L from the summary and keeps its chunk's visible keys >= L as one
+// run of (key, position) entries in ascending position.  One atomic per
+// workgroup reserves the run in the row's entry buffer; the runs of a row
+// tile [0, total) with no gaps, and runs[row][chunk] records where each
+// chunk's run starts and how long it is.  Chunk 0 records L for the finish.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_filter_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ hist, uint32_t* __restrict__ hist2, uint32_t* __restrict__ alloc,
-    RowState* __restrict__ row_state, uint2* __restrict__ runs, uint2* __restrict__ ent,
-    uint32_t cap, int nchunks_max) {
+    const uint32_t* __restrict__ summary, int nsum, uint32_t* __restrict__ alloc,
+    uint32_t* __restrict__ row_L, uint2* __restrict__ runs, uint2* __restrict__ ent, uint32_t cap,
+    int nchunks_max) {
     const int row = blockIdx.y;
     const int c = blockIdx.x;
     const int tid = threadIdx.x;
@@ -243,15 +359,13 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
     const int wave = tid >> 6;
     constexpr int NW = TOPK_THREADS / 64;
     static_assert(TOPK_PER_THREAD * NW == 64, "one wave scans the (e, wave) counts");
-    __shared__ uint32_t lh2[HIST2_BINS];
-    __shared__ uint32_t sh_waves[NW];
-    __shared__ uint32_t sh_res[4];
+    __shared__ ThresholdShared ts;
     __shared__ uint32_t sh_cnt[TOPK_PER_THREAD][NW];   // then the exclusive offsets
     __shared__ uint32_t sh_base;
 
-    // this chunk's scores, in flight while the threshold bin is found and
-    // requested before the row's visible length arrives (they stay inside the
-    // row; the ones past the length are masked below)
+    // this chunk's scores and the row's summary, requested before the row's
+    // visible length arrives (they stay inside the row and its summary; the
+    // scores past the length are masked below)
     // (position = start + e * TOPK_THREADS + tid: ascending order is (e, wave, lane))
     const float* rowp = S + (size_t)row * L_cap;
     const int start = c * TOPK_CHUNK;
@@ -261,17 +375,19 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
         const int s = start + e * TOPK_THREADS + tid;
         sc[e] = s < L_cap ? rowp[s] : 0.0f;
     }
-    constexpr int HPER = TOPK_HIST_BINS / TOPK_THREADS;
-    uint32_t hv[HPER];
-    find_bin_load<HPER, true>(hist + (size_t)row * TOPK_HIST_BINS, hv);
+    const uint32_t* su = summary + (size_t)row * nsum;
+    uint32_t u[SUM_PER];
+#pragma unroll
+    for (int i = 0; i < SUM_PER; ++i) {
+        const int j = i * TOPK_THREADS + tid;
+        u[i] = j < nsum ? su[j] : 0u;
+    }
     const int n = visible_count(kv_len, row, Tq, L_cap);
     if (n <= k) return;
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
     if (c >= nch) return;
-    for (int i = tid; i < HIST2_BINS; i += TOPK_THREADS) lh2[i] = 0;
-    const uint2 th = find_bin_regs<HPER, true>(hv, (uint32_t)k, sh_waves, sh_res);
-    const uint32_t bin1 = th.x;
-    if (c == 0 && tid == 0) row_state[row] = RowState{bin1, th.y};
+    const uint32_t L = summary_threshold(u, (uint32_t)k, ts);
+    if (c == 0 && tid == 0) row_L[row] = L;
 
     uint32_t keys[TOPK_PER_THREAD];
     uint64_t kept[TOPK_PER_THREAD];
@@ -280,10 +396,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
         const int s = start + e * TOPK_THREADS + tid;
         const bool valid = s < n;
         keys[e] = valid ? score_key(sc[e]) : 0u;
-        const uint32_t d = keys[e] >> (32 - TOPK_HIST_BITS);
-        const bool keep = valid && d >= bin1;
-        if (valid && d == bin1) atomicAdd(&lh2[(keys[e] >> 10) & (HIST2_BINS - 1)], 1u);
-        kept[e] = __ballot(keep);
+        kept[e] = __ballot(valid && keys[e] >= L);
         if (lane == 0) sh_cnt[e][wave] = (uint32_t)__popcll(kept[e]);
     }
     __syncthreads();
@@ -310,11 +423,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_classify_kernel(
             if (slot < cap) re[slot] = make_uint2(keys[e], (uint32_t)(start + e * TOPK_THREADS + tid));
         }
     }
-    uint32_t* gh2 = hist2 + (size_t)row * HIST2_BINS;
-    for (int i = tid; i < HIST2_BINS; i += TOPK_THREADS) {
-        const uint32_t v = lh2[i];
-        if (v) atomicAdd(&gh2[i], v);
-    }
 }
 
 // LDS of the finishing step.
@@ -323,47 +431,54 @@ constexpr int FIN_WAVES = FIN_THREADS / 64;
 constexpr int FIN_SPEC = 6;               // entries per thread requested before the total is known
 constexpr int FIN_LDS_PER = ENT_LDS / FIN_THREADS;
 constexpr int FIN_PER = 8;                // entries per thread per compaction tile
-constexpr int COL_MAX = 512;              // entries ranked directly for the exact cut
-static_assert(HIST2_BINS == FIN_THREADS, "one second-digit bin per thread");
+constexpr int FIN_DIGIT = 12;             // bits per radix pass of the exact cut
+constexpr int FIN_BINS = 1 << FIN_DIGIT;
 static_assert(TOPK_MAX_CHUNKS <= FIN_THREADS, "one chunk per thread");
 static_assert(ENT_LDS % FIN_THREADS == 0 && FIN_SPEC <= FIN_LDS_PER, "staging geometry");
+static_assert(FIN_BINS % FIN_THREADS == 0, "digit bins per thread");
 struct FinishShared {
-    uint32_t sh[2048];                    // digit histograms
+    uint32_t sh[FIN_BINS];                // digit histograms
     uint32_t cbase[TOPK_MAX_CHUNKS];      // chunk -> first entry of its run
     uint32_t cstart[TOPK_MAX_CHUNKS + 1]; // chunk -> index of its run's first entry in chunk order
     uint2 lent[ENT_LDS];                  // the row's entries, in allocation order
-    uint2 col[COL_MAX];                   // entries that share the cut's 22-bit key prefix
+    uint2 col[COL_MAX];                   // entries of the cut's bin, ranked directly
     uint32_t ncol;
     uint32_t waves[FIN_WAVES];
+    uint32_t red[2][FIN_WAVES];
     uint32_t res[4];
 };
 
-// Finish: one workgroup per row.  From the threshold bin and the candidates'
-// second-digit histogram it knows the 22-bit prefix of the k-th key; the few
-// entries with that prefix are ranked directly under (key desc, position asc)
-// to give the exact k-th key T and the last selected position s_cut among keys
-// equal to T (radix passes over key bits [9:0] and position bits [20:10],
-// [9:0] take over when very many keys share the prefix).  The runs, taken in
-// chunk order, list the row's candidates in ascending position: every thread
-// takes FIN_PER consecutive entries of that order, and one scan of the
-// threads' selected counts gives each selected position its output slot.
-// If the entry buffer overflowed, the row's scores are re-read instead.
+// Finish: one workgroup per row.  The candidates are the row's keys >= L (at
+// least k of them).  The exact k-th key T and the last selected position
+// s_cut among keys equal to T follow from radix passes over the bits the
+// candidates do not all share (12 bits per pass, highest first): each pass
+// histograms the candidates that match the bits fixed so far and fixes the
+// digit holding the k-th key; once that digit's bin holds at most COL_MAX
+// entries they are ranked directly under (key desc, position asc), and if
+// every key bit gets fixed first, two passes over the position bits of the
+// keys equal to T give s_cut.  The runs, taken in chunk order, list the
+// candidates in ascending position, so one flattened pass (eight consecutive
+// entries per thread, the bounds of the thread's run and of the next one read
+// together, and one block scan of the selected counts) writes the selected
+// positions in order.  If the entry buffer overflowed, the row's scores are
+// read instead of the entries.
 __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ hist2, const uint32_t* __restrict__ alloc,
-    const RowState* __restrict__ row_state, const uint2* __restrict__ runs,
-    const uint2* __restrict__ ent, uint32_t cap, int nchunks_max, int32_t* __restrict__ idx) {
+    const uint32_t* __restrict__ alloc, const uint32_t* __restrict__ row_L,
+    const uint2* __restrict__ runs, const uint2* __restrict__ ent, uint32_t cap, int nchunks_max,
+    int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const uint2* re = ent + (size_t)row * cap;
     // every load of this phase is issued before any is used, and before the
-    // row's visible length arrives: the row state, the second-digit
-    // histogram, the chunk table and the first entries (all inside the row's
-    // workspace; entries past the row's total, chunks past its length and the
-    // whole lot for a row that needs no selection are loaded but never used)
-    const RowState rs = row_state[row];
+    // row's visible length arrives: the entry count, the threshold, the chunk
+    // table and the first entries (all inside the row's workspace; entries
+    // past the row's total, chunks past its length and the whole lot for a
+    // row that needs no selection are loaded but never used)
     const uint32_t total = alloc[row];
-    const uint32_t h2 = hist2[(size_t)row * HIST2_BINS + tid];
+    const uint32_t Lr = row_L[row];
     const uint2 rr_all = tid < nchunks_max ? runs[(size_t)row * nchunks_max + tid] : make_uint2(0u, 0u);
     const uint32_t nspec = cap < (uint32_t)(FIN_SPEC * FIN_THREADS) ? cap : (uint32_t)(FIN_SPEC * FIN_THREADS);
     uint2 v[FIN_SPEC];
@@ -383,7 +498,6 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
     const float* rowp = S + (size_t)row * L_cap;
     const uint2 rr = tid < nch ? rr_all : make_uint2(0u, 0u);
-    const uint32_t bin1 = rs.bin1;
     // 0: entries staged in LDS; 1: read from the entry buffer; 2: buffer overflowed, re-read S
     const int mode = total <= (uint32_t)ENT_LDS ? 0 : (total <= cap ? 1 : 2);
     if (mode == 0) {
@@ -406,105 +520,135 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
             }
         }
     }
-    f.sh[tid] = h2;
     if (tid < nch) f.cbase[tid] = rr.x;
     uint32_t ntot;
     const uint32_t cs = block_exclusive_scan<FIN_THREADS>(tid < nch ? rr.y : 0u, &ntot, f.waves);
     if (tid < nch) f.cstart[tid] = cs;
-    if (tid == 0) {
-        f.cstart[nch] = ntot;
-        f.ncol = 0;
-    }
+    if (tid == 0) f.cstart[nch] = ntot;
     __syncthreads();
 
-    // f(key, pos) for every candidate of the threshold bin
+    // f(key, pos) for every candidate
     auto for_each_cand = [&](auto fn) {
         if (mode == 0) {
             for (uint32_t i = tid; i < total; i += FIN_THREADS) {
                 const uint2 e = f.lent[i];
-                if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
+                fn(e.x, (int)e.y);
             }
         } else if (mode == 1) {
             for (uint32_t i = tid; i < total; i += FIN_THREADS) {
                 const uint2 e = re[i];
-                if ((e.x >> (32 - TOPK_HIST_BITS)) == bin1) fn(e.x, (int)e.y);
+                fn(e.x, (int)e.y);
             }
         } else {
             for (int s = tid; s < n; s += FIN_THREADS) {
                 const uint32_t key = score_key(rowp[s]);
-                if ((key >> (32 - TOPK_HIST_BITS)) == bin1) fn(key, s);
+                if (key >= Lr) fn(key, s);
             }
         }
     };
 
-    uint32_t* sh = f.sh;
-    uint32_t need = (uint32_t)k - rs.above1;     // >= 1 keys still to take from the bin
-    // key bits [19:10]: from the second-digit histogram the classify step built
-    const uint2 r2 = find_bin<1, true, FIN_THREADS>(sh, need, f.waves, f.res);
-    need -= r2.y;                                // >= 1 keys to take among the prefix group
-    const uint32_t pre22 = (bin1 << 10) | r2.x;
-    // the entries with that 22-bit prefix
-    for_each_cand([&](uint32_t key, int s) {
-        if ((key >> 10) == pre22) {
-            const uint32_t slot = atomicAdd(&f.ncol, 1u);
-            if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key, (uint32_t)s);
-        }
+    // largest and smallest candidate key: the bits above the highest bit
+    // they differ in are common to every candidate
+    uint32_t mx = 0u, nmn = 0u;
+    for_each_cand([&](uint32_t key, int) {
+        mx = max(mx, key);
+        nmn = max(nmn, ~key);
     });
+    mx = wave_max_u32(mx);
+    nmn = wave_max_u32(nmn);
+    if (lane == 0) {
+        f.red[0][wave] = mx;
+        f.red[1][wave] = nmn;
+    }
     __syncthreads();
-    const uint32_t m = f.ncol;
-    uint32_t T;
-    int s_cut;
-    if (m <= (uint32_t)COL_MAX) {
-        // rank every collected entry under (key desc, position asc); the one of
-        // rank need-1 is the last selected: its key is T, its position s_cut
-        for (uint32_t t = tid; t < m; t += FIN_THREADS) {
-            const uint2 e = f.col[t];
-            uint32_t rank = 0;
-            for (uint32_t j = 0; j < m; ++j) {
-                const uint2 o = f.col[j];
-                rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
-            }
-            if (rank == need - 1) { f.res[2] = e.x; f.res[3] = e.y; }
-        }
-        __syncthreads();
-        T = f.res[2];
-        s_cut = (int)f.res[3];
-    } else {
-        // key bits [9:0]
-        for (int i = tid; i < 1024; i += FIN_THREADS) sh[i] = 0;
+    uint32_t MX = 0u, NMN = 0u;
+#pragma unroll
+    for (int w = 0; w < FIN_WAVES; ++w) {
+        MX = max(MX, f.red[0][w]);
+        NMN = max(NMN, f.red[1][w]);
+    }
+    const uint32_t diff = MX ^ ~NMN;
+    int hb = diff ? 31 - __builtin_clz(diff) : -1;      // bits above hb are fixed
+    uint32_t fval = hb >= 31 ? 0u : (hb < 0 ? MX : (MX >> (hb + 1)) << (hb + 1));
+    uint32_t fmask = hb >= 31 ? 0u : (hb < 0 ? ~0u : ~((1u << (hb + 1)) - 1u));
+    uint32_t need = (uint32_t)k;                        // keys still to take among the matches
+    uint32_t T = 0u;
+    int s_cut = -1;
+    bool ranked = false;
+    for (;;) {
+        if (hb < 0) break;
+        const int nb = hb + 1 < FIN_DIGIT ? hb + 1 : FIN_DIGIT;
+        const int sh = hb - nb + 1;
+        const uint32_t bm = (1u << nb) - 1u;
+        __syncthreads();                                // previous readers of f.sh are done
+        for (int i = tid; i < FIN_BINS; i += FIN_THREADS) f.sh[i] = 0u;
+        if (tid == 0) f.ncol = 0u;
         __syncthreads();
         for_each_cand([&](uint32_t key, int) {
-            if ((key >> 10) == pre22) atomicAdd(&sh[key & 1023u], 1u);
+            if ((key & fmask) == fval) atomicAdd(&f.sh[(key >> sh) & bm], 1u);
         });
         __syncthreads();
-        const uint2 r3 = find_bin<1, true, FIN_THREADS>(sh, need, f.waves, f.res);
-        need -= r3.y;                            // keys equal to T still to take (>= 1)
-        T = (pre22 << 10) | r3.x;
-        // among keys equal to T, the need-th lowest position: position bits [20:10], then [9:0]
-        for (int i = tid; i < 2048; i += FIN_THREADS) sh[i] = 0;
+        const uint2 r = find_bin<FIN_BINS / FIN_THREADS, true, FIN_THREADS>(f.sh, need, f.waves,
+                                                                             f.res);
+        const uint32_t m = f.sh[r.x];                   // entries of the cut's bin
+        need -= r.y;                                    // >= 1 keys to take from that bin
+        fval |= r.x << sh;
+        fmask |= bm << sh;
+        hb = sh - 1;
+        if (m <= (uint32_t)COL_MAX) {
+            // rank the bin's entries directly under (key desc, position asc);
+            // the one of rank need-1 is the last selected
+            for_each_cand([&](uint32_t key, int s) {
+                if ((key & fmask) == fval) {
+                    const uint32_t slot = atomicAdd(&f.ncol, 1u);
+                    f.col[slot] = make_uint2(key, (uint32_t)s);
+                }
+            });
+            __syncthreads();
+            for (uint32_t t = tid; t < m; t += FIN_THREADS) {
+                const uint2 e = f.col[t];
+                uint32_t rank = 0;
+                for (uint32_t j = 0; j < m; ++j) {
+                    const uint2 o = f.col[j];
+                    rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
+                }
+                if (rank == need - 1) { f.res[2] = e.x; f.res[3] = e.y; }
+            }
+            __syncthreads();
+            T = f.res[2];
+            s_cut = (int)f.res[3];
+            ranked = true;
+            break;
+        }
+    }
+    if (!ranked) {
+        // every key bit is fixed: T = fval, and among the keys equal to T the
+        // need lowest positions are selected (position bits [20:10], then [9:0])
+        T = fval;
+        __syncthreads();
+        for (int i = tid; i < 2048; i += FIN_THREADS) f.sh[i] = 0u;
         __syncthreads();
         for_each_cand([&](uint32_t key, int s) {
-            if (key == T) atomicAdd(&sh[(uint32_t)s >> 10], 1u);
+            if (key == T) atomicAdd(&f.sh[(uint32_t)s >> 10], 1u);
         });
         __syncthreads();
-        const uint2 q2 = find_bin<2, false, FIN_THREADS>(sh, need, f.waves, f.res);
+        const uint2 q2 = find_bin<2048 / FIN_THREADS, false, FIN_THREADS>(f.sh, need, f.waves, f.res);
         const uint32_t p2 = q2.x;
         need -= q2.y;
-        for (int i = tid; i < 1024; i += FIN_THREADS) sh[i] = 0;
+        for (int i = tid; i < 1024; i += FIN_THREADS) f.sh[i] = 0u;
         __syncthreads();
         for_each_cand([&](uint32_t key, int s) {
-            if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&sh[(uint32_t)s & 1023u], 1u);
+            if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&f.sh[(uint32_t)s & 1023u], 1u);
         });
         __syncthreads();
-        const uint32_t p3 = find_bin<1, false, FIN_THREADS>(sh, need, f.waves, f.res).x;
+        const uint32_t p3 = find_bin<1024 / FIN_THREADS, false, FIN_THREADS>(f.sh, need, f.waves, f.res).x;
         s_cut = (int)((p2 << 10) | p3);
     }
     __syncthreads();
 
-    // selected: a key above T, or equal to T at a position <= s_cut (keys of
-    // higher first-digit bins are above T).  Evaluated without branches: the
-    // compiler lost the value of a conditionally written position on the
-    // short-circuit form of this test.
+    // selected: a key above T, or equal to T at a position <= s_cut.
+    // Evaluated without branches: the compiler lost the value of a
+    // conditionally written position on the short-circuit form of this test.
     auto sel_of = [&](uint32_t key, uint32_t s) -> uint32_t {
         return (uint32_t)(key > T) | ((uint32_t)(key == T) & (uint32_t)(s <= (uint32_t)s_cut));
     };
@@ -841,19 +985,25 @@ bool topk_uses_select(int rows, int L_cap) {
     return L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS;
 }
 
-TopkLayout topk_layout(int rows, int L_cap) {
+TopkLayout topk_layout(int rows, int L_cap, int k) {
     TopkLayout L;
     L.rows = rows;
     L.nchunks = (L_cap + TOPK_CHUNK - 1) / TOPK_CHUNK;
+    // wave chunks of 256 positions (4 per 1024-position indexer workgroup)
+    L.nwchunks = (L_cap + 4 * TOPK_WAVE_CHUNK - 1) / (4 * TOPK_WAVE_CHUNK) * 4;
+    // summary keys per wave chunk: about 2k per row in all
+    int M = (int)((2LL * k * TOPK_WAVE_CHUNK + L_cap - 1) / L_cap);
+    L.M = M < 1 ? 1 : (M > TOPK_MAX_M ? TOPK_MAX_M : M);
     uint32_t cap = (uint32_t)(L_cap / 8);
-    const uint32_t lo = (uint32_t)(L_cap < CAND_MIN ? L_cap : CAND_MIN);
+    const uint32_t lo = (uint32_t)(L_cap < 2 * CAND_MIN ? L_cap : 2 * CAND_MIN);
     if (cap < lo) cap = lo;
     cap = (cap + 63u) & ~63u;
     L.cap = cap;
     // the one-workgroup-per-row select kernel needs only the first-digit
-    // histograms; the classify/finish pair also needs the second-digit
-    // histograms, the entry counters and its scratch
-    const bool sel = topk_uses_select(rows, L_cap);
+    // histograms; the filter/finish pair needs the entry counters, the
+    // thresholds, the summary and its entry buffer
+    L.select = topk_uses_select(rows, L_cap);
+    const bool sel = L.select;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -861,12 +1011,12 @@ TopkLayout topk_layout(int rows, int L_cap) {
         return o;
     };
     // counters zeroed at the start of every call come first
-    L.hist = take((size_t)rows * TOPK_HIST_BINS * 4);
-    L.hist2 = take(sel ? 0 : (size_t)rows * HIST2_BINS * 4);
     L.alloc = take(sel ? 0 : (size_t)rows * 4);
+    L.hist = take(sel ? (size_t)rows * TOPK_HIST_BINS * 4 : 0);
     L.zero_bytes = off;
     // scratch overwritten by every call
-    L.row_state = take(sel ? 0 : (size_t)rows * sizeof(RowState));
+    L.row_state = take(sel ? 0 : (size_t)rows * 4);
+    L.summary = take(sel ? 0 : (size_t)rows * L.nwchunks * L.M * 4);
     L.runs = take(sel ? 0 : (size_t)rows * L.nchunks * 8);
     L.ent = take(sel ? 0 : (size_t)rows * cap * 8);
     L.total = off;
@@ -884,38 +1034,46 @@ hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream) {
 
 hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int Tq, int L_cap,
                               int k, int32_t* idx, void* ws, bool counters_clear,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool summary_ready) {
     const int rows = B * Tq;
-    const TopkLayout L = topk_layout(rows, L_cap);
+    const TopkLayout L = topk_layout(rows, L_cap, k);
     char* base = static_cast<char*>(ws);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
-    uint32_t* hist2 = reinterpret_cast<uint32_t*>(base + L.hist2);
-    uint32_t* alloc = reinterpret_cast<uint32_t*>(base + L.alloc);
-    RowState* row_state = reinterpret_cast<RowState*>(base + L.row_state);
-    uint2* runs = reinterpret_cast<uint2*>(base + L.runs);
-    uint2* ent = reinterpret_cast<uint2*>(base + L.ent);
-    if (!counters_clear) {
-        hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.zero_bytes / 4, stream);
-        if (e != hipSuccess) return e;
-    }
-    dim3 grid(L.nchunks, rows);
-    constexpr int CH_MANY = HIST_THREADS * HIST_PER_MANY, CH_FEW = HIST_THREADS * HIST_PER_FEW;
-    const size_t wgs_many = (size_t)rows * ((L_cap + CH_MANY - 1) / CH_MANY);
-    if (wgs_many >= (size_t)HIST_MIN_WGS || (L_cap + CH_FEW - 1) / CH_FEW > HIST_MAX_FEW_CHUNKS)
-        hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_MANY>, dim3((L_cap + CH_MANY - 1) / CH_MANY, rows),
-                           dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
-    else
-        hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_FEW>, dim3((L_cap + CH_FEW - 1) / CH_FEW, rows),
-                           dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
-    if (topk_uses_select(rows, L_cap)) {
+    if (L.select) {
+        uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
+        if (!counters_clear) {
+            hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.zero_bytes / 4, stream);
+            if (e != hipSuccess) return e;
+        }
+        constexpr int CH_MANY = HIST_THREADS * HIST_PER_MANY, CH_FEW = HIST_THREADS * HIST_PER_FEW;
+        const size_t wgs_many = (size_t)rows * ((L_cap + CH_MANY - 1) / CH_MANY);
+        if (wgs_many >= (size_t)HIST_MIN_WGS || (L_cap + CH_FEW - 1) / CH_FEW > HIST_MAX_FEW_CHUNKS)
+            hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_MANY>, dim3((L_cap + CH_MANY - 1) / CH_MANY, rows),
+                               dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
+        else
+            hipLaunchKernelGGL(topk_hist_kernel<HIST_PER_FEW>, dim3((L_cap + CH_FEW - 1) / CH_FEW, rows),
+                               dim3(HIST_THREADS), 0, stream, S, kv_len, Tq, L_cap, k, hist);
         hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(SEL_THREADS), 0, stream, S,
                            kv_len, Tq, L_cap, k, hist, idx);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(TOPK_THREADS), 0, stream, S, kv_len, Tq,
-                       L_cap, k, hist, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks);
+    uint32_t* alloc = reinterpret_cast<uint32_t*>(base + L.alloc);
+    uint32_t* row_L = reinterpret_cast<uint32_t*>(base + L.row_state);
+    uint32_t* summary = reinterpret_cast<uint32_t*>(base + L.summary);
+    uint2* runs = reinterpret_cast<uint2*>(base + L.runs);
+    uint2* ent = reinterpret_cast<uint2*>(base + L.ent);
+    if (!summary_ready) {
+        // the summary kernel also zeroes the entry counters
+        hipLaunchKernelGGL(topk_summary_kernel, dim3(L.nwchunks / 4, rows), dim3(SUM_THREADS), 0,
+                           stream, S, kv_len, Tq, L_cap, L.M, L.nwchunks, summary, alloc);
+    } else if (!counters_clear) {
+        hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.zero_bytes / 4, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(L.nchunks, rows), dim3(TOPK_THREADS), 0, stream, S,
+                       kv_len, Tq, L_cap, k, summary, L.nwchunks * L.M, alloc, row_L, runs, ent,
+                       L.cap, L.nchunks);
     hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(FIN_THREADS), 0, stream, S, kv_len,
-                       Tq, L_cap, k, hist2, alloc, row_state, runs, ent, L.cap, L.nchunks, idx);
+                       Tq, L_cap, k, alloc, row_L, runs, ent, L.cap, L.nchunks, idx);
     return hipGetLastError();
 }
 
