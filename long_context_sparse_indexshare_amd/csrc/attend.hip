@@ -166,7 +166,12 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     static_assert(!KV8 || (F8CH % G::TPR == 0 && RCH <= G::TPR), "FP8 gather geometry");
 
     __shared__ __attribute__((aligned(16))) char tiles[GR][G::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) float xbufs[GR][4][4][64][4];   // partial S^T blocks
+    // per group: partial S^T blocks of the reduce-scatter ([owner wave][slot][lane]),
+    // the waves' row maxima or softmax sums ([wave][lane]), their P rows in bf16
+    __shared__ __attribute__((aligned(16))) float4 xbufs[GR][4][4][64];
+    __shared__ float mbufs[GR][4][64];
+    __shared__ uint32_t pbufs[GR][4][4][64];
+    __shared__ uint32_t s_bad;
     __shared__ int sidx[MAX_SPLIT_SLOTS + TILE_ROWS * GR];
     __shared__ uint32_t tmask[(MAX_SPLIT_SLOTS + TILE_ROWS * GR) / TILE_ROWS + 2];   // valid rows per tile
 
@@ -204,7 +209,9 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     const char* Crb = KV8 ? reinterpret_cast<const char*>(Cr + row0 * (D - DV)) : nullptr;
     const int col0 = vh * G::COLS + kp * G::CW;   // first value column of this wave
     char* tile = tiles[grp];
-    float (*xbuf)[4][64][4] = xbufs[grp];
+    float4 (*xb)[4][64] = xbufs[grp];
+    float (*mbuf)[64] = mbufs[grp];
+    uint32_t (*pbuf)[4][64] = pbufs[grp];
 
     // tiles of the split; group grp takes tiles grp, grp + GR, ...  Every group
     // runs the same number of iterations (a group past the last tile computes
@@ -239,8 +246,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[nb][r] = 0.0f;
-    float m_run = -__builtin_inff();
-    float l_run = 0.0f;
+    float m_run = -__builtin_inff();   // running reference max (log2 units), same in every wave of a head block
 
     // gather: thread (row tid / 8, sub tid % 8) owns chunks sub, sub + 8, ... of
     // one tile row, so one base address and immediate offsets serve all its
@@ -299,8 +305,24 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         if (gsub < RCH) *reinterpret_cast<v4u*>(lrow8 + DV * 2 + gsub * 16) = RR;              \
     }
 
-    // one tile of the online softmax attention, from the LDS tile
-    auto compute_tile = [&](int tile_start) {
+    // one tile of the online softmax attention, from the LDS tile.  The K
+    // split leaves each of the KSP waves of a head block a partial S^T; a
+    // reduce-scatter through LDS gives wave kp the sums of registers
+    // [kp*RG, (kp+1)*RG) (RG = 16/KSP registers: 32/KSP tile rows for both
+    // lane halves), added in kp order, and each wave turns only its own rows
+    // into softmax weights P; the bf16 P rows are then exchanged so every
+    // wave feeds the whole P^T to its PV product.  The reference max: on the
+    // first tile with a valid row it is the tile's max (one more exchange);
+    // afterwards P is computed against the running reference and only when
+    // some wave's rows exceed it by more than RESCALE_SLACK (all waves see the
+    // same maxima, so the decision is the same in each) is the reference
+    // moved, the accumulators rescaled and P computed again.
+    static_assert(G::KSP == 2 || G::KSP == 4, "the K split spans two or four waves");
+    constexpr int RG = 16 / G::KSP;          // registers (of 16) this wave finalizes
+    constexpr int RQ = RG / 4;               // float4 slots per (owner, source) pair
+    float l_own = 0.0f;                      // softmax sum over this wave's rows
+    bool bad = false;                        // a row of this wave exceeded the reference by > RESCALE_SLACK
+    auto compute_tile = [&](int tile_start, bool exact) {
         // ---- partial S^T (32 rows x 32 heads) over this wave's k-steps: every
         // A operand is requested from LDS first, then the MFMAs run in two
         // independent accumulator chains (even and odd k-steps)
@@ -311,8 +333,9 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
             const int ch = 2 * (kp * G::KSW + i) + g;
             a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(arow + ch * 16));
         }
-        // keep the scheduler from sinking the reads between the MFMAs
-        __builtin_amdgcn_sched_barrier(0);
+        // keep the scheduler from sinking the reads between the MFMAs (where
+        // the registers allow: the wide variant holds twice the accumulators)
+        if constexpr (G::NB <= 4) __builtin_amdgcn_sched_barrier(0);
         v16f st, st2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = st2[r] = 0.0f;
@@ -325,91 +348,120 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] += st2[r];
-        // ---- sum the K-split partials of this head block: every wave adds
-        // all of them, its own included, from LDS in kp order, so every wave
-        // of the block holds identical bits (no branch on the wave's place)
-        v16f s;
-        if constexpr (G::KSP == 1) {
-            s = st;
-        } else {
+        // ---- reduce-scatter: every wave posts all its partial registers
+        // (its own share included, so the sum below needs no branch on kp)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-                *reinterpret_cast<float4*>(&xbuf[wave][r4][lane][0]) =
-                    make_float4(st[4 * r4], st[4 * r4 + 1], st[4 * r4 + 2], st[4 * r4 + 3]);
-            lds_barrier();
-            float4 part[G::KSP][4];
+        for (int o = 0; o < G::KSP; ++o)
 #pragma unroll
-            for (int p = 0; p < G::KSP; ++p)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    part[p][r4] = *reinterpret_cast<const float4*>(&xbuf[p * HB + hbl][r4][lane][0]);
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                float4 acc = part[0][r4];
-#pragma unroll
-                for (int p = 1; p < G::KSP; ++p) {
-                    acc.x += part[p][r4].x; acc.y += part[p][r4].y;
-                    acc.z += part[p][r4].z; acc.w += part[p][r4].w;
-                }
-                s[4 * r4] = acc.x; s[4 * r4 + 1] = acc.y; s[4 * r4 + 2] = acc.z; s[4 * r4 + 3] = acc.w;
+            for (int q4 = 0; q4 < RQ; ++q4) {
+                const int r0 = o * RG + 4 * q4;
+                xb[o * HB + hbl][kp * RQ + q4][lane] = make_float4(st[r0], st[r0 + 1], st[r0 + 2], st[r0 + 3]);
             }
+        lds_barrier();
+        float so[RG];                        // this wave's rows: registers kp*RG + i
+#pragma unroll
+        for (int q4 = 0; q4 < RQ; ++q4) {
+            float4 acc = xb[wave][q4][lane];
+#pragma unroll
+            for (int src = 1; src < G::KSP; ++src) {
+                const float4 v = xb[wave][src * RQ + q4][lane];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            so[4 * q4] = acc.x; so[4 * q4 + 1] = acc.y; so[4 * q4 + 2] = acc.z; so[4 * q4 + 3] = acc.w;
         }
         // register r holds tile row 8*(r/4) + 4*g + r%4, head j; rows of -1
         // slots get -inf (tiles without such rows, the usual case, skip this)
         const uint32_t tm = tmask[(tile_start - slot0) / TILE_ROWS];
         if (tm != 0xFFFFFFFFu) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (!((tm >> (8 * (r / 4) + 4 * g + (r % 4))) & 1u)) s[r] = -__builtin_inff();
-        }
-        float mloc = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
-        mloc = xor32_max(mloc) * scale_log2;   // scale > 0 keeps the order
-        // move the reference max only when this tile's max exceeds it by more
-        // than RESCALE_SLACK (always on the first tile with a valid row)
-        const bool move = mloc > m_run + RESCALE_SLACK;
-        if (__ballot(move)) {
-            const float m_new = move ? mloc : m_run;
-            const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
-        }
-        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
-        // ---- the V^T operands of the PV product are requested before the
-        // softmax arithmetic, so their LDS latency overlaps it
-        const int G16 = lane >> 4;
-        const int i16 = lane & 15;
-        v4bf vlo[2][G::NB], vhi[2][G::NB];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int row = 16 * kk + 4 * (G16 >> 1) + (i16 >> 2);
-#pragma unroll
-            for (int nb = 0; nb < G::NB; ++nb) {
-                const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
-                vlo[kk][nb] = lds_read_tr(tile, tile_slot(row) * ROWB + col * 2);
-                vhi[kk][nb] = lds_read_tr(tile, tile_slot(row + 8) * ROWB + col * 2);
+            for (int i = 0; i < RG; ++i) {
+                const int r = kp * RG + i;
+                if (!((tm >> (8 * (r / 4) + 4 * g + (r % 4))) & 1u)) so[i] = -__builtin_inff();
             }
         }
-        float psum = 0.0f;
+        float mloc = so[0];
+#pragma unroll
+        for (int i = 1; i < RG; ++i) mloc = fmaxf(mloc, so[i]);
+        mloc = xor32_max(mloc) * scale_log2;   // scale > 0 keeps the order
+        // the reference: exact (the tile's max over every wave's rows, one more
+        // exchange) on the workgroup's first tile, otherwise the running one,
+        // with P bounded by 2^RESCALE_SLACK unless a row exceeds it (then the
+        // workgroup's tiles are computed again with exact references)
+        if (exact) {
+            mbuf[wave][lane] = mloc;
+            lds_barrier();
+            float m_t = mbuf[hbl][lane];
+#pragma unroll
+            for (int src = 1; src < G::KSP; ++src) m_t = fmaxf(m_t, mbuf[src * HB + hbl][lane]);
+            const bool move = m_t > m_run + RESCALE_SLACK;
+            if (__ballot(move)) {
+                const float m_new = move ? m_t : m_run;
+                const bool had = m_run != -__builtin_inff();
+                const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                m_run = m_new;
+                if (__ballot(had)) {
+                    l_own *= alpha;
+#pragma unroll
+                    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+                }
+            }
+        } else {
+            bad = bad || __ballot(mloc > m_run + RESCALE_SLACK) != 0ull;
+        }
+        // P of this wave's rows, posted in bf16
+        {
+            const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+            float psum = 0.0f;
+#pragma unroll
+            for (int d = 0; d < RG / 2; ++d) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(so[2 * d], scale_log2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(so[2 * d + 1], scale_log2, -m_use));
+                psum += p0;
+                psum += p1;
+                pbuf[wave][d][lane] = (uint32_t)f2bf(p0) | ((uint32_t)f2bf(p1) << 16);
+            }
+            l_own += psum;
+        }
+        // ---- the V^T operands of the PV product (read transposed from the
+        // row-major tile, two reads per operand): with few value blocks they are
+        // requested before the exchange completes, so their LDS latency
+        // overlaps it
+        const int G16 = lane >> 4;
+        const int i16 = lane & 15;
+        constexpr bool PRE_V = G::NB <= 4;
+        v4bf vlo[2][G::NB], vhi[2][G::NB];
+        auto read_v = [&](int kk, int nb) {
+            const int row = 16 * kk + 4 * (G16 >> 1) + (i16 >> 2);
+            const int col = col0 + 32 * nb + 16 * (G16 & 1) + 4 * (i16 & 3);
+            vlo[kk][nb] = lds_read_tr(tile, tile_slot(row) * ROWB + col * 2);
+            vhi[kk][nb] = lds_read_tr(tile, tile_slot(row + 8) * ROWB + col * 2);
+        };
+        if constexpr (PRE_V) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int nb = 0; nb < G::NB; ++nb) read_v(kk, nb);
+        }
+        lds_barrier();
+        // ---- all of P^T as the PV B operand: register r of the tile is owned
+        // by wave r / RG, which posted it as dword (r % RG) / 2
         v8bf pk[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_use));
-            psum += p;
-            pk[r / 8][r % 8] = (__bf16)p;
+        for (int r2 = 0; r2 < 8; ++r2) {
+            const int r = 2 * r2;
+            const uint32_t w2 = pbuf[(r / RG) * HB + hbl][(r % RG) / 2][lane];
+            pk[r / 8][r % 8] = __builtin_bit_cast(__bf16, (uint16_t)(w2 & 0xFFFFu));
+            pk[r / 8][r % 8 + 1] = __builtin_bit_cast(__bf16, (uint16_t)(w2 >> 16));
         }
-        l_run += psum;
 
         // ---- O^T[this wave's columns x heads] += V^T . P^T over the tile's 32 rows
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int nb = 0; nb < G::NB; ++nb) {
+                if constexpr (!PRE_V) read_v(kk, nb);
                 const v4bf lo = vlo[kk][nb], hi = vhi[kk][nb];
                 const v8bf av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[kk], o[nb], 0, 0, 0);
@@ -420,6 +472,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     // software pipeline: the next tile of the group is in flight in registers
     // while the current one is computed from LDS
     auto tile_start = [&](int it) { return slot0 + (it * GR + grp) * TILE_ROWS; };
+    if (threadIdx.x == 0) s_bad = 0u;
     lds_barrier();                          // sidx visible
     v4u rA[KV8 ? 1 : G::GPT];   // native vectors: HIP's uint4 class defeats register promotion
     v4u r8A[KV8 ? F8PT : 1], rrA = v4u{0u, 0u, 0u, 0u};
@@ -478,12 +531,33 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
     if (iters > 0) { ISA_STORE_ANY() }
     if (iters > 1) { ISA_LOAD_ANY(tile_start(1)) }
     lds_barrier();
-    for (int it = 0; it < iters; ++it) {
-        compute_tile(tile_start(it));                        // in flight: tile it+1
-        if (it + 1 >= iters) break;
+    auto tile_loop = [&](bool exact_all) {
+        for (int it = 0; it < iters; ++it) {
+            compute_tile(tile_start(it), exact_all || it == 0);   // in flight: tile it+1
+            if (it + 1 >= iters) break;
+            lds_barrier();
+            ISA_STORE_ANY()
+            if (it + 2 < iters) { ISA_LOAD_ANY(tile_start(it + 2)) }
+            lds_barrier();
+        }
+    };
+    tile_loop(false);
+    // a row above the running reference by more than RESCALE_SLACK (possible
+    // when a group's first tile holds no valid row, or with very uneven
+    // scores): the whole split again, with an exact reference on every tile
+    if (bad) atomicOr(&s_bad, 1u);
+    lds_barrier();
+    if (s_bad) {
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[nb][r] = 0.0f;
+        m_run = -__builtin_inff();
+        l_own = 0.0f;
+        if (iters > 0) { ISA_LOAD_ANY(tile_start(0)) ISA_STORE_ANY() }
+        if (iters > 1) { ISA_LOAD_ANY(tile_start(1)) }
         lds_barrier();
-        ISA_STORE_ANY()
-        if (it + 2 < iters) { ISA_LOAD_ANY(tile_start(it + 2)) }
+        tile_loop(true);
         lds_barrier();
     }
 #undef ISA_LOAD_ANY
@@ -492,6 +566,17 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
 #undef ISA_STORE_TILE8
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
+
+    // the softmax sum of every head over the group's rows: both lane halves,
+    // then the head block's waves in kp order
+    float l_run;
+    {
+        mbuf[wave][lane] = xor32_sum(l_own);
+        lds_barrier();
+        l_run = mbuf[hbl][lane];
+#pragma unroll
+        for (int src = 1; src < G::KSP; ++src) l_run += mbuf[src * HB + hbl][lane];
+    }
 
     // With two groups, group g finishes value blocks [g*NB/2, (g+1)*NB/2): each
     // group hands the other the blocks it does not finish, with its (max, sum),
@@ -541,8 +626,8 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
         m_run = M;
     }
 
-    // softmax denominator of head j over all rows (the lane pair splits them)
-    const float l_tot = xor32_sum(l_run);
+    // softmax denominator of head j over all the workgroup's rows
+    const float l_tot = l_run;
 
     // o[nb] register r holds value column col0 + 32*nb + 8*(r/4) + 4*g + r%4 of head j
     if (splits == 1) {
