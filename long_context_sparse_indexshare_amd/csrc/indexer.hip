@@ -302,7 +302,53 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
         }
     }
 
-    const bool fast = false;
+    // Folded weights: when every head weight of the wave's queries is a power
+    // of two 2^e with e in [-2, 1] and every query byte q keeps 4 * 2^e * q
+    // inside int8, the A operands become q' = 4w * q (a left shift by e + 2),
+    // and w * ReLU(q . k) = ReLU(q' . k) / 4 (w > 0): the head sum is then an
+    // integer sum of ReLUs, converted to fp32 once and scaled by 1/4 (both
+    // exact steps after the one rounding of the conversion, which is the
+    // rounding of the exact score).  The check is per wave; a wave that fails
+    // it takes the fp32 epilogue.
+    bool lane_ok = true;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int t = tw + rb / 2;
+        if (t >= Tq) continue;                     // zero operands: nothing to scale
+        const uint32_t wb = __float_as_uint(w[((size_t)b * Tq + t) * H_I + 32 * (rb % 2) + j]);
+        // 0.25, 0.5, 1, 2 are exponents 125..128 with a zero mantissa
+        const uint32_t ex = (wb >> 23) & 0xFFu;
+        const bool pow2 = (wb & 0x807FFFFFu) == 0u && ex >= 125u && ex <= 128u;
+        const int sh = (int)ex - 125;
+        // a byte times 2^sh fits int8 iff its top sh + 1 bits are equal
+        const uint32_t m = (((0xFFu << (8 - sh)) & 0xFFu) * 0x01010101u) & (pow2 ? ~0u : 0u);
+        uint32_t bad = 0;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t x = (uint32_t)a[rb][ks][c];
+                bad |= (x ^ (x << 1)) & m;
+            }
+        lane_ok = lane_ok && pow2 && bad == 0u;
+    }
+    const bool fast = __ballot(!lane_ok) == 0ull;
+    if (fast) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int t = tw + rb / 2;
+            if (t >= Tq) continue;
+            const uint32_t wb = __float_as_uint(w[((size_t)b * Tq + t) * H_I + 32 * (rb % 2) + j]);
+            const int sh = (int)((wb >> 23) & 0xFFu) - 125;
+            const uint32_t keep = ((0xFFu << sh) & 0xFFu) * 0x01010101u;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    a[rb][ks][c] = (int)(((uint32_t)a[rb][ks][c] << sh) & keep);
+        }
+    }
+
     // as in the decode kernel: unconditional loads, dead lanes read the zero row
     const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_keys);
     auto load_keys = [&](int s0, v4i* bk) {

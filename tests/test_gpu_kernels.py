@@ -73,6 +73,46 @@ def test_indexer_full_int8_range_is_exact():
     assert_scores_bitwise(S, ref, "full-range")
 
 
+@pytest.mark.parametrize("Tq", [2, 70], ids=["decode", "prefill"])
+def test_indexer_full_int8_range_prefill_fallback_is_exact(Tq):
+    # bytes beyond [-64, 63] with weight 1/2 cannot be folded into the int8
+    # operand, so the prefill kernel takes its fp32 epilogue: still exact here
+    B, L_cap, H_I, D_I = 1, 1500, 64, 128
+    g = torch.Generator().manual_seed(19 + Tq)
+    qI = torch.randint(-128, 128, (B, Tq, H_I, D_I), generator=g, dtype=torch.int8)
+    kI = torch.randint(-128, 128, (B, L_cap, D_I), generator=g, dtype=torch.int8)
+    w = torch.ones(B, Tq, H_I) * 0.5
+    kv_len = torch.tensor([L_cap], dtype=torch.int32)
+    _print_case("indexer full range", Tq)
+    ref = oracle.indexer_scores(qI, w, kI, kv_len)
+    S = isa.isa_indexer_scores(dev(qI), dev(w), dev(kI), dev(kv_len))
+    assert_scores_bitwise(S, ref, f"full-range Tq={Tq}")
+
+
+@pytest.mark.parametrize("Tq", [3, 96], ids=["decode", "prefill"])
+def test_indexer_general_weights_within_fp32_bound(Tq):
+    # Weights that are not powers of two (and of either sign) make the head sum
+    # inexact in fp32.  Every product w*ReLU(dot) is rounded once and the H_I
+    # terms are added in fp32, so against the exactly rounded oracle score the
+    # error is at most (H_I + 2) * 2^-24 * sum_h |w_h| ReLU(dot_h), which is the
+    # oracle's score for the weights |w|.
+    B, L_cap, H_I, D_I = 2, 3000, 64, 128
+    g = torch.Generator().manual_seed(31 + Tq)
+    qI = synth.int8_uniform((B, Tq, H_I, D_I), g, "cpu")
+    kI = synth.int8_uniform((B, L_cap, D_I), g, "cpu")
+    w = torch.rand(B, Tq, H_I, generator=g) * 2.0 - 0.7
+    kv_len = torch.tensor([L_cap, 1777], dtype=torch.int32)
+    _print_case("indexer general weights", Tq)
+    ref = oracle.indexer_scores(qI, w, kI, kv_len).astype(np.float64)
+    mag = oracle.indexer_scores(qI, w.abs(), kI, kv_len).astype(np.float64)
+    S = host(isa.isa_indexer_scores(dev(qI), dev(w), dev(kI), dev(kv_len))).numpy().astype(np.float64)
+    vis = np.isfinite(ref)
+    assert np.array_equal(vis, np.isfinite(S))
+    bound = (H_I + 2) * 2.0 ** -24 * mag[vis] + 1e-30
+    err = np.abs(S[vis] - ref[vis])
+    assert np.all(err <= bound), f"max err/bound {float((err / bound).max()):.3g}"
+
+
 # -------------------------------------------------------------------- top-k ----
 
 def _topk_check(S, kv_len, k, name):
