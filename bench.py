@@ -759,7 +759,7 @@ def main():
     stages = {
         "indexer": (1, alg["ix_bytes"], "indexer_scores_kernel<64, 128>"),
         "topk": (1, alg["topk_read_bytes"],
-                 "topk_hist_kernel + topk_classify_kernel + topk_finish_kernel"),
+                 "topk_filter_kernel + topk_finish_kernel"),
         "attend": (wl.n_layers, alg["at_bytes_per_layer"],
                    "sparse_attend_kernel<1, 1, 576, 512, 2, false> + merge_splits_kernel (one layer)"),
     }

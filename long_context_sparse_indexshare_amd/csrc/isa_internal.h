@@ -124,14 +124,15 @@ constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bi
 constexpr int TOPK_WAVE_CHUNK = 256;
 constexpr int TOPK_MAX_M = 16;
 constexpr int TOPK_MAX_SUMMARY = 8192;      // summary keys per row at most (8 per filter thread)
+// Entry slots per filter chunk: one per position, so a chunk's run always fits.
+constexpr int TOPK_SLOT_CAP = TOPK_CHUNK;
 
 struct TopkLayout {
-    size_t alloc, zero_bytes;         // counters: [0, zero_bytes) is cleared per call
+    size_t zero_bytes;                // counters: [0, zero_bytes) is cleared per call
     size_t hist;                      // first-digit histograms (prefill select path)
-    size_t row_state, summary, runs, ent, total;
+    size_t summary, counts, ent, total;
     int rows, nchunks;                // filter chunks of TOPK_CHUNK positions per row
     int nwchunks, M;                  // wave chunks per row, summary keys per wave chunk
-    uint32_t cap;                     // entries per row in the entry buffer
     bool select;                      // one-workgroup-per-row select path (prefill)
 };
 TopkLayout topk_layout(int rows, int L_cap, int k);

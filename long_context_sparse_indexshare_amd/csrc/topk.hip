@@ -17,15 +17,16 @@
 //                scores of distinct visible positions, so at least k scores
 //                are >= L: the k-th largest is >= L), then keeps its chunk's
 //                scores >= L as one run of (key, position) entries in
-//                ascending position.  On random scores L sits a few percent
-//                below the k-th largest, so a row keeps little more than k
-//                entries.
-//   2. finish:   one workgroup per row finds the exact k-th key T and the
-//                position cut among keys equal to T by radix passes over the
-//                bits the candidates do not share, then writes the selected
-//                positions as the ordered stream compaction of the runs taken
-//                chunk by chunk.  If the entry buffer overflowed (a very flat
-//                score distribution) the row's scores are read again.
+//                ascending position, in slots of its own.  L lies within
+//                1/4096 of the summary's key range below its k-th largest
+//                key, so a row keeps little more than k entries.
+//   2. finish:   one workgroup per row holds the candidates in ascending
+//                position (in registers when the runs are short, else staged
+//                in LDS), finds the exact k-th key T and how many keys equal
+//                to T are taken (the lowest positions) by radix passes over
+//                the candidates' key range and a direct ranking of the cut
+//                bin, and writes every selected position straight to its
+//                place after one block scan of (above T, equal to T) counts.
 // With at least 256 rows of at most 262144 positions (a prefill chunk) a
 // first-digit histogram kernel and one workgroup per row
 // (topk_select_kernel) do the work instead.
@@ -39,8 +40,6 @@
 namespace isa {
 
 namespace {
-
-constexpr int CAND_MIN = 16384;
 
 __device__ __forceinline__ int visible_count(const int32_t* kv_len, int row, int Tq, int L_cap) {
     const int b = row / Tq;
@@ -220,11 +219,10 @@ constexpr int COL_MAX = 512;              // entries ranked directly for the exa
 // Summary, for calls whose indexer did not write it: wave w of workgroup c
 // covers positions c*1024 + w*256 + e*64 + lane (e < 4), wave chunk c*4 + w,
 // and writes that chunk's M largest keys; invisible positions take key 0.
-// Chunk 0 also zeroes the row's entry counter for the filter that follows.
 constexpr int SUM_THREADS = 256;
 __global__ __launch_bounds__(SUM_THREADS) void topk_summary_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int M,
-    int nwchunks, uint32_t* __restrict__ summary, uint32_t* __restrict__ alloc) {
+    int nwchunks, uint32_t* __restrict__ summary) {
     const int row = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -241,127 +239,91 @@ __global__ __launch_bounds__(SUM_THREADS) void topk_summary_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) key[e] = base + e * 64 + lane < n ? score_key(v[e]) : 0u;
     wave_top_m<4>(key, M, summary + ((size_t)row * nwchunks + blockIdx.x * 4 + wave) * M);
-    if (blockIdx.x == 0 && threadIdx.x == 0) alloc[row] = 0u;
 }
 
-// Threshold of a row from its summary (nsum keys, SUM_PER per thread, key 0
-// = none): with P the bits every summary key shares, two 8-bit digits of the
-// bits below them are fixed in turn, each the largest digit that still has
-// at least k summary keys at or above it; the threshold is P with those two
-// digits and zeros below (0 when the summary holds fewer than k keys).  The
-// summary keys are scores of distinct visible positions, so at least k of
-// the row's scores are >= the threshold.  Every thread returns the same value.
-constexpr int SUM_PER = TOPK_MAX_SUMMARY / TOPK_THREADS;
-struct ThresholdShared {
-    uint32_t red[3][TOPK_THREADS / 64];   // per wave: count, max, ~min
-    uint32_t h[256];
-    uint32_t res[2];                      // digit, count in the bins above it
-};
+// Radix bins over a key range [lo, hi]: bin = (key - lo) >> sh, with sh the
+// smallest shift that leaves at most RB_BINS bins.  Histograms are stored in
+// descending key order (LDS index RB_BINS - 1 - bin), so the keys at or above
+// a bin are counted by a prefix of the array.
+constexpr int RB_BITS = 12;
+constexpr int RB_BINS = 1 << RB_BITS;
 
-__device__ __forceinline__ uint32_t summary_threshold(const uint32_t (&u)[SUM_PER], uint32_t k,
-                                                      ThresholdShared& t) {
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t r = hi - lo;
+    const int bits = r ? 32 - __builtin_clz(r) : 0;
+    return bits > RB_BITS ? bits - RB_BITS : 0;
+}
+
+// Over a descending histogram h[RB_BINS] (NT threads, four bins each): the
+// first index whose running count reaches need, the count before it and the
+// count in it, returned to every thread (.x, .y, .z).  Two barriers.  The
+// running count must reach need.  tot (NT / 64 words) and res (3 words) are
+// rewritten: every thread must be past its reads of the previous call's
+// values, which a barrier between the calls ensures.
+template <int NT>
+__device__ __forceinline__ uint3 find_cut(const uint32_t* h, uint32_t need, uint32_t* tot,
+                                          uint32_t* res) {
+    static_assert(RB_BINS == 4 * NT, "four bins per thread");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    uint32_t cnt = 0, mx = 0, nmn = 0;                  // nmn = ~(minimum nonzero key)
+    const uint4 q = *reinterpret_cast<const uint4*>(h + 4 * threadIdx.x);
+    const uint32_t local = q.x + q.y + q.z + q.w;
+    const uint32_t inc = wave_inclusive_scan(local);
+    if (lane == 63) tot[wave] = inc;
+    __syncthreads();
+    uint32_t before = inc - local;
 #pragma unroll
-    for (int i = 0; i < SUM_PER; ++i) {
-        cnt += u[i] != 0u;
-        mx = max(mx, u[i]);
-        nmn = max(nmn, u[i] ? ~u[i] : 0u);
-    }
-    cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(cnt), 63);
-    mx = wave_max_u32(mx);
-    nmn = wave_max_u32(nmn);
-    if (lane == 0) {
-        t.red[0][wave] = cnt;
-        t.red[1][wave] = mx;
-        t.red[2][wave] = nmn;
+    for (int w = 0; w < NT / 64; ++w) before += w < wave ? tot[w] : 0u;
+    if (before < need && before + local >= need) {
+        const uint32_t hv[4] = {q.x, q.y, q.z, q.w};
+        uint32_t acc = before;
+        bool found = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!found && acc + hv[i] >= need) {
+                res[0] = 4u * threadIdx.x + i;
+                res[1] = acc;
+                res[2] = hv[i];
+                found = true;
+            }
+            acc += hv[i];
+        }
     }
     __syncthreads();
-    uint32_t C = 0, MX = 0, NMN = 0;
-#pragma unroll
-    for (int w = 0; w < TOPK_THREADS / 64; ++w) {
-        C += t.red[0][w];
-        MX = max(MX, t.red[1][w]);
-        NMN = max(NMN, t.red[2][w]);
-    }
-    if (C < k) return 0u;
-    const uint32_t MN = ~NMN;
-    const uint32_t x = MX ^ MN;
-    if (x == 0u) return MN;                             // every summary key equal
-    int hb = 31 - __builtin_clz(x);                     // highest bit the keys differ in
-    uint32_t fval = hb >= 31 ? 0u : (MX >> (hb + 1)) << (hb + 1);
-    uint32_t fmask = hb >= 31 ? 0u : ~((1u << (hb + 1)) - 1u);
-    uint32_t need = k;
-    for (int pass = 0; pass < 2 && hb >= 0; ++pass) {
-        const int nb = hb + 1 < 8 ? hb + 1 : 8;
-        const int sh = hb - nb + 1;
-        const uint32_t bm = (1u << nb) - 1u;
-        if (threadIdx.x < 256) t.h[threadIdx.x] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < SUM_PER; ++i)
-            if (u[i] && (u[i] & fmask) == fval) atomicAdd(&t.h[(u[i] >> sh) & bm], 1u);
-        __syncthreads();
-        if (wave == 0) {
-            // bins in descending order: lane l holds bins 255-4l .. 252-4l
-            uint32_t hv[4], local = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hv[j] = t.h[255 - 4 * lane - j];
-                local += hv[j];
-            }
-            const uint32_t inc = wave_inclusive_scan(local);
-            const uint32_t before = inc - local;
-            if (before < need && inc >= need) {
-                uint32_t acc = before;
-                int d = 0;
-                uint32_t above = 0;
-                bool found = false;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (!found && acc + hv[j] >= need) {
-                        d = 255 - 4 * lane - j;
-                        above = acc;
-                        found = true;
-                    }
-                    acc += hv[j];
-                }
-                t.res[0] = (uint32_t)d;
-                t.res[1] = above;
-            }
-        }
-        __syncthreads();
-        fval |= t.res[0] << sh;
-        fmask |= bm << sh;
-        need -= t.res[1];
-        hb = sh - 1;
-        __syncthreads();                                // t.h and t.res read before the next pass
-    }
-    return fval;
+    return make_uint3(res[0], res[1], res[2]);
 }
 
 // Filter: every workgroup (4096 positions of one row) derives the row's
 // threshold L from the summary and keeps its chunk's visible keys >= L as one
-// run of (key, position) entries in ascending position.  One atomic per
-// workgroup reserves the run in the row's entry buffer; the runs of a row
-// tile [0, total) with no gaps, and runs[row][chunk] records where each
-// chunk's run starts and how long it is.  Chunk 0 records L for the finish.
+// run of (key, position) entries in ascending position, in the chunk's own
+// entry slots (one per position of the chunk, so no atomics and no
+// overflow), and writes the run's length.  L: with the summary's keys in [MN, MX] histogrammed into RB_BINS
+// bins, the lower edge of the highest bin at which the summary keys at or
+// above it reach k.  The summary keys are scores of distinct visible
+// positions, so at least k scores are >= L, and L lies within one bin width
+// (1/4096 of the summary's key range) below the k-th largest summary key.  A
+// summary with fewer than k keys gives L = 0: every visible position.
+constexpr int SUM_PER = TOPK_MAX_SUMMARY / TOPK_THREADS;
+struct FilterShared {
+    uint32_t h[RB_BINS];
+    uint32_t red[3][TOPK_THREADS / 64];   // per wave: summary key count, max, ~min
+    uint32_t tot[TOPK_THREADS / 64];
+    uint32_t res[3];
+    uint32_t cnt[TOPK_PER_THREAD * (TOPK_THREADS / 64)];   // kept keys per (e, wave)
+};
+
 __global__ __launch_bounds__(TOPK_THREADS) void topk_filter_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ summary, int nsum, uint32_t* __restrict__ alloc,
-    uint32_t* __restrict__ row_L, uint2* __restrict__ runs, uint2* __restrict__ ent, uint32_t cap,
-    int nchunks_max) {
+    const uint32_t* __restrict__ summary, int nsum, uint32_t* __restrict__ counts,
+    uint2* __restrict__ ent, int nchunks_max) {
     const int row = blockIdx.y;
     const int c = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int NW = TOPK_THREADS / 64;
-    static_assert(TOPK_PER_THREAD * NW == 64, "one wave scans the (e, wave) counts");
-    __shared__ ThresholdShared ts;
-    __shared__ uint32_t sh_cnt[TOPK_PER_THREAD][NW];   // then the exclusive offsets
-    __shared__ uint32_t sh_base;
+    static_assert(TOPK_PER_THREAD * NW == 64, "one lane per (e, wave) count");
+    __shared__ FilterShared f;
 
     // this chunk's scores and the row's summary, requested before the row's
     // visible length arrives (they stay inside the row and its summary; the
@@ -386,8 +348,46 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_filter_kernel(
     if (n <= k) return;
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
     if (c >= nch) return;
-    const uint32_t L = summary_threshold(u, (uint32_t)k, ts);
-    if (c == 0 && tid == 0) row_L[row] = L;
+
+    *reinterpret_cast<uint4*>(&f.h[4 * tid]) = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t cnt = 0, mx = 0, nmn = 0;                  // nmn = ~(minimum nonzero key)
+#pragma unroll
+    for (int i = 0; i < SUM_PER; ++i) {
+        cnt += u[i] != 0u;
+        mx = max(mx, u[i]);
+        nmn = max(nmn, u[i] ? ~u[i] : 0u);
+    }
+    cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(cnt), 63);
+    mx = wave_max_u32(mx);
+    nmn = wave_max_u32(nmn);
+    if (lane == 0) {
+        f.red[0][wave] = cnt;
+        f.red[1][wave] = mx;
+        f.red[2][wave] = nmn;
+    }
+    __syncthreads();
+    uint32_t C = 0, MX = 0, NMN = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        C += f.red[0][w];
+        MX = max(MX, f.red[1][w]);
+        NMN = max(NMN, f.red[2][w]);
+    }
+    const uint32_t MN = ~NMN;
+    uint32_t L;
+    if (C < (uint32_t)k) {
+        L = 0u;
+    } else if (MX == MN) {
+        L = MN;
+    } else {
+        const int sh = range_shift(MN, MX);
+#pragma unroll
+        for (int i = 0; i < SUM_PER; ++i)
+            if (u[i]) atomicAdd(&f.h[RB_BINS - 1 - ((u[i] - MN) >> sh)], 1u);
+        __syncthreads();
+        const uint3 r = find_cut<TOPK_THREADS>(f.h, (uint32_t)k, f.tot, f.res);
+        L = MN + ((uint32_t)(RB_BINS - 1 - (int)r.x) << sh);
+    }
 
     uint32_t keys[TOPK_PER_THREAD];
     uint64_t kept[TOPK_PER_THREAD];
@@ -397,95 +397,273 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_filter_kernel(
         const bool valid = s < n;
         keys[e] = valid ? score_key(sc[e]) : 0u;
         kept[e] = __ballot(valid && keys[e] >= L);
-        if (lane == 0) sh_cnt[e][wave] = (uint32_t)__popcll(kept[e]);
+        if (lane == 0) f.cnt[e * NW + wave] = (uint32_t)__popcll(kept[e]);
     }
     __syncthreads();
-    if (wave == 0) {
-        // exclusive scan of the 64 (e, wave) counts in ascending-position order
-        const uint32_t v = sh_cnt[lane / NW][lane % NW];
-        const uint32_t inc = wave_inclusive_scan(v);
-        const uint32_t total = __builtin_amdgcn_readlane(inc, 63);
-        sh_cnt[lane / NW][lane % NW] = inc - v;
-        if (lane == 0) {
-            const uint32_t base = total ? atomicAdd(&alloc[row], total) : 0u;
-            sh_base = base;
-            runs[(size_t)row * nchunks_max + c] = make_uint2(base, total);
-        }
-    }
-    __syncthreads();
-    const uint32_t base = sh_base;
-    uint2* re = ent + (size_t)row * cap;
+    // every wave scans the 64 (e, wave) counts itself, in ascending-position order
+    const uint32_t v = f.cnt[lane];
+    const uint32_t inc = wave_inclusive_scan(v);
+    const uint32_t total = __builtin_amdgcn_readlane(inc, 63);
+    const uint32_t excl = inc - v;
+    uint2* re = ent + ((size_t)row * nchunks_max + c) * TOPK_SLOT_CAP;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int e = 0; e < TOPK_PER_THREAD; ++e) {
+        const uint32_t base = __builtin_amdgcn_readlane(excl, e * NW + wave);
         if ((kept[e] >> lane) & 1ull) {
-            const uint32_t slot = base + sh_cnt[e][wave] + (uint32_t)__popcll(kept[e] & below);
-            if (slot < cap) re[slot] = make_uint2(keys[e], (uint32_t)(start + e * TOPK_THREADS + tid));
+            const uint32_t slot = base + (uint32_t)__popcll(kept[e] & below);
+            if (slot < (uint32_t)TOPK_SLOT_CAP)
+                re[slot] = make_uint2(keys[e], (uint32_t)(start + e * TOPK_THREADS + tid));
         }
+    }
+    if (tid == 0) counts[(size_t)row * nchunks_max + c] = total;
+}
+
+// ---------------------------------------------------------------------------
+// Finish: one workgroup per row.  The candidates are the row's keys >= L (at
+// least k of them), listed chunk by chunk, each chunk's run in ascending
+// position.  Thread t takes chunk t / TPC (TPC = threads per chunk, a power of
+// two) and slots [8 * (t % TPC), +8) of it, so the candidates in thread order
+// are in ascending position; the common case (every run within the slots the
+// threads cover) keeps them in registers from a single round of loads.
+// Otherwise they are staged in LDS in that order, or, past the LDS, read from
+// the entry slots through the runs' starts.
+//   * the exact cut: radix passes over [min, max] of the candidates (4096
+//     bins each, the range of the cut bin next) find the bin holding the k-th
+//     largest key; once that bin holds at most COL_MAX candidates they are
+//     ranked directly under (key desc, position asc), giving the k-th key T
+//     and how many candidates equal to T are taken (needT, the lowest
+//     positions); a bin of width one is the key T itself;
+//   * the output: one block scan over the per-thread counts of candidates
+//     above T and equal to T gives each candidate the number selected before
+//     it (above before + min(equal before, needT)), so it is written straight
+//     to its place in the ascending-position list.
+constexpr int FIN_THREADS = 1024;
+constexpr int FIN_WAVES = FIN_THREADS / 64;
+constexpr int FIN_REG = 8;                          // candidates per thread per tile
+constexpr int FIN_TILE = FIN_THREADS * FIN_REG;
+static_assert(TOPK_MAX_CHUNKS <= FIN_THREADS / 2, "at least two threads per chunk");
+static_assert(FIN_TILE < 65536, "per-tile counts fit 16 bits");
+struct FinishShared {
+    uint32_t h[RB_BINS];
+    uint2 lent[ENT_LDS];                  // staged candidates, ascending position
+    uint2 col[COL_MAX];                   // candidates of the cut bin, ranked directly
+    uint32_t cstart[TOPK_MAX_CHUNKS + 1]; // chunk -> first candidate in position order
+    uint32_t red[3][FIN_WAVES];
+    uint32_t tot[FIN_WAVES];
+    uint32_t tot2[2][FIN_WAVES];
+    uint32_t res[3];
+    uint32_t cut[2];
+    uint32_t ncol;
+};
+
+// Candidate sources of the finish.  Each gives the thread's candidates of a
+// tile in ascending position (tile(T, fn): fn(j, valid, key, pos) for
+// j < FIN_REG) and visits all of its candidates in any order (each(fn)).
+struct SrcRegs {
+    const uint2 (&e)[FIN_REG];
+    uint32_t nvalid;                      // the first nvalid are candidates
+    __device__ int ntiles() const { return 1; }
+    template <class F> __device__ __forceinline__ void tile(int, F fn) const {
+#pragma unroll
+        for (int j = 0; j < FIN_REG; ++j) fn(j, (uint32_t)j < nvalid, e[j].x, e[j].y);
+    }
+    template <class F> __device__ __forceinline__ void each(F fn) const {
+#pragma unroll
+        for (int j = 0; j < FIN_REG; ++j)
+            if ((uint32_t)j < nvalid) fn(e[j].x, e[j].y);
+    }
+};
+struct SrcLds {
+    const uint2* lent;
+    uint32_t ntot;
+    __device__ int ntiles() const { return (int)((ntot + FIN_TILE - 1) / FIN_TILE); }
+    template <class F> __device__ __forceinline__ void tile(int T, F fn) const {
+        const uint32_t i0 = (uint32_t)T * FIN_TILE + threadIdx.x * FIN_REG;
+#pragma unroll
+        for (int j = 0; j < FIN_REG; ++j) {
+            const uint32_t i = i0 + j;
+            const uint2 v = i < ntot ? lent[i] : make_uint2(0u, 0u);
+            fn(j, i < ntot, v.x, v.y);
+        }
+    }
+    template <class F> __device__ __forceinline__ void each(F fn) const {
+        for (uint32_t i = threadIdx.x; i < ntot; i += FIN_THREADS) {
+            const uint2 v = lent[i];
+            fn(v.x, v.y);
+        }
+    }
+};
+struct SrcGlobal {                        // the entry buffer, through the chunk starts
+    const uint2* re;                      // the row's slots
+    const uint32_t* cstart;               // LDS, nch + 1 entries
+    int nch;
+    uint32_t ntot;
+    __device__ int ntiles() const { return (int)((ntot + FIN_TILE - 1) / FIN_TILE); }
+    __device__ __forceinline__ uint2 at(uint32_t i) const {
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cstart[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return re[(size_t)lo * TOPK_SLOT_CAP + (i - cstart[lo])];
+    }
+    template <class F> __device__ __forceinline__ void tile(int T, F fn) const {
+        const uint32_t i0 = (uint32_t)T * FIN_TILE + threadIdx.x * FIN_REG;
+#pragma unroll
+        for (int j = 0; j < FIN_REG; ++j) {
+            const uint32_t i = i0 + j;
+            const uint2 v = i < ntot ? at(i) : make_uint2(0u, 0u);
+            fn(j, i < ntot, v.x, v.y);
+        }
+    }
+    template <class F> __device__ __forceinline__ void each(F fn) const {
+        for (uint32_t i = threadIdx.x; i < ntot; i += FIN_THREADS) {
+            const uint2 v = at(i);
+            fn(v.x, v.y);
+        }
+    }
+};
+// The exact cut and the ordered output over one source.  On entry the
+// histogram is zero, ncol is 0, and every thread has passed a barrier after
+// which [MN, MX] is the candidates' key range.
+template <class Src>
+__device__ __forceinline__ void finish_select(const Src& src, int k, uint32_t MN, uint32_t MX,
+                                              FinishShared& f, int32_t* __restrict__ out) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    uint32_t lo = MN, hi = MX, need = (uint32_t)k;
+    uint32_t T, needT;
+    for (bool first = true;; first = false) {
+        if (lo == hi) {
+            T = lo;
+            needT = need;
+            break;
+        }
+        const int sh = range_shift(lo, hi);
+        if (!first) {
+            // every thread is past its reads of the previous pass's histogram
+            *reinterpret_cast<uint4*>(&f.h[4 * tid]) = make_uint4(0u, 0u, 0u, 0u);
+            if (tid == 0) f.ncol = 0u;
+            __syncthreads();
+        }
+        src.each([&](uint32_t key, uint32_t) {
+            if (key >= lo && key <= hi) atomicAdd(&f.h[RB_BINS - 1 - ((key - lo) >> sh)], 1u);
+        });
+        __syncthreads();
+        const uint3 r = find_cut<FIN_THREADS>(f.h, need, f.tot, f.res);
+        const uint32_t b = (uint32_t)(RB_BINS - 1) - r.x;
+        need -= r.y;                                    // >= 1 keys to take from bin b
+        const uint32_t blo = lo + (b << sh);
+        const uint32_t width = (1u << sh) - 1u;
+        const uint32_t bhi = hi - blo < width ? hi : blo + width;
+        if (sh == 0) {
+            T = blo;
+            needT = need;
+            break;
+        }
+        if (r.z <= (uint32_t)COL_MAX) {
+            src.each([&](uint32_t key, uint32_t pos) {
+                if (key >= blo && key <= bhi) {
+                    const uint32_t slot = atomicAdd(&f.ncol, 1u);
+                    if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key, pos);
+                }
+            });
+            __syncthreads();
+            const uint32_t m = r.z;
+            for (uint32_t t = tid; t < m; t += FIN_THREADS) {
+                const uint2 e = f.col[t];
+                uint32_t rank = 0, eq = 0;
+                for (uint32_t j = 0; j < m; ++j) {
+                    const uint2 o = f.col[j];
+                    rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
+                    eq += (uint32_t)(o.x == e.x) & (uint32_t)(o.y <= e.y);
+                }
+                if (rank == need - 1) {
+                    f.cut[0] = e.x;
+                    f.cut[1] = eq;                      // keys equal to T taken
+                }
+            }
+            __syncthreads();
+            T = f.cut[0];
+            needT = f.cut[1];
+            break;
+        }
+        lo = blo;
+        hi = bhi;
+    }
+
+    // ordered output: per tile, one block scan over (above T, equal to T)
+    // counts packed in 16-bit halves
+    uint32_t a_run = 0, e_run = 0;
+    const int nt = src.ntiles();
+    for (int t = 0; t < nt; ++t) {
+        uint32_t am = 0, em = 0;
+        uint32_t pos[FIN_REG];
+        src.tile(t, [&](int j, bool valid, uint32_t key, uint32_t p) {
+            pos[j] = p;
+            am |= (uint32_t)(valid && key > T) << j;
+            em |= (uint32_t)(valid && key == T) << j;
+        });
+        const uint32_t packed = ((uint32_t)__popc(am) << 16) | (uint32_t)__popc(em);
+        const uint32_t inc = wave_inclusive_scan(packed);
+        if (lane == 63) f.tot2[t & 1][wave] = inc;
+        __syncthreads();
+        uint32_t before = inc - packed, all = 0;
+#pragma unroll
+        for (int w = 0; w < FIN_WAVES; ++w) {
+            const uint32_t x = f.tot2[t & 1][w];
+            before += w < wave ? x : 0u;
+            all += x;
+        }
+        uint32_t a0 = a_run + (before >> 16), e0 = e_run + (before & 0xFFFFu);
+#pragma unroll
+        for (int j = 0; j < FIN_REG; ++j) {
+            if ((am >> j) & 1u) {
+                const uint32_t o = a0 + (e0 < needT ? e0 : needT);
+                if (o < (uint32_t)k) out[o] = (int32_t)pos[j];   // exactly k are selected
+                ++a0;
+            } else if ((em >> j) & 1u) {
+                if (e0 < needT && a0 + e0 < (uint32_t)k) out[a0 + e0] = (int32_t)pos[j];
+                ++e0;
+            }
+        }
+        a_run += all >> 16;
+        e_run += all & 0xFFFFu;
     }
 }
 
-// LDS of the finishing step.
-constexpr int FIN_THREADS = 1024;
-constexpr int FIN_WAVES = FIN_THREADS / 64;
-constexpr int FIN_SPEC = 6;               // entries per thread requested before the total is known
-constexpr int FIN_LDS_PER = ENT_LDS / FIN_THREADS;
-constexpr int FIN_PER = 8;                // entries per thread per compaction tile
-constexpr int FIN_DIGIT = 12;             // bits per radix pass of the exact cut
-constexpr int FIN_BINS = 1 << FIN_DIGIT;
-static_assert(TOPK_MAX_CHUNKS <= FIN_THREADS, "one chunk per thread");
-static_assert(ENT_LDS % FIN_THREADS == 0 && FIN_SPEC <= FIN_LDS_PER, "staging geometry");
-static_assert(FIN_BINS % FIN_THREADS == 0, "digit bins per thread");
-struct FinishShared {
-    uint32_t sh[FIN_BINS];                // digit histograms
-    uint32_t cbase[TOPK_MAX_CHUNKS];      // chunk -> first entry of its run
-    uint32_t cstart[TOPK_MAX_CHUNKS + 1]; // chunk -> index of its run's first entry in chunk order
-    uint2 lent[ENT_LDS];                  // the row's entries, in allocation order
-    uint2 col[COL_MAX];                   // entries of the cut's bin, ranked directly
-    uint32_t ncol;
-    uint32_t waves[FIN_WAVES];
-    uint32_t red[2][FIN_WAVES];
-    uint32_t res[4];
-};
-
-// Finish: one workgroup per row.  The candidates are the row's keys >= L (at
-// least k of them).  The exact k-th key T and the last selected position
-// s_cut among keys equal to T follow from radix passes over the bits the
-// candidates do not all share (12 bits per pass, highest first): each pass
-// histograms the candidates that match the bits fixed so far and fixes the
-// digit holding the k-th key; once that digit's bin holds at most COL_MAX
-// entries they are ranked directly under (key desc, position asc), and if
-// every key bit gets fixed first, two passes over the position bits of the
-// keys equal to T give s_cut.  The runs, taken in chunk order, list the
-// candidates in ascending position, so one flattened pass (eight consecutive
-// entries per thread, the bounds of the thread's run and of the next one read
-// together, and one block scan of the selected counts) writes the selected
-// positions in order.  If the entry buffer overflowed, the row's scores are
-// read instead of the entries.
 __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
-    const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
-    const uint32_t* __restrict__ alloc, const uint32_t* __restrict__ row_L,
-    const uint2* __restrict__ runs, const uint2* __restrict__ ent, uint32_t cap, int nchunks_max,
-    int32_t* __restrict__ idx) {
+    const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k, const uint32_t* __restrict__ counts,
+    const uint2* __restrict__ ent, int nchunks_max, int tpc_log2, int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const uint2* re = ent + (size_t)row * cap;
-    // every load of this phase is issued before any is used, and before the
-    // row's visible length arrives: the entry count, the threshold, the chunk
-    // table and the first entries (all inside the row's workspace; entries
-    // past the row's total, chunks past its length and the whole lot for a
-    // row that needs no selection are loaded but never used)
-    const uint32_t total = alloc[row];
-    const uint32_t Lr = row_L[row];
-    const uint2 rr_all = tid < nchunks_max ? runs[(size_t)row * nchunks_max + tid] : make_uint2(0u, 0u);
-    const uint32_t nspec = cap < (uint32_t)(FIN_SPEC * FIN_THREADS) ? cap : (uint32_t)(FIN_SPEC * FIN_THREADS);
-    uint2 v[FIN_SPEC];
+    __shared__ FinishShared f;
+    const int tpc = 1 << tpc_log2;
+    const int c = tid >> tpc_log2;
+    const int sub = tid & (tpc - 1);
+    const uint32_t slot0 = (uint32_t)sub * FIN_REG;
+    // slots a chunk's threads cover (within the chunk's slots)
+    const uint32_t cover = (uint32_t)tpc * FIN_REG < (uint32_t)TOPK_SLOT_CAP
+                               ? (uint32_t)tpc * FIN_REG : (uint32_t)TOPK_SLOT_CAP;
+    // every load is issued before the row's visible length arrives: the
+    // chunk's run length, the thread's slots (all inside the row's slots;
+    // those past the run are loaded but not used) and the threshold
+    const bool cin = c < nchunks_max;
+    const uint32_t cnt_raw = cin ? counts[(size_t)row * nchunks_max + c] : 0u;
+    const uint2* re = ent + (size_t)row * nchunks_max * TOPK_SLOT_CAP;
+    const uint2* ce = re + (size_t)(cin ? c : 0) * TOPK_SLOT_CAP;
+    uint2 e[FIN_REG];
 #pragma unroll
-    for (int u = 0; u < FIN_SPEC; ++u) {
-        const uint32_t i = u * FIN_THREADS + tid;
-        v[u] = i < nspec ? re[i] : make_uint2(0u, 0u);
+    for (int j = 0; j < FIN_REG; j += 2) {
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        if (cin && slot0 + j < cover) q = *reinterpret_cast<const uint4*>(ce + slot0 + j);
+        e[j] = make_uint2(q.x, q.y);
+        e[j + 1] = make_uint2(q.z, q.w);
     }
     const int n = visible_count(kv_len, row, Tq, L_cap);
     int32_t* out = idx + (size_t)row * k;
@@ -494,264 +672,85 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
         for (int j = tid; j < k; j += FIN_THREADS) out[j] = j < n ? j : -1;
         return;
     }
-    __shared__ FinishShared f;
     const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-    const float* rowp = S + (size_t)row * L_cap;
-    const uint2 rr = tid < nch ? rr_all : make_uint2(0u, 0u);
-    // 0: entries staged in LDS; 1: read from the entry buffer; 2: buffer overflowed, re-read S
-    const int mode = total <= (uint32_t)ENT_LDS ? 0 : (total <= cap ? 1 : 2);
-    if (mode == 0) {
+    const bool mine = c < nch;
+    const uint32_t cnt = mine ? cnt_raw : 0u;
+    const uint32_t capped = cnt;                        // a run never exceeds its slots
+    const uint32_t nvalid = capped > slot0 ? (capped - slot0 < (uint32_t)FIN_REG ? capped - slot0 : FIN_REG) : 0u;
+    const bool slow = mine && cnt > cover;              // a run longer than the slots loaded
+    uint32_t mx = 0u, nmn = 0u;
 #pragma unroll
-        for (int u = 0; u < FIN_SPEC; ++u) {
-            const uint32_t i = u * FIN_THREADS + tid;
-            if (i < total) f.lent[i] = v[u];
-        }
-        if (total > (uint32_t)(FIN_SPEC * FIN_THREADS)) {
-            uint2 w[FIN_LDS_PER - FIN_SPEC];
-#pragma unroll
-            for (int u = 0; u < FIN_LDS_PER - FIN_SPEC; ++u) {
-                const uint32_t i = (FIN_SPEC + u) * FIN_THREADS + tid;
-                w[u] = i < total ? re[i] : make_uint2(0u, 0u);
-            }
-#pragma unroll
-            for (int u = 0; u < FIN_LDS_PER - FIN_SPEC; ++u) {
-                const uint32_t i = (FIN_SPEC + u) * FIN_THREADS + tid;
-                if (i < total) f.lent[i] = w[u];
-            }
+    for (int j = 0; j < FIN_REG; ++j) {
+        if ((uint32_t)j < nvalid) {
+            mx = max(mx, e[j].x);
+            nmn = max(nmn, ~e[j].x);
         }
     }
-    if (tid < nch) f.cbase[tid] = rr.x;
-    uint32_t ntot;
-    const uint32_t cs = block_exclusive_scan<FIN_THREADS>(tid < nch ? rr.y : 0u, &ntot, f.waves);
-    if (tid < nch) f.cstart[tid] = cs;
-    if (tid == 0) f.cstart[nch] = ntot;
-    __syncthreads();
-
-    // f(key, pos) for every candidate
-    auto for_each_cand = [&](auto fn) {
-        if (mode == 0) {
-            for (uint32_t i = tid; i < total; i += FIN_THREADS) {
-                const uint2 e = f.lent[i];
-                fn(e.x, (int)e.y);
-            }
-        } else if (mode == 1) {
-            for (uint32_t i = tid; i < total; i += FIN_THREADS) {
-                const uint2 e = re[i];
-                fn(e.x, (int)e.y);
-            }
-        } else {
-            for (int s = tid; s < n; s += FIN_THREADS) {
-                const uint32_t key = score_key(rowp[s]);
-                if (key >= Lr) fn(key, s);
-            }
-        }
-    };
-
-    // largest and smallest candidate key: the bits above the highest bit
-    // they differ in are common to every candidate
-    uint32_t mx = 0u, nmn = 0u;
-    for_each_cand([&](uint32_t key, int) {
-        mx = max(mx, key);
-        nmn = max(nmn, ~key);
-    });
     mx = wave_max_u32(mx);
     nmn = wave_max_u32(nmn);
+    const uint64_t slow_w = __ballot(slow);
+    *reinterpret_cast<uint4*>(&f.h[4 * tid]) = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) f.ncol = 0u;
     if (lane == 0) {
         f.red[0][wave] = mx;
         f.red[1][wave] = nmn;
+        f.red[2][wave] = slow_w != 0ull;
     }
     __syncthreads();
-    uint32_t MX = 0u, NMN = 0u;
+    uint32_t MX = 0u, NMN = 0u, SLOW = 0u;
 #pragma unroll
     for (int w = 0; w < FIN_WAVES; ++w) {
         MX = max(MX, f.red[0][w]);
         NMN = max(NMN, f.red[1][w]);
+        SLOW |= f.red[2][w];
     }
-    const uint32_t diff = MX ^ ~NMN;
-    int hb = diff ? 31 - __builtin_clz(diff) : -1;      // bits above hb are fixed
-    uint32_t fval = hb >= 31 ? 0u : (hb < 0 ? MX : (MX >> (hb + 1)) << (hb + 1));
-    uint32_t fmask = hb >= 31 ? 0u : (hb < 0 ? ~0u : ~((1u << (hb + 1)) - 1u));
-    uint32_t need = (uint32_t)k;                        // keys still to take among the matches
-    uint32_t T = 0u;
-    int s_cut = -1;
-    bool ranked = false;
-    for (;;) {
-        if (hb < 0) break;
-        const int nb = hb + 1 < FIN_DIGIT ? hb + 1 : FIN_DIGIT;
-        const int sh = hb - nb + 1;
-        const uint32_t bm = (1u << nb) - 1u;
-        __syncthreads();                                // previous readers of f.sh are done
-        for (int i = tid; i < FIN_BINS; i += FIN_THREADS) f.sh[i] = 0u;
-        if (tid == 0) f.ncol = 0u;
-        __syncthreads();
-        for_each_cand([&](uint32_t key, int) {
-            if ((key & fmask) == fval) atomicAdd(&f.sh[(key >> sh) & bm], 1u);
-        });
-        __syncthreads();
-        const uint2 r = find_bin<FIN_BINS / FIN_THREADS, true, FIN_THREADS>(f.sh, need, f.waves,
-                                                                             f.res);
-        const uint32_t m = f.sh[r.x];                   // entries of the cut's bin
-        need -= r.y;                                    // >= 1 keys to take from that bin
-        fval |= r.x << sh;
-        fmask |= bm << sh;
-        hb = sh - 1;
-        if (m <= (uint32_t)COL_MAX) {
-            // rank the bin's entries directly under (key desc, position asc);
-            // the one of rank need-1 is the last selected
-            for_each_cand([&](uint32_t key, int s) {
-                if ((key & fmask) == fval) {
-                    const uint32_t slot = atomicAdd(&f.ncol, 1u);
-                    f.col[slot] = make_uint2(key, (uint32_t)s);
-                }
-            });
-            __syncthreads();
-            for (uint32_t t = tid; t < m; t += FIN_THREADS) {
-                const uint2 e = f.col[t];
-                uint32_t rank = 0;
-                for (uint32_t j = 0; j < m; ++j) {
-                    const uint2 o = f.col[j];
-                    rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
-                }
-                if (rank == need - 1) { f.res[2] = e.x; f.res[3] = e.y; }
-            }
-            __syncthreads();
-            T = f.res[2];
-            s_cut = (int)f.res[3];
-            ranked = true;
-            break;
-        }
-    }
-    if (!ranked) {
-        // every key bit is fixed: T = fval, and among the keys equal to T the
-        // need lowest positions are selected (position bits [20:10], then [9:0])
-        T = fval;
-        __syncthreads();
-        for (int i = tid; i < 2048; i += FIN_THREADS) f.sh[i] = 0u;
-        __syncthreads();
-        for_each_cand([&](uint32_t key, int s) {
-            if (key == T) atomicAdd(&f.sh[(uint32_t)s >> 10], 1u);
-        });
-        __syncthreads();
-        const uint2 q2 = find_bin<2048 / FIN_THREADS, false, FIN_THREADS>(f.sh, need, f.waves, f.res);
-        const uint32_t p2 = q2.x;
-        need -= q2.y;
-        for (int i = tid; i < 1024; i += FIN_THREADS) f.sh[i] = 0u;
-        __syncthreads();
-        for_each_cand([&](uint32_t key, int s) {
-            if (key == T && ((uint32_t)s >> 10) == p2) atomicAdd(&f.sh[(uint32_t)s & 1023u], 1u);
-        });
-        __syncthreads();
-        const uint32_t p3 = find_bin<1024 / FIN_THREADS, false, FIN_THREADS>(f.sh, need, f.waves, f.res).x;
-        s_cut = (int)((p2 << 10) | p3);
-    }
-    __syncthreads();
-
-    // selected: a key above T, or equal to T at a position <= s_cut.
-    // Evaluated without branches: the compiler lost the value of a
-    // conditionally written position on the short-circuit form of this test.
-    auto sel_of = [&](uint32_t key, uint32_t s) -> uint32_t {
-        return (uint32_t)(key > T) | ((uint32_t)(key == T) & (uint32_t)(s <= (uint32_t)s_cut));
-    };
-
-    if (mode == 2) {
-        // overflow: ordered stream compaction over the row's scores
-        constexpr int PER = 8;
-        constexpr int TILE = PER * FIN_THREADS;
-        uint32_t written = 0;
-        for (uint32_t t0 = 0; t0 < (uint32_t)n; t0 += TILE) {
-            const uint32_t v0 = t0 + (uint32_t)tid * PER;
-            uint32_t selmask = 0;
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const uint32_t vv = v0 + u;
-                const uint32_t in = vv < (uint32_t)n ? 1u : 0u;
-                const uint32_t key = in ? score_key(rowp[vv]) : 0u;
-                selmask |= (in & sel_of(key, vv)) << u;
-            }
-            uint32_t tile_total;
-            uint32_t o = written + block_exclusive_scan<FIN_THREADS>((uint32_t)__popc(selmask),
-                                                                     &tile_total, f.waves);
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                if ((selmask >> u) & 1u) {
-                    if (o < (uint32_t)k) out[o] = (int32_t)(v0 + u);   // exactly k are selected
-                    ++o;
-                }
-            }
-            written += tile_total;
-        }
+    if (!SLOW) {
+        finish_select(SrcRegs{e, nvalid}, k, ~NMN, MX, f, out);
         return;
     }
 
-    // ordered compaction over the runs in chunk order; the LDS and global
-    // entry sources are separate instantiations so that no load goes through
-    // a generic pointer
-    auto compact = [&](auto source) {
-        constexpr bool LDS = decltype(source)::value;
-        auto get = [&](uint32_t a) -> uint2 {
-            if constexpr (LDS) return f.lent[a];
-            else return re[a];
-        };
-        uint32_t written = 0;
-        for (uint32_t t0 = 0; t0 < ntot; t0 += FIN_PER * FIN_THREADS) {
-            const uint32_t i0 = t0 + (uint32_t)tid * FIN_PER;
-            // the run holding entry i0: the last chunk whose run starts at or
-            // before it (past the end: the last entry, whose result is masked)
-            const uint32_t a0 = i0 < ntot ? i0 : ntot - 1;
-            int lo = 0, hi = nch - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (f.cstart[mid] <= a0) lo = mid;
-                else hi = mid - 1;
-            }
-            const int c = lo;
-            // The thread's entries lie in run c and, past one boundary, in run
-            // c + 1: both runs' bounds are read at once (clamped indices; run
-            // c + 1 is only used when it exists).  The 64 lanes of a wave span
-            // several boundaries, so a per-entry walk would cost a dependent
-            // LDS read at nearly every step.  Entries past run c + 1 (runs
-            // shorter than FIN_PER entries) take the walk.
-            const int c1 = c + 1 < nch ? c + 1 : nch - 1;
-            const int c2 = c + 2 <= nch ? c + 2 : nch;
-            const uint32_t run_s = f.cstart[c], run_e = f.cstart[c + 1], run_b = f.cbase[c];
-            const uint32_t run_e2 = f.cstart[c2], run_b2 = f.cbase[c1];
-            uint32_t pos[FIN_PER];
-            uint32_t selmask = 0;
-#pragma unroll
-            for (int u = 0; u < FIN_PER; ++u) {
-                const uint32_t i = i0 + u;
-                const uint32_t a = i < ntot ? i : ntot - 1;
-                uint32_t slot;
-                if (a < run_e) {
-                    slot = run_b + (a - run_s);
-                } else if (a < run_e2) {
-                    slot = run_b2 + (a - run_e);
-                } else {
-                    int cc = c + 1;
-                    while (f.cstart[cc + 1] <= a) ++cc;
-                    slot = f.cbase[cc] + (a - f.cstart[cc]);
-                }
-                const uint2 e = get(slot);
-                pos[u] = e.y;
-                selmask |= ((uint32_t)(i < ntot) & sel_of(e.x, e.y)) << u;
-            }
-            uint32_t tile_total;
-            uint32_t o = written + block_exclusive_scan<FIN_THREADS>((uint32_t)__popc(selmask),
-                                                                     &tile_total, f.waves);
-#pragma unroll
-            for (int u = 0; u < FIN_PER; ++u) {
-                if ((selmask >> u) & 1u) {
-                    if (o < (uint32_t)k) out[o] = (int32_t)pos[u];   // exactly k are selected
-                    ++o;
-                }
-            }
-            written += tile_total;
+    // a run longer than the slots loaded: stage the candidates in LDS, or
+    // read them from the entry slots; first the key range over all of them
+    auto range_of = [&](const auto& src) {
+        uint32_t a = 0u, b = 0u;
+        src.each([&](uint32_t key, uint32_t) {
+            a = max(a, key);
+            b = max(b, ~key);
+        });
+        a = wave_max_u32(a);
+        b = wave_max_u32(b);
+        __syncthreads();                                // red is free again
+        if (lane == 0) {
+            f.red[0][wave] = a;
+            f.red[1][wave] = b;
         }
+        __syncthreads();
+        uint32_t A = 0u, B = 0u;
+#pragma unroll
+        for (int w = 0; w < FIN_WAVES; ++w) {
+            A = max(A, f.red[0][w]);
+            B = max(B, f.red[1][w]);
+        }
+        return make_uint2(~B, A);
     };
-    if (mode == 0) compact(std::true_type{});
-    else compact(std::false_type{});
+    uint32_t ntot;
+    const uint32_t cs = block_exclusive_scan<FIN_THREADS>(sub == 0 ? capped : 0u, &ntot, f.tot);
+    if (mine && sub == 0) f.cstart[c] = cs;
+    if (tid == 0) f.cstart[nch] = ntot;
+    __syncthreads();
+    if (ntot <= (uint32_t)ENT_LDS) {
+        if (mine)
+            for (uint32_t s = sub; s < capped; s += (uint32_t)tpc) f.lent[f.cstart[c] + s] = ce[s];
+        __syncthreads();
+        const SrcLds src{f.lent, ntot};
+        const uint2 r = range_of(src);
+        finish_select(src, k, r.x, r.y, f, out);
+    } else {
+        const SrcGlobal src{re, f.cstart, nch, ntot};
+        const uint2 r = range_of(src);
+        finish_select(src, k, r.x, r.y, f, out);
+    }
 }
-
 // ---------------------------------------------------------------------------
 // Many rows of at most SEL_MAX_N positions (prefill): after the histogram
 // kernel, one workgroup of 1024 threads per row does the rest in LDS.  With
@@ -994,14 +993,9 @@ TopkLayout topk_layout(int rows, int L_cap, int k) {
     // summary keys per wave chunk: about 2k per row in all
     int M = (int)((2LL * k * TOPK_WAVE_CHUNK + L_cap - 1) / L_cap);
     L.M = M < 1 ? 1 : (M > TOPK_MAX_M ? TOPK_MAX_M : M);
-    uint32_t cap = (uint32_t)(L_cap / 8);
-    const uint32_t lo = (uint32_t)(L_cap < 2 * CAND_MIN ? L_cap : 2 * CAND_MIN);
-    if (cap < lo) cap = lo;
-    cap = (cap + 63u) & ~63u;
-    L.cap = cap;
     // the one-workgroup-per-row select kernel needs only the first-digit
-    // histograms; the filter/finish pair needs the entry counters, the
-    // thresholds, the summary and its entry buffer
+    // histograms; the filter/finish pair needs the summary, the run lengths
+    // and the entry slots
     L.select = topk_uses_select(rows, L_cap);
     const bool sel = L.select;
     size_t off = 0;
@@ -1011,14 +1005,12 @@ TopkLayout topk_layout(int rows, int L_cap, int k) {
         return o;
     };
     // counters zeroed at the start of every call come first
-    L.alloc = take(sel ? 0 : (size_t)rows * 4);
     L.hist = take(sel ? (size_t)rows * TOPK_HIST_BINS * 4 : 0);
     L.zero_bytes = off;
     // scratch overwritten by every call
-    L.row_state = take(sel ? 0 : (size_t)rows * 4);
     L.summary = take(sel ? 0 : (size_t)rows * L.nwchunks * L.M * 4);
-    L.runs = take(sel ? 0 : (size_t)rows * L.nchunks * 8);
-    L.ent = take(sel ? 0 : (size_t)rows * cap * 8);
+    L.counts = take(sel ? 0 : (size_t)rows * L.nchunks * 4);
+    L.ent = take(sel ? 0 : (size_t)rows * L.nchunks * TOPK_SLOT_CAP * 8);
     L.total = off;
     return L;
 }
@@ -1056,24 +1048,19 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
                            kv_len, Tq, L_cap, k, hist, idx);
         return hipGetLastError();
     }
-    uint32_t* alloc = reinterpret_cast<uint32_t*>(base + L.alloc);
-    uint32_t* row_L = reinterpret_cast<uint32_t*>(base + L.row_state);
     uint32_t* summary = reinterpret_cast<uint32_t*>(base + L.summary);
-    uint2* runs = reinterpret_cast<uint2*>(base + L.runs);
+    uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
     uint2* ent = reinterpret_cast<uint2*>(base + L.ent);
-    if (!summary_ready) {
-        // the summary kernel also zeroes the entry counters
+    if (!summary_ready)
         hipLaunchKernelGGL(topk_summary_kernel, dim3(L.nwchunks / 4, rows), dim3(SUM_THREADS), 0,
-                           stream, S, kv_len, Tq, L_cap, L.M, L.nwchunks, summary, alloc);
-    } else if (!counters_clear) {
-        hipError_t e = launch_clear_u32(reinterpret_cast<uint32_t*>(base), L.zero_bytes / 4, stream);
-        if (e != hipSuccess) return e;
-    }
+                           stream, S, kv_len, Tq, L_cap, L.M, L.nwchunks, summary);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(L.nchunks, rows), dim3(TOPK_THREADS), 0, stream, S,
-                       kv_len, Tq, L_cap, k, summary, L.nwchunks * L.M, alloc, row_L, runs, ent,
-                       L.cap, L.nchunks);
-    hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(FIN_THREADS), 0, stream, S, kv_len,
-                       Tq, L_cap, k, alloc, row_L, runs, ent, L.cap, L.nchunks, idx);
+                       kv_len, Tq, L_cap, k, summary, L.nwchunks * L.M, counts, ent, L.nchunks);
+    // threads per chunk in the finish: FIN_THREADS over the chunk count rounded up to a power of two
+    int tpc_log2 = 10;
+    while ((1 << (10 - tpc_log2)) < L.nchunks) --tpc_log2;
+    hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(FIN_THREADS), 0, stream, kv_len, Tq,
+                       L_cap, k, counts, ent, L.nchunks, tpc_log2, idx);
     return hipGetLastError();
 }
 
