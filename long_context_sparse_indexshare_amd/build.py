@@ -31,11 +31,14 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
 ]
 
-# The indexer's int32 MFMA results feed VALU math at once: with the
-# accumulators in VGPRs no accumulator-to-VGPR moves are needed per element.
-# (The attention kernels need AGPRs for their accumulators and keep the default.)
+# MFMA results in VGPRs where they fit: the indexer's int32 results feed VALU
+# math at once, and the per-query attention kernel's loop-carried accumulators
+# otherwise travel between AGPRs and VGPRs on every tile (several hundred
+# accumulator moves per tile); kernels that need more than 256 registers still
+# place the rest in AGPRs.
 PER_FILE = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 NOISE = "is not a recognized feature for this target"

@@ -758,6 +758,338 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
         lse[(size_t)q * H + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -__builtin_inff();
 }
 
+// ---------------------------------------------------------------------------
+// Many queries (prefill): one workgroup of four waves per query, wave w
+// owning heads [16w, 16w + 16) whole.  Per tile of 32 gathered latent rows
+// (two LDS tile buffers, the next tile in flight in registers, one barrier
+// per tile):
+//   * S^T (32 rows x 16 heads) = C_rows . Q^T on v_mfma_f32_16x16x32_bf16
+//     over all D dims (the wave's Q^T stays in registers): two 16-row blocks,
+//     each summed in two accumulator chains;
+//   * the 16x16 accumulator layout gives lane (g, j) rows 4g..4g+3 and
+//     16+4g..16+4g+3 of head j, which are the B-operand rows of the next
+//     product when its contraction pairs lane group g with those rows: P^T
+//     feeds PV from registers, and a head's tile max takes two lane swaps;
+//   * O^T (DV columns x 16 heads) += V^T . P^T in DV/16 blocks, V^T read
+//     transposed (ds_read_b64_tr_b16) from the row-major tile in the same row
+//     order; rows sit in LDS in the order heads_slot gives, which keeps both
+//     read patterns free of bank conflicts.
+// No wave waits for another except at the tile barrier: there is no K split,
+// so no exchange of partial scores or of P, at the price of every wave
+// reading the whole tile from LDS.  The reference max of a head moves only
+// when its exact tile max exceeds it by more than RESCALE_SLACK.
+constexpr int HW_THREADS = 256;
+// LDS slot of tile row r in the per-query kernel: within each 16-row half,
+// rows 0-7 take the even slots and rows 8-15 the odd ones.  With a row stride
+// of 4 mod 8 words (64 banks), the QK operand reads (16 rows, one 16-byte
+// chunk) touch 16 distinct 4-bank groups for any 16 slots of a half, and each
+// 32-lane half of a transposing V^T read (8 rows, 32 bytes each: rows 0-7 or
+// 8-15 of a half) starts its rows on 8 distinct multiples of 8 banks.
+__device__ __forceinline__ int heads_slot(int r) {
+    return (r & 16) | ((r & 7) << 1) | ((r >> 3) & 1);
+}
+// log2 of the largest P the per-query kernel keeps without moving the reference
+constexpr float HW_HEADROOM = 64.0f;
+
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int DV, bool KV8>
+__global__ __launch_bounds__(HW_THREADS, 1) void attend_heads_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ C, const uint8_t* __restrict__ C8,
+    const uint8_t* __restrict__ Ce, const uint16_t* __restrict__ Cr,
+    const int32_t* __restrict__ idx, int Tq, int H, int L_cap, int k, float scale_log2, int nq,
+    int per_xcd, uint16_t* __restrict__ out, float* __restrict__ lse, PageMap pm) {
+    constexpr int ROWB = D * 2 + 16;              // one 16-byte pad per row (see heads_slot)
+    static_assert((ROWB / 4) % 8 == 4, "pad keeps row starts spread over the banks");
+    constexpr int CH = D * 2 / 16;                // 16-byte chunks per latent row
+    constexpr int CROWB = D * 2;
+    constexpr int TPR = HW_THREADS / TILE_ROWS;   // gather threads per tile row
+    constexpr int GPT = (CH + TPR - 1) / TPR;
+    constexpr int KS = D / 32;                    // k-steps of the QK product
+    constexpr int NBV = DV / 16;                  // 16-column value blocks
+    constexpr int TILE_BYTES = TILE_ROWS * ROWB;
+    constexpr int F8CH = DV / 16;                 // FP8 rows: code chunks,
+    constexpr int F8PT = F8CH / TPR;              //   per gather thread,
+    constexpr int RCH = (D - DV) * 2 / 16;        //   RoPE chunks
+    static_assert(D % 32 == 0 && DV % 16 == 0 && KS % 2 == 0, "k-steps and value blocks");
+    static_assert(!KV8 || (F8CH % TPR == 0 && RCH <= TPR), "FP8 gather geometry");
+
+    __shared__ __attribute__((aligned(16))) char tiles[2][TILE_BYTES];
+    __shared__ int sidx[MAX_SPLIT_SLOTS + TILE_ROWS];
+    __shared__ uint32_t tmask[MAX_SPLIT_SLOTS / TILE_ROWS + 2];   // valid rows per tile
+    __shared__ uint32_t s_bad;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int q = xcd_item(blockIdx.x, per_xcd);   // b * Tq + t
+    if (q >= nq) return;
+    const int b = q / Tq;
+    const int head = 16 * wave + j;
+    const bool head_ok = head < H;
+    const int32_t* qidx = idx + (size_t)q * k;
+    const size_t row0 = pm.table ? 0 : (size_t)b * L_cap;
+    const char* Cb = KV8 ? nullptr : reinterpret_cast<const char*>(C + row0 * D);
+    const char* C8b = KV8 ? reinterpret_cast<const char*>(C8 + row0 * DV) : nullptr;
+    const uint8_t* Ceb = KV8 ? Ce + row0 : nullptr;
+    const char* Crb = KV8 ? reinterpret_cast<const char*>(Cr + row0 * (D - DV)) : nullptr;
+
+    // the query's positions into LDS; invalid ones and the padding up to a
+    // whole tile become -1
+    const int ntiles = (k + TILE_ROWS - 1) / TILE_ROWS;
+    const int padded = ntiles * TILE_ROWS;
+    for (int i = tid; i < padded; i += HW_THREADS) {
+        int s = i < k ? qidx[i] : -1;
+        bool ok = s >= 0 && s < L_cap;
+        if (pm.table != nullptr && ok) {
+            // logical position -> row of the page pool; unallocated pages are skipped
+            const int page = pm.table[(size_t)b * pm.max_blocks + (s >> pm.shift)];
+            ok = page >= 0 && page < pm.n_pages;
+            s = (page << pm.shift) + (s & ((1 << pm.shift) - 1));
+        }
+        sidx[i] = ok ? s : -1;
+        // a wave covers 64 consecutive slots = two tiles: one bit per row
+        const uint64_t bits = __ballot(ok);
+        if (lane == 0) {
+            tmask[i / TILE_ROWS] = (uint32_t)bits;
+            tmask[i / TILE_ROWS + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+
+    // gather: thread (row tid / TPR, sub tid % TPR) owns chunks sub, sub + TPR,
+    // ... of one tile row; rows of -1 slots read a zero row
+    const uintptr_t zero_row = reinterpret_cast<uintptr_t>(g_zero_row);
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(Cb);
+    const uintptr_t c8base = reinterpret_cast<uintptr_t>(C8b);
+    const uintptr_t crbase = reinterpret_cast<uintptr_t>(Crb);
+    const int grow = tid / TPR;
+    const int gsub = tid % TPR;
+    const int lrow_off = heads_slot(grow) * ROWB;
+#define ISA_HW_LOAD(T)                                                                         \
+    {                                                                                          \
+        const int s_ = sidx[(T) * TILE_ROWS + grow];                                           \
+        if constexpr (KV8) {                                                                   \
+            const uintptr_t ca_ = (s_ >= 0 ? c8base + (size_t)s_ * DV : zero_row) + gsub * 16; \
+            _Pragma("unroll") for (int i_ = 0; i_ < F8PT; ++i_)                                \
+                r8[i_] = *(global_v4u_ptr)(ca_ + i_ * TPR * 16);                               \
+            if (gsub < RCH)                                                                    \
+                rr = *(global_v4u_ptr)((s_ >= 0 ? crbase + (size_t)s_ * ((D - DV) * 2)         \
+                                                : zero_row) + gsub * 16);                      \
+            se = s_ >= 0 ? (uint32_t)Ceb[s_] : 0u;                                             \
+        } else {                                                                               \
+            const uintptr_t ra_ = (s_ >= 0 ? cbase + (size_t)s_ * CROWB : zero_row) + gsub * 16; \
+            _Pragma("unroll") for (int i_ = 0; i_ < GPT; ++i_) {                               \
+                if (CH % TPR == 0 || gsub + TPR * i_ < CH)                                     \
+                    r[i_] = *(global_v4u_ptr)(ra_ + i_ * TPR * 16);                            \
+            }                                                                                  \
+        }                                                                                      \
+    }
+#define ISA_HW_STORE(BUF)                                                                      \
+    {                                                                                          \
+        char* const l_ = &tiles[BUF][0] + lrow_off;                                            \
+        if constexpr (KV8) {                                                                   \
+            const float sc_ = __uint_as_float(se << 23);                                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < F8PT; ++i_) {                              \
+                char* d_ = l_ + (gsub + i_ * TPR) * 32;                                        \
+                *reinterpret_cast<v4u*>(d_) = v4u{kv8_dequant_pair<false>(r8[i_][0], sc_),     \
+                                                  kv8_dequant_pair<true>(r8[i_][0], sc_),      \
+                                                  kv8_dequant_pair<false>(r8[i_][1], sc_),     \
+                                                  kv8_dequant_pair<true>(r8[i_][1], sc_)};     \
+                *reinterpret_cast<v4u*>(d_ + 16) = v4u{kv8_dequant_pair<false>(r8[i_][2], sc_), \
+                                                       kv8_dequant_pair<true>(r8[i_][2], sc_),  \
+                                                       kv8_dequant_pair<false>(r8[i_][3], sc_), \
+                                                       kv8_dequant_pair<true>(r8[i_][3], sc_)}; \
+            }                                                                                  \
+            if (gsub < RCH) *reinterpret_cast<v4u*>(l_ + DV * 2 + gsub * 16) = rr;             \
+        } else {                                                                               \
+            _Pragma("unroll") for (int i_ = 0; i_ < GPT; ++i_) {                               \
+                if (CH % TPR == 0 || gsub + TPR * i_ < CH)                                     \
+                    *reinterpret_cast<v4u*>(l_ + gsub * 16 + i_ * TPR * 16) = r[i_];           \
+            }                                                                                  \
+        }                                                                                      \
+    }
+
+    v4u r[KV8 ? 1 : GPT];        // native vectors: HIP's uint4 class defeats register promotion
+    v4u r8[KV8 ? F8PT : 1], rr = v4u{0u, 0u, 0u, 0u};
+    uint32_t se = 0;
+    if (tid == 0) s_bad = 0u;
+    lds_barrier();                                 // sidx and the flag visible
+    // the wave's Q^T: lane (g, j) holds dims 32ks + 8g .. +8 of head j; heads
+    // past H read head 0 (never stored)
+    v8bf qb[KS];
+    {
+        const uint16_t* qrow = Q + ((size_t)q * H + (head_ok ? head : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qb[ks] = __builtin_bit_cast(v8bf, *(global_v4u_ptr)(qrow + 32 * ks + 8 * g));
+    }
+
+    v4f o[NBV];
+    float m_run = -__builtin_inff();     // the head's reference max (log2 units), same in its 4 lanes
+    float l_own = 0.0f;                  // softmax sum over this lane's rows
+    bool bad = false;                    // a tile max above the reference by more than HW_HEADROOM
+    // One pass over the tiles.  EXACT = false: a head's reference is the max
+    // of its first tile with a valid row and stays there (P = 2^(s - ref) is
+    // kept in bf16, whose range holds any P up to 2^HW_HEADROOM); a tile
+    // whose max exceeds the reference by more than that sets `bad`, and the
+    // pass is run again with EXACT = true, which moves the reference to every
+    // tile's max that exceeds it and rescales the accumulators.
+    auto pass = [&](auto exact_tag) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) o[nb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        m_run = -__builtin_inff();
+        l_own = 0.0f;
+        if (ntiles > 0) ISA_HW_LOAD(0)
+        if (ntiles > 0) ISA_HW_STORE(0)
+        if (ntiles > 1) ISA_HW_LOAD(1)
+        lds_barrier();
+        for (int it = 0; it < ntiles; ++it) {
+            const char* tb = &tiles[it & 1][0];
+            // ---- S^T: rows j (block 0) and 16 + j (block 1), dims 32ks + 8g ..;
+            // the A operands of k-step pair p + 2 are requested before the
+            // products of pair p
+            const char* a0p = tb + heads_slot(j) * ROWB + 16 * g;
+            const char* a1p = tb + heads_slot(16 + j) * ROWB + 16 * g;
+            v4f s00 = {0.0f, 0.0f, 0.0f, 0.0f}, s01 = s00, s10 = s00, s11 = s00;
+            v8bf A[3][4];
+            auto lda = [&](int p, v8bf (&d)[4]) {
+                d[0] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(a0p + 128 * p));
+                d[1] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(a1p + 128 * p));
+                d[2] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(a0p + 128 * p + 64));
+                d[3] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(a1p + 128 * p + 64));
+            };
+            lda(0, A[0]);
+            lda(1, A[1]);
+#pragma unroll
+            for (int p = 0; p < KS / 2; ++p) {
+                if (p + 2 < KS / 2) lda(p + 2, A[(p + 2) % 3]);
+                __builtin_amdgcn_sched_barrier(0);
+                const v8bf(&c)[4] = A[p % 3];
+                s00 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[0], qb[2 * p], s00, 0, 0, 0);
+                s10 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[1], qb[2 * p], s10, 0, 0, 0);
+                s01 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[2], qb[2 * p + 1], s01, 0, 0, 0);
+                s11 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[3], qb[2 * p + 1], s11, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the V^T operands of the first value blocks, requested while the
+            // scores finish: lane (g, j) supplies row 4g + j/4 (and 16 + 4g +
+            // j/4), columns 16nb + 4(j%4) .. +4, and receives column 16nb + j of
+            // rows 4g .. 4g+3 (and 16 + 4g ..)
+            const char* vlo = tb + heads_slot(4 * g + (j >> 2)) * ROWB + 8 * (j & 3);
+            const char* vhi = tb + heads_slot(16 + 4 * g + (j >> 2)) * ROWB + 8 * (j & 3);
+            constexpr int VD = 4;                      // value blocks requested ahead
+            v4bf VL[VD], VH[VD];
+#pragma unroll
+            for (int nb = 0; nb < VD; ++nb) {
+                VL[nb] = lds_read_tr(vlo, 32 * nb);
+                VH[nb] = lds_read_tr(vhi, 32 * nb);
+            }
+            v4f s0 = s00 + s01, s1 = s10 + s11;        // rows 4g + i and 16 + 4g + i of head j
+            const uint32_t tm = tmask[it];
+            if (tm != 0xFFFFFFFFu) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (!((tm >> (4 * g + i)) & 1u)) s0[i] = -__builtin_inff();
+                    if (!((tm >> (16 + 4 * g + i)) & 1u)) s1[i] = -__builtin_inff();
+                }
+            }
+            float mloc = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                               fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+            mloc = xor32_max(xor16_max(mloc)) * scale_log2;   // scale > 0 keeps the order
+            if constexpr (EXACT) {
+                const bool move = mloc > m_run + RESCALE_SLACK;
+                if (__ballot(move)) {
+                    const float m_new = move ? mloc : m_run;
+                    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                    m_run = m_new;
+                    l_own *= alpha;
+#pragma unroll
+                    for (int nb = 0; nb < NBV; ++nb) o[nb] *= alpha;
+                }
+            } else {
+                // the accumulators are still zero when the reference is first set
+                if (m_run == -__builtin_inff()) m_run = mloc;
+                bad = bad || mloc > m_run + HW_HEADROOM;
+            }
+            const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+            v8bf pk;
+            float psum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[i], scale_log2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[i], scale_log2, -m_use));
+                psum += p0;
+                psum += p1;
+                pk[i] = (__bf16)p0;
+                pk[4 + i] = (__bf16)p1;
+            }
+            l_own += psum;
+            // ---- O^T += V^T . P^T, the operands of block nb + VD requested
+            // before the product of block nb
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const v4bf lo = VL[nb % VD], hi = VH[nb % VD];
+                if (nb + VD < NBV) {
+                    VL[nb % VD] = lds_read_tr(vlo, 32 * (nb + VD));
+                    VH[nb % VD] = lds_read_tr(vhi, 32 * (nb + VD));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const v8bf av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pk, o[nb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (it + 1 < ntiles) {
+                // the other buffer was last read in the previous iteration, which
+                // every wave finished before that iteration's barrier
+                ISA_HW_STORE((it + 1) & 1)
+                if (it + 2 < ntiles) ISA_HW_LOAD(it + 2)
+                lds_barrier();
+            }
+        }
+    };
+    pass(std::false_type{});
+    // a head whose scores rose far above its first tile's: every wave runs the
+    // query again with exact references (the tile barriers need all of them)
+    if (bad) atomicOr(&s_bad, 1u);
+    lds_barrier();
+    if (s_bad) {
+        lds_barrier();                 // every wave has read the flag and left the tiles
+        pass(std::true_type{});
+    }
+#undef ISA_HW_LOAD
+#undef ISA_HW_STORE
+
+    // the softmax sum of head j over all rows: the four lane groups
+    const float l_tot = xor32_sum(xor16_sum(l_own));
+    if (!head_ok) return;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    // o[nb] lane (g, j) element i: column 16nb + 4g + i of head j
+    uint16_t* orow = out + ((size_t)q * H + head) * DV + 4 * g;
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        ushort4 v;
+        v.x = f2bf(o[nb][0] * inv);
+        v.y = f2bf(o[nb][1] * inv);
+        v.z = f2bf(o[nb][2] * inv);
+        v.w = f2bf(o[nb][3] * inv);
+        *reinterpret_cast<ushort4*>(orow + 16 * nb) = v;
+    }
+    if (lse && g == 0)
+        lse[(size_t)q * H + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * LN2 : -__builtin_inff();
+}
+
 // The latent cache: bf16 rows (C), or FP8 codes, exponents and bf16 RoPE
 // slices (C8, Ce, Cr).
 struct KvSrc {
@@ -850,6 +1182,15 @@ hipError_t dispatch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int 
                            float* lse, void* partials, hipStream_t stream, PageMap pm) {
     const AttendPlan plan = attend_plan(B, Tq, H, D, D_v, k);
     if (D == 576 && D_v == 512) {
+        if (plan.head_blocks == 2 && plan.splits == 1 && k <= MAX_SPLIT_SLOTS) {
+            // many queries: one four-wave workgroup per query, 16 heads per wave
+            const int nq = B * Tq;
+            const int per_xcd = (nq + 7) / 8;
+            hipLaunchKernelGGL((attend_heads_kernel<576, 512, KV8>), dim3(8 * per_xcd),
+                               dim3(HW_THREADS), 0, stream, Q, kv.C, kv.C8, kv.Ce, kv.Cr, idx, Tq,
+                               H, L_cap, k, sm_scale * LOG2E, nq, per_xcd, out, lse, pm);
+            return hipGetLastError();
+        }
         if (plan.head_blocks == 2)
             return launch_attend<2, 1, 576, 512, 1, KV8>(Q, kv, idx, B, Tq, H, L_cap, k, sm_scale,
                                                          out, lse, partials, stream, pm);

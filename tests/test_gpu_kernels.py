@@ -296,6 +296,21 @@ def test_attend_576_many_queries():
     _attend_case(2, 130, 64, 576, 512, 9000, 128, idx, seed=13, name="576 wide")
 
 
+def test_attend_576_many_queries_ragged_k():
+    # the per-query kernel over a k that is not a whole number of tiles, with
+    # sets of every fill, an empty set and invalid slots mid-tile
+    r = np.random.default_rng(16)
+    B, Tq, L_cap, k = 1, 260, 12000, 700
+    idx = np.full((B, Tq, k), -1, dtype=np.int64)
+    for t in range(Tq):
+        m = int(r.integers(0, k + 1)) if t % 3 else k
+        idx[0, t, :m] = np.sort(r.choice(L_cap, size=m, replace=False))
+    idx[0, 7, :] = -1
+    idx[0, 9, 33] = -5
+    idx[0, 9, 34] = L_cap
+    _attend_case(B, Tq, 64, 576, 512, L_cap, k, idx, seed=17, name="576 wide ragged")
+
+
 def test_attend_576_unsplit_two_groups():
     # 160 queries: the 32-head, two-group variant with enough workgroups that
     # the k slots are not split (each group writes its half of the columns)
