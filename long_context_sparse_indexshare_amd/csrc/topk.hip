@@ -385,8 +385,28 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_filter_kernel(
         for (int i = 0; i < SUM_PER; ++i)
             if (u[i]) atomicAdd(&f.h[RB_BINS - 1 - ((u[i] - MN) >> sh)], 1u);
         __syncthreads();
-        const uint3 r = find_cut<TOPK_THREADS>(f.h, (uint32_t)k, f.tot, f.res);
-        L = MN + ((uint32_t)(RB_BINS - 1 - (int)r.x) << sh);
+        if (wave == 0) {
+            // one wave finds the bin (one barrier instead of a block scan's
+            // two): lane l sums bins [64l, 64l + 64), then the crossing
+            // lane's 64 bins one per lane
+            uint32_t local = 0;
+            const uint4* hb = reinterpret_cast<const uint4*>(f.h) + 16 * lane;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint4 x = hb[q];
+                local += x.x + x.y + x.z + x.w;
+            }
+            const uint32_t need = (uint32_t)k;
+            const uint32_t inc = wave_inclusive_scan(local);
+            const int cl = (int)__builtin_ctzll(__ballot(inc >= need && inc - local < need));
+            const uint32_t base = __builtin_amdgcn_readlane(inc - local, cl);
+            const uint32_t cb = f.h[64 * cl + lane];
+            const uint32_t inc2 = base + wave_inclusive_scan(cb);
+            const int bl = (int)__builtin_ctzll(__ballot(inc2 >= need && inc2 - cb < need));
+            if (lane == 0) f.res[0] = MN + ((uint32_t)(RB_BINS - 1 - (64 * cl + bl)) << sh);
+        }
+        __syncthreads();
+        L = f.res[0];
     }
 
     uint32_t keys[TOPK_PER_THREAD];
