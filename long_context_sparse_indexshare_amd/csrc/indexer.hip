@@ -258,7 +258,7 @@ constexpr int PF_MIN_TQ = 2;              // from this many queries per sequence
 constexpr int PF_TARGET_WGS = 1024;       // key splits aim at this many workgroups
 
 template <int D_I>
-__global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
+__global__ __launch_bounds__(IX_THREADS, 2) void indexer_prefill_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
     const int32_t* __restrict__ kv_len, int Tq, int L_cap, int chunk, float* __restrict__ S,
     uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm) {
@@ -277,9 +277,12 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
     const int s_hi = min(s_lo + chunk, L_cap);
     const int len = clamp_len(kv_len[b], L_cap);
 
-    // A operands: block rb holds heads 32*(rb%2) .. +32 of query tw + rb/2
+    // A operands: block rb holds heads 32*(rb%2) .. +32 of query tw + rb/2.
+    // The head weights of the wave's queries sit in LDS (read only by the
+    // fp32 epilogue; the wave writes and reads its own rows, in order), which
+    // keeps 64 registers per lane free for occupancy.
+    __shared__ __attribute__((aligned(16))) float sw[PF_QPW * H_I];
     v4i a[RB][KS];
-    float wr[RB][16];
     int pos[PF_QPWAVE];
 #pragma unroll
     for (int q = 0; q < PF_QPWAVE; ++q) pos[q] = tw + q < Tq ? len - Tq + tw + q : -1;
@@ -295,12 +298,11 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
                                  32 * ks + 16 * g)
                            : v4i{0, 0, 0, 0};
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int h = 32 * (rb % 2) + 8 * (r / 4) + 4 * g + (r % 4);
-            wr[rb][r] = tv ? w[((size_t)b * Tq + t) * H_I + h] : 0.0f;
-        }
     }
+    float* const wq = sw + wave * PF_QPWAVE * H_I;     // this wave's queries' weights
+#pragma unroll
+    for (int q = 0; q < PF_QPWAVE; ++q)
+        wq[q * H_I + lane] = tw + q < Tq ? w[((size_t)b * Tq + tw + q) * H_I + lane] : 0.0f;
 
     // Folded weights: when every head weight of the wave's queries is a power
     // of two 2^e with e in [-2, 1] and every query byte q keeps 4 * 2^e * q
@@ -364,54 +366,62 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
 
     auto run = [&](auto fast_tag) {
         constexpr bool FAST = decltype(fast_tag)::value;
-        // scores of the 32 keys s0 .. s0+31 against both queries, from keys in bk
-        auto step = [&](int s0, const v4i* bk) {
-            const int s = s0 + j;
-            float sum[PF_QPWAVE];
+        // the 16 products of one 32-key block (four accumulator chains, one per
+        // row block, interleaved)
+        auto products = [&](const v4i* bk, v16i (&acc)[RB]) {
 #pragma unroll
-            for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = 0.0f;
-            if (s0 <= pos_max) {
-                if constexpr (FAST) {
-                    // integer ReLU sums; pairs of ReLUs go into one three-input add
-                    int tot[PF_QPWAVE];
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                    for (int q = 0; q < PF_QPWAVE; ++q) tot[q] = 0;
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        v16i acc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc[rb], 0, 0, 0);
+        };
+        // the two queries' scores of a block from its products (lane j: key j)
+        auto scores = [&](const v16i (&acc)[RB], float (&sum)[PF_QPWAVE]) {
+            if constexpr (FAST) {
+                // integer ReLU sums; pairs of ReLUs go into one three-input add
+                int tot[PF_QPWAVE];
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks)
-                            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc, 0, 0, 0);
+                for (int q = 0; q < PF_QPWAVE; ++q) tot[q] = 0;
 #pragma unroll
-                        for (int r = 0; r < 16; r += 2)
-                            tot[rb / 2] += max(acc[r], 0) + max(acc[r + 1], 0);
-                    }
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                    for (int q = 0; q < PF_QPWAVE; ++q) {
-                        // the other half of the heads sits in lane j ^ 32
-                        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)tot[q],
-                                                                        (uint32_t)tot[q], false, false);
-                        sum[q] = (float)((int)r[0] + (int)r[1]) * 0.25f;
-                    }
-                } else {
+                    for (int r = 0; r < 16; r += 2)
+                        tot[rb / 2] += max(acc[rb][r], 0) + max(acc[rb][r + 1], 0);
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        v16i acc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                for (int q = 0; q < PF_QPWAVE; ++q) {
+                    // the other half of the heads sits in lane j ^ 32
+                    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)tot[q],
+                                                                    (uint32_t)tot[q], false, false);
+                    sum[q] = (float)((int)r[0] + (int)r[1]) * 0.25f;
+                }
+            } else {
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks)
-                            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb][ks], bk[ks], acc, 0, 0, 0);
+                for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = 0.0f;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int dot = acc[r];
-                            sum[rb / 2] += wr[rb][r] * (float)(dot > 0 ? dot : 0);
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        // heads 32*(rb%2) + 8*r4 + 4g .. +4 of query rb/2
+                        const v4f wv = *reinterpret_cast<const v4f*>(
+                            wq + (rb / 2) * H_I + 32 * (rb % 2) + 8 * r4 + 4 * g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int dot = acc[rb][4 * r4 + i];
+                            sum[rb / 2] += wv[i] * (float)(dot > 0 ? dot : 0);
                         }
                     }
 #pragma unroll
-                    for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = xor32_sum(sum[q]);
-                }
+                for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = xor32_sum(sum[q]);
             }
+        };
+        // the block's scores, -inf past each query's position or on an
+        // unallocated page (sum is not read for a block no query of the wave sees)
+        auto store = [&](int s0, const float (&sum)[PF_QPWAVE]) {
+            const int s = s0 + j;
             if (g == 0 && s < L_cap) {
-                // positions on an unallocated page score -inf
                 const bool page_ok = pm.table == nullptr || key_block_row(pm, b, L_cap, s0) >= 0;
 #pragma unroll
                 for (int q = 0; q < PF_QPWAVE; ++q) {
@@ -421,16 +431,55 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_prefill_kernel(
                 }
             }
         };
+        // one block's products issued together with another block's scores:
+        // the MFMA chains run under the VALU work (one MFMA per six VALU ops)
+        auto overlapped = [&](const v4i* bk, v16i (&acc_next)[RB], const v16i (&acc)[RB],
+                              float (&sum)[PF_QPWAVE]) {
+            products(bk, acc_next);
+            scores(acc, sum);
+#pragma unroll
+            for (int i = 0; i < RB * KS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+        };
 
-        // two key buffers in turn: the next block is in flight while one is used
-        v4i k0[KS], k1[KS];
-        load_keys(s_lo, k0);
-        for (int s0 = s_lo; s0 < s_hi; s0 += 64) {
-            load_keys(s0 + 32, k1);       // load_keys returns zeros past s_hi
-            step(s0, k0);
-            load_keys(s0 + 64, k0);
-            if (s0 + 32 < s_hi) step(s0 + 32, k1);
+        // Software pipeline over the 32-key blocks the wave's queries see
+        // ([s_lo, s_end)): block i's products are issued with block i-1's
+        // scores (two accumulator sets) while block i+1's keys are in flight
+        // (two key buffers); the blocks past them only get -inf.
+        const int s_vis = pos_max >= s_lo ? ((pos_max - s_lo) / 32 + 1) * 32 + s_lo : s_lo;
+        const int s_end = min(s_hi, s_vis);
+        v4i kb0[KS], kb1[KS];
+        v16i acc0[RB], acc1[RB];
+        float sum[PF_QPWAVE];
+        if (s_lo < s_end) {
+            load_keys(s_lo, kb0);
+            load_keys(s_lo + 32, kb1);
+            products(kb0, acc0);
+            for (int s0 = s_lo;; s0 += 64) {
+                // block s0 (acc0, issued) | block s0 + 32 (kb1) | block s0 + 64 (into kb0)
+                load_keys(s0 + 64, kb0);
+                if (s0 + 32 >= s_end) {
+                    scores(acc0, sum);
+                    store(s0, sum);
+                    break;
+                }
+                overlapped(kb1, acc1, acc0, sum);
+                store(s0, sum);
+                load_keys(s0 + 96, kb1);
+                if (s0 + 64 >= s_end) {
+                    scores(acc1, sum);
+                    store(s0 + 32, sum);
+                    break;
+                }
+                overlapped(kb0, acc0, acc1, sum);
+                store(s0 + 32, sum);
+            }
         }
+#pragma unroll
+        for (int q = 0; q < PF_QPWAVE; ++q) sum[q] = 0.0f;
+        for (int s0 = s_end; s0 < s_hi; s0 += 32) store(s0, sum);
     };
     if (fast) run(std::true_type{});
     else run(std::false_type{});
