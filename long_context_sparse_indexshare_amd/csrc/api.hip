@@ -419,7 +419,10 @@ static isa_status launch_group(const isa_group_args* a, const isa::PageMap& pm,
     // with one query per sequence the indexer also writes the top-k summary
     const isa::TopkLayout tl = isa::topk_layout(a->B * a->Tq, a->L_cap, a->k);
     const bool fused_summary = L.need_index && !tl.select && isa::indexer_writes_summary(a->Tq, a->H_I);
-    uint32_t* summary = fused_summary ? reinterpret_cast<uint32_t*>(topk_ws + tl.summary) : nullptr;
+    const isa::SummaryOut summary =
+        fused_summary ? isa::SummaryOut{reinterpret_cast<uint32_t*>(topk_ws + tl.summary),
+                                        reinterpret_cast<uint8_t*>(topk_ws + tl.codes), tl.M}
+                      : isa::SummaryOut{nullptr, nullptr, 0};
     // each index set: the indexer grid also zeroes the top-k counters
     // (histograms, entry counts), then the top-k runs
     auto index = [&](int l) -> isa_status {
@@ -427,7 +430,7 @@ static isa_status launch_group(const isa_group_args* a, const isa::PageMap& pm,
                                                              a->B, a->Tq, a->H_I, a->D_I, a->L_cap,
                                                              S, reinterpret_cast<uint32_t*>(topk_ws),
                                                              (uint32_t)(L.topk_zero_bytes / 4),
-                                                             stream, pm, summary, tl.M),
+                                                             stream, pm, summary),
                                   "group: indexer launch");
         if (st != ISA_OK) return st;
         return check_hip(isa::launch_topk_select(S, a->kv_len, a->B, a->Tq, a->L_cap, a->k, a->idx,

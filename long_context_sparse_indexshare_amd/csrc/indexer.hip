@@ -63,8 +63,7 @@ template <int H_I, int D_I>
 __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     const int8_t* __restrict__ qI, const float* __restrict__ w, const int8_t* __restrict__ kI,
     const int32_t* __restrict__ kv_len, int Tq, int L_cap, float* __restrict__ S,
-    uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm, uint32_t* __restrict__ summary,
-    int M) {
+    uint32_t* __restrict__ zero, uint32_t zero_n, PageMap pm, SummaryOut summary) {
     grid_clear(zero, zero_n);
     constexpr int QPW = IX_ROWS / H_I;             // queries per workgroup
     constexpr int KS = D_I / 32;                   // MFMA k-steps over the indexer dim
@@ -202,15 +201,21 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     }
     if constexpr (NQL == 1) {
         // the top-k summary of this wave's 256 keys (wave chunk 4 * blockIdx.x
-        // + wave of the query's row): their M largest score keys, invisible
-        // positions counting as none
-        if (summary != nullptr) {
-            uint32_t key[IX_STEPS];
+        // + wave of the query's row; step st of lane j is position code
+        // 32 * st + j): their M largest score keys with their codes,
+        // invisible positions counting as none
+        if (summary.keys != nullptr) {
+            static_assert(IX_STEPS * 32 == TOPK_WAVE_CHUNK && IX_KEYS_PER_STEP == 128,
+                          "a wave's keys are one summary wave chunk");
+            uint32_t key[IX_STEPS], code[IX_STEPS];
 #pragma unroll
-            for (int st = 0; st < IX_STEPS; ++st) key[st] = (visb >> st) & 1u ? score_key(res[st]) : 0u;
-            const size_t row = (size_t)b * Tq + t0;
-            wave_top_m<IX_STEPS>(key, M,
-                                 summary + (row * (gridDim.x * 4) + blockIdx.x * 4 + wave) * M);
+            for (int st = 0; st < IX_STEPS; ++st) {
+                key[st] = (visb >> st) & 1u ? score_key(res[st]) : 0u;
+                code[st] = (uint32_t)(32 * st + j);
+            }
+            const int M = summary.M;
+            const size_t off = (((size_t)b * Tq + t0) * (gridDim.x * 4) + blockIdx.x * 4 + wave) * M;
+            wave_top_m<IX_STEPS>(key, code, M, summary.keys + off, summary.codes + off);
         }
         // the workgroup's IX_KEYS_PER_WG scores are contiguous in S: stage them
         // in LDS in key order, then one 16-byte streaming store per thread
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(IX_THREADS, 2) void indexer_prefill_kernel(
 template <int H_I, int D_I>
 hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const int32_t* kv_len,
                      int B, int Tq, int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                     hipStream_t stream, PageMap pm, uint32_t* summary, int M) {
+                     hipStream_t stream, PageMap pm, SummaryOut summary) {
     constexpr int QPW = IX_ROWS / H_I;
     dim3 grid((L_cap + IX_KEYS_PER_WG - 1) / IX_KEYS_PER_WG, (Tq + QPW - 1) / QPW, B);
     if constexpr (H_I == 64) {
@@ -508,9 +513,9 @@ hipError_t launch_ix(const int8_t* qI, const float* w, const int8_t* kI, const i
             return hipGetLastError();
         }
     }
-    if (QPW != 1) summary = nullptr;      // only the one-query workgroups write it
+    if (QPW != 1) summary.keys = nullptr;  // only the one-query workgroups write it
     hipLaunchKernelGGL((indexer_scores_kernel<H_I, D_I>), grid, dim3(IX_THREADS), 0, stream,
-                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n, pm, summary, M);
+                       qI, w, kI, kv_len, Tq, L_cap, S, zero, zero_n, pm, summary);
     return hipGetLastError();
 }
 
@@ -527,12 +532,12 @@ bool indexer_shape_supported(int H_I, int D_I) {
 #define ISA_IX_CASE(HH, DD)                                                              \
     if (H_I == HH && D_I == DD)                                                          \
         return launch_ix<HH, DD>(qI, w, kI, kv_len, B, Tq, L_cap, S, zero, zero_n, stream, pm, \
-                                 summary, M);
+                                 summary);
 
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
-                                 hipStream_t stream, PageMap pm, uint32_t* summary, int M) {
+                                 hipStream_t stream, PageMap pm, SummaryOut summary) {
     ISA_IX_CASE(64, 128) ISA_IX_CASE(64, 64) ISA_IX_CASE(64, 32)
     ISA_IX_CASE(32, 128) ISA_IX_CASE(32, 64) ISA_IX_CASE(32, 32)
     ISA_IX_CASE(16, 128) ISA_IX_CASE(16, 64) ISA_IX_CASE(16, 32)

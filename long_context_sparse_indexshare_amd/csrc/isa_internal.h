@@ -57,17 +57,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 }
 
 // Top-k summary of a wave's values: the M largest keys (with multiplicity)
-// among the NV keys each lane holds, in descending order, written by lane 0
-// to dst[0, M); key 0 (no value) pads the list when the wave holds fewer.
-// Every lane first sorts its own keys (a small sorting network), then each of
-// the M rounds takes the wave maximum of the lanes' heads and advances the
-// head of the lowest lane holding it.  All 64 lanes must be active.
+// among the NV keys each lane holds, in descending order, each with the
+// 8-bit code of its position (codes[i] belongs to k[i]); lane r < M writes
+// the r-th to dst[r] and its code to cdst[r].  Key 0 (no value) pads the list
+// when the wave holds fewer; which of several equal keys is kept is
+// unspecified.  Every lane first sorts its own (key, code) pairs (a small
+// sorting network), then each of the M rounds takes the wave maximum of the
+// lanes' heads and advances the head of the lowest lane holding it.  All 64
+// lanes must be active.
 template <int NV>
-__device__ __forceinline__ void sort_keys_desc(uint32_t (&k)[NV]) {
+__device__ __forceinline__ void sort_keys_desc(uint32_t (&k)[NV], uint32_t (&c)[NV]) {
     auto cas = [&](int i, int j) {
-        const uint32_t a = k[i], b = k[j];
-        k[i] = max(a, b);
-        k[j] = min(a, b);
+        const bool sw = k[j] > k[i];
+        const uint32_t a = k[i], b = k[j], ca = c[i], cb = c[j];
+        k[i] = sw ? b : a;
+        k[j] = sw ? a : b;
+        c[i] = sw ? cb : ca;
+        c[j] = sw ? ca : cb;
     };
     if constexpr (NV == 4) {
         cas(0, 1); cas(2, 3); cas(0, 2); cas(1, 3); cas(1, 2);
@@ -84,19 +90,32 @@ __device__ __forceinline__ void sort_keys_desc(uint32_t (&k)[NV]) {
 }
 
 template <int NV>
-__device__ __forceinline__ void wave_top_m(uint32_t (&k)[NV], int M, uint32_t* __restrict__ dst) {
-    sort_keys_desc<NV>(k);
+__device__ __forceinline__ void wave_top_m(uint32_t (&k)[NV], uint32_t (&c)[NV], int M,
+                                           uint32_t* __restrict__ dst, uint8_t* __restrict__ cdst) {
+    sort_keys_desc<NV>(k, c);
     const int lane = threadIdx.x & 63;
+    uint32_t mine = 0u, mine_code = 0u;
     for (int r = 0; r < M; ++r) {
         const uint32_t m = wave_max_u32(k[0]);
         const uint64_t hit = __ballot(k[0] == m);
         const int winner = (int)__builtin_ctzll(hit);
-        if (lane == 0) dst[r] = m;
+        const uint32_t code = (uint32_t)__builtin_amdgcn_readlane((int)c[0], winner);
+        if (lane == r) {
+            mine = m;
+            mine_code = code;
+        }
         if (lane == winner) {
 #pragma unroll
-            for (int i = 0; i + 1 < NV; ++i) k[i] = k[i + 1];
+            for (int i = 0; i + 1 < NV; ++i) {
+                k[i] = k[i + 1];
+                c[i] = c[i + 1];
+            }
             k[NV - 1] = 0u;
         }
+    }
+    if (lane < M) {
+        dst[lane] = mine;
+        cdst[lane] = (uint8_t)mine_code;
     }
 }
 
@@ -118,9 +137,11 @@ constexpr int TOPK_PER_THREAD = TOPK_CHUNK / TOPK_THREADS;
 constexpr int TOPK_HIST_BITS = 12;          // first radix digit of the prefill path: key bits [31:20]
 constexpr int TOPK_HIST_BINS = 1 << TOPK_HIST_BITS;
 constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bits
-// The summary: for every run of 256 positions (a "wave chunk"; the indexer's
-// decode workgroup covers 1024 positions with 4 waves), its TOPK_M largest
-// keys.  TOPK_M is chosen per call so the row's summary holds about 2k keys.
+// The summary: for every set of 256 positions (a "wave chunk": the keys one
+// wave of the indexer's decode workgroup scores), its M largest keys and the
+// 8-bit code of each one's position.  Wave chunk 4c + w holds positions
+// 1024c + 32w + 128q + j (q < 8, j < 32), position code 32q + j.  M is
+// chosen per call (topk_layout).
 constexpr int TOPK_WAVE_CHUNK = 256;
 constexpr int TOPK_MAX_M = 16;
 constexpr int TOPK_MAX_SUMMARY = 8192;      // summary keys per row at most (8 per filter thread)
@@ -130,10 +151,18 @@ constexpr int TOPK_SLOT_CAP = TOPK_CHUNK;
 struct TopkLayout {
     size_t zero_bytes;                // counters: [0, zero_bytes) is cleared per call
     size_t hist;                      // first-digit histograms (prefill select path)
-    size_t summary, counts, ent, total;
+    size_t summary, codes, counts, ent, total;
     int rows, nchunks;                // filter chunks of TOPK_CHUNK positions per row
     int nwchunks, M;                  // wave chunks per row, summary keys per wave chunk
     bool select;                      // one-workgroup-per-row select path (prefill)
+    bool direct;                      // one workgroup per row from the summary (decode)
+};
+// Where the indexer writes the top-k summary (keys [rows][nwchunks][M] and
+// their position codes, same shape); keys == nullptr: no summary.
+struct SummaryOut {
+    uint32_t* keys;
+    uint8_t* codes;
+    int M;
 };
 TopkLayout topk_layout(int rows, int L_cap, int k);
 // true when the one-workgroup-per-row select kernel serves (rows, L_cap)
@@ -152,14 +181,14 @@ AttendPlan attend_plan(int B, int Tq, int H, int D, int D_v, int k);
 // Launchers (host side; argument checking happens in the API layer).
 hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t stream);
 // zero[0, zero_n): words the indexer grid also sets to 0 (the top-k counters of
-// the group call that follows), or zero_n = 0.  summary != nullptr: the
-// indexer also writes the top-k summary (M keys per 256-position wave chunk)
+// the group call that follows), or zero_n = 0.  summary.keys != nullptr: the
+// indexer also writes the top-k summary (M keys and codes per wave chunk)
 // when it can (indexer_writes_summary); the caller checks that first.
 hipError_t launch_indexer_scores(const int8_t* qI, const float* w, const int8_t* kI,
                                  const int32_t* kv_len, int B, int Tq, int H_I, int D_I,
                                  int L_cap, float* S, uint32_t* zero, uint32_t zero_n,
                                  hipStream_t stream, PageMap pm = PageMap{nullptr, 0, 0, 0},
-                                 uint32_t* summary = nullptr, int M = 0);
+                                 SummaryOut summary = SummaryOut{nullptr, nullptr, 0});
 bool indexer_writes_summary(int Tq, int H_I);
 // counters_clear: the caller already zeroed the first topk_layout().zero_bytes;
 // summary_ready: the summary in the workspace was written by the indexer

@@ -6,12 +6,15 @@
 // that come first under (score descending, position ascending), listed in
 // ascending position and padded with -1.
 //
-// Scores are compared as order-preserving 32-bit keys.  Few rows of up to
-// 2^21 positions (decode) are spread over many workgroups per row:
-//   0. summary:  for every run of 256 positions, its M largest keys (written
-//                by the indexer's epilogue in the group call, else by a
-//                summary kernel).  M is chosen so the row's summary holds
-//                about 2k keys.
+// Scores are compared as order-preserving 32-bit keys.  Few rows (decode)
+// start from a summary: for every wave chunk of 256 positions, its M largest
+// keys with their positions (written by the indexer's epilogue in the group
+// call, else by a summary kernel).  Rows of at most 262144 positions whose
+// summary holds at least 2k keys then take one workgroup per row
+// (topk_direct_kernel, described there): the candidates come from the
+// summary, and only chunks whose summary may miss a candidate are read
+// again.  Longer rows (up to 2^21 positions) are spread over many
+// workgroups per row, with M chosen so the summary holds about 2k keys:
 //   1. filter:   every workgroup derives from the row's summary a threshold L
 //                with at least k summary keys >= L (the summary's keys are
 //                scores of distinct visible positions, so at least k scores
@@ -217,28 +220,34 @@ constexpr int COL_MAX = 512;              // entries ranked directly for the exa
 
 // ---------------------------------------------------------------------------
 // Summary, for calls whose indexer did not write it: wave w of workgroup c
-// covers positions c*1024 + w*256 + e*64 + lane (e < 4), wave chunk c*4 + w,
-// and writes that chunk's M largest keys; invisible positions take key 0.
+// covers wave chunk 4c + w (positions 1024c + 32w + 128q + j, code 32q + j;
+// lane l takes q = 2e + l / 32 and j = l % 32 for e < 4) and writes its M
+// largest keys with their codes; invisible positions take key 0.
 constexpr int SUM_THREADS = 256;
 __global__ __launch_bounds__(SUM_THREADS) void topk_summary_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int M,
-    int nwchunks, uint32_t* __restrict__ summary) {
+    int nwchunks, uint32_t* __restrict__ summary, uint8_t* __restrict__ codes) {
     const int row = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int base = blockIdx.x * (4 * TOPK_WAVE_CHUNK) + wave * TOPK_WAVE_CHUNK;
+    const int base = blockIdx.x * (4 * TOPK_WAVE_CHUNK) + wave * 32 + (lane & 31);
+    const int qh = lane >> 5;
     const float* rowp = S + (size_t)row * L_cap;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int s = base + e * 64 + lane;
+        const int s = base + (2 * e + qh) * 128;
         v[e] = s < L_cap ? rowp[s] : 0.0f;
     }
     const int n = visible_count(kv_len, row, Tq, L_cap);
-    uint32_t key[4];
+    uint32_t key[4], code[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) key[e] = base + e * 64 + lane < n ? score_key(v[e]) : 0u;
-    wave_top_m<4>(key, M, summary + ((size_t)row * nwchunks + blockIdx.x * 4 + wave) * M);
+    for (int e = 0; e < 4; ++e) {
+        key[e] = base + (2 * e + qh) * 128 < n ? score_key(v[e]) : 0u;
+        code[e] = (uint32_t)((2 * e + qh) * 32 + (lane & 31));
+    }
+    const size_t off = ((size_t)row * nwchunks + blockIdx.x * 4 + wave) * M;
+    wave_top_m<4>(key, code, M, summary + off, codes + off);
 }
 
 // Radix bins over a key range [lo, hi]: bin = (key - lo) >> sh, with sh the
@@ -772,6 +781,455 @@ __global__ __launch_bounds__(FIN_THREADS) void topk_finish_kernel(
     }
 }
 // ---------------------------------------------------------------------------
+// Direct select (decode rows of at most DIR_MAX_N positions whose summary
+// holds at least 2k keys; topk_layout decides): one workgroup per row takes
+// its candidates from the summary, so no kernel runs between the summary and
+// the output.  A wave chunk is "saturated" when its M-th summary key is at
+// least the candidate threshold Lc: an unsaturated chunk's keys >= Lc are
+// exactly its summary keys >= Lc (any other key of the chunk is at most its
+// M-th summary key), so only saturated chunks are read from the scores again.
+//   1. L from the summary as in the filter kernel (Lc = max(L, 1), key 0
+//      being no value): at least k summary keys are >= L, so the row's k-th
+//      key is >= L and every selected position is a candidate;
+//   2. candidates: the summary entries >= Lc of unsaturated chunks (held in
+//      registers) and the keys >= Lc of saturated chunks, read from the
+//      scores and staged in LDS (more than DIR_STAGE: read again in every
+//      pass);
+//   3. the exact cut (T, P), selecting the keys > T and the keys equal to T
+//      at positions <= P: radix passes over the candidates' key range as in
+//      the finish kernel, the cut bin ranked directly once it holds at most
+//      COL_MAX candidates; a bin of one key holding more takes P from a
+//      position bitmap of the candidates equal to T.  With no saturated
+//      chunk the summary's histogram from step 1 is the first pass;
+//   4. the selected positions set bits of an LDS bitmap of the row; a block
+//      scan of the per-thread bit counts gives each thread its first output
+//      slot, and each thread writes the positions of its bits in order.
+constexpr int DIR_THREADS = 1024;
+constexpr int DIR_WAVES = DIR_THREADS / 64;
+constexpr int DIR_PER = 8;                                  // summary entries per thread
+constexpr int DIR_MAX_N = 262144;
+constexpr int DIR_WORDS = DIR_MAX_N / 32;                   // bitmap words
+constexpr int DIR_WPT = DIR_WORDS / DIR_THREADS;            // bitmap words per thread
+constexpr int DIR_MAX_WCHUNKS = DIR_MAX_N / TOPK_WAVE_CHUNK;
+constexpr int DIR_STAGE = 8192;                             // staged candidates of saturated chunks
+constexpr int DIR_UNROLL = 8;                               // score loads in flight per thread
+static_assert(DIR_THREADS * DIR_PER == TOPK_MAX_SUMMARY, "one thread per 8 summary entries");
+static_assert(DIR_WPT == 8, "two 16-byte bitmap reads per thread");
+static_assert(RB_BINS == 4 * DIR_THREADS, "four histogram bins per thread");
+
+struct __attribute__((aligned(16))) DirectShared {
+    uint32_t h[RB_BINS];
+    uint32_t bits[DIR_WORDS];
+    uint2 stage[DIR_STAGE];
+    uint2 col[COL_MAX];
+    uint32_t sat[DIR_MAX_WCHUNKS];        // saturated wave chunks, any order
+    uint32_t red[3][DIR_WAVES];
+    uint32_t tot[DIR_WAVES];
+    uint32_t otot[DIR_WAVES];             // the output scan's wave totals
+    uint32_t res[3];
+    uint32_t cut[2];
+    uint32_t nsat, nstage, ncol;
+};
+
+// Position of code c in wave chunk b.
+__device__ __forceinline__ uint32_t wchunk_pos(uint32_t b, uint32_t c) {
+    return (b >> 2) * 1024u + (b & 3u) * 32u + (c >> 5) * 128u + (c & 31u);
+}
+
+__global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
+    const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
+    const uint32_t* __restrict__ skeys, const uint8_t* __restrict__ scodes, int nw, int M,
+    int32_t* __restrict__ idx) {
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
+    __shared__ DirectShared f;
+
+    // the thread's summary entries (wave chunk blk, entries [8 sub, +8)) and
+    // the chunk's M-th key, requested before the row's visible length arrives
+    const int tpb_log2 = M == 16 ? 1 : 0;               // M / 8 threads per chunk
+    const int blk = tid >> tpb_log2;
+    const int sub = tid & ((1 << tpb_log2) - 1);
+    const bool has = blk < nw;
+    const size_t cbase = ((size_t)row * nw + (has ? blk : 0)) * M;
+    uint4 ka = make_uint4(0u, 0u, 0u, 0u), kb = ka;
+    uint2 cc = make_uint2(0u, 0u);
+    uint32_t Kb = 0u;
+    if (has) {
+        ka = *reinterpret_cast<const uint4*>(skeys + cbase + sub * DIR_PER);
+        kb = *reinterpret_cast<const uint4*>(skeys + cbase + sub * DIR_PER + 4);
+        cc = *reinterpret_cast<const uint2*>(scodes + cbase + sub * DIR_PER);
+        Kb = skeys[cbase + M - 1];
+    }
+    const int n = visible_count(kv_len, row, Tq, L_cap);
+    int32_t* out = idx + (size_t)row * k;
+    if (n <= k) {
+        // every visible position, then -1 padding
+        for (int j = tid; j < k; j += DIR_THREADS) out[j] = j < n ? j : -1;
+        return;
+    }
+    const uint32_t key[DIR_PER] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    uint32_t pos[DIR_PER];
+#pragma unroll
+    for (int i = 0; i < DIR_PER; ++i)
+        pos[i] = wchunk_pos((uint32_t)blk, ((i < 4 ? cc.x : cc.y) >> (8 * (i & 3))) & 0xFFu);
+
+    *reinterpret_cast<uint4*>(&f.h[4 * tid]) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&f.bits[DIR_WPT * tid]) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&f.bits[DIR_WPT * tid + 4]) = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) {
+        f.nsat = 0u;
+        f.nstage = 0u;
+        f.ncol = 0u;
+    }
+    // 1. the summary's nonzero key count and range, then L
+    uint32_t cnt = 0u, mx = 0u, nmn = 0u;                // nmn = ~(minimum nonzero key)
+#pragma unroll
+    for (int i = 0; i < DIR_PER; ++i) {
+        cnt += key[i] != 0u;
+        mx = max(mx, key[i]);
+        nmn = max(nmn, key[i] ? ~key[i] : 0u);
+    }
+    cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(cnt), 63);
+    mx = wave_max_u32(mx);
+    nmn = wave_max_u32(nmn);
+    if (lane == 0) {
+        f.red[0][wave] = cnt;
+        f.red[1][wave] = mx;
+        f.red[2][wave] = nmn;
+    }
+    __syncthreads();
+    uint32_t C = 0u, MX = 0u, NMN = 0u;
+#pragma unroll
+    for (int w = 0; w < DIR_WAVES; ++w) {
+        C += f.red[0][w];
+        MX = max(MX, f.red[1][w]);
+        NMN = max(NMN, f.red[2][w]);
+    }
+    const uint32_t MN = ~NMN;
+    uint32_t L;
+    int sh0 = 0;
+    bool have_cut = false;                               // h holds the summary's histogram
+    uint3 r0 = make_uint3(0u, 0u, 0u);
+    if (C < (uint32_t)k) {
+        L = 0u;
+    } else if (MX == MN) {
+        L = MN;
+    } else {
+        sh0 = range_shift(MN, MX);
+#pragma unroll
+        for (int i = 0; i < DIR_PER; ++i)
+            if (key[i]) atomicAdd(&f.h[RB_BINS - 1 - ((key[i] - MN) >> sh0)], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            // lane l sums bins [64l, 64l + 64), then the crossing lane's 64
+            // bins one per lane: the bin, the count above it, the count in it
+            uint32_t local = 0u;
+            const uint4* hb = reinterpret_cast<const uint4*>(f.h) + 16 * lane;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint4 x = hb[q];
+                local += x.x + x.y + x.z + x.w;
+            }
+            const uint32_t need = (uint32_t)k;
+            const uint32_t inc = wave_inclusive_scan(local);
+            const int cl = (int)__builtin_ctzll(__ballot(inc >= need && inc - local < need));
+            const uint32_t base = __builtin_amdgcn_readlane(inc - local, cl);
+            const uint32_t cbv = f.h[64 * cl + lane];
+            const uint32_t inc2 = base + wave_inclusive_scan(cbv);
+            const int bl = (int)__builtin_ctzll(__ballot(inc2 >= need && inc2 - cbv < need));
+            if (lane == bl) {
+                f.res[0] = (uint32_t)(64 * cl + bl);
+                f.res[1] = inc2 - cbv;
+                f.res[2] = cbv;
+            }
+        }
+        __syncthreads();
+        r0 = make_uint3(f.res[0], f.res[1], f.res[2]);
+        L = MN + ((uint32_t)(RB_BINS - 1 - (int)r0.x) << sh0);
+        have_cut = true;
+    }
+    const uint32_t Lc = L ? L : 1u;
+
+    // 2. saturated chunks into the list; candidates of the others stay in
+    // registers.  When the summary's cut bin is small its entries also go to
+    // the cut list now (used only if no chunk turns out saturated: then the
+    // candidates are the summary entries >= L and the summary's histogram
+    // is theirs).
+    const bool sat = has && Kb >= Lc;
+    uint32_t cmask = 0u;
+#pragma unroll
+    for (int i = 0; i < DIR_PER; ++i) cmask |= (uint32_t)(!sat && key[i] >= Lc) << i;
+    const bool spec = have_cut && r0.z <= (uint32_t)COL_MAX;
+    const uint32_t width0 = (1u << sh0) - 1u;
+    const uint32_t bhi0 = MX - L < width0 ? MX : L + width0;    // the summary's cut bin is [L, bhi0]
+    {
+        const bool lead = sat && sub == 0;
+        const uint64_t lm = __ballot(lead);
+        if (lm) {
+            uint32_t b0 = 0u;
+            if (lane == 0) b0 = atomicAdd(&f.nsat, (uint32_t)__popcll(lm));
+            b0 = __builtin_amdgcn_readfirstlane(b0);
+            if (lead) f.sat[b0 + (uint32_t)__popcll(lm & below)] = (uint32_t)blk;
+        }
+        if (spec) {
+#pragma unroll
+            for (int i = 0; i < DIR_PER; ++i) {
+                if (((cmask >> i) & 1u) && key[i] <= bhi0) {
+                    const uint32_t slot = atomicAdd(&f.ncol, 1u);
+                    if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key[i], pos[i]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t nsat = f.nsat;
+
+    uint32_t* const myw = &f.bits[DIR_WPT * tid];
+    auto load_words = [&](uint32_t (&wv)[DIR_WPT]) {
+        const uint4 x = *reinterpret_cast<const uint4*>(myw);
+        const uint4 y = *reinterpret_cast<const uint4*>(myw + 4);
+        wv[0] = x.x; wv[1] = x.y; wv[2] = x.z; wv[3] = x.w;
+        wv[4] = y.x; wv[5] = y.y; wv[6] = y.z; wv[7] = y.w;
+    };
+    auto set_bit = [&](uint32_t p) { atomicOr(&f.bits[p >> 5], 1u << (p & 31u)); };
+    // the cut list's m entries ranked under (key desc, position asc): the
+    // first need are selected
+    auto mark_ranked = [&](uint32_t m, uint32_t need) {
+        for (uint32_t t = tid; t < m; t += DIR_THREADS) {
+            const uint2 e = f.col[t];
+            uint32_t rank = 0u;
+            for (uint32_t q = 0; q < m; ++q) {
+                const uint2 o = f.col[q];
+                rank += (uint32_t)(o.x > e.x) | ((uint32_t)(o.x == e.x) & (uint32_t)(o.y < e.y));
+            }
+            if (rank < need) set_bit(e.y);
+        }
+    };
+    // 4. once the bitmap holds the k selected positions: each thread's bit
+    // count, one wave scan and the waves' totals give its first output slot
+    auto write_output = [&]() {
+        uint32_t wv[DIR_WPT];
+        load_words(wv);
+        uint32_t local = 0u;
+#pragma unroll
+        for (int w = 0; w < DIR_WPT; ++w) local += (uint32_t)__popc(wv[w]);
+        const uint32_t inc = wave_inclusive_scan(local);
+        if (lane == 63) f.otot[wave] = inc;
+        __syncthreads();
+        uint32_t o = inc - local;
+#pragma unroll
+        for (int w = 0; w < DIR_WAVES; ++w) o += w < wave ? f.otot[w] : 0u;
+#pragma unroll
+        for (int w = 0; w < DIR_WPT; ++w) {
+            uint32_t x = wv[w];
+            while (x) {
+                const uint32_t bit = (uint32_t)__builtin_ctz(x);
+                x &= x - 1u;
+                if (o < (uint32_t)k) out[o] = (int32_t)((uint32_t)(DIR_WPT * tid + w) * 32u + bit);
+                ++o;
+            }
+        }
+    };
+
+    if (nsat == 0u && spec) {
+        // the common case: the cut bin ranked directly, the entries above it
+        // all selected
+        mark_ranked(r0.z, (uint32_t)k - r0.y);
+#pragma unroll
+        for (int i = 0; i < DIR_PER; ++i)
+            if (((cmask >> i) & 1u) && key[i] > bhi0) set_bit(pos[i]);
+        __syncthreads();
+        write_output();
+        return;
+    }
+    if (tid == 0) f.ncol = 0u;              // the cut list starts again (next filled after barriers)
+
+    const uint32_t total = nsat * TOPK_WAVE_CHUNK;
+    const float* rowp = S + (size_t)row * L_cap;
+    // the scores of the saturated chunks, DIR_UNROLL loads in flight per
+    // thread (addresses clamped inside the visible row): fn(keep, key,
+    // position), keep for the keys >= Lc
+    auto scan_saturated = [&](auto fn) {
+        for (uint32_t j0 = 0; j0 < total; j0 += DIR_UNROLL * DIR_THREADS) {
+            float v[DIR_UNROLL];
+            uint32_t sp[DIR_UNROLL];
+#pragma unroll
+            for (int u = 0; u < DIR_UNROLL; ++u) {
+                const uint32_t j = j0 + (uint32_t)(u * DIR_THREADS + tid);
+                const uint32_t jj = j < total ? j : total - 1u;
+                sp[u] = wchunk_pos(f.sat[jj >> 8], jj & 255u);
+                v[u] = rowp[sp[u] < (uint32_t)n ? sp[u] : (uint32_t)n - 1u];
+            }
+#pragma unroll
+            for (int u = 0; u < DIR_UNROLL; ++u) {
+                const uint32_t j = j0 + (uint32_t)(u * DIR_THREADS + tid);
+                const uint32_t kk = j < total && sp[u] < (uint32_t)n ? score_key(v[u]) : 0u;
+                fn(kk >= Lc, kk, sp[u]);
+            }
+        }
+    };
+    if (nsat > 0u) {
+        scan_saturated([&](bool keep, uint32_t kk, uint32_t sp) {
+            const uint64_t km = __ballot(keep);
+            if (km) {
+                uint32_t b0 = 0u;
+                if (lane == 0) b0 = atomicAdd(&f.nstage, (uint32_t)__popcll(km));
+                b0 = __builtin_amdgcn_readfirstlane(b0);
+                if (keep) {
+                    const uint32_t slot = b0 + (uint32_t)__popcll(km & below);
+                    if (slot < (uint32_t)DIR_STAGE) f.stage[slot] = make_uint2(kk, sp);
+                }
+            }
+        });
+        __syncthreads();
+    }
+    const uint32_t nst = f.nstage;
+    const bool overflow = nst > (uint32_t)DIR_STAGE;
+    // every candidate once: fn(key, position)
+    auto each = [&](auto fn) {
+#pragma unroll
+        for (int i = 0; i < DIR_PER; ++i)
+            if ((cmask >> i) & 1u) fn(key[i], pos[i]);
+        if (!overflow) {
+            for (uint32_t j = tid; j < nst; j += DIR_THREADS) {
+                const uint2 e = f.stage[j];
+                fn(e.x, e.y);
+            }
+        } else {
+            scan_saturated([&](bool keep, uint32_t kk, uint32_t sp) {
+                if (keep) fn(kk, sp);
+            });
+        }
+    };
+
+    // 3. the exact cut
+    uint32_t lo, hi, need = (uint32_t)k;
+    const bool pre = nsat == 0u && have_cut;            // the summary's histogram is the first pass
+    if (pre) {
+        lo = MN;
+        hi = MX;
+    } else {
+        uint32_t a = 0u, b = 0u;
+        each([&](uint32_t kk, uint32_t) {
+            a = max(a, kk);
+            b = max(b, ~kk);
+        });
+        a = wave_max_u32(a);
+        b = wave_max_u32(b);
+        if (lane == 0) {                                 // red was last read before a barrier
+            f.red[0][wave] = a;
+            f.red[1][wave] = b;
+        }
+        __syncthreads();
+        uint32_t A = 0u, B = 0u;
+#pragma unroll
+        for (int w = 0; w < DIR_WAVES; ++w) {
+            A = max(A, f.red[0][w]);
+            B = max(B, f.red[1][w]);
+        }
+        lo = ~B;
+        hi = A;
+    }
+    uint32_t T;
+    bool h_dirty = have_cut;
+    for (bool first = true;; first = false) {
+        int sh;
+        uint3 r;
+        if (first && pre) {
+            sh = sh0;
+            r = r0;
+        } else {
+            if (lo == hi) {
+                T = lo;
+                break;
+            }
+            sh = range_shift(lo, hi);
+            if (h_dirty) {
+                // every thread is past its reads of the previous histogram
+                *reinterpret_cast<uint4*>(&f.h[4 * tid]) = make_uint4(0u, 0u, 0u, 0u);
+                __syncthreads();
+            }
+            each([&](uint32_t kk, uint32_t) {
+                if (kk >= lo && kk <= hi) atomicAdd(&f.h[RB_BINS - 1 - ((kk - lo) >> sh)], 1u);
+            });
+            __syncthreads();
+            r = find_cut<DIR_THREADS>(f.h, need, f.tot, f.res);
+            h_dirty = true;
+        }
+        const uint32_t b = (uint32_t)(RB_BINS - 1) - r.x;
+        need -= r.y;                                     // >= 1 keys to take from bin b
+        const uint32_t blo = lo + (b << sh);
+        const uint32_t width = (1u << sh) - 1u;
+        const uint32_t bhi = hi - blo < width ? hi : blo + width;
+        if (r.z <= (uint32_t)COL_MAX) {
+            // the bin's candidates to the cut list, the ones above it selected
+            each([&](uint32_t kk, uint32_t p) {
+                if (kk > bhi) {
+                    set_bit(p);
+                } else if (kk >= blo) {
+                    const uint32_t slot = atomicAdd(&f.ncol, 1u);
+                    if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(kk, p);
+                }
+            });
+            __syncthreads();
+            mark_ranked(r.z, need);
+            __syncthreads();
+            write_output();
+            return;
+        }
+        if (sh == 0) {
+            T = blo;
+            break;
+        }
+        lo = blo;
+        hi = bhi;
+    }
+
+    // a single key T holds the cut: P is the need-th lowest position among
+    // the candidates equal to T (a bitmap of them, scanned)
+    each([&](uint32_t kk, uint32_t p) {
+        if (kk == T) set_bit(p);
+    });
+    __syncthreads();
+    {
+        uint32_t wv[DIR_WPT];
+        load_words(wv);
+        uint32_t local = 0u;
+#pragma unroll
+        for (int w = 0; w < DIR_WPT; ++w) local += (uint32_t)__popc(wv[w]);
+        uint32_t all;
+        const uint32_t before = block_exclusive_scan<DIR_THREADS>(local, &all, f.tot);
+        if (before < need && before + local >= need) {
+            uint32_t rem = need - before;
+#pragma unroll
+            for (int w = 0; w < DIR_WPT; ++w) {
+                const uint32_t c = (uint32_t)__popc(wv[w]);
+                if (rem > 0u && rem <= c) {
+                    uint32_t x = wv[w];
+                    for (uint32_t i = 1; i < rem; ++i) x &= x - 1u;
+                    f.cut[1] = (uint32_t)(DIR_WPT * tid + w) * 32u + (uint32_t)__builtin_ctz(x);
+                    rem = 0u;
+                } else if (rem > 0u) {
+                    rem -= c;
+                }
+            }
+        }
+        *reinterpret_cast<uint4*>(myw) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(myw + 4) = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+    }
+    const uint32_t P = f.cut[1];
+    each([&](uint32_t kk, uint32_t p) {
+        if (kk > T || (kk == T && p <= P)) set_bit(p);
+    });
+    __syncthreads();
+    write_output();
+}
+
+// ---------------------------------------------------------------------------
 // Many rows of at most SEL_MAX_N positions (prefill): after the histogram
 // kernel, one workgroup of 1024 threads per row does the rest in LDS.  With
 // fewer rows than the chip has compute units (decode) the classify/finish
@@ -1010,14 +1468,18 @@ TopkLayout topk_layout(int rows, int L_cap, int k) {
     L.nchunks = (L_cap + TOPK_CHUNK - 1) / TOPK_CHUNK;
     // wave chunks of 256 positions (4 per 1024-position indexer workgroup)
     L.nwchunks = (L_cap + 4 * TOPK_WAVE_CHUNK - 1) / (4 * TOPK_WAVE_CHUNK) * 4;
-    // summary keys per wave chunk: about 2k per row in all
-    int M = (int)((2LL * k * TOPK_WAVE_CHUNK + L_cap - 1) / L_cap);
-    L.M = M < 1 ? 1 : (M > TOPK_MAX_M ? TOPK_MAX_M : M);
     // the one-workgroup-per-row select kernel needs only the first-digit
-    // histograms; the filter/finish pair needs the summary, the run lengths
-    // and the entry slots
+    // histograms; the direct kernel the summary (8 or 16 keys per wave chunk,
+    // up to TOPK_MAX_SUMMARY per row, at least 2k); the filter/finish pair
+    // the summary (about 2k keys per row), the run lengths and the entry slots
     L.select = topk_uses_select(rows, L_cap);
     const bool sel = L.select;
+    const int Md = L.nwchunks * 16 <= TOPK_MAX_SUMMARY ? 16 : 8;
+    L.direct = !sel && L_cap <= DIR_MAX_N && (long long)L.nwchunks * Md >= 2LL * k;
+    int M = (int)((2LL * k * TOPK_WAVE_CHUNK + L_cap - 1) / L_cap);
+    M = M < 1 ? 1 : (M > TOPK_MAX_M ? TOPK_MAX_M : M);
+    L.M = L.direct ? Md : M;
+    const bool runs = !sel && !L.direct;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -1029,8 +1491,9 @@ TopkLayout topk_layout(int rows, int L_cap, int k) {
     L.zero_bytes = off;
     // scratch overwritten by every call
     L.summary = take(sel ? 0 : (size_t)rows * L.nwchunks * L.M * 4);
-    L.counts = take(sel ? 0 : (size_t)rows * L.nchunks * 4);
-    L.ent = take(sel ? 0 : (size_t)rows * L.nchunks * TOPK_SLOT_CAP * 8);
+    L.codes = take(sel ? 0 : (size_t)rows * L.nwchunks * L.M);
+    L.counts = take(runs ? (size_t)rows * L.nchunks * 4 : 0);
+    L.ent = take(runs ? (size_t)rows * L.nchunks * TOPK_SLOT_CAP * 8 : 0);
     L.total = off;
     return L;
 }
@@ -1069,11 +1532,17 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
         return hipGetLastError();
     }
     uint32_t* summary = reinterpret_cast<uint32_t*>(base + L.summary);
+    uint8_t* codes = reinterpret_cast<uint8_t*>(base + L.codes);
     uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
     uint2* ent = reinterpret_cast<uint2*>(base + L.ent);
     if (!summary_ready)
         hipLaunchKernelGGL(topk_summary_kernel, dim3(L.nwchunks / 4, rows), dim3(SUM_THREADS), 0,
-                           stream, S, kv_len, Tq, L_cap, L.M, L.nwchunks, summary);
+                           stream, S, kv_len, Tq, L_cap, L.M, L.nwchunks, summary, codes);
+    if (L.direct) {
+        hipLaunchKernelGGL(topk_direct_kernel, dim3(rows), dim3(DIR_THREADS), 0, stream, S, kv_len,
+                           Tq, L_cap, k, summary, codes, L.nwchunks, L.M, idx);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(topk_filter_kernel, dim3(L.nchunks, rows), dim3(TOPK_THREADS), 0, stream, S,
                        kv_len, Tq, L_cap, k, summary, L.nwchunks * L.M, counts, ent, L.nchunks);
     // threads per chunk in the finish: FIN_THREADS over the chunk count rounded up to a power of two

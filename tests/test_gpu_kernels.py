@@ -208,6 +208,72 @@ def test_topk_reuses_workspace_across_calls():
         assert_idx_equal(idx, ref, f"call {it}")
 
 
+# Few rows of 64K-256K positions take the direct path: one workgroup per row
+# selects from the summary (the M largest keys of every 256-position wave
+# chunk, with their positions) and reads again only the chunks whose summary
+# may miss a candidate ("saturated"), staging their candidates in LDS or, past
+# 8192 of them, reading them in every pass.
+
+def _direct_case(name):
+    r = np.random.default_rng(sum(map(ord, name)))
+    L = 131072
+    if name == "normal":
+        S = r.standard_normal((2, 1, L)).astype(np.float32)
+        return S, [L, L - 777]
+    if name == "ties":
+        S = (r.integers(0, 5000, size=(2, 1, L)) * 0.25).astype(np.float32)
+        return S, [L, 100000]
+    if name == "clustered":
+        # high scores packed into runs: a few saturated chunks (staged), then
+        # more candidates than the stage holds (read in every pass)
+        S = r.standard_normal((3, 1, L)).astype(np.float32)
+        S[0, 0, 5000:8000] += 10.0
+        S[1, 0, 1000:9000] += 10.0
+        S[2, 0, 20000:30000] += 10.0
+        S[2, 0, 20000:30000:3] = 12.0                  # ties inside the run
+        return S, [L, L, L - 5]
+    if name == "short":
+        # few visible positions: the summary holds fewer than k keys
+        S = r.standard_normal((6, 1, L)).astype(np.float32)
+        return S, [3000, 30000, 2049, 2048, 1, 0]
+    if name == "crafted":
+        S = r.standard_normal((6, 1, L)).astype(np.float32)
+        S[1] = 3.5                                      # all equal
+        S[2, 0, ::2] = -0.0                             # -0.0 and +0.0 tie
+        S[3, 0, :] = np.arange(L) % 7                   # duplicates straddle the cut
+        S[4, 0, :] = -np.inf
+        S[4, 0, 5000:5003] = 1.0
+        S[5, 0, :] = np.linspace(-1e30, 1e30, L).astype(np.float32)[::-1]
+        return S, [L - 333] * 6
+    if name == "256K":
+        L = 262144
+        S = r.standard_normal((2, 1, L)).astype(np.float32)
+        S[1, 0, 100000:101500] += 8.0
+        return S, [L, L - 1000]
+    if name == "64K":
+        L = 65536
+        S = (r.integers(0, 20000, size=(2, 1, L)) * 0.125).astype(np.float32)
+        return S, [L, 40000]
+    raise ValueError(name)
+
+
+@pytest.mark.parametrize("name", ["normal", "ties", "clustered", "short", "crafted", "256K", "64K"])
+def test_topk_direct_path(name):
+    S, kv = _direct_case(name)
+    _topk_check(S, torch.tensor(kv, dtype=torch.int32), 2048, f"direct {name}")
+
+
+def test_topk_direct_path_multi_query_rows():
+    # several queries per sequence (each row sees one position more) and a
+    # smaller k
+    r = np.random.default_rng(41)
+    L = 131072
+    S = (r.integers(0, 100000, size=(2, 4, L)) * 0.5).astype(np.float32)
+    S[1, :, 7000:7400] = 1e6
+    kv_len = torch.tensor([L - 3, 90001], dtype=torch.int32)
+    _topk_check(S, kv_len, 1024, "direct multi-query")
+
+
 # Many rows (a prefill chunk) take the one-workgroup-per-row path.
 
 def test_topk_many_rows_causal_ragged():
