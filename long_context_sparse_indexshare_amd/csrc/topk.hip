@@ -6,15 +6,16 @@
 // that come first under (score descending, position ascending), listed in
 // ascending position and padded with -1.
 //
-// Scores are compared as order-preserving 32-bit keys.  Few rows (decode)
-// start from a summary: for every wave chunk of 256 positions, its M largest
-// keys with their positions (written by the indexer's epilogue in the group
+// Scores are compared as order-preserving 32-bit keys.  The selection starts
+// from a summary: for every wave chunk of 256 positions, its M largest keys
+// with their positions (written by the indexer's epilogue in a decode group
 // call, else by a summary kernel).  Rows of at most 262144 positions whose
-// summary holds at least 2k keys then take one workgroup per row
-// (topk_direct_kernel, described there): the candidates come from the
-// summary, and only chunks whose summary may miss a candidate are read
-// again.  Longer rows (up to 2^21 positions) are spread over many
-// workgroups per row, with M chosen so the summary holds about 2k keys:
+// summary holds at least 2k keys (decode rows and long prefill rows alike)
+// then take one workgroup per row (topk_direct_kernel, described there): the
+// candidates come from the summary, and only chunks whose summary may miss a
+// candidate are read again.  Longer rows (up to 2^21 positions) are spread
+// over many workgroups per row, with M chosen so the summary holds about 2k
+// keys:
 //   1. filter:   every workgroup derives from the row's summary a threshold L
 //                with at least k summary keys >= L (the summary's keys are
 //                scores of distinct visible positions, so at least k scores
@@ -30,9 +31,9 @@
 //                the candidates' key range and a direct ranking of the cut
 //                bin, and writes every selected position straight to its
 //                place after one block scan of (above T, equal to T) counts.
-// With at least 256 rows of at most 262144 positions (a prefill chunk) a
-// first-digit histogram kernel and one workgroup per row
-// (topk_select_kernel) do the work instead.
+// Shorter rows (whose summary would hold fewer than 2k keys), when there are
+// at least 256 of them (a prefill chunk), take a first-digit histogram
+// kernel and one workgroup per row (topk_select_kernel) instead.
 // Workgroups never wait on each other inside a kernel: on gfx950 a device-
 // scope fence writes back and invalidates the whole L2 of the XCD, so each
 // hand-over between workgroups goes through a kernel boundary instead.
@@ -1472,10 +1473,10 @@ TopkLayout topk_layout(int rows, int L_cap, int k) {
     // histograms; the direct kernel the summary (8 or 16 keys per wave chunk,
     // up to TOPK_MAX_SUMMARY per row, at least 2k); the filter/finish pair
     // the summary (about 2k keys per row), the run lengths and the entry slots
-    L.select = topk_uses_select(rows, L_cap);
-    const bool sel = L.select;
     const int Md = L.nwchunks * 16 <= TOPK_MAX_SUMMARY ? 16 : 8;
-    L.direct = !sel && L_cap <= DIR_MAX_N && (long long)L.nwchunks * Md >= 2LL * k;
+    L.direct = L_cap <= DIR_MAX_N && (long long)L.nwchunks * Md >= 2LL * k;
+    L.select = !L.direct && topk_uses_select(rows, L_cap);
+    const bool sel = L.select;
     int M = (int)((2LL * k * TOPK_WAVE_CHUNK + L_cap - 1) / L_cap);
     M = M < 1 ? 1 : (M > TOPK_MAX_M ? TOPK_MAX_M : M);
     L.M = L.direct ? Md : M;
