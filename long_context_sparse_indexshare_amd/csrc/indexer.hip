@@ -201,21 +201,27 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
     }
     if constexpr (NQL == 1) {
         // the top-k summary of this wave's 256 keys (wave chunk 4 * blockIdx.x
-        // + wave of the query's row; step st of lane j is position code
+        // + wave of the query's row; step st of key j is position code
         // 32 * st + j): their M largest score keys with their codes,
-        // invisible positions counting as none
+        // invisible positions counting as none.  The lanes with g = 1 take
+        // steps 4-7 of key j from lane j (one lane swap each), so every lane
+        // holds four keys.
         if (summary.keys != nullptr) {
-            static_assert(IX_STEPS * 32 == TOPK_WAVE_CHUNK && IX_KEYS_PER_STEP == 128,
+            static_assert(IX_STEPS == 8 && IX_STEPS * 32 == TOPK_WAVE_CHUNK &&
+                              IX_KEYS_PER_STEP == 128,
                           "a wave's keys are one summary wave chunk");
-            uint32_t key[IX_STEPS], code[IX_STEPS];
+            uint32_t key[4], code[4];
 #pragma unroll
-            for (int st = 0; st < IX_STEPS; ++st) {
-                key[st] = (visb >> st) & 1u ? score_key(res[st]) : 0u;
-                code[st] = (uint32_t)(32 * st + j);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (visb >> i) & 1u ? score_key(res[i]) : 0u;
+                const uint32_t hi = (visb >> (4 + i)) & 1u ? score_key(res[4 + i]) : 0u;
+                const auto r = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+                key[i] = g == 0 ? lo : r[0];             // r[0]: lane j's value
+                code[i] = (uint32_t)(32 * (4 * g + i) + j);
             }
             const int M = summary.M;
             const size_t off = (((size_t)b * Tq + t0) * (gridDim.x * 4) + blockIdx.x * 4 + wave) * M;
-            wave_top_m<IX_STEPS>(key, code, M, summary.keys + off, summary.codes + off);
+            wave_top_m<4>(key, code, M, summary.keys + off, summary.codes + off);
         }
         // the workgroup's IX_KEYS_PER_WG scores are contiguous in S: stage them
         // in LDS in key order, then one 16-byte streaming store per thread
