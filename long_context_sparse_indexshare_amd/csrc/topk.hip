@@ -810,12 +810,10 @@ constexpr int DIR_WAVES = DIR_THREADS / 64;
 constexpr int DIR_PER = 8;                                  // summary entries per thread
 constexpr int DIR_MAX_N = 262144;
 constexpr int DIR_WORDS = DIR_MAX_N / 32;                   // bitmap words
-constexpr int DIR_WPT = DIR_WORDS / DIR_THREADS;            // bitmap words per thread
 constexpr int DIR_MAX_WCHUNKS = DIR_MAX_N / TOPK_WAVE_CHUNK;
 constexpr int DIR_STAGE = 8192;                             // staged candidates of saturated chunks
 constexpr int DIR_UNROLL = 8;                               // score loads in flight per thread
 static_assert(DIR_THREADS * DIR_PER == TOPK_MAX_SUMMARY, "one thread per 8 summary entries");
-static_assert(DIR_WPT == 8, "two 16-byte bitmap reads per thread");
 static_assert(RB_BINS == 4 * DIR_THREADS, "four histogram bins per thread");
 
 struct __attribute__((aligned(16))) DirectShared {
@@ -837,6 +835,9 @@ __device__ __forceinline__ uint32_t wchunk_pos(uint32_t b, uint32_t c) {
     return (b >> 2) * 1024u + (b & 3u) * 32u + (c >> 5) * 128u + (c & 31u);
 }
 
+// WPT: bitmap words per thread (4 covers rows of up to 131072 positions, 8 up
+// to DIR_MAX_N).
+template <int WPT>
 __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
     const float* __restrict__ S, const int32_t* __restrict__ kv_len, int Tq, int L_cap, int k,
     const uint32_t* __restrict__ skeys, const uint8_t* __restrict__ scodes, int nw, int M,
@@ -878,8 +879,10 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
         pos[i] = wchunk_pos((uint32_t)blk, ((i < 4 ? cc.x : cc.y) >> (8 * (i & 3))) & 0xFFu);
 
     *reinterpret_cast<uint4*>(&f.h[4 * tid]) = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&f.bits[DIR_WPT * tid]) = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&f.bits[DIR_WPT * tid + 4]) = make_uint4(0u, 0u, 0u, 0u);
+    static_assert(WPT == 4 || WPT == 8, "one or two 16-byte bitmap accesses per thread");
+#pragma unroll
+    for (int u = 0; u < WPT; u += 4)
+        *reinterpret_cast<uint4*>(&f.bits[WPT * tid + u]) = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) {
         f.nsat = 0u;
         f.nstage = 0u;
@@ -976,11 +979,17 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
             if (lead) f.sat[b0 + (uint32_t)__popcll(lm & below)] = (uint32_t)blk;
         }
         if (spec) {
+            // one LDS atomic per wave and entry index for the list's slots
 #pragma unroll
             for (int i = 0; i < DIR_PER; ++i) {
-                if (((cmask >> i) & 1u) && key[i] <= bhi0) {
-                    const uint32_t slot = atomicAdd(&f.ncol, 1u);
-                    if (slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key[i], pos[i]);
+                const bool in = ((cmask >> i) & 1u) && key[i] <= bhi0;
+                const uint64_t im = __ballot(in);
+                if (im) {
+                    uint32_t b0 = 0u;
+                    if (lane == 0) b0 = atomicAdd(&f.ncol, (uint32_t)__popcll(im));
+                    b0 = __builtin_amdgcn_readfirstlane(b0);
+                    const uint32_t slot = b0 + (uint32_t)__popcll(im & below);
+                    if (in && slot < (uint32_t)COL_MAX) f.col[slot] = make_uint2(key[i], pos[i]);
                 }
             }
         }
@@ -988,12 +997,13 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
     __syncthreads();
     const uint32_t nsat = f.nsat;
 
-    uint32_t* const myw = &f.bits[DIR_WPT * tid];
-    auto load_words = [&](uint32_t (&wv)[DIR_WPT]) {
-        const uint4 x = *reinterpret_cast<const uint4*>(myw);
-        const uint4 y = *reinterpret_cast<const uint4*>(myw + 4);
-        wv[0] = x.x; wv[1] = x.y; wv[2] = x.z; wv[3] = x.w;
-        wv[4] = y.x; wv[5] = y.y; wv[6] = y.z; wv[7] = y.w;
+    uint32_t* const myw = &f.bits[WPT * tid];
+    auto load_words = [&](uint32_t (&wv)[WPT]) {
+#pragma unroll
+        for (int u = 0; u < WPT; u += 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(myw + u);
+            wv[u] = x.x; wv[u + 1] = x.y; wv[u + 2] = x.z; wv[u + 3] = x.w;
+        }
     };
     auto set_bit = [&](uint32_t p) { atomicOr(&f.bits[p >> 5], 1u << (p & 31u)); };
     // the cut list's m entries ranked under (key desc, position asc): the
@@ -1012,11 +1022,11 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
     // 4. once the bitmap holds the k selected positions: each thread's bit
     // count, one wave scan and the waves' totals give its first output slot
     auto write_output = [&]() {
-        uint32_t wv[DIR_WPT];
+        uint32_t wv[WPT];
         load_words(wv);
         uint32_t local = 0u;
 #pragma unroll
-        for (int w = 0; w < DIR_WPT; ++w) local += (uint32_t)__popc(wv[w]);
+        for (int w = 0; w < WPT; ++w) local += (uint32_t)__popc(wv[w]);
         const uint32_t inc = wave_inclusive_scan(local);
         if (lane == 63) f.otot[wave] = inc;
         __syncthreads();
@@ -1024,12 +1034,12 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
 #pragma unroll
         for (int w = 0; w < DIR_WAVES; ++w) o += w < wave ? f.otot[w] : 0u;
 #pragma unroll
-        for (int w = 0; w < DIR_WPT; ++w) {
+        for (int w = 0; w < WPT; ++w) {
             uint32_t x = wv[w];
             while (x) {
                 const uint32_t bit = (uint32_t)__builtin_ctz(x);
                 x &= x - 1u;
-                if (o < (uint32_t)k) out[o] = (int32_t)((uint32_t)(DIR_WPT * tid + w) * 32u + bit);
+                if (o < (uint32_t)k) out[o] = (int32_t)((uint32_t)(WPT * tid + w) * 32u + bit);
                 ++o;
             }
         }
@@ -1196,22 +1206,22 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
     });
     __syncthreads();
     {
-        uint32_t wv[DIR_WPT];
+        uint32_t wv[WPT];
         load_words(wv);
         uint32_t local = 0u;
 #pragma unroll
-        for (int w = 0; w < DIR_WPT; ++w) local += (uint32_t)__popc(wv[w]);
+        for (int w = 0; w < WPT; ++w) local += (uint32_t)__popc(wv[w]);
         uint32_t all;
         const uint32_t before = block_exclusive_scan<DIR_THREADS>(local, &all, f.tot);
         if (before < need && before + local >= need) {
             uint32_t rem = need - before;
 #pragma unroll
-            for (int w = 0; w < DIR_WPT; ++w) {
+            for (int w = 0; w < WPT; ++w) {
                 const uint32_t c = (uint32_t)__popc(wv[w]);
                 if (rem > 0u && rem <= c) {
                     uint32_t x = wv[w];
                     for (uint32_t i = 1; i < rem; ++i) x &= x - 1u;
-                    f.cut[1] = (uint32_t)(DIR_WPT * tid + w) * 32u + (uint32_t)__builtin_ctz(x);
+                    f.cut[1] = (uint32_t)(WPT * tid + w) * 32u + (uint32_t)__builtin_ctz(x);
                     rem = 0u;
                 } else if (rem > 0u) {
                     rem -= c;
@@ -1540,8 +1550,12 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
         hipLaunchKernelGGL(topk_summary_kernel, dim3(L.nwchunks / 4, rows), dim3(SUM_THREADS), 0,
                            stream, S, kv_len, Tq, L_cap, L.M, L.nwchunks, summary, codes);
     if (L.direct) {
-        hipLaunchKernelGGL(topk_direct_kernel, dim3(rows), dim3(DIR_THREADS), 0, stream, S, kv_len,
-                           Tq, L_cap, k, summary, codes, L.nwchunks, L.M, idx);
+        if (L_cap <= DIR_MAX_N / 2)
+            hipLaunchKernelGGL(topk_direct_kernel<4>, dim3(rows), dim3(DIR_THREADS), 0, stream, S,
+                               kv_len, Tq, L_cap, k, summary, codes, L.nwchunks, L.M, idx);
+        else
+            hipLaunchKernelGGL(topk_direct_kernel<8>, dim3(rows), dim3(DIR_THREADS), 0, stream, S,
+                               kv_len, Tq, L_cap, k, summary, codes, L.nwchunks, L.M, idx);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(topk_filter_kernel, dim3(L.nchunks, rows), dim3(TOPK_THREADS), 0, stream, S,
