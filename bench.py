@@ -759,7 +759,8 @@ def main():
     stages = {
         "indexer": (1, alg["ix_bytes"], "indexer_scores_kernel<64, 128>"),
         "topk": (1, alg["topk_read_bytes"],
-                 "topk_filter_kernel + topk_finish_kernel"),
+                 "topk_summary_kernel + topk_direct_kernel<4> (stand-alone call; in the group "
+                 "the indexer's epilogue writes the summary)"),
         "attend": (wl.n_layers, alg["at_bytes_per_layer"],
                    "sparse_attend_kernel<1, 1, 576, 512, 2, false> + merge_splits_kernel (one layer)"),
     }
