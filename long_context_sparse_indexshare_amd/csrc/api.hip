@@ -246,7 +246,7 @@ isa_status isa_topk_select(const float* S, const int32_t* kv_len, int B, int Tq,
     isa_status st = check_topk(S, kv_len, B, Tq, L_cap, k, idx);
     if (st != ISA_OK) return st;
     const size_t need = isa_topk_workspace_bytes(B, Tq, L_cap, k);
-    ISA_CHECK(ws && ws_bytes >= need && aligned(ws, 256), ISA_ERR_WORKSPACE,
+    ISA_CHECK(need == 0 || (ws && ws_bytes >= need && aligned(ws, 256)), ISA_ERR_WORKSPACE,
               "topk: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
     return check_hip(isa::launch_topk_select(S, kv_len, B, Tq, L_cap, k, idx, ws, false,
                                              static_cast<hipStream_t>(stream)),

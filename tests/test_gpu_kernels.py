@@ -208,6 +208,22 @@ def test_topk_reuses_workspace_across_calls():
         assert_idx_equal(idx, ref, f"call {it}")
 
 
+# Decode rows of 32768 positions (the C2 shape): their summary would hold
+# fewer than 2k keys, so they take the filter / finish pair.
+
+def test_topk_32k_rows():
+    r = np.random.default_rng(77)
+    L = 32768
+    S = r.standard_normal((8, 1, L)).astype(np.float32)
+    S[3, 0, 100:3000] += 6.0                         # a clustered block of high scores
+    S[5] = (r.integers(0, 300, size=L) * 0.5).astype(np.float32)   # heavy ties at the cut
+    kv_len = torch.tensor([L, L - 1, 20000, L, 2049, L, 31, L], dtype=torch.int32)
+    _topk_check(S, kv_len, 2048, "32K rows")
+    # several causal queries per sequence, the last seeing all 32768 positions
+    S2 = (r.integers(0, 4000, size=(2, 6, L)) * 0.25).astype(np.float32)
+    _topk_check(S2, torch.tensor([L, 9000], dtype=torch.int32), 2048, "32K causal rows")
+
+
 # Few rows of 64K-256K positions take the direct path: one workgroup per row
 # selects from the summary (the M largest keys of every 256-position wave
 # chunk, with their positions) and reads again only the chunks whose summary
