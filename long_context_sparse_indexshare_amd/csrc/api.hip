@@ -154,7 +154,8 @@ GroupLayout group_layout(const isa_group_args* a) {
     L.topk = off;
     L.topk_zero_bytes = 0;
     if (L.need_index) {
-        const isa::TopkLayout tl = isa::topk_layout((int)rows, a->L_cap, a->k);
+        const isa::TopkLayout tl = isa::topk_layout((int)rows, a->L_cap, a->k,
+                                                    isa::indexer_writes_summary(a->Tq, a->H_I));
         L.topk_zero_bytes = tl.zero_bytes;           // the counters come first
         off += round_up(tl.total);
     }
@@ -417,8 +418,9 @@ static isa_status launch_group(const isa_group_args* a, const isa::PageMap& pm,
     char* topk_ws = ws + L.topk;
     void* attend_ws = ws + L.attend;
     // with one query per sequence the indexer also writes the top-k summary
-    const isa::TopkLayout tl = isa::topk_layout(a->B * a->Tq, a->L_cap, a->k);
-    const bool fused_summary = L.need_index && !tl.select && isa::indexer_writes_summary(a->Tq, a->H_I);
+    const bool ix_summary = isa::indexer_writes_summary(a->Tq, a->H_I);
+    const isa::TopkLayout tl = isa::topk_layout(a->B * a->Tq, a->L_cap, a->k, ix_summary);
+    const bool fused_summary = L.need_index && !tl.select && ix_summary;
     const isa::SummaryOut summary =
         fused_summary ? isa::SummaryOut{reinterpret_cast<uint32_t*>(topk_ws + tl.summary),
                                         reinterpret_cast<uint8_t*>(topk_ws + tl.codes), tl.M}

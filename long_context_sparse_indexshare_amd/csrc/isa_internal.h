@@ -143,7 +143,9 @@ constexpr int TOPK_MAX_CHUNKS = (1 << 21) / TOPK_CHUNK;   // positions fit 21 bi
 // 1024c + 32w + 128q + j (q < 8, j < 32), position code 32q + j.  M is
 // chosen per call (topk_layout).
 constexpr int TOPK_WAVE_CHUNK = 256;
-constexpr int TOPK_MAX_M = 16;
+constexpr int TOPK_MAX_M = 16;              // filter path
+constexpr int TOPK_DIRECT_MAX_M = 32;       // direct path
+constexpr int TOPK_FEW_ROWS = 16;           // direct path: rows whose summary kernel is cheap
 constexpr int TOPK_MAX_SUMMARY = 8192;      // summary keys per row at most (8 per filter thread)
 // Entry slots per filter chunk: one per position, so a chunk's run always fits.
 constexpr int TOPK_SLOT_CAP = TOPK_CHUNK;
@@ -164,7 +166,8 @@ struct SummaryOut {
     uint8_t* codes;
     int M;
 };
-TopkLayout topk_layout(int rows, int L_cap, int k);
+// fused: the indexer's epilogue writes the summary (decode group calls)
+TopkLayout topk_layout(int rows, int L_cap, int k, bool fused = false);
 // true when the one-workgroup-per-row select kernel serves (rows, L_cap)
 bool topk_uses_select(int rows, int L_cap);
 

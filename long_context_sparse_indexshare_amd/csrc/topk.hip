@@ -851,7 +851,7 @@ __global__ __launch_bounds__(DIR_THREADS) void topk_direct_kernel(
 
     // the thread's summary entries (wave chunk blk, entries [8 sub, +8)) and
     // the chunk's M-th key, requested before the row's visible length arrives
-    const int tpb_log2 = M == 16 ? 1 : 0;               // M / 8 threads per chunk
+    const int tpb_log2 = M == 32 ? 2 : (M == 16 ? 1 : 0);   // M / 8 threads per chunk
     const int blk = tid >> tpb_log2;
     const int sub = tid & ((1 << tpb_log2) - 1);
     const bool has = blk < nw;
@@ -1473,7 +1473,7 @@ bool topk_uses_select(int rows, int L_cap) {
     return L_cap <= SEL_MAX_N && rows >= SEL_MIN_ROWS;
 }
 
-TopkLayout topk_layout(int rows, int L_cap, int k) {
+TopkLayout topk_layout(int rows, int L_cap, int k, bool fused) {
     TopkLayout L;
     L.rows = rows;
     L.nchunks = (L_cap + TOPK_CHUNK - 1) / TOPK_CHUNK;
@@ -1483,8 +1483,19 @@ TopkLayout topk_layout(int rows, int L_cap, int k) {
     // histograms; the direct kernel the summary (8 or 16 keys per wave chunk,
     // up to TOPK_MAX_SUMMARY per row, at least 2k); the filter/finish pair
     // the summary (about 2k keys per row), the run lengths and the entry slots
-    const int Md = L.nwchunks * 16 <= TOPK_MAX_SUMMARY ? 16 : 8;
-    L.direct = L_cap <= DIR_MAX_N && (long long)L.nwchunks * Md >= 2LL * k;
+    // direct path: Mmin, the smallest of 8, 16, 32 keys per wave chunk that
+    // gives the row at least 2k summary keys within TOPK_MAX_SUMMARY, or twice
+    // that (up to 32), with which few chunks saturate (a saturated chunk costs
+    // the direct kernel a second read and more passes).  Twice Mmin when the
+    // indexer's epilogue writes the summary or the rows are few; Mmin when a
+    // summary kernel over many rows pays for every key of M (its rounds are
+    // bound by VALU issue)
+    int Mmin = 0;
+    for (int m = 8; m <= TOPK_DIRECT_MAX_M && Mmin == 0; m *= 2)
+        if ((long long)L.nwchunks * m >= 2LL * k && L.nwchunks * m <= TOPK_MAX_SUMMARY) Mmin = m;
+    int Md = fused || rows <= TOPK_FEW_ROWS ? 2 * Mmin : Mmin;
+    while (Md > TOPK_DIRECT_MAX_M || L.nwchunks * Md > TOPK_MAX_SUMMARY) Md /= 2;
+    L.direct = Mmin != 0 && L_cap <= DIR_MAX_N;
     L.select = !L.direct && topk_uses_select(rows, L_cap);
     const bool sel = L.select;
     int M = (int)((2LL * k * TOPK_WAVE_CHUNK + L_cap - 1) / L_cap);
@@ -1522,7 +1533,7 @@ hipError_t launch_topk_select(const float* S, const int32_t* kv_len, int B, int 
                               int k, int32_t* idx, void* ws, bool counters_clear,
                               hipStream_t stream, bool summary_ready) {
     const int rows = B * Tq;
-    const TopkLayout L = topk_layout(rows, L_cap, k);
+    const TopkLayout L = topk_layout(rows, L_cap, k, summary_ready);
     char* base = static_cast<char*>(ws);
     if (L.select) {
         uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
