@@ -266,7 +266,9 @@ __global__ __launch_bounds__(IX_THREADS) void indexer_scores_kernel(
 constexpr int PF_QPWAVE = 2;
 constexpr int PF_QPW = 4 * PF_QPWAVE;     // queries per workgroup
 constexpr int PF_MIN_TQ = 2;              // from this many queries per sequence on
-constexpr int PF_TARGET_WGS = 1024;       // key splits aim at this many workgroups
+// key splits aim at this many workgroups: the ones that fit at once (two per
+// CU), so a few queries per sequence run in one round of long workgroups
+constexpr int PF_TARGET_WGS = 512;
 
 template <int D_I>
 __global__ __launch_bounds__(IX_THREADS, 2) void indexer_prefill_kernel(
