@@ -262,10 +262,13 @@ def _direct_case(name):
         S[5, 0, :] = np.linspace(-1e30, 1e30, L).astype(np.float32)[::-1]
         return S, [L - 333] * 6
     if name == "256K":
+        # 8 summary keys per chunk, 8 bitmap words per thread; the third row's
+        # heavy ties saturate every chunk (more candidates than the stage holds)
         L = 262144
-        S = r.standard_normal((2, 1, L)).astype(np.float32)
+        S = r.standard_normal((3, 1, L)).astype(np.float32)
         S[1, 0, 100000:101500] += 8.0
-        return S, [L, L - 1000]
+        S[2, 0, :] = (np.arange(L) % 3).astype(np.float32)
+        return S, [L, L - 1000, L - 77]
     if name == "64K":
         L = 65536
         S = (r.integers(0, 20000, size=(2, 1, L)) * 0.125).astype(np.float32)
