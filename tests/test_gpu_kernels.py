@@ -396,6 +396,41 @@ def test_attend_576_many_queries_ragged_k():
     _attend_case(B, Tq, 64, 576, 512, L_cap, k, idx, seed=17, name="576 wide ragged")
 
 
+def test_attend_576_many_queries_late_large_score():
+    # the per-query kernel fixes a head's softmax reference at its first tile;
+    # a later row that scores far above it (P about 2^95 times the first
+    # tile's largest, head 17 of query 5) makes the kernel run the query again
+    # with per-tile references.  Query 6 (the same head-17 query) has that row
+    # in its first tile.  The score comes from the row's RoPE columns (keys
+    # only), so the value columns, and the outputs, keep their usual size.
+    r = np.random.default_rng(21)
+    B, Tq, L_cap, k = 1, 256, 3000, 384
+    idx = _random_sets(B, Tq, L_cap, k, k, r)
+    g = torch.Generator().manual_seed(22)
+    Q = synth.normal_bf16((B, Tq, 64, 576), g, "cpu")
+    C = synth.normal_bf16((B, L_cap, 576), g, "cpu")
+    big = int(idx[0, 5, 300])                   # tile 9 of query 5
+    C[0, big, 512:] = (32.0 * Q[0, 5, 17, 512:].float()).to(torch.bfloat16)
+    Q[0, 6, 17] = Q[0, 5, 17]
+    idx[0, 6, 1:] = np.sort(r.choice(np.setdiff1d(np.arange(L_cap), [big]), size=k - 1,
+                                     replace=False))
+    idx[0, 6, 0] = big
+    idx_t = torch.from_numpy(idx.astype(np.int32))
+    scale = 1.0 / math.sqrt(576)
+    ref_out, ref_lse = oracle.sparse_mla_attend(Q, C, idx_t, 512, scale)
+    out, gout = guarded((B, Tq, 64, 512), torch.bfloat16)
+    lse, glse = guarded((B, Tq, 64), torch.float32)
+    isa.isa_sparse_mla_attend(dev(Q), dev(C), dev(idx_t), 512, scale, out=out, lse=lse)
+    gout.check("late large out")
+    glse.check("late large lse")
+    assert_attn_close(out, ref_out, "late large")
+    assert_lse_close(lse, ref_lse, "late large")
+    # head 17 of queries 5 and 6 is that row's value part
+    for t in (5, 6):
+        np.testing.assert_allclose(host(out)[0, t, 17].float().numpy(),
+                                   C[0, big, :512].float().numpy(), rtol=0, atol=1e-2)
+
+
 def test_attend_576_unsplit_two_groups():
     # 160 queries: the 32-head, two-group variant with enough workgroups that
     # the k slots are not split (each group writes its half of the columns)
