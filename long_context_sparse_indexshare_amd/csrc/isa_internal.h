@@ -100,10 +100,13 @@ __device__ __forceinline__ void wave_top_m(uint32_t (&k)[NV], uint32_t (&c)[NV],
         const uint64_t hit = __ballot(k[0] == m);
         const int winner = (int)__builtin_ctzll(hit);
         const uint32_t code = (uint32_t)__builtin_amdgcn_readlane((int)c[0], winner);
-        if (lane == r) {
-            mine = m;
-            mine_code = code;
-        }
+        // the r-th key and its code go straight into lane r (both are
+        // uniform; the lane select is M0, since one VALU instruction reads
+        // one SGPR here); the wait states cover the SGPRs just written by
+        // v_readlane and the M0 write
+        asm("s_nop 4\n\tv_writelane_b32 %0, %2, m0\n\tv_writelane_b32 %1, %3, m0"
+            : "+v"(mine), "+v"(mine_code)
+            : "s"(m), "s"(code), "{m0}"(r));
         if (lane == winner) {
 #pragma unroll
             for (int i = 0; i + 1 < NV; ++i) {
