@@ -107,7 +107,8 @@ __device__ __forceinline__ void wave_top_m(uint32_t (&k)[NV], uint32_t (&c)[NV],
         asm("s_nop 4\n\tv_writelane_b32 %0, %2, m0\n\tv_writelane_b32 %1, %3, m0"
             : "+v"(mine), "+v"(mine_code)
             : "s"(m), "s"(code), "{m0}"(r));
-        if (lane == winner) {
+        // the winner's lane mask straight from the scalar unit (no compare)
+        if (__builtin_amdgcn_inverse_ballot_w64(1ull << winner)) {
 #pragma unroll
             for (int i = 0; i + 1 < NV; ++i) {
                 k[i] = k[i + 1];
