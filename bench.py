@@ -287,7 +287,8 @@ def oracle_baseline(wl, inst, n_seq, torch, q_rows=None):
     return tokens, dt, results, core[0]
 
 
-# committed counter summaries: stage -> (summary file, kernel source it was taken on)
+# committed counter summaries: stage -> (summary file, kernel source it was taken on;
+# the digest covers that file followed by the header every kernel source includes)
 TRAFFIC = {
     "indexer": ("indexer_scores_C2_128K_traffic.txt", "indexer.hip"),
     "attend": ("sparse_attend_C2_128K_traffic.txt", "attend.hip"),
@@ -295,10 +296,17 @@ TRAFFIC = {
 }
 
 
+SHARED_HEADER = "isa_internal.h"
+
+
 def source_digest(path):
+    """sha256 of a kernel source followed by the shared internal header."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in (path, os.path.join(os.path.dirname(path), SHARED_HEADER)):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(stage):

@@ -62,11 +62,14 @@ def test_mtp_seven_step_roofline():
 
 
 def test_traffic_is_null_for_another_kernel_source(tmp_path, monkeypatch):
-    # a tree of its own: ROOT/profiles/<summary>, ROOT/<package>/csrc/attend.hip
+    # a tree of its own: ROOT/profiles/<summary>, ROOT/<package>/csrc/{attend.hip,
+    # the shared header}
     src = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "csrc", "attend.hip")
+    hdr = os.path.join(ROOT, "long_context_sparse_indexshare_amd", "csrc", bench.SHARED_HEADER)
     csrc = tmp_path / "long_context_sparse_indexshare_amd" / "csrc"
     csrc.mkdir(parents=True)
     (csrc / "attend.hip").write_bytes(open(src, "rb").read())
+    (csrc / bench.SHARED_HEADER).write_bytes(open(hdr, "rb").read())
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "good.txt").write_text("# comment: with a colon\ntraffic_bytes_per_launch: 1234\n"
@@ -78,3 +81,7 @@ def test_traffic_is_null_for_another_kernel_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC", {"attend": ("stale.txt", "attend.hip")})
     assert bench.measured_traffic("attend") is None
     assert bench.measured_traffic("topk") is None          # no summary for this stage
+    # a change to the shared header also makes the summary stale
+    monkeypatch.setattr(bench, "TRAFFIC", {"attend": ("good.txt", "attend.hip")})
+    (csrc / bench.SHARED_HEADER).write_bytes(open(hdr, "rb").read() + b"\n")
+    assert bench.measured_traffic("attend") is None
