@@ -431,6 +431,42 @@ def test_attend_576_many_queries_late_large_score():
                                    C[0, big, :512].float().numpy(), rtol=0, atol=1e-2)
 
 
+def test_attend_576_decode_late_large_score():
+    # the decode kernel moves a head's reference only when a row exceeds it by
+    # more than its slack; a row far above it in a group's second tile (slot
+    # 100 of the first split: tile 3, the second tile of group 1) makes the
+    # workgroup run its split again with exact references, and the merge then
+    # weights that split alone.  Sequence 1 has such a row in its first tile.
+    # The other heads of both queries get no RoPE part, so that row scores
+    # like any other for them (a row that dominates a head gives outputs of
+    # up to about 4, where the bf16 roundings of the split partial and of the
+    # output alone exceed the tolerance's absolute bound).
+    r = np.random.default_rng(23)
+    B, Tq, L_cap, k = 2, 1, 5000, 2048
+    idx = _random_sets(B, Tq, L_cap, k, k, r)
+    g = torch.Generator().manual_seed(24)
+    Q = synth.normal_bf16((B, Tq, 64, 576), g, "cpu")
+    C = synth.normal_bf16((B, L_cap, 576), g, "cpu")
+    bigs = (int(idx[0, 0, 100]), int(idx[1, 0, 0]))
+    for b, big in enumerate(bigs):
+        C[b, big, 512:] = (32.0 * Q[b, 0, 17, 512:].float()).to(torch.bfloat16)
+        Q[b, 0, :17, 512:] = 0
+        Q[b, 0, 18:, 512:] = 0
+    idx_t = torch.from_numpy(idx.astype(np.int32))
+    scale = 1.0 / math.sqrt(576)
+    ref_out, ref_lse = oracle.sparse_mla_attend(Q, C, idx_t, 512, scale)
+    out, gout = guarded((B, Tq, 64, 512), torch.bfloat16)
+    lse, glse = guarded((B, Tq, 64), torch.float32)
+    isa.isa_sparse_mla_attend(dev(Q), dev(C), dev(idx_t), 512, scale, out=out, lse=lse)
+    gout.check("decode late large out")
+    glse.check("decode late large lse")
+    assert_attn_close(out, ref_out, "decode late large")
+    assert_lse_close(lse, ref_lse, "decode late large")
+    for b, big in enumerate(bigs):
+        np.testing.assert_allclose(host(out)[b, 0, 17].float().numpy(),
+                                   C[b, big, :512].float().numpy(), rtol=0, atol=1e-2)
+
+
 def test_attend_576_unsplit_two_groups():
     # 160 queries: the 32-head, two-group variant with enough workgroups that
     # the k slots are not split (each group writes its half of the columns)
