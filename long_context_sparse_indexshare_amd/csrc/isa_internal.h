@@ -64,7 +64,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // unspecified.  Every lane first sorts its own (key, code) pairs (a small
 // sorting network), then each of the M rounds takes the wave maximum of the
 // lanes' heads and advances the head of the lowest lane holding it.  All 64
-// lanes must be active.
+// lanes must be active, and M <= 64 (the callers' M is at most 32).
 template <int NV>
 __device__ __forceinline__ void sort_keys_desc(uint32_t (&k)[NV], uint32_t (&c)[NV]) {
     auto cas = [&](int i, int j) {
