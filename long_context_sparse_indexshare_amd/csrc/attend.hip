@@ -761,8 +761,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
 // ---------------------------------------------------------------------------
 // Many queries (prefill): one workgroup of four waves per query, wave w
 // owning heads [16w, 16w + 16) whole.  Per tile of 32 gathered latent rows
-// (two LDS tile buffers, the next tile in flight in registers, one barrier
-// per tile):
+// (two LDS tile buffers; at the start of each tile the next one goes from
+// registers into the other buffer and the one after it is requested; one
+// barrier per tile):
 //   * S^T (32 rows x 16 heads) = C_rows . Q^T on v_mfma_f32_16x16x32_bf16
 //     over all D dims (the wave's Q^T stays in registers): two 16-row blocks,
 //     each summed in two accumulator chains;
@@ -956,6 +957,15 @@ __global__ __launch_bounds__(HW_THREADS, 1) void attend_heads_kernel(
         if (ntiles > 1) ISA_HW_LOAD(1)
         lds_barrier();
         for (int it = 0; it < ntiles; ++it) {
+            // tile it + 1 (in registers since the previous iteration) into the
+            // other buffer first, so its LDS writes overlap this tile's
+            // products, and tile it + 2 requested; the other buffer was last
+            // read in the previous iteration, which every wave finished before
+            // that iteration's barrier
+            if (it + 1 < ntiles) {
+                ISA_HW_STORE((it + 1) & 1)
+                if (it + 2 < ntiles) ISA_HW_LOAD(it + 2)
+            }
             const char* tb = &tiles[it & 1][0];
             // ---- S^T: rows j (block 0) and 16 + j (block 1), dims 32ks + 8g ..;
             // the A operands of k-step pair p + 2 are requested before the
@@ -1050,13 +1060,7 @@ __global__ __launch_bounds__(HW_THREADS, 1) void attend_heads_kernel(
                 o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pk, o[nb], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (it + 1 < ntiles) {
-                // the other buffer was last read in the previous iteration, which
-                // every wave finished before that iteration's barrier
-                ISA_HW_STORE((it + 1) & 1)
-                if (it + 2 < ntiles) ISA_HW_LOAD(it + 2)
-                lds_barrier();
-            }
+            if (it + 1 < ntiles) lds_barrier();   // tile it + 1 visible, tile it read
         }
     };
     pass(std::false_type{});
