@@ -476,6 +476,24 @@ def test_attend_576_unsplit_two_groups():
     _attend_case(2, 80, 64, 576, 512, 5000, 256, idx, seed=15, name="576 unsplit")
 
 
+@pytest.mark.parametrize("B,Tq,k", [(2, 20, 2048), (1, 64, 700), (1, 33, 2048)])
+def test_attend_576_split_sets_of_mixed_fill(B, Tq, k):
+    # tens of queries, the k slots split over workgroups and merged: full
+    # sets, short sets that leave later splits empty, empty sets, invalid
+    # slots and a ragged k
+    r = np.random.default_rng(B * 1000 + Tq)
+    L_cap = 9000
+    idx = np.full((B, Tq, k), -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(Tq):
+            m = [k, 77, 0, int(r.integers(1, k + 1))][(b * Tq + t) % 4]
+            idx[b, t, :m] = np.sort(r.choice(L_cap, size=m, replace=False))
+    idx[0, 1, 5] = -9
+    idx[0, 1, 6] = L_cap + 1
+    _attend_case(B, Tq, 64, 576, 512, L_cap, k, idx, seed=B + Tq + k,
+                 name=f"576 split mixed fill B{B} Tq{Tq} k{k}")
+
+
 def test_attend_160_16_heads():
     r = np.random.default_rng(7)
     idx = _random_sets(1, 50, 1024, 64, 64, r)
