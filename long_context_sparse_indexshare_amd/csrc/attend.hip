@@ -761,9 +761,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
 // ---------------------------------------------------------------------------
 // Many queries (prefill): one workgroup of four waves per query, wave w
 // owning heads [16w, 16w + 16) whole.  Per tile of 32 gathered latent rows
-// (two LDS tile buffers; at the start of each tile the next one goes from
-// registers into the other buffer and the one after it is requested; one
-// barrier per tile):
+// (two LDS tile buffers; during each tile's QK products the next tile goes
+// from registers into the other buffer, then the one after it is requested;
+// one barrier per tile):
 //   * S^T (32 rows x 16 heads) = C_rows . Q^T on v_mfma_f32_16x16x32_bf16
 //     over all D dims (the wave's Q^T stays in registers): two 16-row blocks,
 //     each summed in two accumulator chains;
@@ -957,15 +957,20 @@ __global__ __launch_bounds__(HW_THREADS, 1) void attend_heads_kernel(
         if (ntiles > 1) ISA_HW_LOAD(1)
         lds_barrier();
         for (int it = 0; it < ntiles; ++it) {
-            // tile it + 1 (in registers since the previous iteration) into the
-            // other buffer first, so its LDS writes overlap this tile's
-            // products, and tile it + 2 requested; the other buffer was last
-            // read in the previous iteration, which every wave finished before
-            // that iteration's barrier
-            if (it + 1 < ntiles) {
-                ISA_HW_STORE((it + 1) & 1)
-                if (it + 2 < ntiles) ISA_HW_LOAD(it + 2)
+            // tile it + 1 (in registers since the previous iteration) goes into
+            // the other buffer during this tile's QK products, so its LDS
+            // writes overlap them: a bf16 tile one 16-byte piece per k-step
+            // pair, an FP8 tile (dequantized here) before the products; then
+            // tile it + 2 is requested.  The other buffer was last read in the
+            // previous iteration, which every wave finished before that
+            // iteration's barrier
+            if constexpr (KV8) {
+                if (it + 1 < ntiles) {
+                    ISA_HW_STORE((it + 1) & 1)
+                    if (it + 2 < ntiles) ISA_HW_LOAD(it + 2)
+                }
             }
+            char* const lnext = &tiles[(it + 1) & 1][0] + lrow_off + gsub * 16;
             const char* tb = &tiles[it & 1][0];
             // ---- S^T: rows j (block 0) and 16 + j (block 1), dims 32ks + 8g ..;
             // the A operands of k-step pair p + 2 are requested before the
@@ -991,7 +996,15 @@ __global__ __launch_bounds__(HW_THREADS, 1) void attend_heads_kernel(
                 s10 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[1], qb[2 * p], s10, 0, 0, 0);
                 s01 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[2], qb[2 * p + 1], s01, 0, 0, 0);
                 s11 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c[3], qb[2 * p + 1], s11, 0, 0, 0);
+                if constexpr (!KV8) {
+                    static_assert(KV8 || GPT == KS / 2, "one tile piece per k-step pair");
+                    if (it + 1 < ntiles && (CH % TPR == 0 || gsub + TPR * p < CH))
+                        *reinterpret_cast<v4u*>(lnext + p * TPR * 16) = r[p];
+                }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (!KV8) {
+                if (it + 2 < ntiles) ISA_HW_LOAD(it + 2)
             }
             // the V^T operands of the first value blocks, requested while the
             // scores finish: lane (g, j) supplies row 4g + j/4 (and 16 + 4g +
