@@ -691,7 +691,7 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
 // of that layout (4 columns of one head), so its loads are contiguous across
 // threads.  Every split's partial is requested before any is used.
 constexpr int MERGE_THREADS = 256;
-template <int DV, int VS, int HB, int NB, int CW>
+template <int DV, int VS, int HB, int NB, int CW, int MS>
 __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml, int nq, int H,
     int n_hbg, int splits, int per_xcd, uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -721,23 +721,24 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(
     const float2* mb = part_ml + ((size_t)q * splits * VS + vh) * H;
     const size_t mstride = (size_t)VS * H;                   // float2 between splits
     // every load is issued before any is used, unconditionally: splits past
-    // the last one read the last one again and get weight 0 below
-    float2 ml[MAX_SPLITS];
-    v2u v[MAX_SPLITS];
+    // the last one (up to MS, the smallest of 2, 4, 8, 16 that holds them)
+    // read the last one again and get weight 0 below
+    float2 ml[MS];
+    v2u v[MS];
 #pragma unroll
-    for (int sj = 0; sj < MAX_SPLITS; ++sj) {
+    for (int sj = 0; sj < MS; ++sj) {
         const int sc = sj < splits ? sj : splits - 1;
         ml[sj] = mb[sc * mstride + head_c];
         v[sj] = pb[sc * pstride + threadIdx.x];
     }
     float M = -__builtin_inff();
 #pragma unroll
-    for (int sj = 0; sj < MAX_SPLITS; ++sj) M = fmaxf(M, ml[sj].x);
+    for (int sj = 0; sj < MS; ++sj) M = fmaxf(M, ml[sj].x);
     const float Mu = M == -__builtin_inff() ? 0.0f : M;
     float L = 0.0f;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int sj = 0; sj < MAX_SPLITS; ++sj) {
+    for (int sj = 0; sj < MS; ++sj) {
         // 0 for an empty split or one past the last; weights below 2^-126
         // (flushed by v_exp_f32) are far below the fp32 resolution of the
         // sum, whose largest term has weight 1
@@ -1139,9 +1140,19 @@ hipError_t launch_attend(const uint16_t* Q, KvSrc kv, const int32_t* idx, int B,
         const size_t threads = (size_t)nq * n_hbg * VS * 4 * Gm::NB * 4 * 64;
         const int mwg = (int)((threads + MERGE_THREADS - 1) / MERGE_THREADS);
         const int mper = (mwg + 7) / 8;
-        hipLaunchKernelGGL((merge_splits_kernel<DV, VS, HB, Gm::NB, Gm::CW>), dim3(8 * mper),
-                           dim3(MERGE_THREADS), 0, stream, part_o, part_ml, nq, H, n_hbg,
-                           plan.splits, mper, out, lse);
+        // the merge issues one load per split it may combine: as few as the
+        // call has
+        auto merge = [&](auto ms_tag) {
+            constexpr int MS = decltype(ms_tag)::value;
+            hipLaunchKernelGGL((merge_splits_kernel<DV, VS, HB, Gm::NB, Gm::CW, MS>),
+                               dim3(8 * mper), dim3(MERGE_THREADS), 0, stream, part_o, part_ml,
+                               nq, H, n_hbg, plan.splits, mper, out, lse);
+        };
+        static_assert(MAX_SPLITS == 16, "merge variants for up to 16 splits");
+        if (plan.splits <= 2) merge(std::integral_constant<int, 2>{});
+        else if (plan.splits <= 4) merge(std::integral_constant<int, 4>{});
+        else if (plan.splits <= 8) merge(std::integral_constant<int, 8>{});
+        else merge(std::integral_constant<int, 16>{});
     }
     return hipGetLastError();
 }
