@@ -460,7 +460,10 @@ __global__ __launch_bounds__(IX_THREADS, 2) void indexer_prefill_kernel(
         // Software pipeline over the 32-key blocks the wave's queries see
         // ([s_lo, s_end)): block i's products are issued with block i-1's
         // scores (two accumulator sets) while block i+1's keys are in flight
-        // (two key buffers); the blocks past them only get -inf.
+        // (two key buffers); the blocks past them only get -inf.  Scheduling
+        // barriers keep each block's key loads where they stand, ahead of the
+        // products (left to the scheduler, half of them sank to the end of
+        // the previous block and their latency showed).
         const int s_vis = pos_max >= s_lo ? ((pos_max - s_lo) / 32 + 1) * 32 + s_lo : s_lo;
         const int s_end = min(s_hi, s_vis);
         v4i kb0[KS], kb1[KS];
@@ -472,7 +475,9 @@ __global__ __launch_bounds__(IX_THREADS, 2) void indexer_prefill_kernel(
             products(kb0, acc0);
             for (int s0 = s_lo;; s0 += 64) {
                 // block s0 (acc0, issued) | block s0 + 32 (kb1) | block s0 + 64 (into kb0)
+                __builtin_amdgcn_sched_barrier(0);
                 load_keys(s0 + 64, kb0);
+                __builtin_amdgcn_sched_barrier(0);
                 if (s0 + 32 >= s_end) {
                     scores(acc0, sum);
                     store(s0, sum);
@@ -480,7 +485,9 @@ __global__ __launch_bounds__(IX_THREADS, 2) void indexer_prefill_kernel(
                 }
                 overlapped(kb1, acc1, acc0, sum);
                 store(s0, sum);
+                __builtin_amdgcn_sched_barrier(0);
                 load_keys(s0 + 96, kb1);
+                __builtin_amdgcn_sched_barrier(0);
                 if (s0 + 64 >= s_end) {
                     scores(acc1, sum);
                     store(s0 + 32, sum);
