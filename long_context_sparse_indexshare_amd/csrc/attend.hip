@@ -673,8 +673,10 @@ __global__ __launch_bounds__((AttendGeom<HB, VS, D, DV, GR>::THREADS),
                                     ((uint32_t)f2bf(o[nb][4 * r4 + 1] * inv) << 16);
                 const uint32_t hi = (uint32_t)f2bf(o[nb][4 * r4 + 2] * inv) |
                                     ((uint32_t)f2bf(o[nb][4 * r4 + 3] * inv) << 16);
-                // plain stores: the merge reads them on the same XCD, from L2
-                po[(nb * 4 + r4) * 64 + lane] = v2u{lo, hi};
+                // streaming stores: the merge fetches the partials back from
+                // beyond L2 whatever the store policy (its counted reads hold
+                // them whole), and non-temporal writes cost the layer less
+                __builtin_nontemporal_store(v2u{lo, hi}, &po[(nb * 4 + r4) * 64 + lane]);
             }
         }
         if (head_ok && grp == 0 && kp == 0 && g == 0)
