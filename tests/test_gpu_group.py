@@ -225,3 +225,41 @@ def test_groups_on_two_streams_use_separate_workspaces():
             assert torch.equal(ri, gi), f"rep {rep}: idx differs"
             for l in range(len(ro)):
                 assert torch.equal(ro[l], go[l]), f"rep {rep}: layer {l} differs"
+
+
+@pytest.mark.parametrize("name,wl,lens", [
+    # decode: an empty sequence, one visible position, exactly k, a long one
+    ("decode-mixed-lengths", synth.WORKLOADS["C2"].scaled(name="decode-mixed-lengths", B=4,
+                                                         kv_len=5000, L_cap=5120),
+     [0, 1, 2048, 5000]),
+    # several queries per sequence: empty, shorter than the query count (the
+    # first queries see nothing), dense within k, and past L_cap (clamped)
+    ("multi-query-mixed-lengths", synth.WORKLOADS["C3"].scaled(name="multi-query-mixed-lengths", B=4,
+                                                              Tq=16, kv_len=2990, L_cap=3000),
+     [0, 10, 1500, 3500]),
+])
+def test_group_degenerate_lengths(name, wl, lens):
+    """One group call over sequences of very different lengths (the edge cases
+    of the causal visibility rule) against the oracle, every output guarded."""
+    _print_case("group", name, lens)
+    inp = synth.group_inputs(wl)
+    inp["kv_len"] = torch.tensor(lens, dtype=torch.int32)
+    idx_ref, outs_ref, lses_ref = oracle.group_forward([inp["qI"]], [inp["w"]], [inp["kI"]],
+                                                       inp["kv_len"], inp["Q"], inp["C"], wl.k,
+                                                       wl.D_v, wl.sm_scale)
+    d = _to_dev(inp)
+    idx_g, g_idx = guarded((wl.B, wl.Tq, wl.k), torch.int32)
+    outs_g = [guarded((wl.B, wl.Tq, wl.H, wl.D_v), torch.bfloat16) for _ in range(wl.n_layers)]
+    lse_g = [guarded((wl.B, wl.Tq, wl.H), torch.float32) for _ in range(wl.n_layers)]
+    lse = [t for t, _ in lse_g]
+    idx, outs, _ = isa.isa_group_forward([d["qI"]], [d["w"]], [d["kI"]], d["kv_len"], d["Q"],
+                                         d["C"], wl.k, wl.D_v, wl.sm_scale, idx=idx_g,
+                                         out=[t for t, _ in outs_g], lse=lse)
+    torch.cuda.synchronize()
+    g_idx.check(f"{name} idx")
+    assert_idx_equal(idx, idx_ref, name)
+    for l in range(wl.n_layers):
+        outs_g[l][1].check(f"{name} out {l}")
+        lse_g[l][1].check(f"{name} lse {l}")
+        assert_attn_close(outs[l], outs_ref[l], f"{name} layer {l}")
+        assert_lse_close(lse[l], lses_ref[l], f"{name} layer {l}")
